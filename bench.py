@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Decode throughput of the batched single-token decode step on one MI355X.
+
+Default workload: the Llama-3-8B-shaped Q4 decoder (32 layers, hidden 4096,
+32 Q / 8 KV heads, head_dim 128, intermediate 14336, vocab 128256), M = 32
+sequences at positions drawn uniformly from [2048, 4096] over a synthetic
+fp32 KV context, greedy decoding with the whole step -- embedding gather, every
+layer, LM head, argmax, position advance -- replayed as one captured HIP graph.
+A step is one decode token for all 32 sequences; tok/s = M * steps / time.
+
+Also reported: the M = 1 line (Qwen2.5-0.5B-shaped Q8 decoder after a
+512-token teacher-forced context, 256 greedy steps), the HBM roofline of the
+dominant kernel (split-K flash decoding, timed alone with HIP events on the
+stream it runs on), and the CPU oracle's speed on a bounded sample.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-m1", action="store_true", help="skip the M=1 line")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fd-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def timed_greedy(dd, S, m, first_tok, start_pos, steps, warmup):
+    """Warm up (first call captures the graph), rewind, then time `steps`
+    graph replays.  Returns (seconds, final positions)."""
+    import quantized_gemv_flash_amd as rra
+    dev = "cuda"
+    x = torch.empty((m, S.hidden), device=dev)
+    pos = torch.empty(m, dtype=torch.int32, device=dev)
+    tok = torch.empty(m, dtype=torch.int32, device=dev)
+    logits = torch.empty((m, S.vocab), device=dev)
+    flags = rra.RRA_GRAPH | rra.RRA_STEP_GATHER | rra.RRA_STEP_ADVANCE
+    start_pos_t = torch.as_tensor(start_pos, dtype=torch.int32, device=dev)
+    first_t = torch.as_tensor(first_tok, dtype=torch.int32, device=dev)
+    pos.copy_(start_pos_t)
+    tok.copy_(first_t)
+    for _ in range(max(1, warmup)):
+        dd.model.rra_decode_step(x, pos, tok, m, flags=flags, logits=logits)
+    # rewind: the timed steps overwrite the cache rows the warm-up wrote
+    pos.copy_(start_pos_t)
+    tok.copy_(first_t)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        dd.model.rra_decode_step(x, pos, tok, m, flags=flags, logits=logits)
+    ev1.record()
+    torch.cuda.synchronize()
+    dd.model.rra_model_check()
+    return ev0.elapsed_time(ev1) / 1e3, pos.tolist(), tok.tolist()
+
+
+def build_decoder(S, m, max_len, seed=0):
+    import synth
+    from quantized_gemv_flash_amd.loader import load_decoder
+    W = synth.decoder_weights(S, seed=seed, device="cuda")
+    dd = load_decoder(S, W, m_max=m, max_len=max_len)
+    return W, dd
+
+
+def fill_kv_context(S, dd, lengths, seed=0):
+    import synth
+    for l in range(S.n_layers):
+        for s, L in enumerate(lengths):
+            k, v = synth.kv_context_rows(S, l, s, L, seed=seed, device="cuda")
+            dd.k_caches[l][s, :, :L] = k
+            dd.v_caches[l][s, :, :L] = v
+            del k, v
+
+
+def flash_decode_roofline(S, dd, lens, reps):
+    """Times rra_flash_decode (split-K chunk kernel + its reduce) alone on
+    layer 0's cache at the step's sequence lengths."""
+    import quantized_gemv_flash_amd as rra
+    m, nq, nkv, hd = len(lens), S.n_heads, S.n_kv_heads, S.head_dim
+    max_len = dd.k_caches[0].shape[2]
+    q = torch.randn((m, nq, hd), device="cuda")
+    out = torch.empty_like(q)
+    seq = torch.as_tensor(lens, dtype=torch.int32, device="cuda")
+    chunk = rra.rra_flash_decode_chunk(m, nkv, max_len, 0)
+    ws = torch.empty(rra.rra_flash_decode_workspace_bytes(m, nq, nkv, hd, max_len, 0),
+                     dtype=torch.uint8, device="cuda")
+    args = (q, dd.k_caches[0], dd.v_caches[0], seq, out, m, nq, nkv, hd, max_len, 0, ws)
+    rra.rra_flash_decode(*args)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        rra.rra_flash_decode(*args)
+    ev1.record()
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3 / reps
+    kv_bytes = sum(2 * nkv * L * hd * 4 for L in lens)  # K and V rows read once
+    return sec, kv_bytes, chunk
+
+
+def cpu_baseline(S, W, dd, lengths, first_tok, nseq):
+    """The oracle, as it stands, on one decode step of `nseq` sequences."""
+    import oracle
+    t_setup = time.time()
+    orc = oracle.DecoderOracle(S, W, nseq, max(lengths[:nseq]) + 1)
+    for l in range(S.n_layers):
+        for s in range(nseq):
+            L = lengths[s]
+            orc.set_context(l, s, dd.k_caches[l][s, :, :L], dd.v_caches[l][s, :, :L])
+    x = W.embed[torch.as_tensor(first_tok[:nseq], device="cuda")].cpu().numpy()
+    log(f"oracle setup {time.time() - t_setup:.1f}s")
+    t0 = time.time()
+    orc.step(x, lengths[:nseq])
+    sec = time.time() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return dict(value=nseq / sec, unit="tok/s", cores=threads, kind="oracle",
+                sample=f"one decode step of {nseq} sequences of the same workload "
+                       f"({sec:.2f} s; fp64, {threads} OpenMP threads)")
+
+
+def m1_line(steps_m1=256, ctx=512):
+    import synth
+    S = synth.QWEN25_05B_Q8
+    W, dd = build_decoder(S, 1, S.max_len)
+    ctx_tok = synth.context_tokens(S, 1, ctx).tolist()[0]
+    # teacher-forced context: one eager step per context token, run as graph
+    # replays of a plain (non-gather) step
+    import quantized_gemv_flash_amd as rra
+    x = torch.empty((1, S.hidden), device="cuda")
+    pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = torch.empty((1, S.vocab), device="cuda")
+    emb = W.embed
+    for p in range(ctx):
+        x.copy_(emb[ctx_tok[p]].unsqueeze(0))
+        pos.fill_(p)
+        dd.model.rra_decode_step(x, pos, tok, 1, flags=rra.RRA_GRAPH, logits=lg)
+    torch.cuda.synchronize()
+    first = synth.first_tokens(S, 1).tolist()
+    sec, _, _ = timed_greedy(dd, S, 1, first, [ctx], steps_m1, 3)
+    wbytes = dd.weight_bytes()
+    kv_read = sum(S.n_layers * 2 * S.n_kv_heads * (ctx + i + 1) * S.head_dim * 4
+                  for i in range(steps_m1)) / steps_m1
+    res = dict(workload=f"{S.name} M=1, {ctx}-token context then {steps_m1} greedy steps, one graph",
+               tok_s=steps_m1 / sec, ms_per_step=1e3 * sec / steps_m1,
+               weight_kv_gbs=(wbytes + kv_read) * steps_m1 / sec / 1e9)
+    res["hbm_frac"] = res["weight_kv_gbs"] / HBM_PEAK_GBS
+    del dd, W
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the decode "
+              "step is not sharded across GPUs", file=sys.stderr)
+        sys.exit(2)
+    import synth
+    import quantized_gemv_flash_amd as rra  # noqa: F401  (fails loudly if not built)
+
+    S = synth.LLAMA3_8B_Q4
+    m, steps = S.m, args.steps
+    max_len = max(S.max_len, 4096 + steps)
+    t0 = time.time()
+    W, dd = build_decoder(S, m, max_len)
+    lengths = synth.context_lengths(S, m)
+    fill_kv_context(S, dd, lengths)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s; weights {dd.weight_bytes() / 1e9:.3f} GB")
+    first = synth.first_tokens(S, m).tolist()
+    sec, final_pos, _ = timed_greedy(dd, S, m, first, lengths, steps, args.warmup)
+    tok_s = m * steps / sec
+    ms = 1e3 * sec / steps
+    gstats = dd.model.rra_graph_stats()
+    log(f"{tok_s:.1f} tok/s, {ms:.3f} ms/step, graph {gstats}")
+
+    wbytes = dd.weight_bytes()
+    # KV bytes per step: every cached row read (K and V), averaged over the steps
+    kv_read = sum(S.n_layers * 2 * S.n_kv_heads * (L + i + 1) * S.head_dim * 4
+                  for L in lengths for i in range(steps)) / steps
+    step_gbs = (wbytes + kv_read) / (sec / steps) / 1e9
+
+    fd_sec, fd_bytes, chunk = flash_decode_roofline(S, dd, [p for p in final_pos], args.fd_reps)
+    fd_gbs = fd_bytes / fd_sec / 1e9
+    log(f"flash decode: {fd_sec * 1e6:.1f} us, {fd_gbs:.0f} GB/s (chunk {chunk})")
+
+    m1 = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(S, W, dd, lengths, first, 4)
+        log(f"cpu baseline {cpu}")
+    del dd, W
+    torch.cuda.empty_cache()
+    if not args.no_m1:
+        m1 = m1_line()
+        log(f"m1 {m1}")
+
+    out = {
+        "metric": "decode tok/s at M=1 and M=32; weight+KV stream HBM GB/s as % of peak",
+        "value": tok_s,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{S.name}: M={m}, positions U[2048,4096] over a synthetic fp32 KV "
+                        f"context, {steps} greedy steps, one captured HIP graph per step",
+            "m": m, "weights": "q4 (32 x 4-bit + fp16 scale per block)", "kv_cache": "f32",
+            "max_len": max_len,
+        },
+        "per_sequence_tok_s": tok_s / m,
+        "weight_kv_gbs": step_gbs,
+        "weight_kv_hbm_frac": step_gbs / HBM_PEAK_GBS,
+        "roofline": {
+            "kernel": "rra_flash_decode (fd_chunk_kernel + fd_reduce_kernel), layer-0 cache, "
+                      f"M={m}, chunk {chunk}",
+            "bound": "hbm", "achieved": fd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": fd_gbs / HBM_PEAK_GBS, "traffic": None,
+            "avg_us": fd_sec * 1e6, "algorithmic_bytes": fd_bytes,
+        },
+        "m1": m1,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    if torch.cuda.is_available():
+        _stream = torch.cuda.Stream()  # graph capture needs a non-null stream
+        with torch.cuda.stream(_stream):
+            main()
+        _stream.synchronize()
+    else:
+        main()

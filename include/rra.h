@@ -1,0 +1,278 @@
+/*
+ * rra.h -- C ABI of librra, the MI355X (gfx950) batched single-token decode
+ * step: a weights-once dequantising batched GEMV, split-K flash-decoding
+ * attention over an fp32 KV cache with grouped KV heads, and the RMSNorm /
+ * RoPE / SwiGLU / residual / greedy-argmax steps around them, replayable as
+ * one HIP graph.
+ *
+ * Sources (docs.rs source pages), cited per entry point below:
+ *   [reduces]          realizar 0.8.5, src/cuda/executor/layers/reduces.rs
+ *   [batched_forward]  realizar 0.8.5, src/cuda/executor/layers/batched_forward.rs
+ *   [head_dim]         realizar 0.8.5, src/cuda/executor/head_dim.rs
+ *   [graph]            aprender-serve 0.70.2, src/gguf/cuda/forward_qwen35_cuda_graph.rs
+ *
+ * Conventions for every call:
+ *   - Pointers named as "device" are device (HBM) addresses owned by the
+ *     caller; the library never allocates or frees device memory.  Scratch
+ *     space is a caller-provided workspace whose size a *_workspace_bytes()
+ *     call returns.  Host pointers are named as such.
+ *   - Every call enqueues work only on the stream `s` it is given and returns
+ *     without waiting for it, unless stated otherwise ([reduces]: host-to-device
+ *     copies go on the launch stream so the legacy stream cannot reorder them).
+ *     `s` may be 0 (the null stream) except where stated.
+ *   - All activations are fp32, row-major, sequence-major: [M][...].
+ *   - On a non-RRA_OK return nothing was enqueued unless stated, no partial
+ *     outputs are promised, and rra_last_error() returns a message for the
+ *     calling thread.
+ *   - M (the number of sequences) is 1..32 ([batched_forward]
+ *     forward_batched_to_token_ids rejects batch sizes outside 1..32).
+ */
+#ifndef RRA_H
+#define RRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RRA_VERSION 1
+#define RRA_M_MAX 32
+
+typedef enum rra_status {
+    RRA_OK = 0,
+    RRA_EINVAL = 1,   /* an argument is out of range, null, or inconsistent */
+    RRA_ENOTINIT = 2, /* workspace too small, or model not created */
+    RRA_EHIP = 3,     /* a HIP runtime call failed; message has its text */
+    RRA_ECAPTURE = 4  /* graph capture failed and the eager fallback failed too */
+} rra_status;
+
+/* Weight formats.  Blocks are 32 consecutive elements along K of one row.
+ *   RRA_F32: fp32 weights.
+ *   RRA_Q8 : 32 int8 values q and one fp16 scale per block; w = scale * q.
+ *   RRA_Q4 : 32 unsigned 4-bit values q and one fp16 scale per block;
+ *            w = scale * (q - 8). */
+typedef enum rra_wfmt { RRA_F32 = 0, RRA_Q8 = 1, RRA_Q4 = 2 } rra_wfmt;
+
+/* Storage layouts.
+ *   RRA_PLANAR: F32 float[n][k]; Q8 data int8[n][k]; Q4 data uint8[n][k/2]
+ *     where byte j of a row holds element 2j in its low nibble and element
+ *     2j+1 in its high nibble; scales fp16 bit patterns [n][k/32].
+ *   RRA_TILED (Q8/Q4 only): the layout the GEMV streams.  Rows are grouped in
+ *     tiles of 16 and K in tiles of 128 (Q4) or 64 (Q8), one tile = 1 KiB of
+ *     quantised values followed by its scales (128 B for Q4, 64 B for Q8); the
+ *     scales live inside `data` and `scale` is NULL.  Rows are padded to a
+ *     multiple of 16 and K to a multiple of the K tile with zero-valued
+ *     blocks.  Produced by rra_repack_weight; rra_tiled_bytes gives its size. */
+typedef enum rra_wlayout { RRA_PLANAR = 0, RRA_TILED = 1 } rra_wlayout;
+
+/* A weight matrix W [n][k] (n outputs, k inputs); y = W x. */
+typedef struct rra_weight {
+    int32_t fmt;           /* rra_wfmt */
+    int32_t layout;        /* rra_wlayout; RRA_F32 must be RRA_PLANAR */
+    int64_t n, k;          /* k % 32 == 0 for Q8/Q4 */
+    const void *data;      /* device, see the layouts above */
+    const uint16_t *scale; /* device fp16 bits [n][k/32] (planar Q8/Q4), else NULL */
+} rra_weight;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *rra_last_error(void);
+/* Static name of a status code. */
+const char *rra_status_name(rra_status st);
+int32_t rra_version(void);
+
+/* ------------------------------------------------------------------ layout */
+
+/* Bytes of the RRA_TILED form of an [n][k] weight of format fmt (Q8/Q4);
+ * 0 for an invalid shape or format. */
+size_t rra_tiled_bytes(int32_t fmt, int64_t n, int64_t k);
+
+/* Converts a planar Q8/Q4 weight into the tiled layout at `tiled` (device,
+ * tiled_bytes >= rra_tiled_bytes) and fills *out (host) with its descriptor.
+ * Bit-exact: no value is changed, only moved.  EINVAL on F32, on a non-planar
+ * input, on k % 32 != 0 or on a short buffer. */
+rra_status rra_repack_weight(const rra_weight *planar, void *tiled, size_t tiled_bytes,
+                             rra_weight *out, hipStream_t s);
+
+/* Inverse of rra_repack_weight: writes the planar data (device, Q8 int8[n][k]
+ * or Q4 uint8[n][k/2]) and scales (device fp16 bits [n][k/32]). */
+rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uint16_t *scale,
+                             hipStream_t s);
+
+/* -------------------------------------------------------- batched GEMV (a3)
+ * [batched_forward] forward_batched_to_token_ids: batched GEMV kernels read
+ * and dequantise every weight block once for all M inputs.
+ *   y[i][r] = sum_c W[r][c] * x[i][c]   for i < m, r < n.
+ * w   : F32 planar, or Q8/Q4 tiled (planar Q8/Q4 -> EINVAL, repack first).
+ * x   : device fp32 [m][k]; |x| must stay below 65504 for Q8/Q4 (the
+ *       activations enter the matrix cores as an fp16 high part plus an fp16
+ *       low part).
+ * y   : device fp32 [m][n]; must not overlap x.
+ * ws  : device scratch for split-K partial sums, or NULL (then K is not split);
+ *       when non-NULL ws_bytes must be >= rra_batched_gemv_workspace_bytes.
+ * Results do not depend on the stream, the call or the run (no atomics). */
+size_t rra_batched_gemv_workspace_bytes(const rra_weight *w, int32_t m);
+rra_status rra_batched_gemv(const rra_weight *w, const float *x, float *y, int32_t m,
+                            void *ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------- KV scatter (a5)
+ * [head_dim] flash_decoding_attention_into, step 1: this token's K and V rows
+ * are written into the caches at the sequence's position.
+ *   k_cache[i][g][pos[i]][d] = k_rows[i][g*hd + d], same for V,
+ *   for i < m, g < nkv, d < hd.
+ * k_rows, v_rows : device fp32 [m][nkv*hd].
+ * k_cache, v_cache : device fp32 [>= m][nkv][max_len][hd].
+ * pos : device uint32 [m] (read on the device, so the call is graph-safe).
+ * A sequence with pos[i] >= max_len is not written (no out-of-bounds store).
+ * Pure copy: bit-exact. */
+rra_status rra_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
+                          float *v_cache, const uint32_t *pos, int32_t m, int32_t nkv,
+                          int32_t hd, int32_t max_len, hipStream_t s);
+
+/* ------------------------------------------------ flash decoding (a6, a7)
+ * [head_dim] flash_decoding_attention_into: the cache is split into chunks
+ * processed in parallel, then the partial results are combined with softmax
+ * rescaling; Q has num_heads heads, K/V num_kv_heads.
+ *   out[i][h] = sum_{t < seq_len[i]} softmax_t(<q[i][h], K[i][g][t]> / sqrt(hd))
+ *               * V[i][g][t],   g = h / (nq / nkv).
+ * q   : device fp32 [m][nq][hd];  out : device fp32 [m][nq][hd].
+ * k_cache, v_cache : device fp32 [>= m][nkv][max_len][hd].
+ * seq_len : device uint32 [m]; values are clamped to max_len; a sequence with
+ *       seq_len 0 leaves its out rows untouched.
+ * hd in {64, 128}; nq % nkv == 0; nq / nkv <= 8.
+ * chunk : rows per split, a multiple of 32 in [32, 1024], or 0 to let the
+ *       library choose from (m, nkv, max_len).
+ * ws  : device scratch, ws_bytes >= rra_flash_decode_workspace_bytes(...) with
+ *       the same chunk argument. */
+size_t rra_flash_decode_workspace_bytes(int32_t m, int32_t nq, int32_t nkv, int32_t hd,
+                                        int32_t max_len, int32_t chunk);
+int32_t rra_flash_decode_chunk(int32_t m, int32_t nkv, int32_t max_len, int32_t chunk);
+rra_status rra_flash_decode(const float *q, const float *k_cache, const float *v_cache,
+                            const uint32_t *seq_len, float *out, int32_t m, int32_t nq,
+                            int32_t nkv, int32_t hd, int32_t max_len, int32_t chunk,
+                            void *ws, size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------- step kernels
+ * Exposed for per-step parity checks; rra_decode_step uses fused forms. */
+
+/* RMSNorm (a2, a9, a12; [batched_forward] batched_output_norm_lm_head_argmax:
+ * one launch for all M rows): out[i] = x[i] / sqrt(mean(x[i]^2) + eps) * gamma.
+ * x, out: device fp32 [m][h] (may alias); gamma: device fp32 [h]. */
+rra_status rra_rmsnorm(const float *x, const float *gamma, float *out, int32_t m, int32_t h,
+                       float eps, hipStream_t s);
+
+/* RoPE table for rra_rope: device fp32 [max_len][hd/2][2] holding (cos, sin)
+ * of pos * theta^(-2i/hd), computed in fp64 on the host and rounded once.
+ * Synchronous: returns after the copy has completed. */
+rra_status rra_rope_table(float *table, int32_t max_len, int32_t hd, double theta,
+                          hipStream_t s);
+
+/* RoPE (a4; [graph] module doc: the position is read from device memory):
+ * rotates every head of z in place by pos[i]: for each pair (j, j + hd/2),
+ * (a, b) -> (a cos - b sin, a sin + b cos).  z: device fp32 [m][n_heads][hd];
+ * pos: device uint32 [m]; a sequence with pos >= max_len is left unchanged. */
+rra_status rra_rope(float *z, const uint32_t *pos, const float *table, int32_t m,
+                    int32_t n_heads, int32_t hd, int32_t max_len, hipStream_t s);
+
+/* SwiGLU (a10; [graph] module doc names the fused SwiGLU):
+ * out[i][j] = silu(gate[i][j]) * up[i][j], silu(z) = z / (1 + e^-z).
+ * All device fp32 [m][n]; out may alias gate or up. */
+rra_status rra_swiglu(const float *gate, const float *up, float *out, int32_t m, int32_t n,
+                      hipStream_t s);
+
+/* Greedy argmax (a14; [reduces] gpu_argmax / batched_gpu_argmax: block-level
+ * (max, index) pairs, then a final reduce, for all M rows with no host sync):
+ * tok[i] = the lowest index among the maximal logits[i][*].  NaN logits are
+ * never selected.  logits: device fp32 [m][v]; tok: device uint32 [m]. */
+size_t rra_argmax_workspace_bytes(int32_t m, int32_t v);
+rra_status rra_argmax(const float *logits, uint32_t *tok, int32_t m, int32_t v, void *ws,
+                      size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------- decode step (a1-a15)
+ * [batched_forward] forward_batched_to_token_ids: M embeddings and M positions
+ * in, every layer, then output norm -> LM head -> argmax, M token ids out.
+ * Layer body (a Llama pre-norm block):
+ *   u = rmsnorm(x, attn_gamma); [q k v] = Wqkv u; rope(q, k); scatter k, v
+ *   at pos; a = attention(q, cache, pos + 1); x += Wo a;
+ *   u = rmsnorm(x, ffn_gamma); x += Wd (silu(Wg u) * Wu u).
+ * Tail: logits = W_lm rmsnorm(x, out_gamma); tok = argmax(logits). */
+typedef struct rra_layer_desc {
+    rra_weight wqkv;          /* [(nq + 2 nkv) hd][hidden]: q rows, k rows, v rows */
+    rra_weight wo;            /* [hidden][nq hd] */
+    rra_weight wgu;           /* [2 inter][hidden]: gate rows, then up rows */
+    rra_weight wd;            /* [hidden][inter] */
+    const float *attn_gamma;  /* device [hidden] */
+    const float *ffn_gamma;   /* device [hidden] */
+    float *k_cache;           /* device [m_max][nkv][max_len][hd] */
+    float *v_cache;           /* device [m_max][nkv][max_len][hd] */
+} rra_layer_desc;
+
+typedef struct rra_model_desc {
+    int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab;
+    float rms_eps;
+    double rope_theta;
+    int32_t max_len;               /* cache rows per sequence */
+    int32_t m_max;                 /* cache slots; every step has m <= m_max <= 32 */
+    const rra_layer_desc *layers;  /* host array [n_layers], copied at create */
+    const float *out_gamma;        /* device [hidden] */
+    rra_weight lm_head;            /* [vocab][hidden] */
+    const float *embed;            /* device [vocab][hidden] fp32, or NULL (needed for RRA_STEP_GATHER) */
+    int32_t attn_chunk;            /* flash-decode rows per split, 0 = library choice */
+} rra_model_desc;
+
+typedef struct rra_model rra_model;
+
+/* Step flags. */
+#define RRA_GRAPH 1        /* run as a captured HIP graph (captured on the first
+                              call for a given (m, flags, pointers) key, replayed
+                              after; [graph] module doc, [batched_forward]
+                              forward_batched_to_token_ids_graphed) */
+#define RRA_STEP_GATHER 2  /* x[i] = embed[tok[i]] first (tok read as input) */
+#define RRA_STEP_ADVANCE 4 /* pos[i] += 1 after the step */
+
+size_t rra_model_workspace_bytes(const rra_model_desc *d);
+
+/* Validates d, lays the workspace out (device, ws_bytes >=
+ * rra_model_workspace_bytes(d)), fills its RoPE table on stream s (and waits
+ * for it), and returns a host handle in *out.  Weights, caches and gammas are
+ * referenced, not copied: they must outlive the model. */
+rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t ws_bytes, hipStream_t s,
+                            rra_model **out);
+
+/* One decode step for sequences 0..m-1.
+ * x      : device fp32 [m][hidden], in/out: the step input (embedding rows)
+ *          and, on return, the final residual stream (before the output norm).
+ * pos    : device uint32 [m], this token's position per sequence; the K/V rows
+ *          are written there and attention covers rows [0, pos]; a position
+ *          >= max_len writes nothing, and is reported by rra_model_check.
+ * tok    : device uint32 [m], out (and in under RRA_STEP_GATHER).
+ * tok_host : host uint32 [m] or NULL.  When non-NULL the call waits for the
+ *          stream and copies the ids there (the one sync of the step).
+ * logits : device fp32 [m][vocab] or NULL (then an internal buffer is used).
+ * flags  : RRA_GRAPH | RRA_STEP_GATHER | RRA_STEP_ADVANCE.  RRA_GRAPH needs a
+ *          non-null stream.  If capture fails the step runs eagerly.
+ * Writes k_cache/v_cache[l][i][*][pos[i]] for every layer. */
+rra_status rra_decode_step(rra_model *mdl, float *x, uint32_t *pos, uint32_t *tok,
+                           uint32_t *tok_host, float *logits, int32_t m, int32_t flags,
+                           hipStream_t s);
+
+/* Waits for stream s and reports (and clears) a device-side error: RRA_EINVAL
+ * if a step saw a position >= max_len since the last check. */
+rra_status rra_model_check(rra_model *mdl, hipStream_t s);
+
+/* Graph counters ([graph] decode_graph_replays: the evidence that decode ran
+ * through the graph): captures made, replays launched, and kernel nodes in the
+ * most recent graph.  Any pointer may be NULL. */
+rra_status rra_graph_stats(const rra_model *mdl, uint64_t *captures, uint64_t *replays,
+                           uint32_t *kernels);
+
+/* Releases the host handle and its graphs (not the caller's memory). */
+void rra_model_destroy(rra_model *mdl);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RRA_H */

@@ -57,17 +57,20 @@ void orc_dequant_row(int fmt, const void *data, const uint16_t *scale, int64_t k
         for (int64_t i = 0; i < k; ++i) out[i] = (double)w[i];
     } else if (fmt == ORC_Q8) {
         const int8_t *q = (const int8_t *)data + row * k;
-        for (int64_t i = 0; i < k; ++i) {
-            double s = orc_f16_to_f64(scale[row * nb + i / ORC_QBLOCK]);
-            out[i] = s * (double)q[i];
+        for (int64_t b = 0; b < nb; ++b) {
+            double s = orc_f16_to_f64(scale[row * nb + b]);
+            for (int64_t i = b * ORC_QBLOCK; i < (b + 1) * ORC_QBLOCK; ++i)
+                out[i] = s * (double)q[i];
         }
     } else {
         const uint8_t *q = (const uint8_t *)data + row * (k / 2);
-        for (int64_t i = 0; i < k; ++i) {
-            double s = orc_f16_to_f64(scale[row * nb + i / ORC_QBLOCK]);
-            uint8_t byte = q[i / 2];
-            int nib = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
-            out[i] = s * (double)(nib - 8);
+        for (int64_t b = 0; b < nb; ++b) {
+            double s = orc_f16_to_f64(scale[row * nb + b]);
+            for (int64_t i = b * ORC_QBLOCK; i < (b + 1) * ORC_QBLOCK; ++i) {
+                uint8_t byte = q[i / 2];
+                int nib = (i % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+                out[i] = s * (double)(nib - 8);
+            }
         }
     }
 }

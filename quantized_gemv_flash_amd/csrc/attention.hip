@@ -1,0 +1,370 @@
+// attention.hip -- KV-cache scatter and split-K flash-decoding attention.
+//
+// [head_dim] flash_decoding_attention_into: the new K/V row is written into
+// the cache at the sequence's position; the cached rows are split into chunks
+// processed in parallel, each giving a partial softmax result, and a second
+// pass combines the partials with softmax (log-sum-exp) rescaling.  Q has nq
+// heads; K/V have nkv heads, query head h reading KV head h / (nq / nkv).
+//
+// MI355X design.  One 256-thread workgroup per (chunk, KV head, sequence)
+// serves all G = nq/nkv query heads of its KV head, so every cached K/V byte
+// is read from HBM exactly once per step (the pages' kernel runs one 32-lane
+// group per *query* head).  Scores: 8 lanes per cached row, each lane a 128-bit
+// load per 32 columns, dot products for the G heads, 3-step butterfly.  The G
+// score rows of the chunk live in LDS; one wave per head forms max / exp /
+// sum; values: hd/4 lanes per row with 128-bit loads, G accumulators per lane,
+// then a cross-wave sum in LDS.  The grid covers max_len / chunk chunks and a
+// workgroup past seq_len returns at once, so a captured graph stays valid as
+// positions advance.
+#include "rra_internal.h"
+
+#include <algorithm>
+
+namespace rra {
+namespace {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict__ k_rows,
+                                                         const float *__restrict__ v_rows,
+                                                         float *__restrict__ kc,
+                                                         float *__restrict__ vc,
+                                                         const uint32_t *__restrict__ pos, int nkv,
+                                                         int hd, int max_len) {
+    const int m = blockIdx.x;
+    const uint32_t p = pos[m];
+    if (p >= (uint32_t)max_len) return;
+    const int row = nkv * hd;
+    for (int idx = threadIdx.x; idx < row; idx += blockDim.x) {
+        const int g = idx / hd, d = idx - g * hd;
+        const size_t dst = (((size_t)m * nkv + g) * max_len + p) * hd + d;
+        kc[dst] = k_rows[(size_t)m * row + idx];
+        vc[dst] = v_rows[(size_t)m * row + idx];
+    }
+}
+
+// Partial result of chunk c for query head h of sequence m:
+//   part_o[((m*nq + h)*nc_max + c)*HD + d] = sum_t p_t v_t[d] / l,
+//   part_lse[(m*nq + h)*nc_max + c]      = max_t s_t + ln l,
+// with s_t = <q_h, k_t>/sqrt(HD), p_t = e^(s_t - max), l = sum_t p_t.
+template <int HD, int G>
+__global__ __launch_bounds__(256) void fd_chunk_kernel(
+    const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
+    const uint32_t *__restrict__ seq_len, float *__restrict__ part_o,
+    float *__restrict__ part_lse, int nq, int nkv, int max_len, int chunk, int nc_max) {
+    const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
+    const int L = (int)min(seq_len[m], (uint32_t)max_len);
+    const int t0 = c * chunk;
+    if (t0 >= L) return;
+    const int n = min(chunk, L - t0);
+
+    extern __shared__ float smem[];
+    float *sc = smem;                 // [G][chunk] scores, then probabilities
+    float *red = smem + G * chunk;    // [4 waves][G][HD]
+    float *stat = red + 4 * G * HD;   // [G] max, [G] sum
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t row0 = ((size_t)m * nkv + g) * max_len + t0;
+    const float *K = kc + row0 * HD;
+    const float *V = vc + row0 * HD;
+
+    // ---- scores
+    constexpr int F4 = HD / 32;  // 128-bit loads per lane per row
+    const int e = lane & 7, ks = lane >> 3;
+    const float qscale = 1.0f / sqrtf((float)HD);
+    float4 qr[G][F4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float *qh = q + ((size_t)m * nq + g * G + h) * HD;
+#pragma unroll
+        for (int i = 0; i < F4; ++i) {
+            float4 v = *reinterpret_cast<const float4 *>(qh + 4 * (e + 8 * i));
+            qr[h][i] = make_float4(v.x * qscale, v.y * qscale, v.z * qscale, v.w * qscale);
+        }
+    }
+    for (int base = 0; base < n; base += 64) {
+        float4 kv[2][F4];
+        int tt[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            tt[u] = base + u * 32 + wave * 8 + ks;
+            if (tt[u] < n) {
+#pragma unroll
+                for (int i = 0; i < F4; ++i)
+                    kv[u][i] = *reinterpret_cast<const float4 *>(K + (size_t)tt[u] * HD +
+                                                                 4 * (e + 8 * i));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float s[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float a = 0.f;
+                if (tt[u] < n) {
+#pragma unroll
+                    for (int i = 0; i < F4; ++i) {
+                        a = fmaf(qr[h][i].x, kv[u][i].x, a);
+                        a = fmaf(qr[h][i].y, kv[u][i].y, a);
+                        a = fmaf(qr[h][i].z, kv[u][i].z, a);
+                        a = fmaf(qr[h][i].w, kv[u][i].w, a);
+                    }
+                }
+                a += __shfl_xor(a, 1, 64);
+                a += __shfl_xor(a, 2, 64);
+                a += __shfl_xor(a, 4, 64);
+                s[h] = a;
+            }
+            if (tt[u] < n) {
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    if (e == (h & 7)) sc[h * chunk + tt[u]] = s[h];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- per-head max, exponentials, sum
+    for (int h = wave; h < G; h += 4) {
+        float mx = -INFINITY;
+        for (int t = lane; t < n; t += 64) mx = fmaxf(mx, sc[h * chunk + t]);
+        mx = wave_max(mx);
+        float l = 0.f;
+        for (int t = lane; t < n; t += 64) {
+            const float p = expf(sc[h * chunk + t] - mx);
+            sc[h * chunk + t] = p;
+            l += p;
+        }
+        l = wave_sum(l);
+        if (lane == 0) {
+            stat[h] = mx;
+            stat[G + h] = l;
+        }
+    }
+    __syncthreads();
+
+    // ---- probability-weighted values
+    constexpr int LPK = HD / 4, KPW = 64 / LPK;
+    const int d4 = lane % LPK, kslot = lane / LPK;
+    float4 o[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) o[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t = wave * KPW + kslot; t < n; t += 4 * KPW * 2) {
+        const int t2 = t + 4 * KPW;
+        const float4 v0 = *reinterpret_cast<const float4 *>(V + (size_t)t * HD + 4 * d4);
+        float4 v1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t2 < n) v1 = *reinterpret_cast<const float4 *>(V + (size_t)t2 * HD + 4 * d4);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p0 = sc[h * chunk + t];
+            o[h].x = fmaf(p0, v0.x, o[h].x);
+            o[h].y = fmaf(p0, v0.y, o[h].y);
+            o[h].z = fmaf(p0, v0.z, o[h].z);
+            o[h].w = fmaf(p0, v0.w, o[h].w);
+            if (t2 < n) {
+                const float p1 = sc[h * chunk + t2];
+                o[h].x = fmaf(p1, v1.x, o[h].x);
+                o[h].y = fmaf(p1, v1.y, o[h].y);
+                o[h].z = fmaf(p1, v1.z, o[h].z);
+                o[h].w = fmaf(p1, v1.w, o[h].w);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            o[h].x += __shfl_xor(o[h].x, off, 64);
+            o[h].y += __shfl_xor(o[h].y, off, 64);
+            o[h].z += __shfl_xor(o[h].z, off, 64);
+            o[h].w += __shfl_xor(o[h].w, off, 64);
+        }
+    }
+    if (kslot == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+            *reinterpret_cast<float4 *>(red + (wave * G + h) * HD + 4 * d4) = o[h];
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < G * HD; idx += blockDim.x) {
+        const int h = idx / HD, d = idx - h * HD;
+        const float v = red[(0 * G + h) * HD + d] + red[(1 * G + h) * HD + d] +
+                        red[(2 * G + h) * HD + d] + red[(3 * G + h) * HD + d];
+        part_o[(((size_t)m * nq + g * G + h) * nc_max + c) * HD + d] = v / stat[G + h];
+    }
+    if (tid < G)
+        part_lse[((size_t)m * nq + g * G + tid) * nc_max + c] = stat[tid] + logf(stat[G + tid]);
+}
+
+// out[m][h] = sum_c w_c o~_c / sum_c w_c, w_c = e^(lse_c - max lse), over the
+// chunks that hold rows of the sequence.  One wave per (head, sequence).
+template <int HD>
+__global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__ part_o,
+                                                       const float *__restrict__ part_lse,
+                                                       const uint32_t *__restrict__ seq_len,
+                                                       float *__restrict__ out, int nq, int max_len,
+                                                       int chunk, int nc_max) {
+    const int h = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
+    const int L = (int)min(seq_len[m], (uint32_t)max_len);
+    if (L <= 0) return;
+    const int nc = (L + chunk - 1) / chunk;
+    const float *lse = part_lse + ((size_t)m * nq + h) * nc_max;
+    float mx = -INFINITY;
+    for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
+    mx = wave_max(mx);
+    constexpr int PER = HD / 64;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    float wsum = 0.f;
+    const float *po = part_o + ((size_t)m * nq + h) * nc_max * HD;
+    for (int c = 0; c < nc; ++c) {
+        const float w = expf(lse[c] - mx);
+        wsum += w;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, po[(size_t)c * HD + lane + 64 * j], acc[j]);
+    }
+    float *o = out + ((size_t)m * nq + h) * HD;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) o[lane + 64 * j] = acc[j] / wsum;
+}
+
+template <int HD, int G>
+rra_status launch_chunk(const float *q, const float *kc, const float *vc, const uint32_t *lens,
+                        float *po, float *pl, int m, int nq, int nkv, int max_len, int chunk,
+                        int nc_max, hipStream_t s) {
+    const size_t shm = sizeof(float) * ((size_t)G * chunk + 4 * G * HD + 2 * G);
+    hipLaunchKernelGGL((fd_chunk_kernel<HD, G>), dim3(nc_max, nkv, m), dim3(256), shm, s, q, kc,
+                       vc, lens, po, pl, nq, nkv, max_len, chunk, nc_max);
+    return check_launch("fd_chunk_kernel");
+}
+
+template <int HD>
+rra_status launch_chunk_hd(int G, const float *q, const float *kc, const float *vc,
+                           const uint32_t *lens, float *po, float *pl, int m, int nq, int nkv,
+                           int max_len, int chunk, int nc_max, hipStream_t s) {
+    switch (G) {
+#define RRA_G(gv) \
+    case gv: return launch_chunk<HD, gv>(q, kc, vc, lens, po, pl, m, nq, nkv, max_len, chunk, nc_max, s);
+        RRA_G(1) RRA_G(2) RRA_G(3) RRA_G(4) RRA_G(5) RRA_G(6) RRA_G(7) RRA_G(8)
+#undef RRA_G
+        default: return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", G);
+    }
+}
+
+}  // namespace
+
+int fd_choose_chunk(int m, int nkv, int max_len, int chunk) {
+    if (chunk > 0) return chunk;
+    // About 4096 workgroups over the full cache span (16 per compute unit).
+    int64_t want = (int64_t)m * nkv * max_len / 4096;
+    int c = 32;
+    while (c * 2 <= want && c < 512) c *= 2;
+    return c;
+}
+
+size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk) {
+    const int nc_max = (int)cdiv(max_len, chunk);
+    return (size_t)m * nq * nc_max * (size_t)(hd + 1);
+}
+
+rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
+                             float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
+                             int max_len, hipStream_t s) {
+    hipLaunchKernelGGL(kv_scatter_kernel, dim3(m), dim3(256), 0, s, k_rows, v_rows, k_cache,
+                       v_cache, pos, nkv, hd, max_len);
+    return check_launch("kv_scatter_kernel");
+}
+
+rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
+                               const uint32_t *seq_len, float *out, int m, int nq, int nkv,
+                               int hd, int max_len, int chunk, float *part, hipStream_t s) {
+    const int G = nq / nkv;
+    const int nc_max = (int)cdiv(max_len, chunk);
+    float *po = part;
+    float *pl = part + (size_t)m * nq * nc_max * hd;
+    if (hd == 128)
+        RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, po, pl, m, nq, nkv, max_len,
+                                     chunk, nc_max, s));
+    else
+        RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, po, pl, m, nq, nkv, max_len,
+                                    chunk, nc_max, s));
+    if (hd == 128)
+        hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,
+                           out, nq, max_len, chunk, nc_max);
+    else
+        hipLaunchKernelGGL(fd_reduce_kernel<64>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len, out,
+                           nq, max_len, chunk, nc_max);
+    return check_launch("fd_reduce_kernel");
+}
+
+}  // namespace rra
+
+using namespace rra;
+
+extern "C" rra_status rra_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
+                                     float *v_cache, const uint32_t *pos, int32_t m, int32_t nkv,
+                                     int32_t hd, int32_t max_len, hipStream_t s) {
+    clear_error();
+    if (!k_rows || !v_rows || !k_cache || !v_cache || !pos)
+        return fail(RRA_EINVAL, "rra_kv_scatter: null argument");
+    if (m < 1 || m > RRA_M_MAX) return fail(RRA_EINVAL, "rra_kv_scatter: m=%d not in 1..32", m);
+    if (nkv < 1 || hd < 1 || max_len < 1)
+        return fail(RRA_EINVAL, "rra_kv_scatter: nkv=%d hd=%d max_len=%d", nkv, hd, max_len);
+    return launch_kv_scatter(k_rows, v_rows, k_cache, v_cache, pos, m, nkv, hd, max_len, s);
+}
+
+static rra_status fd_validate(int32_t m, int32_t nq, int32_t nkv, int32_t hd, int32_t max_len,
+                              int32_t chunk) {
+    if (m < 1 || m > RRA_M_MAX) return fail(RRA_EINVAL, "flash decode: m=%d not in 1..32", m);
+    if (hd != 64 && hd != 128) return fail(RRA_EINVAL, "flash decode: hd=%d not 64 or 128", hd);
+    if (nkv < 1 || nq < 1 || nq % nkv || nq / nkv > 8)
+        return fail(RRA_EINVAL, "flash decode: nq=%d nkv=%d (need nq %% nkv == 0, nq/nkv <= 8)",
+                    nq, nkv);
+    if (max_len < 1) return fail(RRA_EINVAL, "flash decode: max_len=%d", max_len);
+    if (chunk != 0 && (chunk < 32 || chunk > 1024 || chunk % 32))
+        return fail(RRA_EINVAL, "flash decode: chunk=%d (0, or a multiple of 32 in 32..1024)",
+                    chunk);
+    return RRA_OK;
+}
+
+extern "C" int32_t rra_flash_decode_chunk(int32_t m, int32_t nkv, int32_t max_len, int32_t chunk) {
+    return fd_choose_chunk(m, nkv, max_len, chunk);
+}
+
+extern "C" size_t rra_flash_decode_workspace_bytes(int32_t m, int32_t nq, int32_t nkv, int32_t hd,
+                                                   int32_t max_len, int32_t chunk) {
+    if (fd_validate(m, nq, nkv, hd, max_len, chunk) != RRA_OK) {
+        clear_error();
+        return 0;
+    }
+    const int c = fd_choose_chunk(m, nkv, max_len, chunk);
+    return sizeof(float) * fd_partials_floats(m, nq, hd, max_len, c);
+}
+
+extern "C" rra_status rra_flash_decode(const float *q, const float *k_cache, const float *v_cache,
+                                       const uint32_t *seq_len, float *out, int32_t m, int32_t nq,
+                                       int32_t nkv, int32_t hd, int32_t max_len, int32_t chunk,
+                                       void *ws, size_t ws_bytes, hipStream_t s) {
+    clear_error();
+    if (!q || !k_cache || !v_cache || !seq_len || !out || !ws)
+        return fail(RRA_EINVAL, "rra_flash_decode: null argument");
+    RRA_TRY(fd_validate(m, nq, nkv, hd, max_len, chunk));
+    const size_t need = rra_flash_decode_workspace_bytes(m, nq, nkv, hd, max_len, chunk);
+    if (ws_bytes < need)
+        return fail(RRA_ENOTINIT, "rra_flash_decode: workspace has %zu bytes, needs %zu", ws_bytes,
+                    need);
+    const int c = fd_choose_chunk(m, nkv, max_len, chunk);
+    return launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len, c,
+                               static_cast<float *>(ws), s);
+}

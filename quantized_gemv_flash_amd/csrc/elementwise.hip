@@ -1,0 +1,308 @@
+// elementwise.hip -- RMSNorm, RoPE, SwiGLU, greedy argmax, embedding gather,
+// and the fused epilogues the decode step runs after each GEMV (split-K sum +
+// residual + RMSNorm; split-K sum + RoPE + KV scatter; split-K sum + SwiGLU).
+//
+// Readings of the steps the pages name without defining (a Llama-style block):
+//   RMSNorm  x / sqrt(mean(x^2) + eps) * gamma
+//   RoPE     pairs (j, j + hd/2) rotated by pos * theta^(-2j/hd); the cos/sin
+//            table is built in fp64 on the host and rounded once to fp32
+//   SwiGLU   silu(gate) * up, silu(z) = z / (1 + e^-z)
+//   argmax   lowest index among the maximal logits ([reduces] gpu_argmax:
+//            block-level (max, index) pairs, then a final reduce)
+#include "rra_internal.h"
+
+#include <cmath>
+
+namespace rra {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over a 256-thread block; every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float *sh) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    const int nw = blockDim.x >> 6;
+    for (int i = 0; i < nw; ++i) t += sh[i];
+    __syncthreads();
+    return t;
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x,
+                                                      const float *__restrict__ gamma,
+                                                      float *out, int h, float eps) {
+    __shared__ float sh[4];
+    const float *xr = x + (size_t)blockIdx.x * h;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < h; i += blockDim.x) ss = fmaf(xr[i], xr[i], ss);
+    ss = block_sum(ss, sh);
+    const float inv = 1.0f / sqrtf(ss / (float)h + eps);
+    float *o = out + (size_t)blockIdx.x * h;
+    for (int i = threadIdx.x; i < h; i += blockDim.x) o[i] = xr[i] * inv * gamma[i];
+}
+
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
+    const float *__restrict__ part, int split, long long split_stride, float *__restrict__ x,
+    const float *__restrict__ gamma, float *__restrict__ u, int h, float eps) {
+    __shared__ float sh[4];
+    const size_t base = (size_t)blockIdx.x * h;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < h; i += blockDim.x) {
+        float v = x[base + i];
+        for (int s = 0; s < split; ++s) v += part[(size_t)s * split_stride + base + i];
+        x[base + i] = v;
+        ss = fmaf(v, v, ss);
+    }
+    ss = block_sum(ss, sh);
+    const float inv = 1.0f / sqrtf(ss / (float)h + eps);
+    for (int i = threadIdx.x; i < h; i += blockDim.x) u[base + i] = x[base + i] * inv * gamma[i];
+}
+
+// Grid (m, nq + 2 nkv heads), hd/2 threads: thread j handles pair (j, j + hd/2).
+__global__ void qkv_post_kernel(const float *__restrict__ part, int split, long long split_stride,
+                                const uint32_t *__restrict__ pos, const float *__restrict__ table,
+                                float *__restrict__ q_out, float *__restrict__ kc,
+                                float *__restrict__ vc, uint32_t *__restrict__ seq_len,
+                                uint32_t *__restrict__ err, int nq, int nkv, int hd, int max_len) {
+    const int m = blockIdx.x, head = blockIdx.y, j = threadIdx.x, half = hd >> 1;
+    const int nrow = (nq + 2 * nkv) * hd;
+    const uint32_t p = pos[m];
+    const bool ok = p < (uint32_t)max_len;
+    const size_t b = (size_t)m * nrow + (size_t)head * hd;
+    float a = 0.f, c = 0.f;
+    for (int s = 0; s < split; ++s) {
+        a += part[(size_t)s * split_stride + b + j];
+        c += part[(size_t)s * split_stride + b + j + half];
+    }
+    if (head < nq + nkv && ok) {
+        const float cs = table[((size_t)p * half + j) * 2], sn = table[((size_t)p * half + j) * 2 + 1];
+        const float ra = a * cs - c * sn, rc = a * sn + c * cs;
+        a = ra;
+        c = rc;
+    }
+    if (head < nq) {
+        float *qo = q_out + ((size_t)m * nq + head) * hd;
+        qo[j] = a;
+        qo[j + half] = c;
+    } else if (ok) {
+        const bool is_k = head < nq + nkv;
+        const int g = is_k ? head - nq : head - nq - nkv;
+        float *dst = (is_k ? kc : vc) + (((size_t)m * nkv + g) * max_len + p) * hd;
+        dst[j] = a;
+        dst[j + half] = c;
+    }
+    if (head == 0 && j == 0) {
+        seq_len[m] = ok ? p + 1 : (uint32_t)max_len;
+        if (!ok) err[0] = 1u;
+    }
+}
+
+__global__ void rope_kernel(float *__restrict__ z, const uint32_t *__restrict__ pos,
+                            const float *__restrict__ table, int n_heads, int hd, int max_len) {
+    const int m = blockIdx.x, head = blockIdx.y, j = threadIdx.x, half = hd >> 1;
+    const uint32_t p = pos[m];
+    if (p >= (uint32_t)max_len) return;
+    float *zr = z + ((size_t)m * n_heads + head) * hd;
+    const float cs = table[((size_t)p * half + j) * 2], sn = table[((size_t)p * half + j) * 2 + 1];
+    const float a = zr[j], c = zr[j + half];
+    zr[j] = a * cs - c * sn;
+    zr[j + half] = a * sn + c * cs;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__global__ void swiglu_kernel(const float *gate, const float *up, float *out, int n,
+                              long long gate_stride, long long up_stride, long long total) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const long long m = i / n, j = i - m * n;
+    out[i] = silu(gate[m * gate_stride + j]) * up[m * up_stride + j];
+}
+
+__global__ void swiglu_reduce_kernel(const float *__restrict__ part, int split,
+                                     long long split_stride, float *__restrict__ act, int inter,
+                                     long long total) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const long long m = i / inter, j = i - m * inter;
+    const size_t gi = (size_t)m * 2 * inter + j, ui = gi + inter;
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < split; ++s) {
+        g += part[(size_t)s * split_stride + gi];
+        u += part[(size_t)s * split_stride + ui];
+    }
+    act[i] = silu(g) * u;
+}
+
+__global__ void embed_gather_kernel(const float *__restrict__ embed, const uint32_t *__restrict__ tok,
+                                    float *__restrict__ x, int h, int vocab) {
+    const int m = blockIdx.x;
+    const uint32_t t = tok[m];
+    float *xr = x + (size_t)m * h;
+    if (t >= (uint32_t)vocab) {
+        for (int i = threadIdx.x; i < h; i += blockDim.x) xr[i] = 0.f;
+        return;
+    }
+    const float *er = embed + (size_t)t * h;
+    for (int i = threadIdx.x; i < h; i += blockDim.x) xr[i] = er[i];
+}
+
+// (v2, i2) beats (v1, i1) if larger, or equal with a lower index.  NaN never wins.
+__device__ __forceinline__ void arg_combine(float &v1, uint32_t &i1, float v2, uint32_t i2) {
+    if (v2 > v1 || (v2 == v1 && i2 < i1)) {
+        v1 = v2;
+        i1 = i2;
+    }
+}
+
+constexpr int kArgmaxPerBlock = 4096;  // 256 threads x 16 logits
+
+__global__ __launch_bounds__(256) void argmax_pass1_kernel(const float *__restrict__ logits,
+                                                           float *__restrict__ bv,
+                                                           uint32_t *__restrict__ bi, int v,
+                                                           int nb) {
+    __shared__ float sv[4];
+    __shared__ uint32_t si[4];
+    const int blk = blockIdx.x, m = blockIdx.y;
+    const float *l = logits + (size_t)m * v;
+    float best = -INFINITY;
+    uint32_t bidx = 0xFFFFFFFFu;
+#pragma unroll 4
+    for (int i = 0; i < kArgmaxPerBlock / 256; ++i) {
+        const int idx = blk * kArgmaxPerBlock + i * 256 + threadIdx.x;
+        if (idx < v) arg_combine(best, bidx, l[idx], (uint32_t)idx);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        arg_combine(best, bidx, __shfl_xor(best, off, 64), __shfl_xor(bidx, off, 64));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sv[wave] = best;
+        si[wave] = bidx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) arg_combine(best, bidx, sv[w], si[w]);
+        bv[(size_t)m * nb + blk] = best;
+        bi[(size_t)m * nb + blk] = bidx;
+    }
+}
+
+__global__ __launch_bounds__(256) void argmax_pass2_kernel(const float *__restrict__ bv,
+                                                           const uint32_t *__restrict__ bi,
+                                                           uint32_t *__restrict__ tok,
+                                                           uint32_t *__restrict__ pos_advance,
+                                                           int nb) {
+    __shared__ float sv[4];
+    __shared__ uint32_t si[4];
+    const int m = blockIdx.x;
+    float best = -INFINITY;
+    uint32_t bidx = 0xFFFFFFFFu;
+    for (int i = threadIdx.x; i < nb; i += blockDim.x)
+        arg_combine(best, bidx, bv[(size_t)m * nb + i], bi[(size_t)m * nb + i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        arg_combine(best, bidx, __shfl_xor(best, off, 64), __shfl_xor(bidx, off, 64));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sv[wave] = best;
+        si[wave] = bidx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) arg_combine(best, bidx, sv[w], si[w]);
+        tok[m] = bidx == 0xFFFFFFFFu ? 0u : bidx;
+        if (pos_advance) pos_advance[m] += 1u;
+    }
+}
+
+}  // namespace
+
+rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m, int h, float eps,
+                          hipStream_t s) {
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(m), dim3(256), 0, s, x, gamma, out, h, eps);
+    return check_launch("rmsnorm_kernel");
+}
+
+rra_status launch_residual_rmsnorm(const float *part, int split, size_t split_stride, float *x,
+                                   const float *gamma, float *u, int m, int h, float eps,
+                                   hipStream_t s) {
+    hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(m), dim3(256), 0, s, part, split,
+                       (long long)split_stride, x, gamma, u, h, eps);
+    return check_launch("residual_rmsnorm_kernel");
+}
+
+rra_status launch_qkv_post(const float *part, int split, size_t split_stride, const uint32_t *pos,
+                           const float *table, float *q_out, float *k_cache, float *v_cache,
+                           uint32_t *seq_len, uint32_t *err, int m, int nq, int nkv, int hd,
+                           int max_len, hipStream_t s) {
+    hipLaunchKernelGGL(qkv_post_kernel, dim3(m, nq + 2 * nkv), dim3(hd / 2), 0, s, part, split,
+                       (long long)split_stride, pos, table, q_out, k_cache, v_cache, seq_len, err,
+                       nq, nkv, hd, max_len);
+    return check_launch("qkv_post_kernel");
+}
+
+rra_status launch_rope(float *z, const uint32_t *pos, const float *table, int m, int n_heads,
+                       int hd, int max_len, hipStream_t s) {
+    hipLaunchKernelGGL(rope_kernel, dim3(m, n_heads), dim3(hd / 2), 0, s, z, pos, table, n_heads,
+                       hd, max_len);
+    return check_launch("rope_kernel");
+}
+
+rra_status launch_swiglu(const float *gate, const float *up, float *out, int m, int n,
+                         size_t gate_stride, size_t up_stride, hipStream_t s) {
+    const long long total = (long long)m * n;
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, gate, up,
+                       out, n, (long long)gate_stride, (long long)up_stride, total);
+    return check_launch("swiglu_kernel");
+}
+
+rra_status launch_swiglu_reduce(const float *part, int split, size_t split_stride, float *act,
+                                int m, int inter, hipStream_t s) {
+    const long long total = (long long)m * inter;
+    hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
+                       part, split, (long long)split_stride, act, inter, total);
+    return check_launch("swiglu_reduce_kernel");
+}
+
+rra_status launch_embed_gather(const float *embed, const uint32_t *tok, float *x, int m, int h,
+                               int vocab, hipStream_t s) {
+    hipLaunchKernelGGL(embed_gather_kernel, dim3(m), dim3(256), 0, s, embed, tok, x, h, vocab);
+    return check_launch("embed_gather_kernel");
+}
+
+size_t argmax_ws_bytes(int m, int v) {
+    const size_t nb = (size_t)cdiv(v, kArgmaxPerBlock);
+    return align_up((size_t)m * nb * sizeof(float), 256) + (size_t)m * nb * sizeof(uint32_t);
+}
+
+rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void *ws,
+                         uint32_t *pos_advance, hipStream_t s) {
+    const int nb = (int)cdiv(v, kArgmaxPerBlock);
+    float *bv = static_cast<float *>(ws);
+    uint32_t *bi = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
+                                                align_up((size_t)m * nb * sizeof(float), 256));
+    hipLaunchKernelGGL(argmax_pass1_kernel, dim3(nb, m), dim3(256), 0, s, logits, bv, bi, v, nb);
+    RRA_TRY(check_launch("argmax_pass1_kernel"));
+    hipLaunchKernelGGL(argmax_pass2_kernel, dim3(m), dim3(256), 0, s, bv, bi, tok, pos_advance, nb);
+    return check_launch("argmax_pass2_kernel");
+}
+
+void rope_table_host(float *table, int max_len, int hd, double theta) {
+    const int half = hd / 2;
+    for (int p = 0; p < max_len; ++p)
+        for (int j = 0; j < half; ++j) {
+            const double ang = (double)p * std::pow(theta, -2.0 * j / hd);
+            table[((size_t)p * half + j) * 2] = (float)std::cos(ang);
+            table[((size_t)p * half + j) * 2 + 1] = (float)std::sin(ang);
+        }
+}
+
+}  // namespace rra

@@ -1,0 +1,491 @@
+// model.cpp -- host side of librra: error reporting, argument validation, the
+// standalone step entry points, and the decode step with its HIP graph cache.
+//
+// [batched_forward] forward_batched_to_token_ids / ..._graphed and
+// [graph] (module doc, graph_step, graph_capture): the whole step -- every
+// layer, the output norm, the LM head and the argmax -- is one graph whose
+// per-token inputs (positions, token ids, the step input) sit at fixed device
+// addresses; a graph is keyed by those addresses and by M, captured on first
+// use and replayed after; a failed capture leaves the stream out of capture
+// mode and the step runs eagerly instead.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "rra_internal.h"
+
+namespace rra {
+
+static thread_local std::string g_error;
+
+rra_status fail(rra_status st, const char *fmt, ...) {
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    if (verbose()) fprintf(stderr, "[rra] %s: %s\n", rra_status_name(st), buf);
+    return st;
+}
+
+void clear_error() { g_error.clear(); }
+
+bool verbose() {
+    static const bool v = [] {
+        const char *e = getenv("RRA_VERBOSE");
+        return e && *e && strcmp(e, "0") != 0;
+    }();
+    return v;
+}
+
+rra_status check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(RRA_EHIP, "launch of %s failed: %s", what, hipGetErrorString(e));
+    return RRA_OK;
+}
+
+rra_status validate_weight(const rra_weight *w, const char *what, bool need_tiled_q) {
+    if (!w) return fail(RRA_EINVAL, "%s: null weight", what);
+    if (w->fmt != RRA_F32 && w->fmt != RRA_Q8 && w->fmt != RRA_Q4)
+        return fail(RRA_EINVAL, "%s: unknown weight format %d", what, w->fmt);
+    if (w->n <= 0 || w->k <= 0 || w->n > (1LL << 30) || w->k > (1LL << 24))
+        return fail(RRA_EINVAL, "%s: bad shape %lld x %lld", what, (long long)w->n,
+                    (long long)w->k);
+    if (!w->data) return fail(RRA_EINVAL, "%s: null weight data", what);
+    if (w->fmt == RRA_F32) {
+        if (w->layout != RRA_PLANAR) return fail(RRA_EINVAL, "%s: F32 weights are planar", what);
+        return RRA_OK;
+    }
+    if (w->k % 32) return fail(RRA_EINVAL, "%s: k=%lld is not a multiple of 32", what, (long long)w->k);
+    if (w->layout == RRA_PLANAR) {
+        if (need_tiled_q)
+            return fail(RRA_EINVAL, "%s: planar Q8/Q4 weight; convert it with rra_repack_weight",
+                        what);
+        if (!w->scale) return fail(RRA_EINVAL, "%s: planar Q8/Q4 weight without scales", what);
+        return RRA_OK;
+    }
+    if (w->layout != RRA_TILED) return fail(RRA_EINVAL, "%s: unknown layout %d", what, w->layout);
+    return RRA_OK;
+}
+
+}  // namespace rra
+
+using namespace rra;
+
+// ---------------------------------------------------------------- basics
+extern "C" const char *rra_last_error(void) { return g_error.c_str(); }
+
+extern "C" const char *rra_status_name(rra_status st) {
+    switch (st) {
+        case RRA_OK: return "RRA_OK";
+        case RRA_EINVAL: return "RRA_EINVAL";
+        case RRA_ENOTINIT: return "RRA_ENOTINIT";
+        case RRA_EHIP: return "RRA_EHIP";
+        case RRA_ECAPTURE: return "RRA_ECAPTURE";
+    }
+    return "RRA_UNKNOWN";
+}
+
+extern "C" int32_t rra_version(void) { return RRA_VERSION; }
+
+// ---------------------------------------------------------------- step kernels
+extern "C" rra_status rra_rmsnorm(const float *x, const float *gamma, float *out, int32_t m,
+                                  int32_t h, float eps, hipStream_t s) {
+    clear_error();
+    if (!x || !gamma || !out) return fail(RRA_EINVAL, "rra_rmsnorm: null argument");
+    if (m < 1 || m > RRA_M_MAX || h < 1) return fail(RRA_EINVAL, "rra_rmsnorm: m=%d h=%d", m, h);
+    if (!(eps >= 0.f)) return fail(RRA_EINVAL, "rra_rmsnorm: eps must be >= 0");
+    return launch_rmsnorm(x, gamma, out, m, h, eps, s);
+}
+
+extern "C" rra_status rra_rope_table(float *table, int32_t max_len, int32_t hd, double theta,
+                                     hipStream_t s) {
+    clear_error();
+    if (!table) return fail(RRA_EINVAL, "rra_rope_table: null table");
+    if (max_len < 1 || hd < 2 || hd % 2 || !(theta > 0.0))
+        return fail(RRA_EINVAL, "rra_rope_table: max_len=%d hd=%d theta=%g", max_len, hd, theta);
+    std::vector<float> host((size_t)max_len * hd);
+    rope_table_host(host.data(), max_len, hd, theta);
+    RRA_TRY_HIP(hipMemcpyAsync(table, host.data(), host.size() * sizeof(float),
+                               hipMemcpyHostToDevice, s));
+    RRA_TRY_HIP(hipStreamSynchronize(s));
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_rope(float *z, const uint32_t *pos, const float *table, int32_t m,
+                               int32_t n_heads, int32_t hd, int32_t max_len, hipStream_t s) {
+    clear_error();
+    if (!z || !pos || !table) return fail(RRA_EINVAL, "rra_rope: null argument");
+    if (m < 1 || m > RRA_M_MAX || n_heads < 1 || hd < 2 || hd % 2 || hd > 2048 || max_len < 1)
+        return fail(RRA_EINVAL, "rra_rope: m=%d heads=%d hd=%d max_len=%d", m, n_heads, hd, max_len);
+    return launch_rope(z, pos, table, m, n_heads, hd, max_len, s);
+}
+
+extern "C" rra_status rra_swiglu(const float *gate, const float *up, float *out, int32_t m,
+                                 int32_t n, hipStream_t s) {
+    clear_error();
+    if (!gate || !up || !out) return fail(RRA_EINVAL, "rra_swiglu: null argument");
+    if (m < 1 || m > RRA_M_MAX || n < 1) return fail(RRA_EINVAL, "rra_swiglu: m=%d n=%d", m, n);
+    return launch_swiglu(gate, up, out, m, n, (size_t)n, (size_t)n, s);
+}
+
+extern "C" size_t rra_argmax_workspace_bytes(int32_t m, int32_t v) {
+    if (m < 1 || m > RRA_M_MAX || v < 1) return 0;
+    return argmax_ws_bytes(m, v);
+}
+
+extern "C" rra_status rra_argmax(const float *logits, uint32_t *tok, int32_t m, int32_t v,
+                                 void *ws, size_t ws_bytes, hipStream_t s) {
+    clear_error();
+    if (!logits || !tok || !ws) return fail(RRA_EINVAL, "rra_argmax: null argument");
+    if (m < 1 || m > RRA_M_MAX || v < 1) return fail(RRA_EINVAL, "rra_argmax: m=%d v=%d", m, v);
+    const size_t need = argmax_ws_bytes(m, v);
+    if (ws_bytes < need)
+        return fail(RRA_ENOTINIT, "rra_argmax: workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return launch_argmax(logits, tok, m, v, ws, nullptr, s);
+}
+
+// ---------------------------------------------------------------- model
+struct GraphKey {
+    int32_t m, flags;
+    const void *x, *pos, *tok, *logits;
+    bool operator==(const GraphKey &o) const {
+        return m == o.m && flags == o.flags && x == o.x && pos == o.pos && tok == o.tok &&
+               logits == o.logits;
+    }
+};
+
+struct GraphEntry {
+    GraphKey key;
+    hipGraphExec_t exec;
+    uint32_t kernels;
+};
+
+struct rra_model {
+    rra_model_desc d{};
+    std::vector<rra_layer_desc> layers;
+    int chunk = 0;
+    // workspace carve-up
+    float *u = nullptr, *part = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr;
+    float *fd = nullptr, *logits = nullptr, *rope = nullptr;
+    uint32_t *lens = nullptr, *err = nullptr;
+    void *argmax_ws = nullptr;
+    // per-M plans (index m)
+    GemvPlan plan_qkv[RRA_M_MAX + 1], plan_o[RRA_M_MAX + 1], plan_gu[RRA_M_MAX + 1],
+        plan_d[RRA_M_MAX + 1], plan_lm[RRA_M_MAX + 1];
+    std::vector<GraphEntry> graphs;
+    uint64_t captures = 0, replays = 0;
+    uint32_t last_kernels = 0;
+};
+
+namespace {
+
+struct Layout {
+    size_t u, part, q, lens, attn, act, fd, logits, argmax, rope, err, total;
+};
+
+size_t part_floats(const rra_model_desc &d, const rra_layer_desc &l) {
+    size_t best = 0;
+    for (int m = 1; m <= d.m_max; ++m) {
+        const rra_weight *ws[4] = {&l.wqkv, &l.wo, &l.wgu, &l.wd};
+        for (const rra_weight *w : ws) {
+            const GemvPlan p = gemv_plan(*w, m);
+            best = std::max(best, (size_t)p.split * (size_t)m * (size_t)w->n);
+        }
+    }
+    return best;
+}
+
+Layout layout_of(const rra_model_desc &d, int chunk) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const size_t M = (size_t)d.m_max;
+    size_t partf = 0;
+    for (int i = 0; i < d.n_layers; ++i) partf = std::max(partf, part_floats(d, d.layers[i]));
+    L.u = take(4 * M * d.hidden);
+    L.part = take(4 * partf);
+    L.q = take(4 * M * d.n_heads * d.head_dim);
+    L.lens = take(4 * M);
+    L.attn = take(4 * M * d.n_heads * d.head_dim);
+    L.act = take(4 * M * d.intermediate);
+    L.fd = take(4 * fd_partials_floats((int)M, d.n_heads, d.head_dim, d.max_len, chunk));
+    L.logits = take(4 * M * (size_t)d.vocab);
+    L.argmax = take(argmax_ws_bytes((int)M, d.vocab));
+    L.rope = take(4 * (size_t)d.max_len * d.head_dim);
+    L.err = take(256);
+    L.total = off;
+    return L;
+}
+
+rra_status check_shape(const rra_weight &w, int64_t n, int64_t k, const char *what) {
+    RRA_TRY(validate_weight(&w, what, true));
+    if (w.n != n || w.k != k)
+        return fail(RRA_EINVAL, "%s: shape %lld x %lld, expected %lld x %lld", what,
+                    (long long)w.n, (long long)w.k, (long long)n, (long long)k);
+    return RRA_OK;
+}
+
+rra_status validate_desc(const rra_model_desc *d) {
+    if (!d) return fail(RRA_EINVAL, "model: null descriptor");
+    if (d->n_layers < 1 || d->hidden < 1 || d->n_heads < 1 || d->n_kv_heads < 1 ||
+        d->intermediate < 1 || d->vocab < 1)
+        return fail(RRA_EINVAL, "model: non-positive dimension");
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(RRA_EINVAL, "model: head_dim=%d not 64 or 128", d->head_dim);
+    if (d->n_heads % d->n_kv_heads || d->n_heads / d->n_kv_heads > 8)
+        return fail(RRA_EINVAL, "model: n_heads=%d n_kv_heads=%d (need a group size 1..8)",
+                    d->n_heads, d->n_kv_heads);
+    if (d->hidden % 4 || d->intermediate % 4)
+        return fail(RRA_EINVAL, "model: hidden and intermediate must be multiples of 4");
+    if (d->m_max < 1 || d->m_max > RRA_M_MAX)
+        return fail(RRA_EINVAL, "model: m_max=%d not in 1..32", d->m_max);
+    if (d->max_len < 1) return fail(RRA_EINVAL, "model: max_len=%d", d->max_len);
+    if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.0))
+        return fail(RRA_EINVAL, "model: bad rms_eps or rope_theta");
+    if (d->attn_chunk != 0 && (d->attn_chunk < 32 || d->attn_chunk > 1024 || d->attn_chunk % 32))
+        return fail(RRA_EINVAL, "model: attn_chunk=%d", d->attn_chunk);
+    if (!d->layers || !d->out_gamma) return fail(RRA_EINVAL, "model: null layers or out_gamma");
+    const int64_t H = d->hidden, hd = d->head_dim, nq = d->n_heads, nkv = d->n_kv_heads,
+                  I = d->intermediate;
+    for (int i = 0; i < d->n_layers; ++i) {
+        const rra_layer_desc &l = d->layers[i];
+        RRA_TRY(check_shape(l.wqkv, (nq + 2 * nkv) * hd, H, "layer wqkv"));
+        RRA_TRY(check_shape(l.wo, H, nq * hd, "layer wo"));
+        RRA_TRY(check_shape(l.wgu, 2 * I, H, "layer wgu"));
+        RRA_TRY(check_shape(l.wd, H, I, "layer wd"));
+        if (!l.attn_gamma || !l.ffn_gamma || !l.k_cache || !l.v_cache)
+            return fail(RRA_EINVAL, "layer %d: null gamma or cache", i);
+    }
+    RRA_TRY(check_shape(d->lm_head, d->vocab, H, "lm_head"));
+    return RRA_OK;
+}
+
+// Every launch of one decode step, in stream order.
+rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, float *logits,
+                        int m, int flags, hipStream_t s) {
+    const rra_model_desc &d = M->d;
+    const int H = d.hidden, nq = d.n_heads, nkv = d.n_kv_heads, hd = d.head_dim,
+              I = d.intermediate;
+    const int nqkv = (nq + 2 * nkv) * hd;
+    if (flags & RRA_STEP_GATHER) RRA_TRY(launch_embed_gather(d.embed, tok, x, m, H, d.vocab, s));
+    RRA_TRY(launch_rmsnorm(x, M->layers[0].attn_gamma, M->u, m, H, d.rms_eps, s));
+    for (int l = 0; l < d.n_layers; ++l) {
+        const rra_layer_desc &L = M->layers[l];
+        const float *next_gamma =
+            (l + 1 < d.n_layers) ? M->layers[l + 1].attn_gamma : d.out_gamma;
+        // attention block
+        const GemvPlan &pq = M->plan_qkv[m];
+        RRA_TRY(launch_gemv(L.wqkv, pq, M->u, m, M->part, (size_t)m * nqkv, s));
+        RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
+                                L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd, d.max_len,
+                                s));
+        RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
+                                    d.max_len, M->chunk, M->fd, s));
+        const GemvPlan &po = M->plan_o[m];
+        RRA_TRY(launch_gemv(L.wo, po, M->attn, m, M->part, (size_t)m * H, s));
+        RRA_TRY(launch_residual_rmsnorm(M->part, po.split, (size_t)m * H, x, L.ffn_gamma, M->u, m,
+                                        H, d.rms_eps, s));
+        // feed-forward block
+        const GemvPlan &pg = M->plan_gu[m];
+        RRA_TRY(launch_gemv(L.wgu, pg, M->u, m, M->part, (size_t)m * 2 * I, s));
+        RRA_TRY(launch_swiglu_reduce(M->part, pg.split, (size_t)m * 2 * I, M->act, m, I, s));
+        const GemvPlan &pd = M->plan_d[m];
+        RRA_TRY(launch_gemv(L.wd, pd, M->act, m, M->part, (size_t)m * H, s));
+        RRA_TRY(launch_residual_rmsnorm(M->part, pd.split, (size_t)m * H, x, next_gamma, M->u, m,
+                                        H, d.rms_eps, s));
+    }
+    RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], M->u, m, logits, 0, s));
+    return launch_argmax(logits, tok, m, d.vocab, M->argmax_ws,
+                         (flags & RRA_STEP_ADVANCE) ? pos : nullptr, s);
+}
+
+}  // namespace
+
+extern "C" size_t rra_model_workspace_bytes(const rra_model_desc *d) {
+    if (validate_desc(d) != RRA_OK) return 0;
+    const int chunk = fd_choose_chunk(d->m_max, d->n_kv_heads, d->max_len, d->attn_chunk);
+    return layout_of(*d, chunk).total;
+}
+
+extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t ws_bytes,
+                                       hipStream_t s, rra_model **out) {
+    clear_error();
+    if (!out) return fail(RRA_EINVAL, "rra_model_create: null out");
+    *out = nullptr;
+    RRA_TRY(validate_desc(d));
+    if (!ws) return fail(RRA_EINVAL, "rra_model_create: null workspace");
+    const int chunk = fd_choose_chunk(d->m_max, d->n_kv_heads, d->max_len, d->attn_chunk);
+    const Layout L = layout_of(*d, chunk);
+    if (ws_bytes < L.total)
+        return fail(RRA_ENOTINIT, "rra_model_create: workspace has %zu bytes, needs %zu", ws_bytes,
+                    L.total);
+    auto *M = new rra_model();
+    M->d = *d;
+    M->layers.assign(d->layers, d->layers + d->n_layers);
+    M->d.layers = M->layers.data();
+    M->chunk = chunk;
+    char *b = static_cast<char *>(ws);
+    M->u = reinterpret_cast<float *>(b + L.u);
+    M->part = reinterpret_cast<float *>(b + L.part);
+    M->q = reinterpret_cast<float *>(b + L.q);
+    M->lens = reinterpret_cast<uint32_t *>(b + L.lens);
+    M->attn = reinterpret_cast<float *>(b + L.attn);
+    M->act = reinterpret_cast<float *>(b + L.act);
+    M->fd = reinterpret_cast<float *>(b + L.fd);
+    M->logits = reinterpret_cast<float *>(b + L.logits);
+    M->argmax_ws = b + L.argmax;
+    M->rope = reinterpret_cast<float *>(b + L.rope);
+    M->err = reinterpret_cast<uint32_t *>(b + L.err);
+    for (int m = 1; m <= d->m_max; ++m) {
+        const rra_layer_desc &l0 = d->layers[0];
+        M->plan_qkv[m] = gemv_plan(l0.wqkv, m);
+        M->plan_o[m] = gemv_plan(l0.wo, m);
+        M->plan_gu[m] = gemv_plan(l0.wgu, m);
+        M->plan_d[m] = gemv_plan(l0.wd, m);
+        GemvPlan lm = gemv_plan(d->lm_head, m);
+        lm.kt_per_split = d->lm_head.fmt == RRA_F32 ? 1 : (int)cdiv(d->lm_head.k, tile_k(d->lm_head.fmt));
+        lm.split = 1;
+        M->plan_lm[m] = lm;
+    }
+    std::vector<float> table((size_t)d->max_len * d->head_dim);
+    rope_table_host(table.data(), d->max_len, d->head_dim, d->rope_theta);
+    const uint32_t zero[64] = {0};
+    hipError_t e = hipMemcpyAsync(M->rope, table.data(), table.size() * sizeof(float),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(M->err, zero, sizeof zero, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete M;
+        return fail(RRA_EHIP, "rra_model_create: %s", hipGetErrorString(e));
+    }
+    *out = M;
+    return RRA_OK;
+}
+
+extern "C" void rra_model_destroy(rra_model *M) {
+    if (!M) return;
+    for (GraphEntry &g : M->graphs) (void)hipGraphExecDestroy(g.exec);
+    delete M;
+}
+
+extern "C" rra_status rra_graph_stats(const rra_model *M, uint64_t *captures, uint64_t *replays,
+                                      uint32_t *kernels) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_graph_stats: null model");
+    if (captures) *captures = M->captures;
+    if (replays) *replays = M->replays;
+    if (kernels) *kernels = M->last_kernels;
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_model_check(rra_model *M, hipStream_t s) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_model_check: null model");
+    uint32_t flag = 0;
+    const uint32_t zero = 0;
+    RRA_TRY_HIP(hipMemcpyAsync(&flag, M->err, sizeof flag, hipMemcpyDeviceToHost, s));
+    RRA_TRY_HIP(hipStreamSynchronize(s));
+    if (flag) {
+        RRA_TRY_HIP(hipMemcpyAsync(M->err, &zero, sizeof zero, hipMemcpyHostToDevice, s));
+        RRA_TRY_HIP(hipStreamSynchronize(s));
+        return fail(RRA_EINVAL, "a decode step saw a position >= max_len (%d)", M->d.max_len);
+    }
+    return RRA_OK;
+}
+
+static rra_status capture_and_launch(rra_model *M, const GraphKey &key, float *x, uint32_t *pos,
+                                     uint32_t *tok, float *logits, int m, int flags,
+                                     hipStream_t s) {
+    // Stream capture in thread-local mode ([reduces] try_graph_capture): a
+    // failed capture cannot poison other threads' work.  End the capture
+    // whatever happened, so the stream always leaves capture mode.
+    RRA_TRY_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    const rra_status body = enqueue_step(M, x, pos, tok, logits, m, flags, s);
+    hipGraph_t graph = nullptr;
+    const hipError_t end = hipStreamEndCapture(s, &graph);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    (void)hipStreamIsCapturing(s, &cs);
+    if (cs != hipStreamCaptureStatusNone) (void)hipStreamSynchronize(s);
+    if (body != RRA_OK || end != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        (void)hipGetLastError();
+        if (verbose())
+            fprintf(stderr, "[rra] graph capture failed for M=%d (%s); running eagerly\n", m,
+                    end != hipSuccess ? hipGetErrorString(end) : rra_last_error());
+        return RRA_ECAPTURE;
+    }
+    size_t nodes = 0;
+    (void)hipGraphGetNodes(graph, nullptr, &nodes);
+    hipGraphExec_t exec = nullptr;
+    const hipError_t inst = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (inst != hipSuccess) {
+        (void)hipGetLastError();
+        return RRA_ECAPTURE;
+    }
+    if (M->graphs.size() >= 16) {  // small cache: drop the oldest graph
+        (void)hipGraphExecDestroy(M->graphs.front().exec);
+        M->graphs.erase(M->graphs.begin());
+    }
+    M->graphs.push_back(GraphEntry{key, exec, (uint32_t)nodes});
+    M->captures++;
+    M->last_kernels = (uint32_t)nodes;
+    if (verbose())
+        fprintf(stderr, "[rra] captured decode graph: M=%d, %zu kernels\n", m, nodes);
+    // Capture records without running: launch it now so this call's outputs
+    // are real ([batched_forward] forward_batched_to_token_ids_graphed).
+    RRA_TRY_HIP(hipGraphLaunch(exec, s));
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_decode_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok,
+                                      uint32_t *tok_host, float *logits, int32_t m, int32_t flags,
+                                      hipStream_t s) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_decode_step: null model");
+    if (!x || !pos || !tok) return fail(RRA_EINVAL, "rra_decode_step: null x, pos or tok");
+    if (m < 1 || m > M->d.m_max)
+        return fail(RRA_EINVAL, "rra_decode_step: m=%d not in 1..m_max=%d", m, M->d.m_max);
+    if (flags & ~(RRA_GRAPH | RRA_STEP_GATHER | RRA_STEP_ADVANCE))
+        return fail(RRA_EINVAL, "rra_decode_step: unknown flags 0x%x", flags);
+    if ((flags & RRA_STEP_GATHER) && !M->d.embed)
+        return fail(RRA_EINVAL, "rra_decode_step: RRA_STEP_GATHER needs an embedding table");
+    if ((flags & RRA_GRAPH) && !s)
+        return fail(RRA_EINVAL, "rra_decode_step: RRA_GRAPH needs a non-null stream");
+    float *lg = logits ? logits : M->logits;
+    if (flags & RRA_GRAPH) {
+        const GraphKey key{m, flags & ~RRA_GRAPH, x, pos, tok, lg};
+        GraphEntry *hit = nullptr;
+        for (GraphEntry &g : M->graphs)
+            if (g.key == key) hit = &g;
+        if (hit) {
+            RRA_TRY_HIP(hipGraphLaunch(hit->exec, s));
+            M->replays++;
+            M->last_kernels = hit->kernels;
+        } else {
+            const rra_status st = capture_and_launch(M, key, x, pos, tok, lg, m, flags, s);
+            if (st != RRA_OK) {
+                clear_error();
+                const rra_status eager = enqueue_step(M, x, pos, tok, lg, m, flags, s);
+                if (eager != RRA_OK) return fail(RRA_ECAPTURE, "capture and eager step failed: %s",
+                                                 rra_last_error());
+            }
+        }
+    } else {
+        RRA_TRY(enqueue_step(M, x, pos, tok, lg, m, flags, s));
+    }
+    if (tok_host) {
+        RRA_TRY_HIP(hipMemcpyAsync(tok_host, tok, sizeof(uint32_t) * m, hipMemcpyDeviceToHost, s));
+        RRA_TRY_HIP(hipStreamSynchronize(s));
+    }
+    return RRA_OK;
+}

@@ -1,0 +1,106 @@
+// Internal declarations shared by librra's sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+
+#include "rra.h"
+
+namespace rra {
+
+// Records a thread-local message and returns `st`.
+rra_status fail(rra_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+bool verbose();
+
+#define RRA_TRY_HIP(call)                                                               \
+    do {                                                                                \
+        hipError_t e_ = (call);                                                         \
+        if (e_ != hipSuccess)                                                           \
+            return ::rra::fail(RRA_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+#define RRA_TRY(expr)                       \
+    do {                                    \
+        rra_status st_ = (expr);            \
+        if (st_ != RRA_OK) return st_;      \
+    } while (0)
+
+// Checks the launch status of the kernel just enqueued.
+rra_status check_launch(const char *what);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ tiles
+// A tile covers 16 rows and KT columns: 1 KiB of quantised values, then the
+// scales of its 16 rows x NB blocks.
+constexpr int kRowTile = 16;
+inline int tile_k(int fmt) { return fmt == RRA_Q4 ? 128 : 64; }
+inline int tile_blocks(int fmt) { return fmt == RRA_Q4 ? 4 : 2; }
+inline int tile_bytes(int fmt) { return fmt == RRA_Q4 ? 1024 + 128 : 1024 + 64; }
+
+rra_status validate_weight(const rra_weight *w, const char *what, bool need_tiled_q);
+
+// ------------------------------------------------------------------ GEMV
+// How one GEMV is spread over the chip: `split` K-splits, each writing
+// partial sums [split][m][n]; `rpw` row tiles per wave (256-thread groups of
+// 4 waves).
+struct GemvPlan {
+    int split = 1;
+    int rpw = 1;
+    int kt_per_split = 1;
+};
+GemvPlan gemv_plan(const rra_weight &w, int m);
+// Enqueues the GEMV; the result (or its K-split partial sums) goes to
+// out[split][m][n] with out_split_stride floats between splits.
+rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const float *x, int m, float *out,
+                       size_t out_split_stride, hipStream_t s);
+// y[i][r] = sum over `split` partial planes (+ y[i][r] if accumulate).
+rra_status launch_reduce_splits(const float *part, int split, size_t split_stride, float *y,
+                                int m, int n, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+int fd_choose_chunk(int m, int nkv, int max_len, int chunk);
+size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk);
+rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
+                             float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
+                             int max_len, hipStream_t s);
+rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
+                               const uint32_t *seq_len, float *out, int m, int nq, int nkv,
+                               int hd, int max_len, int chunk, float *part, hipStream_t s);
+
+// ------------------------------------------------------------------ elementwise
+rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m, int h,
+                          float eps, hipStream_t s);
+rra_status launch_rope(float *z, const uint32_t *pos, const float *table, int m, int n_heads,
+                       int hd, int max_len, hipStream_t s);
+rra_status launch_swiglu(const float *gate, const float *up, float *out, int m, int n,
+                         size_t gate_stride, size_t up_stride, hipStream_t s);
+size_t argmax_ws_bytes(int m, int v);
+rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void *ws,
+                         uint32_t *pos_advance, hipStream_t s);
+void rope_table_host(float *table, int max_len, int hd, double theta);
+
+// Fused epilogues used by the decode step.
+// x[i] += sum_s part[s][i]; u[i] = rmsnorm(x[i]) * gamma.
+rra_status launch_residual_rmsnorm(const float *part, int split, size_t split_stride, float *x,
+                                   const float *gamma, float *u, int m, int h, float eps,
+                                   hipStream_t s);
+// qkv = sum_s part[s]; rope(q, k) at pos; q -> q_out [m][nq][hd]; k, v rows
+// scattered into the caches at pos; seq_len[i] = min(pos[i] + 1, max_len);
+// pos >= max_len sets *err.
+rra_status launch_qkv_post(const float *part, int split, size_t split_stride, const uint32_t *pos,
+                           const float *table, float *q_out, float *k_cache, float *v_cache,
+                           uint32_t *seq_len, uint32_t *err, int m, int nq, int nkv, int hd,
+                           int max_len, hipStream_t s);
+// act[i][j] = silu(sum_s part[s][i][j]) * sum_s part[s][i][inter + j].
+rra_status launch_swiglu_reduce(const float *part, int split, size_t split_stride, float *act,
+                                int m, int inter, hipStream_t s);
+rra_status launch_embed_gather(const float *embed, const uint32_t *tok, float *x, int m, int h,
+                               int vocab, hipStream_t s);
+
+}  // namespace rra

@@ -1,0 +1,49 @@
+"""Shared helpers of the GPU parity tests (no arithmetic of the method)."""
+import numpy as np
+import torch
+
+DEV = "cuda"
+
+# Tolerances: fp32 attention and hidden outputs rel 1e-4 / abs 1e-5
+# (|gpu - oracle| <= 1e-5 + 1e-4 |oracle|); logits abs 1e-3; argmax compared
+# unless the oracle's top-2 gap is below 1e-3.
+RTOL, ATOL = 1e-4, 1e-5
+LOGIT_ATOL = 1e-3
+TIE_GAP = 1e-3
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def assert_close(gpu, ref, rtol=RTOL, atol=ATOL, what=""):
+    g = np.asarray(host(gpu) if hasattr(gpu, "detach") else gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    err = np.abs(g - r)
+    bound = atol + rtol * np.abs(r)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; worst at "
+                             f"{i}: gpu={g[i]!r} oracle={r[i]!r} |d|={err[i]:.3g}")
+
+
+def assert_tokens(gpu_tok, orc_tok, orc_gap, orc_logits, what=""):
+    """Greedy ids agree unless the oracle's top-2 gap is < 1e-3; then the GPU's
+    id must still be one of the oracle's near-maximal logits."""
+    for i, (g, o, gap) in enumerate(zip(gpu_tok, orc_tok, orc_gap)):
+        if gap >= TIE_GAP:
+            assert int(g) == int(o), f"{what} seq {i}: gpu token {g} != oracle {o} (gap {gap:.3g})"
+        else:
+            l = orc_logits[i]
+            assert l[int(g)] >= l.max() - TIE_GAP, f"{what} seq {i}: near-tie token {g} invalid"
+
+
+def u32(values, device=DEV):
+    """uint32 device buffer (stored as int32; values < 2^31)."""
+    return torch.tensor(list(values), dtype=torch.int32, device=device)
+
+
+def banner(*parts):
+    print("[case]", *parts, flush=True)

@@ -1,0 +1,228 @@
+"""Parity of the whole decode step (rra_decode_step) with the CPU oracle.
+
+The oracle runs on the same seeded bytes.  Where greedy ids could differ
+(oracle top-2 gap < 1e-3) the GPU is teacher-forced with the oracle's ids, so
+no value computed on the GPU ever enters the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemv_flash_amd as rra
+import synth
+from gpu_common import DEV, LOGIT_ATOL, assert_close, assert_tokens, banner, host, u32
+from quantized_gemv_flash_amd.loader import load_decoder
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def side_stream():
+    """Every test runs on its own (default-priority) stream: graph capture
+    needs a stream other than the legacy null stream."""
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        yield s
+    s.synchronize()
+
+
+class Run:
+    """Fixed-address step buffers (graph-safe) for one device decoder."""
+
+    def __init__(self, S, W, m, max_len, attn_chunk=0):
+        self.S, self.W, self.m = S, W, m
+        self.dd = load_decoder(S, W, m_max=m, max_len=max_len, attn_chunk=attn_chunk)
+        self.x = torch.empty((m, S.hidden), device=DEV)
+        self.pos = torch.zeros(m, dtype=torch.int32, device=DEV)
+        self.tok = torch.zeros(m, dtype=torch.int32, device=DEV)
+        self.logits = torch.empty((m, S.vocab), device=DEV)
+
+    def step(self, tokens, positions, flags=0):
+        self.x.copy_(self.W.embed[torch.as_tensor(tokens, device=DEV)])
+        self.pos.copy_(torch.as_tensor(positions, dtype=torch.int32))
+        ids = self.dd.model.rra_decode_step(self.x, self.pos, self.tok, self.m, flags=flags,
+                                            logits=self.logits, tok_host=True)
+        return ids, self.x.clone(), self.logits.clone()
+
+    def fill_context(self, lengths, orc=None, orc_seqs=()):
+        for l in range(self.S.n_layers):
+            for s in range(self.m):
+                k, v = synth.kv_context_rows(self.S, l, s, lengths[s], device=DEV)
+                self.dd.k_caches[l][s, :, :lengths[s]] = k
+                self.dd.v_caches[l][s, :, :lengths[s]] = v
+                if orc is not None and s in orc_seqs:
+                    orc.set_context(l, orc_seqs.index(s), k, v)
+
+
+def compare_step(gpu, orc_out, what):
+    ids, hid, logits = gpu
+    assert_close(hid, orc_out["hidden"], what=f"{what} hidden")
+    assert_close(logits, orc_out["logits"], rtol=0.0, atol=LOGIT_ATOL, what=f"{what} logits")
+    assert_tokens(ids, orc_out["tok"], orc_out["gap"], orc_out["logits"], what=f"{what} tokens")
+
+
+# ---------------------------------------------------------------- tiny fp32
+def test_tiny_f32_sixteen_greedy_steps():
+    S = synth.TINY_LLAMA_F32
+    banner("decode", S.name)
+    W = synth.decoder_weights(S, seed=0, device=DEV, gamma="random")
+    run = Run(S, W, 1, S.max_len)
+    orc = oracle.DecoderOracle(S, W, 1, S.max_len)
+    tok = synth.first_tokens(S, 1).tolist()
+    for step in range(S.steps):
+        gpu = run.step(tok, [step])
+        o = orc.step(host(W.embed[torch.as_tensor(tok, device=DEV)]), [step])
+        compare_step(gpu, o, f"step {step}")
+        tok = o["tok"].tolist()
+
+
+def test_tiny_f32_batched_equals_separate_bitwise():
+    S = synth.TINY_LLAMA_F32
+    W = synth.decoder_weights(S, seed=3, device=DEV, gamma="random")
+    m = 3
+    both = Run(S, W, m, S.max_len)
+    ones = [Run(S, W, 1, S.max_len) for _ in range(m)]
+    toks = synth.first_tokens(S, m, seed=3).tolist()
+    starts = [0, 2, 5]
+    for step in range(6):
+        pos = [s + step for s in starts]
+        ids_b, hid_b, lg_b = both.step(toks, pos)
+        for i in range(m):
+            ids_1, hid_1, lg_1 = ones[i].step([toks[i]], [pos[i]])
+            assert ids_1[0] == ids_b[i]
+            assert torch.equal(hid_1[0], hid_b[i]) and torch.equal(lg_1[0], lg_b[i])
+        toks = ids_b
+
+
+def test_graph_replay_equals_eager_bitwise():
+    S = synth.TINY_LLAMA_F32
+    W = synth.decoder_weights(S, seed=1, device=DEV, gamma="random")
+    eager, graph = Run(S, W, 2, S.max_len), Run(S, W, 2, S.max_len)
+    toks = synth.first_tokens(S, 2, seed=1).tolist()
+    steps = 10
+    for step in range(steps):
+        a = eager.step(toks, [step, step + 1])
+        b = graph.step(toks, [step, step + 1], flags=rra.RRA_GRAPH)
+        assert a[0] == b[0]
+        assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+        toks = a[0]
+    st = graph.dd.model.rra_graph_stats()
+    assert st["captures"] == 1 and st["replays"] == steps - 1 and st["kernels"] > 0
+    for l in range(S.n_layers):
+        assert torch.equal(eager.dd.k_caches[l], graph.dd.k_caches[l])
+        assert torch.equal(eager.dd.v_caches[l], graph.dd.v_caches[l])
+
+
+def test_device_greedy_loop_gather_advance_in_graph():
+    # The step reads the previous ids, gathers their embeddings and advances
+    # the positions on the device; graph replays equal the eager loop.
+    S = synth.TINY_LLAMA_F32
+    W = synth.decoder_weights(S, seed=2, device=DEV)
+    flags = rra.RRA_STEP_GATHER | rra.RRA_STEP_ADVANCE
+    runs = [Run(S, W, 2, S.max_len), Run(S, W, 2, S.max_len)]
+    first = synth.first_tokens(S, 2, seed=2).tolist()
+    seqs = []
+    for r, extra in zip(runs, (0, rra.RRA_GRAPH)):
+        r.tok.copy_(torch.as_tensor(first, dtype=torch.int32))
+        r.pos.zero_()
+        ids = []
+        for _ in range(12):
+            r.dd.model.rra_decode_step(r.x, r.pos, r.tok, 2, flags=flags | extra, logits=r.logits)
+            ids.append(host(r.tok).tolist())
+        torch.cuda.synchronize()
+        assert host(r.pos).tolist() == [12, 12]
+        seqs.append(ids)
+    assert seqs[0] == seqs[1]
+    assert runs[1].dd.model.rra_graph_stats()["replays"] == 11
+
+
+def test_position_past_cache_is_reported_not_written():
+    S = synth.TINY_LLAMA_F32
+    W = synth.decoder_weights(S, seed=4, device=DEV)
+    run = Run(S, W, 1, 8)
+    run.step([3], [2])
+    run.dd.model.rra_model_check()
+    before = [c.clone() for c in run.dd.k_caches]
+    run.step([3], [8])  # == max_len
+    with pytest.raises(rra.RraError, match="max_len"):
+        run.dd.model.rra_model_check()
+    run.dd.model.rra_model_check()  # cleared
+    for a, b in zip(before, run.dd.k_caches):
+        assert torch.equal(a, b)
+
+
+def test_graph_recaptures_on_new_buffers():
+    S = synth.TINY_LLAMA_F32
+    W = synth.decoder_weights(S, seed=5, device=DEV)
+    run = Run(S, W, 1, S.max_len)
+    run.step([1], [0], flags=rra.RRA_GRAPH)
+    run.step([2], [1], flags=rra.RRA_GRAPH)
+    run.logits = torch.empty_like(run.logits)  # new logits buffer -> new key
+    run.step([3], [2], flags=rra.RRA_GRAPH)
+    st = run.dd.model.rra_graph_stats()
+    assert st["captures"] == 2 and st["replays"] == 1
+
+
+# ---------------------------------------------------------------- quantised decoders
+def test_qwen05b_q8_context_then_greedy():
+    # Full 24-layer Q8 decoder at M=1: 8 teacher-forced context steps on random
+    # token ids, then 8 greedy steps (the bench runs the 512-token context).
+    S = synth.QWEN25_05B_Q8
+    banner("decode", S.name)
+    W = synth.decoder_weights(S, seed=0, device=DEV)
+    run = Run(S, W, 1, 64)
+    orc = oracle.DecoderOracle(S, W, 1, 64)
+    ctx = synth.context_tokens(S, 1, 8).tolist()[0]
+    tok = [ctx[0]]
+    for step in range(16):
+        if step < 8:
+            tok = [ctx[step]]
+        gpu = run.step(tok, [step])
+        o = orc.step(host(W.embed[torch.as_tensor(tok, device=DEV)]), [step])
+        compare_step(gpu, o, f"step {step}")
+        tok = o["tok"].tolist()
+
+
+def test_qwen15b_q4_batch4_context1024():
+    S = synth.QWEN25_15B_Q4
+    banner("decode", S.name)
+    m = 4
+    W = synth.decoder_weights(S, seed=0, device=DEV)
+    run = Run(S, W, m, S.max_len)
+    orc = oracle.DecoderOracle(S, W, m, S.max_len)
+    lens = synth.context_lengths(S, m)
+    run.fill_context(lens, orc, list(range(m)))
+    tok = synth.first_tokens(S, m).tolist()
+    for step in range(2):
+        pos = [L + step for L in lens]
+        gpu = run.step(tok, pos, flags=rra.RRA_GRAPH)
+        o = orc.step(host(W.embed[torch.as_tensor(tok, device=DEV)]), pos)
+        compare_step(gpu, o, f"step {step}")
+        tok = o["tok"].tolist()
+
+
+def test_llama8b_q4_batch32_graph_sampled_sequences():
+    # Full 32-layer Q4 decoder, 32 sequences at positions in [2048, 4096], one
+    # captured graph; the oracle checks two sampled sequences.
+    S = synth.LLAMA3_8B_Q4
+    banner("decode", S.name)
+    m = S.m
+    W = synth.decoder_weights(S, seed=0, device=DEV)
+    run = Run(S, W, m, S.max_len)
+    sample = [0, 29]
+    orc = oracle.DecoderOracle(S, W, len(sample), S.max_len)
+    lens = synth.context_lengths(S, m)
+    run.fill_context(lens, orc, sample)
+    tok = synth.first_tokens(S, m).tolist()
+    for step in range(2):
+        pos = [L + step for L in lens]
+        ids, hid, logits = run.step(tok, pos, flags=rra.RRA_GRAPH)
+        xs = host(W.embed[torch.as_tensor([tok[i] for i in sample], device=DEV)])
+        o = orc.step(xs, [pos[i] for i in sample])
+        compare_step(([ids[i] for i in sample], hid[sample], logits[sample]), o, f"step {step}")
+        for j, i in enumerate(sample):
+            tok[i] = int(o["tok"][j])
+        tok = [tok[i] if i in sample else ids[i] for i in range(m)]
+    assert run.dd.model.rra_graph_stats()["replays"] == 1

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/rra.h declares, and rejects bad arguments before any
+device work."""
+import ctypes
+
+import pytest
+import torch
+
+import quantized_gemv_flash_amd as rra
+
+
+def test_library_exports_every_declared_function():
+    names = rra.header_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(rra.lib, n)]
+    assert not missing, missing
+    assert rra.lib.rra_version() == 1
+
+
+def test_status_names():
+    assert rra.lib.rra_status_name(0) == b"RRA_OK"
+    assert rra.lib.rra_status_name(4) == b"RRA_ECAPTURE"
+
+
+@pytest.mark.parametrize("fmt,n,k,expect", [
+    ("q4", 37, 96, 3 * 1 * 1152),        # ragged rows and a partial K tile
+    ("q4", 128256, 4096, 8016 * 32 * 1152),
+    ("q8", 1152, 896, 72 * 14 * 1088),
+    ("q8", 16, 32, 1 * 1 * 1088),
+    ("q4", 16, 33, 0),                     # K not a multiple of 32
+    ("f32", 16, 32, 0),                    # fp32 is never tiled
+])
+def test_tiled_bytes(fmt, n, k, expect):
+    assert rra.rra_tiled_bytes(fmt, n, k) == expect
+
+
+def _fake_weight(fmt, n, k, layout=rra.RRA_TILED):
+    t = torch.zeros(16, dtype=torch.uint8)  # never dereferenced: validation fails first
+    return rra.Weight(fmt, n, k, t, t if layout == rra.RRA_PLANAR and fmt != "f32" else None, layout)
+
+
+@pytest.mark.parametrize("m", [0, 33, -1])
+def test_gemv_rejects_bad_batch(m):
+    w = _fake_weight("q4", 64, 128)
+    x = torch.zeros(4)
+    with pytest.raises(rra.RraError) as e:
+        rra.rra_batched_gemv(w, x, x, m)
+    assert e.value.status == rra.RRA_EINVAL and "1..32" in str(e.value)
+
+
+def test_gemv_rejects_planar_quantised_weight():
+    w = _fake_weight("q8", 64, 128, rra.RRA_PLANAR)
+    x = torch.zeros(4)
+    with pytest.raises(rra.RraError) as e:
+        rra.rra_batched_gemv(w, x, x, 1)
+    assert "rra_repack_weight" in str(e.value)
+
+
+def test_gemv_rejects_k_not_multiple_of_32():
+    w = _fake_weight("q4", 64, 100)
+    x = torch.zeros(4)
+    with pytest.raises(rra.RraError, match="multiple of 32"):
+        rra.rra_batched_gemv(w, x, x, 1)
+
+
+def test_gemv_workspace_sizes():
+    # A long-K matrix with few rows is split over K; its workspace holds the
+    # partial sums of every split.
+    w = _fake_weight("q4", 4096, 14336)
+    nb = rra.rra_batched_gemv_workspace_bytes(w, 32)
+    assert nb > 0 and nb % (32 * 4096 * 4) == 0
+    assert rra.rra_batched_gemv_workspace_bytes(w, 0) == 0
+
+
+def test_flash_decode_sizes_and_validation():
+    # chunk chosen from (m, nkv, max_len); partials are m*nq*nc*(hd+1) floats
+    c = rra.rra_flash_decode_chunk(32, 8, 8192, 0)
+    assert c in (32, 64, 128, 256, 512)
+    nc = -(-8192 // c)
+    assert rra.rra_flash_decode_workspace_bytes(32, 32, 8, 128, 8192, 0) == 32 * 32 * nc * 129 * 4
+    assert rra.rra_flash_decode_workspace_bytes(1, 14, 2, 64, 768, 64) == 14 * 12 * 65 * 4
+    assert rra.rra_flash_decode_workspace_bytes(1, 12, 8, 128, 64, 0) == 0   # nq % nkv
+    assert rra.rra_flash_decode_workspace_bytes(1, 8, 1, 96, 64, 0) == 0     # hd
+    assert rra.rra_flash_decode_workspace_bytes(1, 8, 1, 64, 64, 48) == 0    # chunk % 32
+    t = torch.zeros(4)
+    with pytest.raises(rra.RraError, match="group size|nq/nkv"):
+        rra.rra_flash_decode(t, t, t, t, t, 1, 18, 2, 64, 16, 0, t)
+
+
+def test_kv_scatter_and_step_kernels_validate_before_launch():
+    t = torch.zeros(4)
+    with pytest.raises(rra.RraError, match="1..32"):
+        rra.rra_kv_scatter(t, t, t, t, t, 0, 1, 64, 16)
+    with pytest.raises(rra.RraError):
+        rra.rra_rmsnorm(t, t, t, 1, 0, 1e-6)
+    with pytest.raises(rra.RraError):
+        rra.rra_rope(t, t, t, 1, 1, 63, 16)
+    with pytest.raises(rra.RraError):
+        rra.rra_swiglu(t, t, t, 40, 4)
+    ws = torch.zeros(4)
+    with pytest.raises(rra.RraError) as e:
+        rra.rra_argmax(t, t, 2, 100000, ws)   # workspace too small
+    assert e.value.status == rra.RRA_ENOTINIT
+
+
+def test_model_descriptor_validation():
+    t = torch.zeros(16)
+    w = _fake_weight("q4", 64, 128)
+    layer = dict(wqkv=w, wo=w, wgu=w, wd=w, attn_gamma=t, ffn_gamma=t, k_cache=t, v_cache=t)
+    with pytest.raises(rra.RraError, match="shape"):
+        rra.Model(n_layers=1, hidden=128, n_heads=2, n_kv_heads=1, head_dim=64, intermediate=256,
+                  vocab=64, rms_eps=1e-6, rope_theta=1e4, max_len=16, m_max=1, layers=[layer],
+                  out_gamma=t, lm_head=w)
+    with pytest.raises(rra.RraError, match="head_dim"):
+        rra.Model(n_layers=1, hidden=128, n_heads=2, n_kv_heads=1, head_dim=96, intermediate=256,
+                  vocab=64, rms_eps=1e-6, rope_theta=1e4, max_len=16, m_max=1, layers=[layer],
+                  out_gamma=t, lm_head=w)
+    with pytest.raises(rra.RraError, match="m_max"):
+        rra.Model(n_layers=1, hidden=128, n_heads=2, n_kv_heads=1, head_dim=64, intermediate=256,
+                  vocab=64, rms_eps=1e-6, rope_theta=1e4, max_len=16, m_max=40, layers=[layer],
+                  out_gamma=t, lm_head=w)
+
+
+def test_decode_step_rejects_null_model():
+    st = rra.lib.rra_decode_step(None, None, None, None, None, None, 1, 0, None)
+    assert st == rra.RRA_ENOTINIT
