@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fd-reps", type=int, default=20)
+    ap.add_argument("--only-m1", action="store_true", help="run only the M=1 line")
+    ap.add_argument("--m1-steps", type=int, default=256)
     return ap.parse_args()
 
 
@@ -177,6 +179,9 @@ def main():
         sys.exit(2)
     import synth
     import quantized_gemv_flash_amd as rra  # noqa: F401  (fails loudly if not built)
+    if args.only_m1:
+        print(json.dumps({"m1": m1_line(args.m1_steps)}), flush=True)
+        return
 
     S = synth.LLAMA3_8B_Q4
     m, steps = S.m, args.steps
@@ -212,7 +217,7 @@ def main():
     del dd, W
     torch.cuda.empty_cache()
     if not args.no_m1:
-        m1 = m1_line()
+        m1 = m1_line(args.m1_steps)
         log(f"m1 {m1}")
 
     out = {

@@ -111,8 +111,12 @@ rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uint16_t *scal
  *       activations enter the matrix cores as an fp16 high part plus an fp16
  *       low part).
  * y   : device fp32 [m][n]; must not overlap x.
- * ws  : device scratch for split-K partial sums, or NULL (then K is not split);
- *       when non-NULL ws_bytes must be >= rra_batched_gemv_workspace_bytes.
+ * ws  : device scratch, ws_bytes >= rra_batched_gemv_workspace_bytes(w, m),
+ *       owned by the caller and reused freely after the call completes on s.
+ *       It holds the activations converted once into the matrix-core operand
+ *       image (Q8/Q4) and the split-K partial sums (when K is split).  May be
+ *       NULL only when that size is 0; otherwise a missing or short ws gives
+ *       RRA_ENOTINIT and nothing is launched.
  * Results do not depend on the stream, the call or the run (no atomics). */
 size_t rra_batched_gemv_workspace_bytes(const rra_weight *w, int32_t m);
 rra_status rra_batched_gemv(const rra_weight *w, const float *x, float *y, int32_t m,

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librra.so")
 SOURCES = ["gemv.hip", "attention.hip", "elementwise.hip", "model.cpp"]
-HEADERS = [os.path.join(CSRC, "rra_internal.h"), os.path.join(INCLUDE, "rra.h")]
+HEADERS = [os.path.join(CSRC, h) for h in ("rra_internal.h", "frag.h")] + [os.path.join(INCLUDE, "rra.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -27,6 +27,9 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source extra flags: the GEMV keeps MFMA accumulators in ordinary VGPRs,
+# so the per-block scale FMAs read them without v_accvgpr_read copies.
+EXTRA = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
@@ -35,7 +38,7 @@ def _compile(src: str) -> str:
     dep = max([os.path.getmtime(path)] + [os.path.getmtime(h) for h in HEADERS])
     if os.path.exists(obj) and os.path.getmtime(obj) >= dep and os.environ.get("RRA_REBUILD") != "1":
         return obj
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", path, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

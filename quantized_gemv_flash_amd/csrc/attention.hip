@@ -16,6 +16,7 @@
 // then a cross-wave sum in LDS.  The grid covers max_len / chunk chunks and a
 // workgroup past seq_len returns at once, so a captured graph stays valid as
 // positions advance.
+#include "frag.h"
 #include "rra_internal.h"
 
 #include <algorithm>
@@ -61,6 +62,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
     const uint32_t *__restrict__ seq_len, float *__restrict__ part_o,
     float *__restrict__ part_lse, int nq, int nkv, int max_len, int chunk, int nc_max) {
+    constexpr int GP = (G + 3) & ~3;  // probabilities stored key-major, G padded to 4
     const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
     const int L = (int)min(seq_len[m], (uint32_t)max_len);
     const int t0 = c * chunk;
@@ -68,8 +70,8 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const int n = min(chunk, L - t0);
 
     extern __shared__ float smem[];
-    float *sc = smem;                 // [G][chunk] scores, then probabilities
-    float *red = smem + G * chunk;    // [4 waves][G][HD]
+    float *sc = smem;                 // [chunk][GP] scores, then probabilities
+    float *red = smem + GP * chunk;   // [4 waves][G][HD]
     float *stat = red + 4 * G * HD;   // [G] max, [G] sum
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -77,8 +79,9 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *K = kc + row0 * HD;
     const float *V = vc + row0 * HD;
 
-    // ---- scores
+    // ---- scores: 8 lanes per cached row, 4 rows per lane per round
     constexpr int F4 = HD / 32;  // 128-bit loads per lane per row
+    constexpr int UK = 4;
     const int e = lane & 7, ks = lane >> 3;
     const float qscale = 1.0f / sqrtf((float)HD);
     float4 qr[G][F4];
@@ -91,33 +94,29 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             qr[h][i] = make_float4(v.x * qscale, v.y * qscale, v.z * qscale, v.w * qscale);
         }
     }
-    for (int base = 0; base < n; base += 64) {
-        float4 kv[2][F4];
-        int tt[2];
+    for (int base = 0; base < n; base += 32 * UK) {
+        float4 kv[UK][F4];
+        int tt[UK];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < UK; ++u) {
             tt[u] = base + u * 32 + wave * 8 + ks;
-            if (tt[u] < n) {
+            const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
 #pragma unroll
-                for (int i = 0; i < F4; ++i)
-                    kv[u][i] = *reinterpret_cast<const float4 *>(K + (size_t)tt[u] * HD +
-                                                                 4 * (e + 8 * i));
-            }
+            for (int i = 0; i < F4; ++i)
+                kv[u][i] = *reinterpret_cast<const float4 *>(K + (size_t)tc * HD + 4 * (e + 8 * i));
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < UK; ++u) {
             float s[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float a = 0.f;
-                if (tt[u] < n) {
 #pragma unroll
-                    for (int i = 0; i < F4; ++i) {
-                        a = fmaf(qr[h][i].x, kv[u][i].x, a);
-                        a = fmaf(qr[h][i].y, kv[u][i].y, a);
-                        a = fmaf(qr[h][i].z, kv[u][i].z, a);
-                        a = fmaf(qr[h][i].w, kv[u][i].w, a);
-                    }
+                for (int i = 0; i < F4; ++i) {
+                    a = fmaf(qr[h][i].x, kv[u][i].x, a);
+                    a = fmaf(qr[h][i].y, kv[u][i].y, a);
+                    a = fmaf(qr[h][i].z, kv[u][i].z, a);
+                    a = fmaf(qr[h][i].w, kv[u][i].w, a);
                 }
                 a += __shfl_xor(a, 1, 64);
                 a += __shfl_xor(a, 2, 64);
@@ -127,7 +126,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             if (tt[u] < n) {
 #pragma unroll
                 for (int h = 0; h < G; ++h)
-                    if (e == (h & 7)) sc[h * chunk + tt[u]] = s[h];
+                    if (e == (h & 7)) sc[tt[u] * GP + h] = s[h];
             }
         }
     }
@@ -136,12 +135,12 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     // ---- per-head max, exponentials, sum
     for (int h = wave; h < G; h += 4) {
         float mx = -INFINITY;
-        for (int t = lane; t < n; t += 64) mx = fmaxf(mx, sc[h * chunk + t]);
+        for (int t = lane; t < n; t += 64) mx = fmaxf(mx, sc[t * GP + h]);
         mx = wave_max(mx);
         float l = 0.f;
         for (int t = lane; t < n; t += 64) {
-            const float p = expf(sc[h * chunk + t] - mx);
-            sc[h * chunk + t] = p;
+            const float p = expf(sc[t * GP + h] - mx);
+            sc[t * GP + h] = p;
             l += p;
         }
         l = wave_sum(l);
@@ -152,30 +151,39 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     }
     __syncthreads();
 
-    // ---- probability-weighted values
-    constexpr int LPK = HD / 4, KPW = 64 / LPK;
+    // ---- probability-weighted values: hd/4 lanes per row, 8 rows per lane in flight
+    constexpr int LPK = HD / 4, KPW = 64 / LPK, UV = 8;
     const int d4 = lane % LPK, kslot = lane / LPK;
     float4 o[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) o[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t = wave * KPW + kslot; t < n; t += 4 * KPW * 2) {
-        const int t2 = t + 4 * KPW;
-        const float4 v0 = *reinterpret_cast<const float4 *>(V + (size_t)t * HD + 4 * d4);
-        float4 v1 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t2 < n) v1 = *reinterpret_cast<const float4 *>(V + (size_t)t2 * HD + 4 * d4);
+    for (int tb = wave * KPW + kslot; tb < n; tb += 4 * KPW * UV) {
+        float4 v[UV];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float p0 = sc[h * chunk + t];
-            o[h].x = fmaf(p0, v0.x, o[h].x);
-            o[h].y = fmaf(p0, v0.y, o[h].y);
-            o[h].z = fmaf(p0, v0.z, o[h].z);
-            o[h].w = fmaf(p0, v0.w, o[h].w);
-            if (t2 < n) {
-                const float p1 = sc[h * chunk + t2];
-                o[h].x = fmaf(p1, v1.x, o[h].x);
-                o[h].y = fmaf(p1, v1.y, o[h].y);
-                o[h].z = fmaf(p1, v1.z, o[h].z);
-                o[h].w = fmaf(p1, v1.w, o[h].w);
+        for (int u = 0; u < UV; ++u) {
+            const int t = min(tb + u * 4 * KPW, n - 1);  // clamped; rows past n are skipped
+            v[u] = *reinterpret_cast<const float4 *>(V + (size_t)t * HD + 4 * d4);
+        }
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int t = tb + u * 4 * KPW;
+            if (t < n) {
+                float p[GP];
+#pragma unroll
+                for (int h4 = 0; h4 < GP; h4 += 4) {
+                    const float4 pv = *reinterpret_cast<const float4 *>(sc + t * GP + h4);
+                    p[h4] = pv.x;
+                    p[h4 + 1] = pv.y;
+                    p[h4 + 2] = pv.z;
+                    p[h4 + 3] = pv.w;
+                }
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    o[h].x = fmaf(p[h], v[u].x, o[h].x);
+                    o[h].y = fmaf(p[h], v[u].y, o[h].y);
+                    o[h].z = fmaf(p[h], v[u].z, o[h].z);
+                    o[h].w = fmaf(p[h], v[u].w, o[h].w);
+                }
             }
         }
     }
@@ -207,43 +215,67 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
 }
 
 // out[m][h] = sum_c w_c o~_c / sum_c w_c, w_c = e^(lse_c - max lse), over the
-// chunks that hold rows of the sequence.  One wave per (head, sequence).
+// chunks that hold rows of the sequence.  One wave per (head, sequence).  With
+// fo.img set, the head's slice is also written as the output projection's
+// activation image (the last head also zeros the groups in [nq hd, kpad)).
 template <int HD>
 __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__ part_o,
                                                        const float *__restrict__ part_lse,
                                                        const uint32_t *__restrict__ seq_len,
                                                        float *__restrict__ out, int nq, int max_len,
-                                                       int chunk, int nc_max) {
+                                                       int chunk, int nc_max, FragOut fo) {
+    __shared__ float so[HD];
     const int h = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
-    const int L = (int)min(seq_len[m], (uint32_t)max_len);
-    if (L <= 0) return;
-    const int nc = (L + chunk - 1) / chunk;
-    const float *lse = part_lse + ((size_t)m * nq + h) * nc_max;
-    float mx = -INFINITY;
-    for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
-    mx = wave_max(mx);
     constexpr int PER = HD / 64;
+    const int L = (int)min(seq_len[m], (uint32_t)max_len);
     float acc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-    float wsum = 0.f;
-    const float *po = part_o + ((size_t)m * nq + h) * nc_max * HD;
-    for (int c = 0; c < nc; ++c) {
-        const float w = expf(lse[c] - mx);
-        wsum += w;
+    if (L > 0) {
+        const int nc = (L + chunk - 1) / chunk;
+        const float *lse = part_lse + ((size_t)m * nq + h) * nc_max;
+        float mx = -INFINITY;
+        for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
+        mx = wave_max(mx);
+        float wsum = 0.f;
+        const float *po = part_o + ((size_t)m * nq + h) * nc_max * HD;
+        for (int c = 0; c < nc; ++c) {
+            const float w = expf(lse[c] - mx);
+            wsum += w;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, po[(size_t)c * HD + lane + 64 * j], acc[j]);
+            for (int j = 0; j < PER; ++j)
+                acc[j] = fmaf(w, po[(size_t)c * HD + lane + 64 * j], acc[j]);
+        }
+        float *o = out + ((size_t)m * nq + h) * HD;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            acc[j] /= wsum;
+            o[lane + 64 * j] = acc[j];
+        }
     }
-    float *o = out + ((size_t)m * nq + h) * HD;
+    if (!fo.img) return;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) o[lane + 64 * j] = acc[j] / wsum;
+    for (int j = 0; j < PER; ++j) so[lane + 64 * j] = acc[j];
+    __syncthreads();
+    if (lane < HD / 8) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = so[lane * 8 + e];
+        write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, h * HD + lane * 8, v);
+    }
+    if (h == nq - 1) {
+        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k0 = nq * HD + lane * 8; k0 < fo.kpad; k0 += 64 * 8)
+            write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, z);
+    }
 }
 
 template <int HD, int G>
 rra_status launch_chunk(const float *q, const float *kc, const float *vc, const uint32_t *lens,
                         float *po, float *pl, int m, int nq, int nkv, int max_len, int chunk,
                         int nc_max, hipStream_t s) {
-    const size_t shm = sizeof(float) * ((size_t)G * chunk + 4 * G * HD + 2 * G);
+    constexpr int GP = (G + 3) & ~3;
+    const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * G);
     hipLaunchKernelGGL((fd_chunk_kernel<HD, G>), dim3(nc_max, nkv, m), dim3(256), shm, s, q, kc,
                        vc, lens, po, pl, nq, nkv, max_len, chunk, nc_max);
     return check_launch("fd_chunk_kernel");
@@ -288,7 +320,9 @@ rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_
 
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
-                               int hd, int max_len, int chunk, float *part, hipStream_t s) {
+                               int hd, int max_len, int chunk, float *part, hipStream_t s,
+                               const FragOut *fo) {
+    const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
     const int nc_max = (int)cdiv(max_len, chunk);
     float *po = part;
@@ -301,10 +335,10 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                     chunk, nc_max, s));
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,
-                           out, nq, max_len, chunk, nc_max);
+                           out, nq, max_len, chunk, nc_max, img);
     else
         hipLaunchKernelGGL(fd_reduce_kernel<64>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len, out,
-                           nq, max_len, chunk, nc_max);
+                           nq, max_len, chunk, nc_max, img);
     return check_launch("fd_reduce_kernel");
 }
 

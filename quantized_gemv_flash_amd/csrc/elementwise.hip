@@ -9,12 +9,57 @@
 //   SwiGLU   silu(gate) * up, silu(z) = z / (1 + e^-z)
 //   argmax   lowest index among the maximal logits ([reduces] gpu_argmax:
 //            block-level (max, index) pairs, then a final reduce)
+#include "frag.h"
 #include "rra_internal.h"
 
 #include <cmath>
 
 namespace rra {
 namespace {
+
+// Sum over K-split partial planes, 4 independent loads in flight per step.
+__device__ __forceinline__ float sum_splits(const float *__restrict__ p, int split,
+                                           long long stride) {
+    float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
+    int s = 0;
+    for (; s + 4 <= split; s += 4) {
+        a += p[(size_t)s * stride];
+        b += p[(size_t)(s + 1) * stride];
+        c += p[(size_t)(s + 2) * stride];
+        d += p[(size_t)(s + 3) * stride];
+    }
+    for (; s < split; ++s) a += p[(size_t)s * stride];
+    return (a + b) + (c + d);
+}
+
+// Same over 4 consecutive columns (16-byte loads).
+__device__ __forceinline__ float4 sum_splits4(const float *__restrict__ p, int split,
+                                              long long stride) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    int s = 0;
+    for (; s + 2 <= split; s += 2) {
+        const float4 u = *reinterpret_cast<const float4 *>(p + (size_t)s * stride);
+        const float4 v = *reinterpret_cast<const float4 *>(p + (size_t)(s + 1) * stride);
+        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+        b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+    }
+    if (s < split) {
+        const float4 u = *reinterpret_cast<const float4 *>(p + (size_t)s * stride);
+        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    }
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+__device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -48,21 +93,48 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x,
     for (int i = threadIdx.x; i < h; i += blockDim.x) o[i] = xr[i] * inv * gamma[i];
 }
 
-__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
-    const float *__restrict__ part, int split, long long split_stride, float *__restrict__ x,
-    const float *__restrict__ gamma, float *__restrict__ u, int h, float eps) {
+// Grid (ceil(h / 2048), m), 256 threads, one 8-column group per thread:
+// x[m][c] += sum_s part[s][m][c] (split may be 0: x unchanged); the chunk's
+// sum of squares of the updated row -> ss[m * nchunks + chunk]; xg = x * gamma
+// (fp32) and, when fo.img is set, its GEMV activation image (zeros for the
+// groups in [h, kpad)).  The next GEMV forms RMSNorm from ss (NormIn).
+__global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restrict__ part, int split,
+                                                          long long split_stride,
+                                                          float *__restrict__ x,
+                                                          float *__restrict__ ss,
+                                                          const float *__restrict__ gamma,
+                                                          float *__restrict__ xg, int h,
+                                                          FragOut fo) {
     __shared__ float sh[4];
-    const size_t base = (size_t)blockIdx.x * h;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < h; i += blockDim.x) {
-        float v = x[base + i];
-        for (int s = 0; s < split; ++s) v += part[(size_t)s * split_stride + base + i];
-        x[base + i] = v;
-        ss = fmaf(v, v, ss);
+    const int ch = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
+    const int k0 = (ch * 256 + threadIdx.x) * 8;
+    const size_t base = (size_t)m * h + k0;
+    float sq = 0.f;
+    if (k0 < h) {
+        float v[8];
+        load8(x + base, v);
+        if (split > 0) {
+            const float4 a = sum_splits4(part + base, split, split_stride);
+            const float4 b = sum_splits4(part + base + 4, split, split_stride);
+            v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+            v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+            store8(x + base, v);
+        }
+        float gv[8];
+        load8(gamma + k0, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sq = fmaf(v[e], v[e], sq);
+            gv[e] *= v[e];
+        }
+        store8(xg + base, gv);
+        if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, gv);
+    } else if (fo.img && k0 < fo.kpad) {
+        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, z);
     }
-    ss = block_sum(ss, sh);
-    const float inv = 1.0f / sqrtf(ss / (float)h + eps);
-    for (int i = threadIdx.x; i < h; i += blockDim.x) u[base + i] = x[base + i] * inv * gamma[i];
+    sq = block_sum(sq, sh);
+    if (threadIdx.x == 0) ss[(size_t)m * nch + ch] = sq;
 }
 
 // Grid (m, nq + 2 nkv heads), hd/2 threads: thread j handles pair (j, j + hd/2).
@@ -76,11 +148,8 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
     const uint32_t p = pos[m];
     const bool ok = p < (uint32_t)max_len;
     const size_t b = (size_t)m * nrow + (size_t)head * hd;
-    float a = 0.f, c = 0.f;
-    for (int s = 0; s < split; ++s) {
-        a += part[(size_t)s * split_stride + b + j];
-        c += part[(size_t)s * split_stride + b + j + half];
-    }
+    float a = sum_splits(part + b + j, split, split_stride);
+    float c = sum_splits(part + b + j + half, split, split_stride);
     if (head < nq + nkv && ok) {
         const float cs = table[((size_t)p * half + j) * 2], sn = table[((size_t)p * half + j) * 2 + 1];
         const float ra = a * cs - c * sn, rc = a * sn + c * cs;
@@ -126,19 +195,31 @@ __global__ void swiglu_kernel(const float *gate, const float *up, float *out, in
     out[i] = silu(gate[m * gate_stride + j]) * up[m * up_stride + j];
 }
 
+// act[m][j] = silu(sum_s part[s][m][j]) * sum_s part[s][m][inter + j], one
+// 8-column group per thread; also the down GEMV's activation image.
+// Grid (ceil(kpad / 8 / 256), m).
 __global__ void swiglu_reduce_kernel(const float *__restrict__ part, int split,
                                      long long split_stride, float *__restrict__ act, int inter,
-                                     long long total) {
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const long long m = i / inter, j = i - m * inter;
-    const size_t gi = (size_t)m * 2 * inter + j, ui = gi + inter;
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < split; ++s) {
-        g += part[(size_t)s * split_stride + gi];
-        u += part[(size_t)s * split_stride + ui];
+                                     FragOut fo) {
+    const int m = blockIdx.y;
+    const int k0 = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (k0 < inter) {
+        const size_t gi = (size_t)m * 2 * inter + k0, ui = gi + inter;
+        float v[8];
+        const float4 g0 = sum_splits4(part + gi, split, split_stride);
+        const float4 g1 = sum_splits4(part + gi + 4, split, split_stride);
+        const float4 u0 = sum_splits4(part + ui, split, split_stride);
+        const float4 u1 = sum_splits4(part + ui + 4, split, split_stride);
+        v[0] = silu(g0.x) * u0.x; v[1] = silu(g0.y) * u0.y;
+        v[2] = silu(g0.z) * u0.z; v[3] = silu(g0.w) * u0.w;
+        v[4] = silu(g1.x) * u1.x; v[5] = silu(g1.y) * u1.y;
+        v[6] = silu(g1.z) * u1.z; v[7] = silu(g1.w) * u1.w;
+        store8(act + (size_t)m * inter + k0, v);
+        if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, v);
+    } else if (fo.img && k0 < fo.kpad) {
+        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, z);
     }
-    act[i] = silu(g) * u;
 }
 
 __global__ void embed_gather_kernel(const float *__restrict__ embed, const uint32_t *__restrict__ tok,
@@ -231,12 +312,12 @@ rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m,
     return check_launch("rmsnorm_kernel");
 }
 
-rra_status launch_residual_rmsnorm(const float *part, int split, size_t split_stride, float *x,
-                                   const float *gamma, float *u, int m, int h, float eps,
-                                   hipStream_t s) {
-    hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(m), dim3(256), 0, s, part, split,
-                       (long long)split_stride, x, gamma, u, h, eps);
-    return check_launch("residual_rmsnorm_kernel");
+rra_status launch_residual_ss(const float *part, int split, size_t split_stride, float *x,
+                              float *ss, const float *gamma, float *xg, int m, int h,
+                              const FragOut &fo, hipStream_t s) {
+    hipLaunchKernelGGL(residual_ss_kernel, dim3((unsigned)ss_parts(h), m), dim3(256), 0, s, part,
+                       split, (long long)split_stride, x, ss, gamma, xg, h, fo);
+    return check_launch("residual_ss_kernel");
 }
 
 rra_status launch_qkv_post(const float *part, int split, size_t split_stride, const uint32_t *pos,
@@ -265,10 +346,10 @@ rra_status launch_swiglu(const float *gate, const float *up, float *out, int m, 
 }
 
 rra_status launch_swiglu_reduce(const float *part, int split, size_t split_stride, float *act,
-                                int m, int inter, hipStream_t s) {
-    const long long total = (long long)m * inter;
-    hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
-                       part, split, (long long)split_stride, act, inter, total);
+                                int m, int inter, const FragOut &fo, hipStream_t s) {
+    const int groups = (int)cdiv(std::max(inter, fo.img ? fo.kpad : inter), 8);
+    hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)cdiv(groups, 256), m), dim3(256), 0, s,
+                       part, split, (long long)split_stride, act, inter, fo);
     return check_launch("swiglu_reduce_kernel");
 }
 

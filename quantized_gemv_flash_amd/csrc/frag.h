@@ -1,0 +1,77 @@
+// frag.h -- the activation "B-operand image" shared by the GEMV (consumer) and
+// the kernels that produce GEMV inputs.
+//
+// The Q8/Q4 GEMV multiplies on the matrix cores with the fp32 activation x
+// split as x = hi + lo (hi = fp16(x), lo = fp16(x - hi)).  Instead of every
+// GEMV workgroup converting x again, the producer of a GEMV input writes it
+// once in the exact layout the GEMV copies into LDS:
+//
+//   per K tile kt (KT = 128 for Q4, 64 for Q8; NB = KT / 32 blocks), for
+//   block b, column tile c (16 sequences), part h (0 = hi, 1 = lo): a 1 KiB
+//   fragment of 64 slots x 16 bytes at
+//       ((((kt * NB + b) * CT + c) * 2 + h) * 1024 + slot * 16;
+//   slot frag_slot(j, r, b) holds the 8 fp16 values of sequence 16c + r,
+//   elements kt*KT + 32b + 8j + [0..8) in the order the weight operand uses
+//   (Q4: 0,2,4,6,1,3,5,7; Q8: 0..7).
+//
+// CT = 1 for M <= 16 sequences, 2 for M <= 32.  Elements k >= K up to the K
+// tile end must be written as zeros.
+#pragma once
+
+#include "rra_internal.h"
+
+namespace rra {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+inline int frag_ct(int m) { return m > 16 ? 2 : 1; }
+inline size_t frag_image_bytes(int fmt, int ct, int64_t k) {
+    return (size_t)cdiv(k, tile_k(fmt)) * (size_t)tile_blocks(fmt) * (size_t)ct * 2 * 1024;
+}
+
+// LDS/image slot of B-operand lane (j, r) (lane = 16j + r) in the fragment of
+// block b.  A 16-lane read phase (fixed j) is a permutation of 16 consecutive
+// slots; a 16-lane write phase covering every (b, j) of one row r hits 16
+// distinct bank groups.
+template <int FMT>
+__device__ __forceinline__ int frag_slot(int j, int r, int b) {
+    const int swz = (FMT == RRA_Q4) ? (j * 4 + b) : (j * 4 + b * 2);
+    return j * 16 + ((r ^ swz) & 15);
+}
+
+// Splits 8 consecutive fp32 activations (k order) into hi/lo fp16 operands.
+template <int FMT>
+__device__ __forceinline__ void split8(const float (&v)[8], half8_t &hi, half8_t &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int src = (FMT == RRA_Q4) ? ((e < 4) ? 2 * e : 2 * (e - 4) + 1) : e;
+        const _Float16 h = (_Float16)v[src];
+        hi[e] = h;
+        lo[e] = (_Float16)(v[src] - (float)h);
+    }
+}
+
+// Writes the group x[m][k0 .. k0+8) (k0 % 8 == 0) into an image with `ct`
+// column tiles.
+template <int FMT>
+__device__ __forceinline__ void write_frag8(uint8_t *img, int ct, int m, int k0,
+                                            const float (&v)[8]) {
+    constexpr int KT = (FMT == RRA_Q4) ? 128 : 64, NB = KT / 32;
+    const int kt = k0 / KT, kk = k0 - kt * KT, b = kk >> 5, j = (kk & 31) >> 3;
+    half8_t hi, lo;
+    split8<FMT>(v, hi, lo);
+    const size_t base = ((((size_t)kt * NB + b) * ct + (m >> 4)) * 2) * 1024 +
+                        (size_t)frag_slot<FMT>(j, m & 15, b) * 16;
+    *reinterpret_cast<half8_t *>(img + base) = hi;
+    *reinterpret_cast<half8_t *>(img + base + 1024) = lo;
+}
+
+__device__ __forceinline__ void write_frag8_fmt(int fmt, uint8_t *img, int ct, int m, int k0,
+                                                const float (&v)[8]) {
+    if (fmt == RRA_Q4)
+        write_frag8<RRA_Q4>(img, ct, m, k0, v);
+    else
+        write_frag8<RRA_Q8>(img, ct, m, k0, v);
+}
+
+}  // namespace rra

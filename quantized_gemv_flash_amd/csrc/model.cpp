@@ -15,6 +15,7 @@
 #include <string>
 #include <vector>
 
+#include "frag.h"
 #include "rra_internal.h"
 
 namespace rra {
@@ -170,10 +171,11 @@ struct rra_model {
     std::vector<rra_layer_desc> layers;
     int chunk = 0;
     // workspace carve-up
-    float *u = nullptr, *part = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr;
+    float *ss = nullptr, *xg = nullptr, *part = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr;
     float *fd = nullptr, *logits = nullptr, *rope = nullptr;
     uint32_t *lens = nullptr, *err = nullptr;
     void *argmax_ws = nullptr;
+    uint8_t *img = nullptr;  // activation image of the next Q8/Q4 GEMV
     // per-M plans (index m)
     GemvPlan plan_qkv[RRA_M_MAX + 1], plan_o[RRA_M_MAX + 1], plan_gu[RRA_M_MAX + 1],
         plan_d[RRA_M_MAX + 1], plan_lm[RRA_M_MAX + 1];
@@ -185,8 +187,24 @@ struct rra_model {
 namespace {
 
 struct Layout {
-    size_t u, part, q, lens, attn, act, fd, logits, argmax, rope, err, total;
+    size_t ss, xg, img, part, q, lens, attn, act, fd, logits, argmax, rope, err, total;
 };
+
+// Largest activation image any GEMV of the model reads (0 if all are fp32).
+size_t image_bytes(const rra_model_desc &d) {
+    const int ct = frag_ct(d.m_max);
+    size_t best = 0;
+    auto need = [&](const rra_weight &w) {
+        if (w.fmt != RRA_F32) best = std::max(best, frag_image_bytes(w.fmt, ct, w.k));
+    };
+    const rra_layer_desc &l = d.layers[0];
+    need(l.wqkv);
+    need(l.wo);
+    need(l.wgu);
+    need(l.wd);
+    need(d.lm_head);
+    return best;
+}
 
 size_t part_floats(const rra_model_desc &d, const rra_layer_desc &l) {
     size_t best = 0;
@@ -211,7 +229,9 @@ Layout layout_of(const rra_model_desc &d, int chunk) {
     const size_t M = (size_t)d.m_max;
     size_t partf = 0;
     for (int i = 0; i < d.n_layers; ++i) partf = std::max(partf, part_floats(d, d.layers[i]));
-    L.u = take(4 * M * d.hidden);
+    L.ss = take(4 * M * ss_parts(d.hidden));
+    L.xg = take(4 * M * d.hidden);
+    L.img = take(image_bytes(d));
     L.part = take(4 * partf);
     L.q = take(4 * M * d.n_heads * d.head_dim);
     L.lens = take(4 * M);
@@ -244,8 +264,8 @@ rra_status validate_desc(const rra_model_desc *d) {
     if (d->n_heads % d->n_kv_heads || d->n_heads / d->n_kv_heads > 8)
         return fail(RRA_EINVAL, "model: n_heads=%d n_kv_heads=%d (need a group size 1..8)",
                     d->n_heads, d->n_kv_heads);
-    if (d->hidden % 4 || d->intermediate % 4)
-        return fail(RRA_EINVAL, "model: hidden and intermediate must be multiples of 4");
+    if (d->hidden % 8 || d->intermediate % 8)
+        return fail(RRA_EINVAL, "model: hidden and intermediate must be multiples of 8");
     if (d->m_max < 1 || d->m_max > RRA_M_MAX)
         return fail(RRA_EINVAL, "model: m_max=%d not in 1..32", d->m_max);
     if (d->max_len < 1) return fail(RRA_EINVAL, "model: max_len=%d", d->max_len);
@@ -264,9 +284,24 @@ rra_status validate_desc(const rra_model_desc *d) {
         RRA_TRY(check_shape(l.wd, H, I, "layer wd"));
         if (!l.attn_gamma || !l.ffn_gamma || !l.k_cache || !l.v_cache)
             return fail(RRA_EINVAL, "layer %d: null gamma or cache", i);
+        const rra_layer_desc &l0 = d->layers[0];
+        if (l.wqkv.fmt != l0.wqkv.fmt || l.wo.fmt != l0.wo.fmt || l.wgu.fmt != l0.wgu.fmt ||
+            l.wd.fmt != l0.wd.fmt)
+            return fail(RRA_EINVAL, "layer %d: weight formats differ from layer 0's", i);
     }
     RRA_TRY(check_shape(d->lm_head, d->vocab, H, "lm_head"));
     return RRA_OK;
+}
+
+// Where the producer of a GEMV's input writes its activation image: nowhere
+// for fp32 weights (the GEMV reads the fp32 rows).
+FragOut image_for(const rra_model *M, const rra_weight &w, int m) {
+    if (w.fmt == RRA_F32) return FragOut{nullptr, 0, 1, 0};
+    const int kt = tile_k(w.fmt);
+    return FragOut{M->img, w.fmt, frag_ct(m), (int)(cdiv(w.k, kt) * kt)};
+}
+const void *gemv_input(const rra_model *M, const rra_weight &w, const float *rows) {
+    return w.fmt == RRA_F32 ? static_cast<const void *>(rows) : M->img;
 }
 
 // Every launch of one decode step, in stream order.
@@ -277,33 +312,46 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, fl
               I = d.intermediate;
     const int nqkv = (nq + 2 * nkv) * hd;
     if (flags & RRA_STEP_GATHER) RRA_TRY(launch_embed_gather(d.embed, tok, x, m, H, d.vocab, s));
-    RRA_TRY(launch_rmsnorm(x, M->layers[0].attn_gamma, M->u, m, H, d.rms_eps, s));
+    const int np = ss_parts(H);
+    const NormIn nrm{M->ss, np, d.rms_eps};
+    // RMSNorm is formed inside each consuming GEMV from per-chunk sums of
+    // squares of x; the first ones come from the step input.  Each producer
+    // also writes the next GEMV's activation image.
+    const rra_layer_desc &L0 = M->layers[0];
+    RRA_TRY(launch_residual_ss(nullptr, 0, 0, x, M->ss, L0.attn_gamma, M->xg, m, H,
+                               image_for(M, L0.wqkv, m), s));
     for (int l = 0; l < d.n_layers; ++l) {
         const rra_layer_desc &L = M->layers[l];
-        const float *next_gamma =
-            (l + 1 < d.n_layers) ? M->layers[l + 1].attn_gamma : d.out_gamma;
         // attention block
         const GemvPlan &pq = M->plan_qkv[m];
-        RRA_TRY(launch_gemv(L.wqkv, pq, M->u, m, M->part, (size_t)m * nqkv, s));
+        RRA_TRY(launch_gemv(L.wqkv, pq, gemv_input(M, L.wqkv, M->xg), m, M->part, (size_t)m * nqkv,
+                            s, &nrm));
         RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
                                 L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd, d.max_len,
                                 s));
+        const FragOut fo_o = image_for(M, L.wo, m);
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
-                                    d.max_len, M->chunk, M->fd, s));
+                                    d.max_len, M->chunk, M->fd, s, &fo_o));
         const GemvPlan &po = M->plan_o[m];
-        RRA_TRY(launch_gemv(L.wo, po, M->attn, m, M->part, (size_t)m * H, s));
-        RRA_TRY(launch_residual_rmsnorm(M->part, po.split, (size_t)m * H, x, L.ffn_gamma, M->u, m,
-                                        H, d.rms_eps, s));
+        RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part, (size_t)m * H, s));
+        RRA_TRY(launch_residual_ss(M->part, po.split, (size_t)m * H, x, M->ss, L.ffn_gamma, M->xg, m,
+                                   H, image_for(M, L.wgu, m), s));
         // feed-forward block
         const GemvPlan &pg = M->plan_gu[m];
-        RRA_TRY(launch_gemv(L.wgu, pg, M->u, m, M->part, (size_t)m * 2 * I, s));
-        RRA_TRY(launch_swiglu_reduce(M->part, pg.split, (size_t)m * 2 * I, M->act, m, I, s));
+        RRA_TRY(launch_gemv(L.wgu, pg, gemv_input(M, L.wgu, M->xg), m, M->part, (size_t)m * 2 * I, s,
+                            &nrm));
+        RRA_TRY(launch_swiglu_reduce(M->part, pg.split, (size_t)m * 2 * I, M->act, m, I,
+                                     image_for(M, L.wd, m), s));
         const GemvPlan &pd = M->plan_d[m];
-        RRA_TRY(launch_gemv(L.wd, pd, M->act, m, M->part, (size_t)m * H, s));
-        RRA_TRY(launch_residual_rmsnorm(M->part, pd.split, (size_t)m * H, x, next_gamma, M->u, m,
-                                        H, d.rms_eps, s));
+        RRA_TRY(launch_gemv(L.wd, pd, gemv_input(M, L.wd, M->act), m, M->part, (size_t)m * H, s));
+        const bool last = l + 1 == d.n_layers;
+        const float *next_gamma = last ? d.out_gamma : M->layers[l + 1].attn_gamma;
+        const rra_weight &next_w = last ? d.lm_head : M->layers[l + 1].wqkv;
+        RRA_TRY(launch_residual_ss(M->part, pd.split, (size_t)m * H, x, M->ss, next_gamma, M->xg,
+                                   m, H, image_for(M, next_w, m), s));
     }
-    RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], M->u, m, logits, 0, s));
+    RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits, 0, s,
+                        &nrm));
     return launch_argmax(logits, tok, m, d.vocab, M->argmax_ws,
                          (flags & RRA_STEP_ADVANCE) ? pos : nullptr, s);
 }
@@ -334,7 +382,9 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     M->d.layers = M->layers.data();
     M->chunk = chunk;
     char *b = static_cast<char *>(ws);
-    M->u = reinterpret_cast<float *>(b + L.u);
+    M->ss = reinterpret_cast<float *>(b + L.ss);
+    M->xg = reinterpret_cast<float *>(b + L.xg);
+    M->img = reinterpret_cast<uint8_t *>(b + L.img);
     M->part = reinterpret_cast<float *>(b + L.part);
     M->q = reinterpret_cast<float *>(b + L.q);
     M->lens = reinterpret_cast<uint32_t *>(b + L.lens);

@@ -55,13 +55,35 @@ struct GemvPlan {
     int kt_per_split = 1;
 };
 GemvPlan gemv_plan(const rra_weight &w, int m);
+// RMSNorm folded into a GEMV.  The GEMV input holds x[m][k] * gamma[k] (the
+// producer applies gamma) and every output of row m is multiplied by
+// inv[m] = 1 / sqrt(ss[m] / K + eps), ss[m] = sum of the `nparts` partial sums
+// of squares of the un-scaled row x[m], ss[m*nparts + p]: since inv[m] is one
+// scalar per row, W (x gamma inv) = inv (W (x gamma)).
+struct NormIn {
+    const float *ss;  // [M][nparts], or nullptr: no norm
+    int nparts;
+    float eps;
+};
 // Enqueues the GEMV; the result (or its K-split partial sums) goes to
-// out[split][m][n] with out_split_stride floats between splits.
-rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const float *x, int m, float *out,
-                       size_t out_split_stride, hipStream_t s);
+// out[split][m][n] with out_split_stride floats between splits.  For Q8/Q4
+// weights `x` is the activation image (frag.h) with frag_ct(m) column tiles;
+// for F32 weights it is fp32 [m][k].
+rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, int m, float *out,
+                       size_t out_split_stride, hipStream_t s, const NormIn *nrm = nullptr);
+// Converts fp32 x [m][k] into the activation image of a Q8/Q4 GEMV.
+rra_status launch_x_to_image(const float *x, uint8_t *img, int fmt, int m, int k, hipStream_t s);
 // y[i][r] = sum over `split` partial planes (+ y[i][r] if accumulate).
 rra_status launch_reduce_splits(const float *part, int split, size_t split_stride, float *y,
                                 int m, int n, hipStream_t s);
+
+// Where a producer writes the next GEMV's activation image (frag.h).
+struct FragOut {
+    uint8_t *img;  // nullptr: no image (fp32 weights)
+    int fmt;       // RRA_Q8 / RRA_Q4
+    int ct;        // column tiles (1 for m <= 16, 2 otherwise)
+    int kpad;      // K rounded up to the K tile; groups in [K, kpad) are zeros
+};
 
 // ------------------------------------------------------------------ attention
 int fd_choose_chunk(int m, int nkv, int max_len, int chunk);
@@ -71,7 +93,8 @@ rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_
                              int max_len, hipStream_t s);
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
-                               int hd, int max_len, int chunk, float *part, hipStream_t s);
+                               int hd, int max_len, int chunk, float *part, hipStream_t s,
+                               const FragOut *fo = nullptr);
 
 // ------------------------------------------------------------------ elementwise
 rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m, int h,
@@ -86,10 +109,14 @@ rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void 
 void rope_table_host(float *table, int max_len, int hd, double theta);
 
 // Fused epilogues used by the decode step.
-// x[i] += sum_s part[s][i]; u[i] = rmsnorm(x[i]) * gamma.
-rra_status launch_residual_rmsnorm(const float *part, int split, size_t split_stride, float *x,
-                                   const float *gamma, float *u, int m, int h, float eps,
-                                   hipStream_t s);
+// x[i] += sum_s part[s][i] (split may be 0); per 2048-column chunk c the sum
+// of squares of the updated row, ss[i * ss_parts(h) + c]; and xg = x * gamma,
+// the input of the next RMSNorm-fused GEMV (fp32, and its image if fo.img).
+// h % 8 == 0.
+rra_status launch_residual_ss(const float *part, int split, size_t split_stride, float *x,
+                              float *ss, const float *gamma, float *xg, int m, int h,
+                              const FragOut &fo, hipStream_t s);
+inline int ss_parts(int h) { return (int)cdiv(h, 2048); }
 // qkv = sum_s part[s]; rope(q, k) at pos; q -> q_out [m][nq][hd]; k, v rows
 // scattered into the caches at pos; seq_len[i] = min(pos[i] + 1, max_len);
 // pos >= max_len sets *err.
@@ -97,9 +124,10 @@ rra_status launch_qkv_post(const float *part, int split, size_t split_stride, co
                            const float *table, float *q_out, float *k_cache, float *v_cache,
                            uint32_t *seq_len, uint32_t *err, int m, int nq, int nkv, int hd,
                            int max_len, hipStream_t s);
-// act[i][j] = silu(sum_s part[s][i][j]) * sum_s part[s][i][inter + j].
+// act[i][j] = silu(sum_s part[s][i][j]) * sum_s part[s][i][inter + j], and
+// its activation image for the down GEMV.
 rra_status launch_swiglu_reduce(const float *part, int split, size_t split_stride, float *act,
-                                int m, int inter, hipStream_t s);
+                                int m, int inter, const FragOut &fo, hipStream_t s);
 rra_status launch_embed_gather(const float *embed, const uint32_t *tok, float *x, int m, int h,
                                int vocab, hipStream_t s);
 

@@ -58,7 +58,7 @@ class Run:
 
 def compare_step(gpu, orc_out, what):
     ids, hid, logits = gpu
-    assert_close(hid, orc_out["hidden"], what=f"{what} hidden")
+    assert_close(hid, orc_out["hidden"], what=f"{what} hidden", row_scale=True)
     assert_close(logits, orc_out["logits"], rtol=0.0, atol=LOGIT_ATOL, what=f"{what} logits")
     assert_tokens(ids, orc_out["tok"], orc_out["gap"], orc_out["logits"], what=f"{what} tokens")
 

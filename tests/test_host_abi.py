@@ -64,12 +64,27 @@ def test_gemv_rejects_k_not_multiple_of_32():
 
 
 def test_gemv_workspace_sizes():
-    # A long-K matrix with few rows is split over K; its workspace holds the
-    # partial sums of every split.
+    # Q8/Q4: the activation image (per 32-column block, 16 sequences per column
+    # tile, an fp16 high and low part: 2 x 1 KiB), then the split-K partial sums.
     w = _fake_weight("q4", 4096, 14336)
     nb = rra.rra_batched_gemv_workspace_bytes(w, 32)
-    assert nb > 0 and nb % (32 * 4096 * 4) == 0
+    img = (14336 // 32) * 2 * 2 * 1024
+    assert nb > img and (nb - img) % (32 * 4096 * 4) == 0
     assert rra.rra_batched_gemv_workspace_bytes(w, 0) == 0
+    # a short matrix is not split: the image alone (one column tile for m <= 16)
+    w = _fake_weight("q8", 16, 64)
+    assert rra.rra_batched_gemv_workspace_bytes(w, 1) == 2 * 1 * 2 * 1024
+    assert rra.rra_batched_gemv_workspace_bytes(w, 17) == 2 * 2 * 2 * 1024
+    w = _fake_weight("f32", 16, 64, rra.RRA_PLANAR)
+    assert rra.rra_batched_gemv_workspace_bytes(w, 1) == 0
+
+
+def test_gemv_requires_workspace():
+    w = _fake_weight("q8", 64, 128)
+    x = torch.zeros(4)
+    with pytest.raises(rra.RraError) as e:
+        rra.rra_batched_gemv(w, x, x, 1)
+    assert e.value.status == rra.RRA_ENOTINIT and "workspace" in str(e.value)
 
 
 def test_flash_decode_sizes_and_validation():
