@@ -12,7 +12,7 @@
 //       ((((kt * NB + b) * CT + c) * 2 + h) * 1024 + slot * 16;
 //   slot frag_slot(j, r, b) holds the 8 fp16 values of sequence 16c + r,
 //   elements kt*KT + 32b + 8j + [0..8) in the order the weight operand uses
-//   (Q4: 0,2,4,6,1,3,5,7; Q8: 0..7).
+//   (Q4: 0,4,1,5,2,6,3,7; Q8: 0..7).
 //
 // CT = 1 for M <= 16 sequences, 2 for M <= 32.  Elements k >= K up to the K
 // tile end must be written as zeros.
@@ -44,7 +44,7 @@ template <int FMT>
 __device__ __forceinline__ void split8(const float (&v)[8], half8_t &hi, half8_t &lo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int src = (FMT == RRA_Q4) ? ((e < 4) ? 2 * e : 2 * (e - 4) + 1) : e;
+        const int src = (FMT == RRA_Q4) ? (e >> 1) + 4 * (e & 1) : e;
         const _Float16 h = (_Float16)v[src];
         hi[e] = h;
         lo[e] = (_Float16)(v[src] - (float)h);

@@ -56,6 +56,27 @@ __device__ __forceinline__ uint32_t u32_at(const uint4 &v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// Q4: one dword = 8 nibbles of a group (byte u holds element 2u low, 2u+1
+// high) -> fp16 (q - 8) in element order [0, 4, 1, 5, 2, 6, 3, 7].  Each pair
+// comes from one v_and_or_b32 that drops two nibbles into the mantissas of
+// the fp16 pair 1024 + n (low nibbles) or 1024 + 16 n (high nibbles), and one
+// packed fp16 op that maps it to n - 8 (exact: small integers).
+__device__ __forceinline__ half8_t dequant_q4(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    const half2_t lo_a = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | 0x64006400u);
+    const half2_t hi_a = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | 0x64006400u);
+    const half2_t lo_b = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | 0x64006400u);
+    const half2_t hi_b = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | 0x64006400u);
+    const half2_t k1032 = {(_Float16)1032.f, (_Float16)1032.f};
+    const half2_t r16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2_t k72 = {(_Float16)-72.f, (_Float16)-72.f};
+    const half2_t e04 = lo_a - k1032;
+    const half2_t e15 = __builtin_elementwise_fma(hi_a, r16, k72);
+    const half2_t e26 = lo_b - k1032;
+    const half2_t e37 = __builtin_elementwise_fma(hi_b, r16, k72);
+    return half8_t{e04[0], e04[1], e15[0], e15[1], e26[0], e26[1], e37[0], e37[1]};
+}
+
 // Two fp16 values 1024 + byte from bytes 0,1 (pair_lo) or 2,3 (pair_hi) of v:
 // one v_perm_b32 against 0x64 bytes (fp16 0x64XX = 1024 + XX for XX < 256).
 // v_perm_b32 selector bytes 0-3 pick bytes of its second operand, 4-7 of its
@@ -65,18 +86,6 @@ __device__ __forceinline__ uint32_t pair_lo(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t v) {
     return __builtin_amdgcn_perm(v, 0x64646464u, 0x00070006u);
-}
-
-// Q4: one dword = 8 nibbles of a group (byte u holds element 2u low, 2u+1 high)
-// -> fp16 (q - 8) in element order [0, 2, 4, 6, 1, 3, 5, 7].
-__device__ __forceinline__ half8_t dequant_q4(uint32_t w) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    uint4 v;
-    v.x = pk_sub(pair_lo(lo), 1032.f);
-    v.y = pk_sub(pair_hi(lo), 1032.f);
-    v.z = pk_sub(pair_lo(hi), 1032.f);
-    v.w = pk_sub(pair_hi(hi), 1032.f);
-    return __builtin_bit_cast(half8_t, v);
 }
 
 // Q8: two dwords = int8 elements 0..7 of a group -> fp16 q in element order.
@@ -91,10 +100,22 @@ __device__ __forceinline__ half8_t dequant_q8(uint32_t d0, uint32_t d1) {
 }
 
 // 16 bytes of global memory -> LDS at `lds` + 16 * lane (LDS-DMA).  `lds` must
-// be the same for the whole wave.
+// be the same for the whole wave.  Issued as inline assembly on purpose: the
+// compiler cannot tell which LDS buffer a DMA fills and would otherwise wait
+// for every DMA in flight (vmcnt(0)) before any LDS read, serialising the
+// pipeline.  The caller waits for its DMA explicitly (wait_vm) before the
+// barrier that publishes the buffer.  M0 holds the LDS base; s_nop covers the
+// M0 -> LDS-DMA hazard.
 __device__ __forceinline__ void dma16(const void *src, void *lds) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(base), "v"(src)
+        : "memory", "m0");
 }
 
 // Waits until at most N vector-memory instructions of this wave are in
@@ -105,194 +126,230 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// LDS barrier without a memory fence.  A fence would wait for every vector
+// memory operation in flight (vmcnt(0)), including the weight loads issued
+// for later chunks; instead the caller waits for exactly the LDS-DMA it needs
+// (wait_vm) and this waits for the wave's own LDS reads (lgkmcnt(0)).  The
+// asm "memory" clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int FMT, int CT, int RPW>
+struct QGemv {
+    using F = TileFmt<FMT>;
+    static constexpr int NB = F::NB, TB = F::TB;
+    static constexpr int FRAG = NB * CT * 2;       // 1 KiB image fragments per K tile
+    static constexpr int SB = TB - 1024;           // scale bytes per tile
+    static constexpr int SCH = 4 * RPW * SB / 16;  // 16-byte scale pieces per K tile
+    static constexpr int XB = FRAG * 1024;         // image bytes per K tile
+    static constexpr int XDW = FRAG / 4;           // image DMAs per wave per K tile
+    static_assert(FRAG % 4 == 0 && SCH <= 64, "DMA split over the 4 waves");
+    typedef uint4 Ring[RPW];
+    typedef floatx4 Acc[RPW][CT];
+
+    const uint8_t *wt, *ximg;
+    int lane, g, wave, n_rt, rt_wg, rt0, nkt, kt_begin, kt_end;
+
+    // LDS-DMA of K tile kt_begin + c: XDW image fragments per wave, and the
+    // workgroup's scales (wave 0).  A tile past the split end (the look-ahead
+    // of the last step, never computed) is clamped to the last valid one.
+    __device__ __forceinline__ void stage(int c, uint8_t *xd, uint8_t *sd) const {
+        const int kt = min(kt_begin + c, kt_end - 1);
+#pragma unroll
+        for (int j = 0; j < XDW; ++j) {
+            const int f = wave + 4 * j;
+            dma16(ximg + ((size_t)kt * FRAG + f) * 1024 + lane * 16, xd + f * 1024);
+        }
+        if (wave == 0) {  // piece e -> (row tile, piece)
+            const int e = min(lane, SCH - 1);
+            const int piece = e % (SB / 16), rr = e / (SB / 16);
+            const int rt = min(rt_wg + rr, n_rt - 1);
+            dma16(wt + ((size_t)rt * nkt + kt) * TB + 1024 + piece * 16, sd);
+        }
+    }
+
+    // Quantised values of K tile kt_begin + c for this wave's row tiles,
+    // straight into registers (no arithmetic on them here: that would make
+    // the wave wait for the load at once).
+    __device__ __forceinline__ void issue(Ring &q, int c) const {
+        const int kt = min(kt_begin + c, kt_end - 1);
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int rt = min(rt0 + r, n_rt - 1);
+            q[r] = *reinterpret_cast<const uint4 *>(wt + ((size_t)rt * nkt + kt) * TB + lane * 16);
+        }
+    }
+
+    // Dequantise + MFMA + block scale of one K tile (always one inside the
+    // split).  Branch-free: row tiles past N repeat the last tile's values
+    // (never stored).
+    __device__ __forceinline__ void compute(const Ring &q, const uint8_t *xs, const uint8_t *ss,
+                                            Acc &acc) const {
+        // scales of this wave's row tiles: rows 4g+i, blocks b at (g, i, b)
+        _Float16 sh[RPW][4 * NB];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const uint8_t *sp = ss + (wave * RPW + r) * SB;
+            if (FMT == RRA_Q4) {
+                const half8_t h0 = *reinterpret_cast<const half8_t *>(sp + 32 * g);
+                const half8_t h1 = *reinterpret_cast<const half8_t *>(sp + 32 * g + 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sh[r][e] = h0[e];
+                    sh[r][8 + e] = h1[e];
+                }
+            } else {
+                const half8_t h0 = *reinterpret_cast<const half8_t *>(sp + 16 * g);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sh[r][e] = h0[e];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            // one block's B fragments at a time (a compiler memory barrier keeps
+            // all four from being loaded up front, which costs registers)
+            asm volatile("" ::: "memory");
+            half8_t Bh[CT], Bl[CT];
+            const int slot = frag_slot<FMT>(lane >> 4, lane & 15, b);
+#pragma unroll
+            for (int cc = 0; cc < CT; ++cc) {
+                Bh[cc] = *reinterpret_cast<const half8_t *>(xs + ((b * CT + cc) * 2 + 0) * 1024 + slot * 16);
+                Bl[cc] = *reinterpret_cast<const half8_t *>(xs + ((b * CT + cc) * 2 + 1) * 1024 + slot * 16);
+            }
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const uint4 qv = q[r];
+                const half8_t a = (FMT == RRA_Q4)
+                                      ? dequant_q4(u32_at(qv, b))
+                                      : dequant_q8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1));
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc) {
+                    floatx4 tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        a, Bh[cc], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Bl[cc], tt, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[r][cc][i] = fmaf((float)sh[r][i * NB + b], tt[i], acc[r][cc][i]);
+                }
+            }
+        }
+    }
+
+    // One pipeline iteration (K tile c): DMA of tile c+1 into xw/sw and its
+    // weight loads into qf, compute of tile c from qc and xr/sr, then a wait
+    // for everything in flight (tile c+1's data) and a barrier.  The DMA is
+    // invisible to the compiler (inline asm); the full wait keeps its own
+    // count of the register loads exact.
+    __device__ __forceinline__ void step(const Ring &qc, Ring &qf, int c, uint8_t *xw,
+                                         uint8_t *sw, const uint8_t *xr, const uint8_t *sr,
+                                         Acc &acc) const {
+        stage(c + 1, xw, sw);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(qf, c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(qc, xr, sr, acc);
+        wait_vm<0>();
+        lds_barrier();
+    }
+};
+
 // Grid (row blocks of 64*RPW rows, K splits); 256 threads = 4 waves; wave w
 // owns row tiles [(blockIdx.x*4 + w)*RPW, +RPW).  The split's K tiles are
-// processed KTW at a time ("chunks") in a software pipeline; iteration c:
-//   1. LDS-DMA of chunk c+1's activation image and scales into the other LDS
-//      buffer;
-//   2. loads of chunk c+2's quantised values into registers (a ring of 3);
-//   3. dequantise + MFMA + block scale of chunk c (registers + LDS);
-//   4. wait for step 1 only (vector memory ops retire in issue order, so this
-//      never waits for step 2), barrier.
-// Each chunk of weights thus has two compute periods to arrive.  Outputs are
-// multiplied by inv[m] (RMSNorm, when nrm.ss is set) and written to
-// out[split][m][n] (split_stride floats apart).
-template <int FMT, int CT, int RPW, int KTW>
+// processed in a two-stage software pipeline (QGemv::step): while tile c is
+// computed from registers and one LDS buffer, tile c+1's weights load into
+// the other register set and its activation image and scales into the other
+// LDS buffer by LDS-DMA.  Outputs are multiplied by inv[m] (RMSNorm, when
+// nrm.ss is set) and written to out[split][m][n] (split_stride floats apart).
+template <int FMT, int CT, int RPW>
 __global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__ wt,
                                                      const uint8_t *__restrict__ ximg,
                                                      float *__restrict__ out, int M, int N, int K,
                                                      int nkt, int kt_per_split,
                                                      long long split_stride, NormIn nrm) {
-    using F = TileFmt<FMT>;
-    constexpr int NB = F::NB, TB = F::TB, MP = 16 * CT;
-    constexpr int FRAG = NB * CT * 2;              // 1 KiB image fragments per K tile
-    constexpr int SB = TB - 1024;                  // scale bytes per tile
-    constexpr int SCH = 4 * RPW * KTW * SB / 16;   // 16-byte scale pieces per chunk
-    constexpr int SCW = (SCH + 63) / 64;           // DMA wave-instructions for them
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][KTW][FRAG * 1024];
-    __shared__ __attribute__((aligned(16))) uint8_t sl[2][SCW * 1024];
-    __shared__ float inv_s[MP];
+    using G = QGemv<FMT, CT, RPW>;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::XB];
+    __shared__ __attribute__((aligned(16))) uint8_t sl[2][1024];
 
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n_rt = (N + 15) >> 4;
-    const int rt_wg = blockIdx.x * 4 * RPW;  // first row tile of the workgroup
-    const int rt0 = rt_wg + wave * RPW;
-    const int kt_begin = blockIdx.y * kt_per_split;
-    const int kt_end = min(nkt, kt_begin + kt_per_split);
-    const int nch = (kt_end - kt_begin + KTW - 1) / KTW;
+    G p;
+    p.wt = wt;
+    p.ximg = ximg;
+    p.lane = threadIdx.x & 63;
+    p.g = p.lane >> 4;
+    p.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    p.n_rt = (N + 15) >> 4;
+    p.rt_wg = blockIdx.x * 4 * RPW;
+    p.rt0 = p.rt_wg + p.wave * RPW;
+    p.nkt = nkt;
+    p.kt_begin = blockIdx.y * kt_per_split;
+    p.kt_end = min(nkt, p.kt_begin + kt_per_split);
+    const int nch = p.kt_end - p.kt_begin;
 
-    if (tid < MP) {
-        float inv = 1.f;
-        if (nrm.ss) {
-            float sq = 0.f;
-            if (tid < M)
-                for (int p = 0; p < nrm.nparts; ++p) sq += nrm.ss[tid * nrm.nparts + p];
-            inv = 1.0f / sqrtf(sq / (float)K + nrm.eps);
+    // RMSNorm: the first SSP partial sums of squares of this lane's columns,
+    // loaded now (clamped, fixed count) and summed once the prologue has
+    // waited for its loads anyway.
+    constexpr int SSP = 4;
+    float sv[CT][SSP];
+    if (nrm.ss) {
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) {
+            const int m = min(16 * cc + (p.lane & 15), M - 1);
+#pragma unroll
+            for (int q = 0; q < SSP; ++q)
+                sv[cc][q] = nrm.ss[(size_t)m * nrm.nparts + min(q, nrm.nparts - 1)];
         }
-        inv_s[tid] = inv;
     }
 
-    // K tiles of a chunk past the split end reuse the last valid tile's data
-    // (finite) with its quantised values replaced by zeros.
-    auto stage = [&](int c, int buf) {
-        const int kt0 = kt_begin + c * KTW;
-        for (int f = wave; f < KTW * FRAG; f += 4) {
-            const int t = f / FRAG, fr = f - t * FRAG;
-            const int kt = min(kt0 + t, kt_end - 1);
-            dma16(ximg + ((size_t)kt * FRAG + fr) * 1024 + lane * 16, xs[buf][t] + fr * 1024);
-        }
-        for (int i = wave; i < SCW; i += 4) {  // scale piece e -> (row tile, K tile, piece)
-            const int e = min(i * 64 + lane, SCH - 1);
-            const int piece = e % (SB / 16), tt = (e / (SB / 16)) % KTW, rr = e / (SB / 16) / KTW;
-            const int rt = min(rt_wg + rr, n_rt - 1), kt = min(kt0 + tt, kt_end - 1);
-            dma16(wt + ((size_t)rt * nkt + kt) * TB + 1024 + piece * 16, sl[buf] + i * 1024);
-        }
-    };
-    auto issue = [&](uint4 (&q)[KTW][RPW], int c) {
-        const int kt0 = kt_begin + c * KTW;
-#pragma unroll
-        for (int t = 0; t < KTW; ++t)
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                const int rt = min(rt0 + r, n_rt - 1), kt = min(kt0 + t, kt_end - 1);
-                const uint4 v = *reinterpret_cast<const uint4 *>(
-                    wt + ((size_t)rt * nkt + kt) * TB + lane * 16);
-                // past the split end: values that dequantise to zero, by masking
-                // (the load is always issued: the wait counts below rely on it)
-                const uint32_t keep = (kt0 + t < kt_end) ? 0xFFFFFFFFu : 0u;
-                const uint32_t z = (FMT == RRA_Q4) ? (0x88888888u & ~keep) : 0u;
-                q[t][r] = uint4{(v.x & keep) | z, (v.y & keep) | z, (v.z & keep) | z,
-                                (v.w & keep) | z};
-            }
-    };
-
-    floatx4 acc[RPW][CT];
+    typename G::Acc acc;
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
-        for (int c = 0; c < CT; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int cc = 0; cc < CT; ++cc) acc[r][cc] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Branch-free: row tiles past N repeat the last tile's values (never stored).
-    auto compute = [&](const uint4 (&q)[KTW][RPW], int buf) {
+    typename G::Ring q0, q1;
+    p.stage(0, xs[0], sl[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    p.issue(q0, 0);
+    wait_vm<0>();
+    lds_barrier();
+    float sq[CT];
 #pragma unroll
-        for (int t = 0; t < KTW; ++t) {
-            const uint8_t *bp = xs[buf][t];
-            // scales of this wave's row tiles for K tile t: rows 4g+i, blocks b
-            _Float16 sh[RPW][4 * NB];
+    for (int cc = 0; cc < CT; ++cc) {
+        sq[cc] = 0.f;
+        if (nrm.ss) {
 #pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                const uint8_t *sp = sl[buf] + (((wave * RPW + r) * KTW) + t) * SB;
-                if (FMT == RRA_Q4) {
-                    const half8_t h0 = *reinterpret_cast<const half8_t *>(sp + 32 * g);
-                    const half8_t h1 = *reinterpret_cast<const half8_t *>(sp + 32 * g + 16);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        sh[r][e] = h0[e];
-                        sh[r][8 + e] = h1[e];
-                    }
-                } else {
-                    const half8_t h0 = *reinterpret_cast<const half8_t *>(sp + 16 * g);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sh[r][e] = h0[e];
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                half8_t Bh[CT], Bl[CT];
-                const int slot = frag_slot<FMT>(lane >> 4, lane & 15, b);
-#pragma unroll
-                for (int c = 0; c < CT; ++c) {
-                    Bh[c] = *reinterpret_cast<const half8_t *>(bp + ((b * CT + c) * 2 + 0) * 1024 + slot * 16);
-                    Bl[c] = *reinterpret_cast<const half8_t *>(bp + ((b * CT + c) * 2 + 1) * 1024 + slot * 16);
-                }
-#pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                    const uint4 qv = q[t][r];
-                    const half8_t a = (FMT == RRA_Q4)
-                                          ? dequant_q4(u32_at(qv, b))
-                                          : dequant_q8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1));
-#pragma unroll
-                    for (int c = 0; c < CT; ++c) {
-                        floatx4 tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            a, Bh[c], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                        tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Bl[c], tt, 0, 0, 0);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[r][c][i] = fmaf((float)sh[r][i * NB + b], tt[i], acc[r][c][i]);
-                    }
-                }
-            }
+            for (int q = 0; q < SSP; ++q) sq[cc] += (q < nrm.nparts) ? sv[cc][q] : 0.f;
         }
-    };
-
-    // The LDS written by DMA must be complete before the barrier: wait for
-    // the DMA but not for the weight loads issued after it (KTW*RPW each).
-    uint4 q0[KTW][RPW], q1[KTW][RPW], q2[KTW][RPW];
-    stage(0, 0);
-    __builtin_amdgcn_sched_barrier(0);  // keep every DMA ahead of the weight loads
-    issue(q0, 0);
-    if (nch > 1) {
-        issue(q1, 1);
-        wait_vm<2 * KTW * RPW>();
-    } else {
-        wait_vm<KTW * RPW>();
     }
-    __syncthreads();
-    // qc: chunk c (landed); chunk c+1 in flight; qf: chunk c+2 (issued here)
-    auto iter = [&](const uint4 (&qc)[KTW][RPW], uint4 (&qf)[KTW][RPW], int c) {
-        if (c + 1 < nch) stage(c + 1, (c + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 2 < nch) issue(qf, c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(qc, c & 1);
-        if (c + 2 < nch)
-            wait_vm<KTW * RPW>();
-        else
-            wait_vm<0>();
-        __syncthreads();
-    };
-    for (int c = 0; c < nch; c += 3) {
-        iter(q0, q2, c);
-        if (c + 1 < nch) iter(q1, q0, c + 1);
-        if (c + 2 < nch) iter(q2, q1, c + 2);
+    // tile c lives in buffer c & 1 and register set c & 1
+    int c = 0;
+    for (; c + 1 < nch; c += 2) {
+        p.step(q0, q1, c, xs[1], sl[1], xs[0], sl[0], acc);
+        p.step(q1, q0, c + 1, xs[0], sl[0], xs[1], sl[1], acc);
     }
+    if (c < nch) p.compute(q0, xs[0], sl[0], acc);
 
     // Result layout of a 16x16 MFMA: lane holds rows 4g..4g+3 of column lane%16.
     float *o = out + (size_t)blockIdx.y * split_stride;
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int rt = rt0 + r;
-        if (rt >= n_rt) continue;
+    for (int cc = 0; cc < CT; ++cc) {
+        const int m = 16 * cc + (p.lane & 15);
+        if (m >= M) continue;
+        float iv = 1.f;
+        if (nrm.ss) {
+            float t = sq[cc];
+            for (int q = SSP; q < nrm.nparts; ++q) t += nrm.ss[(size_t)m * nrm.nparts + q];
+            iv = 1.0f / sqrtf(t / (float)K + nrm.eps);
+        }
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            const int m = 16 * c + (lane & 15);
-            if (m >= M) continue;
-            const float iv = inv_s[m];
+        for (int r = 0; r < RPW; ++r) {
+            const int rt = p.rt0 + r;
+            if (rt >= p.n_rt) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = rt * 16 + 4 * g + i;
-                if (row < N) o[(size_t)m * N + row] = acc[r][c][i] * iv;
+                const int row = rt * 16 + 4 * p.g + i;
+                if (row < N) o[(size_t)m * N + row] = acc[r][cc][i] * iv;
             }
         }
     }
@@ -472,19 +529,13 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ tiled, uint8_t *__rest
     }
 }
 
-// K tiles per chunk: 16 KiB of activation image per chunk and LDS buffer.
-constexpr int ktw_of(int fmt, int ct) {
-    return fmt == RRA_Q4 ? (ct == 2 ? 1 : 2) : (ct == 2 ? 2 : 4);
-}
-
 template <int FMT, int CT, int RPW>
 rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m, float *out,
                     size_t stride, const NormIn &nrm, hipStream_t s) {
     const int n_rt = (int)cdiv(w.n, 16);
     const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
     dim3 grid((unsigned)cdiv(n_rt, 4 * RPW), (unsigned)p.split);
-    constexpr int KTW = ktw_of(FMT, CT);
-    hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW, KTW>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW>), grid, dim3(256), 0, s,
                        static_cast<const uint8_t *>(w.data), img, out, m, (int)w.n, (int)w.k, nkt,
                        p.kt_per_split, (long long)stride, nrm);
     return check_launch("gemv_q_kernel");
@@ -508,16 +559,16 @@ GemvPlan gemv_plan(const rra_weight &w, int m) {
     if (w.fmt == RRA_F32) return p;
     const int n_rt = (int)cdiv(w.n, 16);
     const int nkt = (int)cdiv(w.k, tile_k(w.fmt));
-    const int ktw = ktw_of(w.fmt, frag_ct(m));
-    // Row tiles per wave: 2, or 1 when that leaves too few row blocks.
-    p.rpw = 2;
-    if (cdiv(n_rt, 4 * p.rpw) < 128) p.rpw = 1;
+    // Row tiles per wave: 2 (fewer activation bytes per weight byte), or 1
+    // when that leaves fewer than 128 row blocks.
+    p.rpw = cdiv(n_rt, 8) >= 128 ? 2 : 1;
     const int n_rb = (int)cdiv(n_rt, 4 * p.rpw);
-    // K splits: aim for ~1024 workgroups (4 per compute unit), each split at
-    // least one chunk of K tiles.
-    const int target = 1024;
-    int split = (int)std::max<int64_t>(1, cdiv(target, n_rb));
-    split = std::min<int>(split, (int)cdiv(nkt, ktw));
+    // K splits: a power of two giving about 768 workgroups (3 per compute
+    // unit).  The plan depends on the weight shape only, never on m, so a
+    // sequence's result is bit-identical whatever batch it is computed in.
+    (void)m;
+    int split = 1;
+    while (split * 2 * n_rb <= 768 && split * 2 <= nkt) split *= 2;
     p.kt_per_split = (int)cdiv(nkt, split);
     p.split = (int)cdiv(nkt, p.kt_per_split);
     return p;
