@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--fd-reps", type=int, default=20)
     ap.add_argument("--only-m1", action="store_true", help="run only the M=1 line")
     ap.add_argument("--m1-steps", type=int, default=256)
+    ap.add_argument("--fd-only", action="store_true",
+                    help="run only the flash-decode launches (layer-sized synthetic cache at the "
+                         "workload's lengths) and a plain copy of known size, for counter runs")
     return ap.parse_args()
 
 
@@ -119,6 +122,56 @@ def flash_decode_roofline(S, dd, lens, reps):
     return sec, kv_bytes, chunk
 
 
+def fd_only(S, steps, reps):
+    """Flash decoding alone on one layer-sized synthetic cache at the lengths
+    the timed steps end at, then a plain device copy of known size (the
+    reference for scaling the HBM byte counters)."""
+    import synth
+    m, nkv, hd = S.m, S.n_kv_heads, S.head_dim
+    max_len = max(S.max_len, 4096 + steps)
+    lens = [L + steps for L in synth.context_lengths(S, m)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    kc = torch.randn((m, nkv, max_len, hd), device="cuda", generator=g)
+    vc = torch.randn((m, nkv, max_len, hd), device="cuda", generator=g)
+
+    class _Caches:
+        k_caches, v_caches = [kc], [vc]
+    sec, nbytes, chunk = flash_decode_roofline(S, _Caches, lens, reps)
+    del kc, vc
+    src = torch.randn(COPY_BYTES // 4, device="cuda", generator=g)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return dict(fd_us=sec * 1e6, fd_bytes=nbytes, chunk=chunk, copy_bytes=COPY_BYTES)
+
+
+COPY_BYTES = 1 << 30
+COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "flash_decode_llama3_8b_m32.md")
+ATTENTION_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_gemv_flash_amd",
+                             "csrc", "attention.hip")
+
+
+def counter_traffic():
+    """HBM bytes per rra_flash_decode launch from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None
+    once the attention source has changed since they were taken."""
+    import hashlib
+    try:
+        with open(COUNTERS) as f:
+            line = [l for l in f.read().splitlines() if l.startswith("traffic_json: ")][0]
+        rec = json.loads(line[len("traffic_json: "):])
+        with open(ATTENTION_SRC, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["attention_hip_sha256"]:
+                return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, IndexError, ValueError, KeyError):
+        return None
+
+
 def cpu_baseline(S, W, dd, lengths, first_tok, nseq):
     """The oracle, as it stands, on one decode step of `nseq` sequences."""
     import oracle
@@ -181,6 +234,10 @@ def main():
     import quantized_gemv_flash_amd as rra  # noqa: F401  (fails loudly if not built)
     if args.only_m1:
         print(json.dumps({"m1": m1_line(args.m1_steps)}), flush=True)
+        return
+    if args.fd_only:
+        print(json.dumps({"fd_only": fd_only(synth.LLAMA3_8B_Q4, args.steps, args.fd_reps)}),
+              flush=True)
         return
 
     S = synth.LLAMA3_8B_Q4
@@ -246,7 +303,8 @@ def main():
             "kernel": "rra_flash_decode (fd_chunk_kernel + fd_reduce_kernel), layer-0 cache, "
                       f"M={m}, chunk {chunk}",
             "bound": "hbm", "achieved": fd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": fd_gbs / HBM_PEAK_GBS, "traffic": None,
+            "frac": fd_gbs / HBM_PEAK_GBS, "traffic": counter_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-scaled)",
             "avg_us": fd_sec * 1e6, "algorithmic_bytes": fd_bytes,
         },
         "m1": m1,
