@@ -238,13 +238,23 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
         for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
         mx = wave_max(mx);
         float wsum = 0.f;
+        for (int c = lane; c < nc; c += 64) wsum += expf(lse[c] - mx);
+        wsum = wave_sum(wsum);
+        // chunks 8 at a time, every load issued before any is used
         const float *po = part_o + ((size_t)m * nq + h) * nc_max * HD;
-        for (int c = 0; c < nc; ++c) {
-            const float w = expf(lse[c] - mx);
-            wsum += w;
+        for (int c0 = 0; c0 < nc; c0 += 8) {
+            float v[8][PER], w[8];
 #pragma unroll
-            for (int j = 0; j < PER; ++j)
-                acc[j] = fmaf(w, po[(size_t)c * HD + lane + 64 * j], acc[j]);
+            for (int j = 0; j < 8; ++j) {
+                const int cj = min(c0 + j, nc - 1);
+                w[j] = (c0 + j < nc) ? expf(lse[cj] - mx) : 0.f;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) v[j][i] = po[(size_t)cj * HD + lane + 64 * i];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < PER; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
         }
         float *o = out + ((size_t)m * nq + h) * HD;
 #pragma unroll

@@ -17,37 +17,42 @@
 namespace rra {
 namespace {
 
-// Sum over K-split partial planes, 4 independent loads in flight per step.
+// Sum over the `split` K-split planes of a GEMV result (stride floats
+// apart), in plane order.  Up to 8 planes are loaded at once (clamped
+// addresses, unconditional loads), so the latency is paid once per 8 planes,
+// not once per plane.
 __device__ __forceinline__ float sum_splits(const float *__restrict__ p, int split,
                                            long long stride) {
-    float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
-    int s = 0;
-    for (; s + 4 <= split; s += 4) {
-        a += p[(size_t)s * stride];
-        b += p[(size_t)(s + 1) * stride];
-        c += p[(size_t)(s + 2) * stride];
-        d += p[(size_t)(s + 3) * stride];
+    float acc = 0.f;
+    for (int s0 = 0; s0 < split; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = p[(size_t)min(s0 + j, split - 1) * stride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += (s0 + j < split) ? v[j] : 0.f;
     }
-    for (; s < split; ++s) a += p[(size_t)s * stride];
-    return (a + b) + (c + d);
+    return acc;
 }
 
 // Same over 4 consecutive columns (16-byte loads).
 __device__ __forceinline__ float4 sum_splits4(const float *__restrict__ p, int split,
                                               long long stride) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    int s = 0;
-    for (; s + 2 <= split; s += 2) {
-        const float4 u = *reinterpret_cast<const float4 *>(p + (size_t)s * stride);
-        const float4 v = *reinterpret_cast<const float4 *>(p + (size_t)(s + 1) * stride);
-        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
-        b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < split; s0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = *reinterpret_cast<const float4 *>(p + (size_t)min(s0 + j, split - 1) * stride);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool in = s0 + j < split;
+            acc.x += in ? v[j].x : 0.f;
+            acc.y += in ? v[j].y : 0.f;
+            acc.z += in ? v[j].z : 0.f;
+            acc.w += in ? v[j].w : 0.f;
+        }
     }
-    if (s < split) {
-        const float4 u = *reinterpret_cast<const float4 *>(p + (size_t)s * stride);
-        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
-    }
-    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    return acc;
 }
 
 __device__ __forceinline__ void load8(const float *p, float (&v)[8]) {

@@ -253,6 +253,73 @@ struct QGemv {
         wait_vm<0>();
         lds_barrier();
     }
+
+    // RMSNorm inputs: the first SSP partial sums of squares of this lane's
+    // columns, loaded early (clamped, fixed count) and summed after a wait.
+    static constexpr int SSP = 4;
+    __device__ __forceinline__ void load_ss(const NormIn &nrm, int M, float (&sv)[CT][SSP]) const {
+        if (!nrm.ss) return;
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) {
+            const int m = min(16 * cc + (lane & 15), M - 1);
+#pragma unroll
+            for (int q = 0; q < SSP; ++q)
+                sv[cc][q] = nrm.ss[(size_t)m * nrm.nparts + min(q, nrm.nparts - 1)];
+        }
+    }
+    __device__ __forceinline__ void sum_ss(const NormIn &nrm, const float (&sv)[CT][SSP],
+                                           float (&sq)[CT]) const {
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) {
+            sq[cc] = 0.f;
+            if (nrm.ss) {
+#pragma unroll
+                for (int q = 0; q < SSP; ++q) sq[cc] += (q < nrm.nparts) ? sv[cc][q] : 0.f;
+            }
+        }
+    }
+
+    // Result layout of a 16x16 MFMA: lane holds rows 4g..4g+3 of column
+    // lane%16.  Multiplies by inv[m] (RMSNorm, when nrm.ss is set).
+    __device__ __forceinline__ void store(const Acc &acc, const float (&sq)[CT], const NormIn &nrm,
+                                          float *o, int M, int N, int K) const {
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) {
+            const int m = 16 * cc + (lane & 15);
+            if (m >= M) continue;
+            float iv = 1.f;
+            if (nrm.ss) {
+                float t = sq[cc];
+                for (int q = SSP; q < nrm.nparts; ++q) t += nrm.ss[(size_t)m * nrm.nparts + q];
+                iv = 1.0f / sqrtf(t / (float)K + nrm.eps);
+            }
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int rt = rt0 + r;
+                if (rt >= n_rt) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = rt * 16 + 4 * g + i;
+                    if (row < N) o[(size_t)m * N + row] = acc[r][cc][i] * iv;
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void init(const uint8_t *wt_, const uint8_t *ximg_, int N, int nkt_,
+                                         int kt_per_split) {
+        wt = wt_;
+        ximg = ximg_;
+        lane = threadIdx.x & 63;
+        g = lane >> 4;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        n_rt = (N + 15) >> 4;
+        rt_wg = blockIdx.x * 4 * RPW;
+        rt0 = rt_wg + wave * RPW;
+        nkt = nkt_;
+        kt_begin = blockIdx.y * kt_per_split;
+        kt_end = min(nkt, kt_begin + kt_per_split);
+    }
 };
 
 // Grid (row blocks of 64*RPW rows, K splits); 256 threads = 4 waves; wave w
@@ -273,33 +340,11 @@ __global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__
     __shared__ __attribute__((aligned(16))) uint8_t sl[2][1024];
 
     G p;
-    p.wt = wt;
-    p.ximg = ximg;
-    p.lane = threadIdx.x & 63;
-    p.g = p.lane >> 4;
-    p.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    p.n_rt = (N + 15) >> 4;
-    p.rt_wg = blockIdx.x * 4 * RPW;
-    p.rt0 = p.rt_wg + p.wave * RPW;
-    p.nkt = nkt;
-    p.kt_begin = blockIdx.y * kt_per_split;
-    p.kt_end = min(nkt, p.kt_begin + kt_per_split);
+    p.init(wt, ximg, N, nkt, kt_per_split);
     const int nch = p.kt_end - p.kt_begin;
 
-    // RMSNorm: the first SSP partial sums of squares of this lane's columns,
-    // loaded now (clamped, fixed count) and summed once the prologue has
-    // waited for its loads anyway.
-    constexpr int SSP = 4;
-    float sv[CT][SSP];
-    if (nrm.ss) {
-#pragma unroll
-        for (int cc = 0; cc < CT; ++cc) {
-            const int m = min(16 * cc + (p.lane & 15), M - 1);
-#pragma unroll
-            for (int q = 0; q < SSP; ++q)
-                sv[cc][q] = nrm.ss[(size_t)m * nrm.nparts + min(q, nrm.nparts - 1)];
-        }
-    }
+    float sv[CT][G::SSP];
+    p.load_ss(nrm, M, sv);
 
     typename G::Acc acc;
 #pragma unroll
@@ -314,14 +359,7 @@ __global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__
     wait_vm<0>();
     lds_barrier();
     float sq[CT];
-#pragma unroll
-    for (int cc = 0; cc < CT; ++cc) {
-        sq[cc] = 0.f;
-        if (nrm.ss) {
-#pragma unroll
-            for (int q = 0; q < SSP; ++q) sq[cc] += (q < nrm.nparts) ? sv[cc][q] : 0.f;
-        }
-    }
+    p.sum_ss(nrm, sv, sq);
     // tile c lives in buffer c & 1 and register set c & 1
     int c = 0;
     for (; c + 1 < nch; c += 2) {
@@ -329,30 +367,55 @@ __global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__
         p.step(q1, q0, c + 1, xs[0], sl[0], xs[1], sl[1], acc);
     }
     if (c < nch) p.compute(q0, xs[0], sl[0], acc);
+    p.store(acc, sq, nrm, out + (size_t)blockIdx.y * split_stride, M, N, K);
+}
 
-    // Result layout of a 16x16 MFMA: lane holds rows 4g..4g+3 of column lane%16.
-    float *o = out + (size_t)blockIdx.y * split_stride;
+// Short splits (at most NT K tiles): every K tile's image, scales and
+// weights are requested up front -- all LDS-DMA first, then the weight
+// loads -- so the workgroup pays one memory round trip instead of one per
+// tile.  Tiles past the split end are clamped copies, never computed.
+// Because no DMA follows a weight load, the compiler's own count of the
+// loads in flight matches the hardware's and it adds no waits.
+template <int FMT, int CT, int RPW, int NT>
+__global__ __launch_bounds__(256) void gemv_q_short_kernel(const uint8_t *__restrict__ wt,
+                                                           const uint8_t *__restrict__ ximg,
+                                                           float *__restrict__ out, int M, int N,
+                                                           int K, int nkt, int kt_per_split,
+                                                           long long split_stride, NormIn nrm) {
+    using G = QGemv<FMT, CT, RPW>;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[NT][G::XB];
+    __shared__ __attribute__((aligned(16))) uint8_t sl[NT][1024];
+
+    G p;
+    p.init(wt, ximg, N, nkt, kt_per_split);
+    const int nch = p.kt_end - p.kt_begin;
+
+    float sv[CT][G::SSP];
+    p.load_ss(nrm, M, sv);
 #pragma unroll
-    for (int cc = 0; cc < CT; ++cc) {
-        const int m = 16 * cc + (p.lane & 15);
-        if (m >= M) continue;
-        float iv = 1.f;
-        if (nrm.ss) {
-            float t = sq[cc];
-            for (int q = SSP; q < nrm.nparts; ++q) t += nrm.ss[(size_t)m * nrm.nparts + q];
-            iv = 1.0f / sqrtf(t / (float)K + nrm.eps);
-        }
+    for (int t = 0; t < NT; ++t) p.stage(t, xs[t], sl[t]);
+    __builtin_amdgcn_sched_barrier(0);
+    typename G::Ring q[NT];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const int rt = p.rt0 + r;
-            if (rt >= p.n_rt) continue;
+    for (int t = 0; t < NT; ++t) p.issue(q[t], t);
+    __builtin_amdgcn_sched_barrier(0);
+
+    typename G::Acc acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = rt * 16 + 4 * p.g + i;
-                if (row < N) o[(size_t)m * N + row] = acc[r][cc][i] * iv;
-            }
-        }
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) acc[r][cc] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    wait_vm<NT * RPW>();  // every DMA landed; weight loads may be in flight
+    lds_barrier();
+    float sq[CT];
+    p.sum_ss(nrm, sv, sq);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t < nch) p.compute(q[t], xs[t], sl[t], acc);
     }
+    wait_vm<0>();  // nothing in flight when the workgroup ends
+    p.store(acc, sq, nrm, out + (size_t)blockIdx.y * split_stride, M, N, K);
 }
 
 // Writes x (fp32 [M][K], canonical) as the B-operand image of a GEMV with
@@ -418,19 +481,18 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const float *__restrict__
     }
 }
 
-// y = sum over the split planes, 4 independent loads in flight per step.
+// y = sum over the split planes in plane order, up to 8 loads in flight.
 __device__ __forceinline__ float sum_splits(const float *__restrict__ p, int split,
                                            long long stride) {
-    float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
-    int s = 0;
-    for (; s + 4 <= split; s += 4) {
-        a += p[(size_t)s * stride];
-        b += p[(size_t)(s + 1) * stride];
-        c += p[(size_t)(s + 2) * stride];
-        d += p[(size_t)(s + 3) * stride];
+    float acc = 0.f;
+    for (int s0 = 0; s0 < split; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = p[(size_t)min(s0 + j, split - 1) * stride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += (s0 + j < split) ? v[j] : 0.f;
     }
-    for (; s < split; ++s) a += p[(size_t)s * stride];
-    return (a + b) + (c + d);
+    return acc;
 }
 
 __global__ void reduce_splits_kernel(const float *__restrict__ part, int split,
@@ -535,9 +597,19 @@ rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, 
     const int n_rt = (int)cdiv(w.n, 16);
     const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
     dim3 grid((unsigned)cdiv(n_rt, 4 * RPW), (unsigned)p.split);
-    hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW>), grid, dim3(256), 0, s,
-                       static_cast<const uint8_t *>(w.data), img, out, m, (int)w.n, (int)w.k, nkt,
-                       p.kt_per_split, (long long)stride, nrm);
+    const auto *wd = static_cast<const uint8_t *>(w.data);
+    if (p.kt_per_split <= 2) {
+        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, 2>), grid, dim3(256), 0, s, wd, img,
+                           out, m, (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
+        return check_launch("gemv_q_short_kernel");
+    }
+    if (p.kt_per_split <= 4) {
+        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, 4>), grid, dim3(256), 0, s, wd, img,
+                           out, m, (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
+        return check_launch("gemv_q_short_kernel");
+    }
+    hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW>), grid, dim3(256), 0, s, wd, img, out, m,
+                       (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
     return check_launch("gemv_q_kernel");
 }
 
