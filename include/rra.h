@@ -237,6 +237,16 @@ typedef struct rra_model rra_model;
 #define RRA_STEP_GATHER 2  /* x[i] = embed[tok[i]] first (tok read as input) */
 #define RRA_STEP_ADVANCE 4 /* pos[i] += 1 after the step */
 
+/* A slot whose position is RRA_POS_NONE is empty ([head_dim]
+ * flash_decoding_attention_into: a sequence with nothing to attend to is
+ * skipped, the done-mask early exit).  Continuous batching: a slot leaves by
+ * setting its position to RRA_POS_NONE and joins by setting a real position,
+ * on the device, between steps, with no recapture of the step graph.  The
+ * step leaves an empty slot's cache rows, tok and pos unchanged and does not
+ * gather its x row; its x and logits rows after the step are unspecified.
+ * The other slots' results do not depend on empty slots in any way. */
+#define RRA_POS_NONE 0xFFFFFFFFu
+
 size_t rra_model_workspace_bytes(const rra_model_desc *d);
 
 /* Validates d, lays the workspace out (device, ws_bytes >=
@@ -250,8 +260,9 @@ rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t ws_bytes, 
  * x      : device fp32 [m][hidden], in/out: the step input (embedding rows)
  *          and, on return, the final residual stream (before the output norm).
  * pos    : device uint32 [m], this token's position per sequence; the K/V rows
- *          are written there and attention covers rows [0, pos]; a position
- *          >= max_len writes nothing, and is reported by rra_model_check.
+ *          are written there and attention covers rows [0, pos]; RRA_POS_NONE
+ *          marks an empty slot (see above); any other position >= max_len
+ *          writes nothing, and is reported by rra_model_check.
  * tok    : device uint32 [m], out (and in under RRA_STEP_GATHER).
  * tok_host : host uint32 [m] or NULL.  When non-NULL the call waits for the
  *          stream and copies the ids there (the one sync of the step).

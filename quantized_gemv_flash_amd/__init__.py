@@ -23,6 +23,8 @@ RRA_OK, RRA_EINVAL, RRA_ENOTINIT, RRA_EHIP, RRA_ECAPTURE = 0, 1, 2, 3, 4
 RRA_F32, RRA_Q8, RRA_Q4 = 0, 1, 2
 RRA_PLANAR, RRA_TILED = 0, 1
 RRA_GRAPH, RRA_STEP_GATHER, RRA_STEP_ADVANCE = 1, 2, 4
+RRA_POS_NONE = 0xFFFFFFFF  # empty batch slot; -1 in an int32 position tensor
+POS_NONE_I32 = -1
 FMT = {"f32": RRA_F32, "q8": RRA_Q8, "q4": RRA_Q4}
 
 

@@ -151,7 +151,7 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
     const int m = blockIdx.x, head = blockIdx.y, j = threadIdx.x, half = hd >> 1;
     const int nrow = (nq + 2 * nkv) * hd;
     const uint32_t p = pos[m];
-    const bool ok = p < (uint32_t)max_len;
+    const bool ok = p < (uint32_t)max_len;  // also false for an empty slot (RRA_POS_NONE)
     const size_t b = (size_t)m * nrow + (size_t)head * hd;
     float a = sum_splits(part + b + j, split, split_stride);
     float c = sum_splits(part + b + j + half, split, split_stride);
@@ -173,8 +173,9 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
         dst[j + half] = c;
     }
     if (head == 0 && j == 0) {
-        seq_len[m] = ok ? p + 1 : (uint32_t)max_len;
-        if (!ok) err[0] = 1u;
+        // an empty slot attends to nothing; any other bad position is an error
+        seq_len[m] = ok ? p + 1 : (p == RRA_POS_NONE ? 0u : (uint32_t)max_len);
+        if (!ok && p != RRA_POS_NONE) err[0] = 1u;
     }
 }
 
@@ -228,8 +229,10 @@ __global__ void swiglu_reduce_kernel(const float *__restrict__ part, int split,
 }
 
 __global__ void embed_gather_kernel(const float *__restrict__ embed, const uint32_t *__restrict__ tok,
-                                    float *__restrict__ x, int h, int vocab) {
+                                    const uint32_t *__restrict__ pos, float *__restrict__ x, int h,
+                                    int vocab) {
     const int m = blockIdx.x;
+    if (pos[m] == RRA_POS_NONE) return;  // empty slot: x row left as it is
     const uint32_t t = tok[m];
     float *xr = x + (size_t)m * h;
     if (t >= (uint32_t)vocab) {
@@ -284,11 +287,12 @@ __global__ __launch_bounds__(256) void argmax_pass1_kernel(const float *__restri
 __global__ __launch_bounds__(256) void argmax_pass2_kernel(const float *__restrict__ bv,
                                                            const uint32_t *__restrict__ bi,
                                                            uint32_t *__restrict__ tok,
-                                                           uint32_t *__restrict__ pos_advance,
-                                                           int nb) {
+                                                           uint32_t *__restrict__ pos,
+                                                           int advance, int nb) {
     __shared__ float sv[4];
     __shared__ uint32_t si[4];
     const int m = blockIdx.x;
+    if (pos && pos[m] == RRA_POS_NONE) return;  // empty slot: tok and pos unchanged
     float best = -INFINITY;
     uint32_t bidx = 0xFFFFFFFFu;
     for (int i = threadIdx.x; i < nb; i += blockDim.x)
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(256) void argmax_pass2_kernel(const float *__restri
     if (threadIdx.x == 0) {
         for (int w = 1; w < 4; ++w) arg_combine(best, bidx, sv[w], si[w]);
         tok[m] = bidx == 0xFFFFFFFFu ? 0u : bidx;
-        if (pos_advance) pos_advance[m] += 1u;
+        if (advance) pos[m] += 1u;
     }
 }
 
@@ -358,9 +362,9 @@ rra_status launch_swiglu_reduce(const float *part, int split, size_t split_strid
     return check_launch("swiglu_reduce_kernel");
 }
 
-rra_status launch_embed_gather(const float *embed, const uint32_t *tok, float *x, int m, int h,
-                               int vocab, hipStream_t s) {
-    hipLaunchKernelGGL(embed_gather_kernel, dim3(m), dim3(256), 0, s, embed, tok, x, h, vocab);
+rra_status launch_embed_gather(const float *embed, const uint32_t *tok, const uint32_t *pos,
+                               float *x, int m, int h, int vocab, hipStream_t s) {
+    hipLaunchKernelGGL(embed_gather_kernel, dim3(m), dim3(256), 0, s, embed, tok, pos, x, h, vocab);
     return check_launch("embed_gather_kernel");
 }
 
@@ -370,14 +374,15 @@ size_t argmax_ws_bytes(int m, int v) {
 }
 
 rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void *ws,
-                         uint32_t *pos_advance, hipStream_t s) {
+                         uint32_t *pos, bool advance, hipStream_t s) {
     const int nb = (int)cdiv(v, kArgmaxPerBlock);
     float *bv = static_cast<float *>(ws);
     uint32_t *bi = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
                                                 align_up((size_t)m * nb * sizeof(float), 256));
     hipLaunchKernelGGL(argmax_pass1_kernel, dim3(nb, m), dim3(256), 0, s, logits, bv, bi, v, nb);
     RRA_TRY(check_launch("argmax_pass1_kernel"));
-    hipLaunchKernelGGL(argmax_pass2_kernel, dim3(m), dim3(256), 0, s, bv, bi, tok, pos_advance, nb);
+    hipLaunchKernelGGL(argmax_pass2_kernel, dim3(m), dim3(256), 0, s, bv, bi, tok, pos,
+                       (pos && advance) ? 1 : 0, nb);
     return check_launch("argmax_pass2_kernel");
 }
 

@@ -147,7 +147,7 @@ extern "C" rra_status rra_argmax(const float *logits, uint32_t *tok, int32_t m, 
     const size_t need = argmax_ws_bytes(m, v);
     if (ws_bytes < need)
         return fail(RRA_ENOTINIT, "rra_argmax: workspace has %zu bytes, needs %zu", ws_bytes, need);
-    return launch_argmax(logits, tok, m, v, ws, nullptr, s);
+    return launch_argmax(logits, tok, m, v, ws, nullptr, false, s);
 }
 
 // ---------------------------------------------------------------- model
@@ -311,7 +311,8 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, fl
     const int H = d.hidden, nq = d.n_heads, nkv = d.n_kv_heads, hd = d.head_dim,
               I = d.intermediate;
     const int nqkv = (nq + 2 * nkv) * hd;
-    if (flags & RRA_STEP_GATHER) RRA_TRY(launch_embed_gather(d.embed, tok, x, m, H, d.vocab, s));
+    if (flags & RRA_STEP_GATHER)
+        RRA_TRY(launch_embed_gather(d.embed, tok, pos, x, m, H, d.vocab, s));
     const int np = ss_parts(H);
     const NormIn nrm{M->ss, np, d.rms_eps};
     // RMSNorm is formed inside each consuming GEMV from per-chunk sums of
@@ -352,8 +353,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, fl
     }
     RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits, 0, s,
                         &nrm));
-    return launch_argmax(logits, tok, m, d.vocab, M->argmax_ws,
-                         (flags & RRA_STEP_ADVANCE) ? pos : nullptr, s);
+    return launch_argmax(logits, tok, m, d.vocab, M->argmax_ws, pos, (flags & RRA_STEP_ADVANCE) != 0, s);
 }
 
 }  // namespace

@@ -104,8 +104,11 @@ rra_status launch_rope(float *z, const uint32_t *pos, const float *table, int m,
 rra_status launch_swiglu(const float *gate, const float *up, float *out, int m, int n,
                          size_t gate_stride, size_t up_stride, hipStream_t s);
 size_t argmax_ws_bytes(int m, int v);
+// tok[i] = argmax of logits row i (lowest index among equal maxima).  With
+// pos: rows whose pos is RRA_POS_NONE are skipped (tok, pos unchanged), and
+// pos[i] += 1 for the others when advance is set.
 rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void *ws,
-                         uint32_t *pos_advance, hipStream_t s);
+                         uint32_t *pos, bool advance, hipStream_t s);
 void rope_table_host(float *table, int max_len, int hd, double theta);
 
 // Fused epilogues used by the decode step.
@@ -128,7 +131,8 @@ rra_status launch_qkv_post(const float *part, int split, size_t split_stride, co
 // its activation image for the down GEMV.
 rra_status launch_swiglu_reduce(const float *part, int split, size_t split_stride, float *act,
                                 int m, int inter, const FragOut &fo, hipStream_t s);
-rra_status launch_embed_gather(const float *embed, const uint32_t *tok, float *x, int m, int h,
-                               int vocab, hipStream_t s);
+// x[i] = embed[tok[i]] for every slot whose pos is not RRA_POS_NONE.
+rra_status launch_embed_gather(const float *embed, const uint32_t *tok, const uint32_t *pos,
+                               float *x, int m, int h, int vocab, hipStream_t s);
 
 }  // namespace rra

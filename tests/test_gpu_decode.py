@@ -165,6 +165,73 @@ def test_graph_recaptures_on_new_buffers():
     assert st["captures"] == 2 and st["replays"] == 1
 
 
+def test_continuous_batching_slots_join_and_leave():
+    # Four cache slots, one captured graph: slot 0 runs throughout, slot 1 is
+    # empty and joins with a new sequence at step 4, slot 2 leaves at step 6
+    # and takes a new sequence at step 8, slot 3 stays empty.  Every active
+    # slot matches its own single-sequence oracle; empty slots keep their
+    # cache rows, token and position.
+    S = synth.TINY_LLAMA_F32
+    banner("continuous batching", S.name)
+    W = synth.decoder_weights(S, seed=6, device=DEV, gamma="random")
+    m, steps = 4, 10
+    run = Run(S, W, m, S.max_len)
+    first = synth.first_tokens(S, 8, seed=6).tolist()
+    # (slot, first step, last step, first token) per sequence
+    seqs = [(0, 0, 9, first[0]), (1, 4, 9, first[1]), (2, 0, 5, first[2]), (2, 8, 9, first[3])]
+    orcs = [oracle.DecoderOracle(S, W, 1, S.max_len) for _ in seqs]
+    cur = [t for (_, _, _, t) in seqs]
+    none = rra.POS_NONE_I32
+    for step in range(steps):
+        owner = {}
+        for i, (slot, a, b, _) in enumerate(seqs):
+            if a <= step <= b:
+                owner[slot] = i
+        toks = [cur[owner[s]] if s in owner else 0 for s in range(m)]
+        pos = [step - seqs[owner[s]][1] if s in owner else none for s in range(m)]
+        tok_before = host(run.tok).tolist()
+        empty = [s for s in range(m) if s not in owner]
+        caches_before = [(run.dd.k_caches[l][empty].clone(), run.dd.v_caches[l][empty].clone())
+                         for l in range(S.n_layers)]
+        ids, hid, logits = run.step(toks, pos, flags=rra.RRA_GRAPH)
+        for s, i in owner.items():
+            o = orcs[i].step(host(W.embed[torch.as_tensor([cur[i]], device=DEV)]), [pos[s]])
+            compare_step(([ids[s]], hid[s:s + 1], logits[s:s + 1]), o, f"step {step} slot {s}")
+            cur[i] = int(o["tok"][0])
+        for s in empty:
+            assert ids[s] == tok_before[s], f"empty slot {s} token changed"
+        for l, (kb, vb) in enumerate(caches_before):
+            assert torch.equal(kb, run.dd.k_caches[l][empty]) and torch.equal(vb, run.dd.v_caches[l][empty])
+        run.dd.model.rra_model_check()  # an empty slot is not an error
+    st = run.dd.model.rra_graph_stats()
+    assert st["captures"] == 1 and st["replays"] == steps - 1
+
+
+def test_empty_slots_in_device_greedy_loop():
+    # Under RRA_STEP_GATHER | RRA_STEP_ADVANCE an empty slot keeps its token
+    # and is not advanced; the active slots equal a batch without the empty
+    # slots, bit for bit.
+    S = synth.TINY_LLAMA_F32
+    W = synth.decoder_weights(S, seed=7, device=DEV)
+    flags = rra.RRA_GRAPH | rra.RRA_STEP_GATHER | rra.RRA_STEP_ADVANCE
+    first = synth.first_tokens(S, 2, seed=7).tolist()
+    full = Run(S, W, 4, S.max_len)
+    full.tok.copy_(torch.as_tensor([first[0], 11, first[1], 12], dtype=torch.int32))
+    full.pos.copy_(torch.as_tensor([0, rra.POS_NONE_I32, 3, rra.POS_NONE_I32], dtype=torch.int32))
+    pair = Run(S, W, 2, S.max_len)
+    pair.tok.copy_(torch.as_tensor(first, dtype=torch.int32))
+    pair.pos.copy_(torch.as_tensor([0, 3], dtype=torch.int32))
+    for _ in range(6):
+        full.dd.model.rra_decode_step(full.x, full.pos, full.tok, 4, flags=flags, logits=full.logits)
+        pair.dd.model.rra_decode_step(pair.x, pair.pos, pair.tok, 2, flags=flags, logits=pair.logits)
+        torch.cuda.synchronize()
+        t4, t2 = host(full.tok).tolist(), host(pair.tok).tolist()
+        assert [t4[0], t4[2]] == t2 and t4[1] == 11 and t4[3] == 12
+        assert torch.equal(full.logits[[0, 2]], pair.logits)
+    p4 = host(full.pos).tolist()
+    assert p4 == [6, rra.POS_NONE_I32, 9, rra.POS_NONE_I32]
+
+
 # ---------------------------------------------------------------- quantised decoders
 def test_qwen05b_q8_context_then_greedy():
     # Full 24-layer Q8 decoder at M=1: 8 teacher-forced context steps on random
