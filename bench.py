@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--fd-reps", type=int, default=20)
     ap.add_argument("--only-m1", action="store_true", help="run only the M=1 line")
     ap.add_argument("--m1-steps", type=int, default=256)
+    ap.add_argument("--m1-ctx", type=int, default=512, help="context tokens of the M=1 line")
     ap.add_argument("--fd-only", action="store_true",
                     help="run only the flash-decode launches (layer-sized synthetic cache at the "
                          "workload's lengths) and a plain copy of known size, for counter runs")
@@ -237,7 +238,7 @@ def main():
     import synth
     import quantized_gemv_flash_amd as rra  # noqa: F401  (fails loudly if not built)
     if args.only_m1:
-        print(json.dumps({"m1": m1_line(args.m1_steps)}), flush=True)
+        print(json.dumps({"m1": m1_line(args.m1_steps, args.m1_ctx)}), flush=True)
         return
     if args.fd_only:
         print(json.dumps({"fd_only": fd_only(synth.LLAMA3_8B_Q4, args.steps, args.fd_reps)}),
@@ -278,7 +279,7 @@ def main():
     del dd, W
     torch.cuda.empty_cache()
     if not args.no_m1:
-        m1 = m1_line(args.m1_steps)
+        m1 = m1_line(args.m1_steps, args.m1_ctx)
         log(f"m1 {m1}")
 
     out = {

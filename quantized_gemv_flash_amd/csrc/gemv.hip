@@ -99,23 +99,29 @@ __device__ __forceinline__ half8_t dequant_q8(uint32_t d0, uint32_t d1) {
     return __builtin_bit_cast(half8_t, v);
 }
 
-// 16 bytes of global memory -> LDS at `lds` + 16 * lane (LDS-DMA).  `lds` must
-// be the same for the whole wave.  Issued as inline assembly on purpose: the
-// compiler cannot tell which LDS buffer a DMA fills and would otherwise wait
-// for every DMA in flight (vmcnt(0)) before any LDS read, serialising the
-// pipeline.  The caller waits for its DMA explicitly (wait_vm) before the
-// barrier that publishes the buffer.  M0 holds the LDS base; s_nop covers the
-// M0 -> LDS-DMA hazard.
-__device__ __forceinline__ void dma16(const void *src, void *lds) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds);
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes of global memory -> LDS at byte address `lds` + 16 * lane
+// (LDS-DMA).  `lds` must be the same for the whole wave.  Issued as inline
+// assembly on purpose: the compiler cannot tell which LDS buffer a DMA fills
+// and would otherwise wait for every DMA in flight (vmcnt(0)) before any LDS
+// read, serialising the pipeline.  The caller waits for its DMA explicitly
+// (wait_vm) before the barrier that publishes the buffer.  M0 holds the LDS
+// address; s_nop covers the M0 -> LDS-DMA hazard.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off"
         :
-        : "s"(base), "v"(src)
+        : "s"(lds), "v"(src)
         : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(const void *src, void *lds) {
+    dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(lds)));
 }
 
 // Waits until at most N vector-memory instructions of this wave are in
@@ -168,6 +174,44 @@ struct QGemv {
             const int rt = min(rt_wg + rr, n_rt - 1);
             dma16(wt + ((size_t)rt * nkt + kt) * TB + 1024 + piece * 16, sd);
         }
+    }
+
+    // Addresses of one K tile for this lane; the next tile's are a constant
+    // stride away, so the main loop only adds (no clamping: it never looks
+    // past the split's last tile).
+    struct Cursor {
+        const uint8_t *x;       // image fragment `wave` of the tile, this lane's 16 B
+        const uint8_t *s;       // scale piece of this lane (wave 0)
+        const uint8_t *w[RPW];  // this lane's 16 B of each of the wave's row tiles
+    };
+    __device__ __forceinline__ Cursor cursor(int c) const {
+        Cursor k;
+        const int kt = kt_begin + c;
+        k.x = ximg + ((size_t)kt * FRAG + wave) * 1024 + lane * 16;
+        const int e = min(lane, SCH - 1);
+        const int rts = min(rt_wg + e / (SB / 16), n_rt - 1);
+        k.s = wt + ((size_t)rts * nkt + kt) * TB + 1024 + (e % (SB / 16)) * 16;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+            k.w[r] = wt + ((size_t)min(rt0 + r, n_rt - 1) * nkt + kt) * TB + lane * 16;
+        return k;
+    }
+    __device__ __forceinline__ void advance(Cursor &k) const {
+        k.x += FRAG * 1024;
+        k.s += TB;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) k.w[r] += TB;
+    }
+    // stage()/issue() at a cursor; xd, sd are LDS byte addresses of the buffers.
+    __device__ __forceinline__ void stage_at(const Cursor &k, uint32_t xd, uint32_t sd) const {
+#pragma unroll
+        for (int j = 0; j < XDW; ++j)
+            dma16(k.x + (size_t)4 * j * 1024, xd + (uint32_t)(wave + 4 * j) * 1024);
+        if (wave == 0) dma16(k.s, sd);
+    }
+    __device__ __forceinline__ void issue_at(const Cursor &k, Ring &q) const {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) q[r] = *reinterpret_cast<const uint4 *>(k.w[r]);
     }
 
     // Quantised values of K tile kt_begin + c for this wave's row tiles,
@@ -237,17 +281,17 @@ struct QGemv {
         }
     }
 
-    // One pipeline iteration (K tile c): DMA of tile c+1 into xw/sw and its
-    // weight loads into qf, compute of tile c from qc and xr/sr, then a wait
-    // for everything in flight (tile c+1's data) and a barrier.  The DMA is
-    // invisible to the compiler (inline asm); the full wait keeps its own
-    // count of the register loads exact.
-    __device__ __forceinline__ void step(const Ring &qc, Ring &qf, int c, uint8_t *xw,
-                                         uint8_t *sw, const uint8_t *xr, const uint8_t *sr,
+    // One pipeline iteration: DMA of the next tile (cursor kn) into xw/sw and
+    // its weight loads into qf, compute of the current tile from qc and xr/sr,
+    // then a wait for everything in flight (the next tile's data) and a
+    // barrier.  The DMA is invisible to the compiler (inline asm); the full
+    // wait keeps its own count of the register loads exact.
+    __device__ __forceinline__ void step(const Ring &qc, Ring &qf, const Cursor &kn, uint32_t xw,
+                                         uint32_t sw, const uint8_t *xr, const uint8_t *sr,
                                          Acc &acc) const {
-        stage(c + 1, xw, sw);
+        stage_at(kn, xw, sw);
         __builtin_amdgcn_sched_barrier(0);
-        issue(qf, c + 1);
+        issue_at(kn, qf);
         __builtin_amdgcn_sched_barrier(0);
         compute(qc, xr, sr, acc);
         wait_vm<0>();
@@ -360,13 +404,24 @@ __global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__
     lds_barrier();
     float sq[CT];
     p.sum_ss(nrm, sv, sq);
-    // tile c lives in buffer c & 1 and register set c & 1
+    // Tile c lives in buffer c & 1 and register set c & 1.  Every step
+    // prefetches a tile inside the split; the last tile is computed alone.
+    const uint32_t x0 = lds_addr(xs[0]), x1 = lds_addr(xs[1]);
+    const uint32_t s0 = lds_addr(sl[0]), s1 = lds_addr(sl[1]);
+    typename G::Cursor kn = p.cursor(nch > 1 ? 1 : 0);
     int c = 0;
-    for (; c + 1 < nch; c += 2) {
-        p.step(q0, q1, c, xs[1], sl[1], xs[0], sl[0], acc);
-        p.step(q1, q0, c + 1, xs[0], sl[0], xs[1], sl[1], acc);
+    for (; c + 2 < nch; c += 2) {
+        p.step(q0, q1, kn, x1, s1, xs[0], sl[0], acc);
+        p.advance(kn);
+        p.step(q1, q0, kn, x0, s0, xs[1], sl[1], acc);
+        p.advance(kn);
     }
-    if (c < nch) p.compute(q0, xs[0], sl[0], acc);
+    if (c + 1 < nch) {
+        p.step(q0, q1, kn, x1, s1, xs[0], sl[0], acc);
+        p.compute(q1, xs[1], sl[1], acc);
+    } else if (c < nch) {
+        p.compute(q0, xs[0], sl[0], acc);
+    }
     p.store(acc, sq, nrm, out + (size_t)blockIdx.y * split_stride, M, N, K);
 }
 
