@@ -274,7 +274,7 @@ def main():
     m1 = None
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(S, W, dd, lengths, first, 8, 3)
+        cpu = cpu_baseline(S, W, dd, lengths, first, 8, 4)
         log(f"cpu baseline {cpu}")
     del dd, W
     torch.cuda.empty_cache()

@@ -151,7 +151,9 @@ struct QGemv {
     static constexpr int SCH = 4 * RPW * SB / 16;  // 16-byte scale pieces per K tile
     static constexpr int XB = FRAG * 1024;         // image bytes per K tile
     static constexpr int XDW = FRAG / 4;           // image DMAs per wave per K tile
-    static_assert(FRAG % 4 == 0 && SCH <= 64, "DMA split over the 4 waves");
+    static constexpr int SCW = (SCH + 63) / 64;    // waves that DMA one scale piece each
+    static constexpr int SCB = SCW * 1024;         // scale bytes per LDS buffer
+    static_assert(FRAG % 4 == 0 && SCW <= 4, "DMA split over the 4 waves");
     typedef uint4 Ring[RPW];
     typedef floatx4 Acc[RPW][CT];
 
@@ -159,7 +161,7 @@ struct QGemv {
     int lane, g, wave, n_rt, rt_wg, rt0, nkt, kt_begin, kt_end;
 
     // LDS-DMA of K tile kt_begin + c: XDW image fragments per wave, and the
-    // workgroup's scales (wave 0).  A tile past the split end (the look-ahead
+    // workgroup's scales (waves < SCW, 64 pieces each).  A tile past the split end (the look-ahead
     // of the last step, never computed) is clamped to the last valid one.
     __device__ __forceinline__ void stage(int c, uint8_t *xd, uint8_t *sd) const {
         const int kt = min(kt_begin + c, kt_end - 1);
@@ -168,11 +170,11 @@ struct QGemv {
             const int f = wave + 4 * j;
             dma16(ximg + ((size_t)kt * FRAG + f) * 1024 + lane * 16, xd + f * 1024);
         }
-        if (wave == 0) {  // piece e -> (row tile, piece)
-            const int e = min(lane, SCH - 1);
+        if (wave < SCW) {  // piece e -> (row tile, piece)
+            const int e = min(wave * 64 + lane, SCH - 1);
             const int piece = e % (SB / 16), rr = e / (SB / 16);
             const int rt = min(rt_wg + rr, n_rt - 1);
-            dma16(wt + ((size_t)rt * nkt + kt) * TB + 1024 + piece * 16, sd);
+            dma16(wt + ((size_t)rt * nkt + kt) * TB + 1024 + piece * 16, sd + wave * 1024);
         }
     }
 
@@ -181,14 +183,14 @@ struct QGemv {
     // past the split's last tile).
     struct Cursor {
         const uint8_t *x;       // image fragment `wave` of the tile, this lane's 16 B
-        const uint8_t *s;       // scale piece of this lane (wave 0)
+        const uint8_t *s;       // scale piece of this lane (waves < SCW)
         const uint8_t *w[RPW];  // this lane's 16 B of each of the wave's row tiles
     };
     __device__ __forceinline__ Cursor cursor(int c) const {
         Cursor k;
         const int kt = kt_begin + c;
         k.x = ximg + ((size_t)kt * FRAG + wave) * 1024 + lane * 16;
-        const int e = min(lane, SCH - 1);
+        const int e = min(wave * 64 + lane, SCH - 1);
         const int rts = min(rt_wg + e / (SB / 16), n_rt - 1);
         k.s = wt + ((size_t)rts * nkt + kt) * TB + 1024 + (e % (SB / 16)) * 16;
 #pragma unroll
@@ -207,7 +209,7 @@ struct QGemv {
 #pragma unroll
         for (int j = 0; j < XDW; ++j)
             dma16(k.x + (size_t)4 * j * 1024, xd + (uint32_t)(wave + 4 * j) * 1024);
-        if (wave == 0) dma16(k.s, sd);
+        if (wave < SCW) dma16(k.s, sd + (uint32_t)wave * 1024);
     }
     __device__ __forceinline__ void issue_at(const Cursor &k, Ring &q) const {
 #pragma unroll
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__
                                                      long long split_stride, NormIn nrm) {
     using G = QGemv<FMT, CT, RPW>;
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::XB];
-    __shared__ __attribute__((aligned(16))) uint8_t sl[2][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t sl[2][G::SCB];
 
     G p;
     p.init(wt, ximg, N, nkt, kt_per_split);
@@ -439,7 +441,7 @@ __global__ __launch_bounds__(256) void gemv_q_short_kernel(const uint8_t *__rest
                                                            long long split_stride, NormIn nrm) {
     using G = QGemv<FMT, CT, RPW>;
     __shared__ __attribute__((aligned(16))) uint8_t xs[NT][G::XB];
-    __shared__ __attribute__((aligned(16))) uint8_t sl[NT][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t sl[NT][G::SCB];
 
     G p;
     p.init(wt, ximg, N, nkt, kt_per_split);
