@@ -41,8 +41,8 @@ _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "oracle.c")
 _LIB = os.path.join(_DIR, "liboracle.so")
 
-F32, Q8, Q4 = 0, 1, 2
-_FMT = {"f32": F32, "q8": Q8, "q4": Q4}
+F32, Q8, Q4, FP8 = 0, 1, 2, 3
+_FMT = {"f32": F32, "q8": Q8, "q4": Q4, "fp8": FP8}
 
 
 def build(force: bool = False) -> str:
@@ -67,6 +67,8 @@ def lib():
         P, I64, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
         L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.orc_f16_to_f64.restype = D
+        L.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_to_f64.restype = D
         L.orc_dequant_row.argtypes = [ctypes.c_int, P, P, I64, I64, P]
         L.orc_dequant_row.restype = None
         L.orc_gemv.argtypes = [ctypes.c_int, P, P, I64, I64, P, I64, P, I64, P]
@@ -101,6 +103,10 @@ def _np(t):
 # --------------------------------------------------------------------------
 def f16_to_f64(bits: int) -> float:
     return lib().orc_f16_to_f64(int(bits) & 0xFFFF)
+
+
+def e4m3_to_f64(code: int) -> float:
+    return lib().orc_e4m3_to_f64(int(code) & 0xFF)
 
 
 def dequant(fmt: str, data, scale, n: int, k: int, rows: Sequence[int]) -> np.ndarray:

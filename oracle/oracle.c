@@ -15,7 +15,9 @@
  *   [head_dim]        realizar 0.8.5, src/cuda/executor/head_dim.rs
  * and the block formats of the quantised workloads (Q8: 32 int8 values and one
  * fp16 scale per block, value = scale*q; Q4: 32 unsigned 4-bit values and one
- * fp16 scale, value = scale*(q-8)).
+ * fp16 scale, value = scale*(q-8)).  FP8 (the pages' other weight precision,
+ * [batched_forward] LM-head notes) is 32 OCP FP8 E4M3 values and one fp16
+ * scale per block, value = scale*e4m3(q).
  */
 #include <math.h>
 #include <stdint.h>
@@ -25,6 +27,7 @@
 #define ORC_F32 0
 #define ORC_Q8 1
 #define ORC_Q4 2
+#define ORC_FP8 3
 #define ORC_QBLOCK 32
 
 /* IEEE 754 binary16 -> binary64, from the bit fields: sign, 5-bit exponent
@@ -44,11 +47,30 @@ double orc_f16_to_f64(uint16_t h) {
     return sign ? -v : v;
 }
 
+/* OCP 8-bit floating point E4M3 -> binary64, from the bit fields: sign,
+ * 4-bit exponent (bias 7), 3-bit fraction; exponent 0 encodes subnormals
+ * 2^-6 * f/8; there is no infinity, and exponent 15 with fraction 7 is NaN
+ * (so the largest finite magnitude is 1.75 * 2^8 = 448). */
+double orc_e4m3_to_f64(uint8_t c) {
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 0xF;
+    int f = c & 0x7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -9); /* 2^-6 * f / 2^3 */
+    else if (e == 15 && f == 7)
+        v = NAN;
+    else
+        v = ldexp(1.0 + (double)f / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
 /* Dequantised row `row` of an [n][k] weight in the planar layout:
  *   F32: data is float[n][k];
  *   Q8 : data is int8[n][k], scale is fp16[n][k/32]; w = scale * q;
  *   Q4 : data is uint8[n][k/2] (byte j: element 2j low nibble, 2j+1 high
- *        nibble), scale fp16[n][k/32]; w = scale * (q - 8). */
+ *        nibble), scale fp16[n][k/32]; w = scale * (q - 8);
+ *   FP8: data is E4M3 codes uint8[n][k], scale fp16[n][k/32]; w = scale * e4m3(q). */
 void orc_dequant_row(int fmt, const void *data, const uint16_t *scale, int64_t k,
                      int64_t row, double *out) {
     int64_t nb = k / ORC_QBLOCK;
@@ -61,6 +83,13 @@ void orc_dequant_row(int fmt, const void *data, const uint16_t *scale, int64_t k
             double s = orc_f16_to_f64(scale[row * nb + b]);
             for (int64_t i = b * ORC_QBLOCK; i < (b + 1) * ORC_QBLOCK; ++i)
                 out[i] = s * (double)q[i];
+        }
+    } else if (fmt == ORC_FP8) {
+        const uint8_t *q = (const uint8_t *)data + row * k;
+        for (int64_t b = 0; b < nb; ++b) {
+            double s = orc_f16_to_f64(scale[row * nb + b]);
+            for (int64_t i = b * ORC_QBLOCK; i < (b + 1) * ORC_QBLOCK; ++i)
+                out[i] = s * orc_e4m3_to_f64(q[i]);
         }
     } else {
         const uint8_t *q = (const uint8_t *)data + row * (k / 2);

@@ -39,7 +39,7 @@ class Decoder:
     head_dim: int
     intermediate: int
     vocab: int
-    fmt: str  # "f32" | "q8" | "q4"
+    fmt: str  # "f32" | "q8" | "q4" | "fp8"
     rms_eps: float = 1e-6
     rope_theta: float = 1e4
     weight_std: float = 0.02
@@ -154,6 +154,28 @@ def quantize_q8(w: torch.Tensor):
     return q.contiguous(), s16.view(torch.int16).contiguous()
 
 
+E4M3_MAX = 448.0
+
+
+def quantize_fp8(w: torch.Tensor):
+    """fp32 [N][K] -> (E4M3 codes uint8 [N][K], scale fp16-bits int16 [N][K/32]).
+
+    Per block of 32: scale = maxabs/448 (the largest finite E4M3 magnitude),
+    stored as fp16 (round to nearest even); q = E4M3(w / scale), round to
+    nearest even, clamped to +-448 first (the fp16 rounding of the scale can
+    push a ratio just past 448).  All-zero block: scale 0, every code 0.
+    """
+    n, k = w.shape
+    assert k % QBLOCK == 0, "FP8 blocks need K to be a multiple of 32"
+    b = w.reshape(n, k // QBLOCK, QBLOCK)
+    s16 = (b.abs().amax(dim=2) / E4M3_MAX).to(torch.float16)
+    s = s16.to(torch.float32).unsqueeze(2)
+    safe = torch.where(s > 0, s, torch.ones_like(s))
+    r = torch.where(s > 0, b / safe, torch.zeros_like(b)).clamp_(-E4M3_MAX, E4M3_MAX)
+    q = r.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, k)
+    return q.contiguous(), s16.view(torch.int16).contiguous()
+
+
 def quantize_q4(w: torch.Tensor):
     """fp32 [N][K] -> (packed uint8 [N][K/2], scale fp16-bits int16 [N][K/32]).
 
@@ -182,6 +204,8 @@ def quantize(w: torch.Tensor, fmt: str):
         return quantize_q8(w)
     if fmt == "q4":
         return quantize_q4(w)
+    if fmt == "fp8":
+        return quantize_fp8(w)
     raise ValueError(f"unknown weight format {fmt!r}")
 
 

@@ -73,7 +73,46 @@ def _brute_row_q8(row_bytes: bytes, scales, k):
             for i, v in enumerate(vals)]
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q8"])
+def _e4m3_exact(code: int) -> Fraction:
+    # OCP E4M3 written out from its bit fields: sign, exponent bias 7, 3-bit
+    # fraction, exponent 0 subnormal (2^-6 * f/8).
+    sign = -1 if code & 0x80 else 1
+    e, f = (code >> 3) & 0xF, code & 0x7
+    assert not (e == 15 and f == 7), "NaN code"
+    mag = Fraction(f, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(f, 8)) * Fraction(2) ** (e - 7)
+    return sign * mag
+
+
+def _brute_row_fp8(row_bytes: bytes, scales, k):
+    return [Fraction(np.array([scales[i // 32]], np.uint16).view(np.float16).item()) * _e4m3_exact(c)
+            for i, c in enumerate(row_bytes)]
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(got), nan)  # 0x7F, 0xFF
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_fp8_worked_example():
+    # One row, K = 64 (two blocks).  Block 0 scale 0.5 (fp16 0x3800), block 1
+    # scale 2 (0x4000).  E4M3 0x7E = 1.75 * 2^8 = 448 (the largest finite),
+    # 0xFE = -448, 0x38 = 1.0, 0x3C = 1.5, 0x08 = 2^-6 (smallest normal),
+    # 0x01 = 2^-9 (smallest subnormal), 0x80 = -0.
+    row = np.zeros(64, np.uint8)
+    row[[0, 1, 2, 3, 4, 5, 6, 32, 33]] = [0x7E, 0xFE, 0x38, 0x3C, 0x08, 0x01, 0x80, 0x3C, 0x01]
+    scale = np.array([[0x3800, 0x4000]], np.uint16)
+    got = oracle.dequant("fp8", row.reshape(1, 64), scale, 1, 64, [0])[0]
+    want = np.zeros(64)
+    want[[0, 1, 2, 3, 4, 5, 6]] = [224.0, -224.0, 0.5, 0.75, 2.0 ** -7, 2.0 ** -10, -0.0]
+    want[[32, 33]] = [3.0, 2.0 ** -8]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8", "fp8"])
 def test_gemv_integer_exact_brute_force(fmt):
     # Power-of-two scales and small-integer x make every partial sum exact in
     # fp64, so the oracle must equal exact rational arithmetic bit for bit.
@@ -84,9 +123,13 @@ def test_gemv_integer_exact_brute_force(fmt):
     if fmt == "q4":
         data = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
         rows = [_brute_row_q4(data[r].tobytes(), scales[r], k) for r in range(n)]
-    else:
+    elif fmt == "q8":
         data = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
         rows = [_brute_row_q8(data[r].tobytes(), scales[r], k) for r in range(n)]
+    else:
+        codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)  # no NaN
+        data = codes[rng.integers(0, codes.size, size=(n, k))]
+        rows = [_brute_row_fp8(data[r].tobytes(), scales[r], k) for r in range(n)]
     x = rng.integers(-9, 10, size=(m, k)).astype(np.float64)
     y = oracle.gemv(fmt, data, scales, n, k, x)
     for mi in range(m):
@@ -125,6 +168,13 @@ def test_quantiser_roundtrip_is_close():
         deq = oracle.dequant(fmt, d, s, 8, 64, range(8))
         step = np.repeat(s.numpy().view(np.float16).astype(np.float64), 32, axis=1)
         assert np.all(np.abs(deq - w.numpy()) <= 0.5 * step * (1 + 1e-3) + 1e-9)
+    # FP8: within half a unit in the last place of E4M3 (3 fraction bits, so a
+    # relative 2^-4), or half the subnormal step (2^-10) times the scale.
+    d, s = synth.quantize(w, "fp8")
+    deq = oracle.dequant("fp8", d, s, 8, 64, range(8))
+    sc = np.repeat(s.numpy().view(np.float16).astype(np.float64), 32, axis=1)
+    bound = np.maximum(np.abs(w.numpy()) * 2.0 ** -4, sc * 2.0 ** -10)
+    assert np.all(np.abs(deq - w.numpy()) <= bound * (1 + 1e-3) + 1e-12)
 
 
 # ---------------------------------------------------------------- RMSNorm
