@@ -11,7 +11,8 @@ A step is one decode token for all 32 sequences; tok/s = M * steps / time.
 Also reported: the M = 1 line (Qwen2.5-0.5B-shaped Q8 decoder after a
 512-token teacher-forced context, 256 greedy steps), the HBM roofline of the
 dominant kernel (split-K flash decoding, timed alone with HIP events on the
-stream it runs on), and the CPU oracle's speed on a bounded sample.
+stream it runs on), the FP8 block format on the GEMV at the LM-head shape, and
+the CPU oracle's speed on a bounded sample.
 
 Prints one JSON line.
 """
@@ -197,6 +198,41 @@ def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps):
                        f"workload ({sec:.1f} s; fp64, {threads} OpenMP threads)")
 
 
+def fp8_gemv_line(reps=20):
+    """The FP8 (E4M3) block format on the weights-once GEMV at the LM-head shape
+    of the 8B-shaped decoder (128256 x 4096): rra_batched_gemv (activation
+    image + GEMV) timed with HIP events at M = 1 and 32."""
+    import synth
+    import quantized_gemv_flash_amd as rra
+    n, k = 128256, 4096
+    data, scale = synth.weight(n, k, "fp8", 0.02, 0, "bench_fp8_lm", "cuda")
+    w = rra.device_weight(data, scale, "fp8")
+    del data, scale
+    wbytes = n * k * 34 / 32  # codes + one fp16 scale per 32
+    res = dict(shape=f"{n}x{k} fp8 (E4M3 + fp16 scale per 32)", weight_bytes=wbytes)
+    for m in (1, 32):
+        x = torch.randn((m, k), device="cuda")
+        y = torch.empty((m, n), device="cuda")
+        ws = torch.empty(max(4, rra.rra_batched_gemv_workspace_bytes(w, m)), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(3):
+            rra.rra_batched_gemv(w, x, y, m, ws)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            rra.rra_batched_gemv(w, x, y, m, ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        sec = ev0.elapsed_time(ev1) / 1e3 / reps
+        res[f"m{m}_us"] = sec * 1e6
+        res[f"m{m}_gbs"] = wbytes / sec / 1e9
+        res[f"m{m}_hbm_frac"] = wbytes / sec / 1e9 / HBM_PEAK_GBS
+    del w
+    torch.cuda.empty_cache()
+    return res
+
+
 def m1_line(steps_m1=256, ctx=512):
     import synth
     S = synth.QWEN25_05B_Q8
@@ -281,6 +317,8 @@ def main():
     if not args.no_m1:
         m1 = m1_line(args.m1_steps, args.m1_ctx)
         log(f"m1 {m1}")
+    fp8 = fp8_gemv_line()
+    log(f"fp8 gemv {fp8}")
 
     out = {
         "metric": "decode tok/s at M=1 and M=32; weight+KV stream HBM GB/s as % of peak",
@@ -313,6 +351,7 @@ def main():
             "avg_us": fd_sec * 1e6, "algorithmic_bytes": fd_bytes,
         },
         "m1": m1,
+        "fp8_gemv": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -54,16 +54,23 @@ typedef enum rra_status {
  *   RRA_F32: fp32 weights.
  *   RRA_Q8 : 32 int8 values q and one fp16 scale per block; w = scale * q.
  *   RRA_Q4 : 32 unsigned 4-bit values q and one fp16 scale per block;
- *            w = scale * (q - 8). */
-typedef enum rra_wfmt { RRA_F32 = 0, RRA_Q8 = 1, RRA_Q4 = 2 } rra_wfmt;
+ *            w = scale * (q - 8).
+ *   RRA_FP8: 32 OCP FP8 E4M3 codes q (sign, 4-bit exponent with bias 7,
+ *            3-bit fraction; no infinity; S.1111.111 is NaN) and one fp16
+ *            scale per block; w = scale * e4m3(q).  The pages run the LM head
+ *            in FP8 ([batched_forward] batched_output_norm_lm_head_argmax);
+ *            here it is one more block format of the same weights-once GEMV,
+ *            usable for any matrix. */
+typedef enum rra_wfmt { RRA_F32 = 0, RRA_Q8 = 1, RRA_Q4 = 2, RRA_FP8 = 3 } rra_wfmt;
 
 /* Storage layouts.
- *   RRA_PLANAR: F32 float[n][k]; Q8 data int8[n][k]; Q4 data uint8[n][k/2]
- *     where byte j of a row holds element 2j in its low nibble and element
- *     2j+1 in its high nibble; scales fp16 bit patterns [n][k/32].
- *   RRA_TILED (Q8/Q4 only): the layout the GEMV streams.  Rows are grouped in
- *     tiles of 16 and K in tiles of 128 (Q4) or 64 (Q8), one tile = 1 KiB of
- *     quantised values followed by its scales (128 B for Q4, 64 B for Q8); the
+ *   RRA_PLANAR: F32 float[n][k]; Q8 data int8[n][k]; FP8 data uint8 codes
+ *     [n][k]; Q4 data uint8[n][k/2] where byte j of a row holds element 2j in
+ *     its low nibble and element 2j+1 in its high nibble; scales fp16 bit
+ *     patterns [n][k/32].
+ *   RRA_TILED (Q8/Q4/FP8): the layout the GEMV streams.  Rows are grouped in
+ *     tiles of 16 and K in tiles of 128 (Q4) or 64 (Q8, FP8), one tile = 1 KiB
+ *     of quantised values followed by its scales (128 B for Q4, 64 B else); the
  *     scales live inside `data` and `scale` is NULL.  Rows are padded to a
  *     multiple of 16 and K to a multiple of the K tile with zero-valued
  *     blocks.  Produced by rra_repack_weight; rra_tiled_bytes gives its size. */

@@ -223,6 +223,7 @@ class DecoderOracle:
     def __init__(self, shape, weights, n_seq: int, max_len: int):
         self.s = shape
         self.fmt = shape.fmt
+        self.lm_fmt = getattr(shape, "lm_format", shape.fmt)
         self.n_seq = n_seq
         self.max_len = max_len
 
@@ -281,6 +282,6 @@ class DecoderOracle:
         for l in range(len(self.layers)):
             x = self.layer(l, x, pos)
         u = rmsnorm(x, self.out_gamma, self.s.rms_eps)
-        logits = self._mv(self.lm_head, self.s.vocab, self.s.hidden, u)
+        logits = gemv(self.lm_fmt, self.lm_head[0], self.lm_head[1], self.s.vocab, self.s.hidden, u)
         tok, gap = argmax(logits)
         return dict(hidden=x, logits=logits, tok=tok, gap=gap)

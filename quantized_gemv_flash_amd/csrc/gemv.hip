@@ -43,6 +43,8 @@ template <>
 struct TileFmt<RRA_Q8> {
     static constexpr int KT = 64, NB = 2, TB = 1024 + 64;
 };
+template <>
+struct TileFmt<RRA_FP8> : TileFmt<RRA_Q8> {};  // one byte per value, same tiles
 
 __device__ __forceinline__ uint32_t pk_sub(uint32_t p, float c) {
     half2_t h = __builtin_bit_cast(half2_t, p);
@@ -86,6 +88,17 @@ __device__ __forceinline__ uint32_t pair_lo(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t v) {
     return __builtin_amdgcn_perm(v, 0x64646464u, 0x00070006u);
+}
+
+// FP8 (OCP E4M3): two dwords = codes of elements 0..7 -> fp16, exactly (E4M3
+// values are a subset of fp16), in element order.  v_cvt_scalef32_pk_f16_fp8
+// converts two codes (bytes 0,1 or 2,3 of a dword) at a time; scale 1.
+__device__ __forceinline__ half8_t dequant_fp8(uint32_t d0, uint32_t d1) {
+    const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+    const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+    const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+    const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+    return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Q8: two dwords = int8 elements 0..7 of a group -> fp16 q in element order.
@@ -267,9 +280,10 @@ struct QGemv {
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 const uint4 qv = q[r];
-                const half8_t a = (FMT == RRA_Q4)
-                                      ? dequant_q4(u32_at(qv, b))
-                                      : dequant_q8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1));
+                const half8_t a =
+                    (FMT == RRA_Q4)    ? dequant_q4(u32_at(qv, b))
+                    : (FMT == RRA_FP8) ? dequant_fp8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1))
+                                       : dequant_q8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1));
 #pragma unroll
                 for (int cc = 0; cc < CT; ++cc) {
                     floatx4 tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -716,6 +730,7 @@ rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, in
     }
     const auto *img = static_cast<const uint8_t *>(x);
     if (w.fmt == RRA_Q4) return launch_fmt<RRA_Q4>(w, p, img, m, out, stride, n, s);
+    if (w.fmt == RRA_FP8) return launch_fmt<RRA_FP8>(w, p, img, m, out, stride, n, s);
     return launch_fmt<RRA_Q8>(w, p, img, m, out, stride, n, s);
 }
 
@@ -743,7 +758,7 @@ rra_status launch_reduce_splits(const float *part, int split, size_t split_strid
 using namespace rra;
 
 extern "C" size_t rra_tiled_bytes(int32_t fmt, int64_t n, int64_t k) {
-    if ((fmt != RRA_Q4 && fmt != RRA_Q8) || n <= 0 || k <= 0 || k % 32) return 0;
+    if (!is_quantised(fmt) || n <= 0 || k <= 0 || k % 32) return 0;
     return (size_t)cdiv(n, 16) * (size_t)cdiv(k, tile_k(fmt)) * (size_t)tile_bytes(fmt);
 }
 
@@ -751,8 +766,8 @@ extern "C" rra_status rra_repack_weight(const rra_weight *planar, void *tiled, s
                                         rra_weight *out, hipStream_t s) {
     clear_error();
     if (!planar || !tiled || !out) return fail(RRA_EINVAL, "rra_repack_weight: null argument");
-    if (planar->fmt != RRA_Q4 && planar->fmt != RRA_Q8)
-        return fail(RRA_EINVAL, "rra_repack_weight: only Q8/Q4 weights are tiled");
+    if (!is_quantised(planar->fmt))
+        return fail(RRA_EINVAL, "rra_repack_weight: only Q8/Q4/FP8 weights are tiled");
     if (planar->layout != RRA_PLANAR)
         return fail(RRA_EINVAL, "rra_repack_weight: input must be planar");
     RRA_TRY(validate_weight(planar, "rra_repack_weight", false));
@@ -782,8 +797,8 @@ extern "C" rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uin
                                         hipStream_t s) {
     clear_error();
     if (!tiled || !data || !scale) return fail(RRA_EINVAL, "rra_unpack_weight: null argument");
-    if ((tiled->fmt != RRA_Q4 && tiled->fmt != RRA_Q8) || tiled->layout != RRA_TILED)
-        return fail(RRA_EINVAL, "rra_unpack_weight: input must be a tiled Q8/Q4 weight");
+    if (!is_quantised(tiled->fmt) || tiled->layout != RRA_TILED)
+        return fail(RRA_EINVAL, "rra_unpack_weight: input must be a tiled Q8/Q4/FP8 weight");
     RRA_TRY(validate_weight(tiled, "rra_unpack_weight", true));
     const int nkt = (int)cdiv(tiled->k, tile_k(tiled->fmt));
     const long long tiles = cdiv(tiled->n, 16) * (long long)nkt;

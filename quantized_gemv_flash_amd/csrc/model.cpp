@@ -51,7 +51,7 @@ rra_status check_launch(const char *what) {
 
 rra_status validate_weight(const rra_weight *w, const char *what, bool need_tiled_q) {
     if (!w) return fail(RRA_EINVAL, "%s: null weight", what);
-    if (w->fmt != RRA_F32 && w->fmt != RRA_Q8 && w->fmt != RRA_Q4)
+    if (w->fmt != RRA_F32 && !is_quantised(w->fmt))
         return fail(RRA_EINVAL, "%s: unknown weight format %d", what, w->fmt);
     if (w->n <= 0 || w->k <= 0 || w->n > (1LL << 30) || w->k > (1LL << 24))
         return fail(RRA_EINVAL, "%s: bad shape %lld x %lld", what, (long long)w->n,
@@ -64,9 +64,9 @@ rra_status validate_weight(const rra_weight *w, const char *what, bool need_tile
     if (w->k % 32) return fail(RRA_EINVAL, "%s: k=%lld is not a multiple of 32", what, (long long)w->k);
     if (w->layout == RRA_PLANAR) {
         if (need_tiled_q)
-            return fail(RRA_EINVAL, "%s: planar Q8/Q4 weight; convert it with rra_repack_weight",
+            return fail(RRA_EINVAL, "%s: planar quantised weight; convert it with rra_repack_weight",
                         what);
-        if (!w->scale) return fail(RRA_EINVAL, "%s: planar Q8/Q4 weight without scales", what);
+        if (!w->scale) return fail(RRA_EINVAL, "%s: planar quantised weight without scales", what);
         return RRA_OK;
     }
     if (w->layout != RRA_TILED) return fail(RRA_EINVAL, "%s: unknown layout %d", what, w->layout);

@@ -39,6 +39,8 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // A tile covers 16 rows and KT columns: 1 KiB of quantised values, then the
 // scales of its 16 rows x NB blocks.
 constexpr int kRowTile = 16;
+// Q8 and FP8 share one tile geometry (one byte per value); Q4 has its own.
+inline bool is_quantised(int fmt) { return fmt == RRA_Q8 || fmt == RRA_Q4 || fmt == RRA_FP8; }
 inline int tile_k(int fmt) { return fmt == RRA_Q4 ? 128 : 64; }
 inline int tile_blocks(int fmt) { return fmt == RRA_Q4 ? 4 : 2; }
 inline int tile_bytes(int fmt) { return fmt == RRA_Q4 ? 1024 + 128 : 1024 + 64; }
@@ -80,7 +82,7 @@ rra_status launch_reduce_splits(const float *part, int split, size_t split_strid
 // Where a producer writes the next GEMV's activation image (frag.h).
 struct FragOut {
     uint8_t *img;  // nullptr: no image (fp32 weights)
-    int fmt;       // RRA_Q8 / RRA_Q4
+    int fmt;       // the consumer's format: RRA_Q4, or RRA_Q8 / RRA_FP8 (same image)
     int ct;        // column tiles (1 for m <= 16, 2 otherwise)
     int kpad;      // K rounded up to the K tile; groups in [K, kpad) are zeros
 };

@@ -55,8 +55,9 @@ def load_decoder(shape, weights, m_max: int, max_len: int, attn_chunk: int = 0,
         d.update(attn_gamma=lw.attn_gamma, ffn_gamma=lw.ffn_gamma, k_cache=kc, v_cache=vc)
         layers.append(d)
         keep.append(d)
-    lm = device_weight(weights.lm_head[0], weights.lm_head[1], S.fmt, stream)
-    if drop_planar and S.fmt != "f32":
+    lm_fmt = getattr(S, "lm_format", S.fmt)
+    lm = device_weight(weights.lm_head[0], weights.lm_head[1], lm_fmt, stream)
+    if drop_planar and lm_fmt != "f32":
         weights.lm_head = (None, None)
     model = Model(n_layers=len(layers), hidden=S.hidden, n_heads=S.n_heads,
                   n_kv_heads=S.n_kv_heads, head_dim=S.head_dim, intermediate=S.intermediate,

@@ -52,10 +52,15 @@ class Decoder:
     #   "kv:N"      cache rows [0, N) filled with seeded N(0,1) K and V
     #   "kv:A-B"    per-sequence length drawn uniformly from [A, B]
     context: str = "none"
+    lm_fmt: Optional[str] = None  # LM-head format when it differs from `fmt`
 
     @property
     def qkv_rows(self) -> int:
         return (self.n_heads + 2 * self.n_kv_heads) * self.head_dim
+
+    @property
+    def lm_format(self) -> str:
+        return self.lm_fmt or self.fmt
 
 
 @dataclasses.dataclass(frozen=True)
@@ -99,6 +104,16 @@ LLAMA3_8B_Q4 = Decoder(
 
 WORKLOADS = {w.name: w for w in (TINY_LLAMA_F32, QWEN25_05B_Q8, FLASH_DECODE_M32,
                                  QWEN25_15B_Q4, LLAMA3_8B_Q4)}
+
+# Test shapes for the FP8 block format (not workloads of the pages): a small
+# all-FP8 decoder, and a Q4 decoder with an FP8 LM head (the pages' split).
+SMALL_LLAMA_FP8 = Decoder(
+    name="small-llama-fp8", n_layers=2, hidden=256, n_heads=4, n_kv_heads=2,
+    head_dim=64, intermediate=704, vocab=1024, fmt="fp8", m=2, steps=8, max_len=16)
+SMALL_LLAMA_Q4_FP8_HEAD = Decoder(
+    name="small-llama-q4-fp8-head", n_layers=2, hidden=256, n_heads=4, n_kv_heads=2,
+    head_dim=64, intermediate=704, vocab=1024, fmt="q4", lm_fmt="fp8", m=2, steps=8,
+    max_len=16)
 
 
 # --------------------------------------------------------------------------
@@ -264,7 +279,7 @@ def decoder_weights(w: Decoder, seed: int = 0, device="cpu", gamma: str = "ones"
     return DecoderWeights(
         layers=[decoder_layer(w, l, seed, device, gamma) for l in range(n)],
         out_gamma=_gamma(w.hidden, gamma, seed, "out_gamma", device),
-        lm_head=weight(w.vocab, w.hidden, w.fmt, w.weight_std, seed, "lm_head", device),
+        lm_head=weight(w.vocab, w.hidden, w.lm_format, w.weight_std, seed, "lm_head", device),
         embed=normal((w.vocab, w.hidden), 1.0, seed, "embed", device),
     )
 

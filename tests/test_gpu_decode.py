@@ -233,6 +233,24 @@ def test_empty_slots_in_device_greedy_loop():
 
 
 # ---------------------------------------------------------------- quantised decoders
+@pytest.mark.parametrize("S", [synth.SMALL_LLAMA_FP8, synth.SMALL_LLAMA_Q4_FP8_HEAD],
+                         ids=lambda S: S.name)
+def test_fp8_weights_small_decoder(S):
+    # FP8 (E4M3) blocks for every matrix, and a Q4 decoder with an FP8 LM head:
+    # two sequences, greedy steps in one graph, against the oracle.
+    banner("decode", S.name)
+    W = synth.decoder_weights(S, seed=0, device=DEV, gamma="random")
+    run = Run(S, W, S.m, S.max_len)
+    orc = oracle.DecoderOracle(S, W, S.m, S.max_len)
+    tok = synth.first_tokens(S, S.m).tolist()
+    for step in range(S.steps):
+        pos = [step, step + 3]
+        gpu = run.step(tok, pos, flags=rra.RRA_GRAPH)
+        o = orc.step(host(W.embed[torch.as_tensor(tok, device=DEV)]), pos)
+        compare_step(gpu, o, f"step {step}")
+        tok = o["tok"].tolist()
+
+
 def test_qwen05b_q8_context_then_greedy():
     # Full 24-layer Q8 decoder at M=1: 8 teacher-forced context steps on random
     # token ids, then 8 greedy steps (the bench runs the 512-token context).

@@ -14,7 +14,7 @@ POW2_SCALES = np.array([0x3C00, 0x3800, 0x4000, 0x3400, 0x2C00], np.uint16)  # 1
 
 
 # ---------------------------------------------------------------- layout
-@pytest.mark.parametrize("fmt", ["q4", "q8"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "fp8"])
 @pytest.mark.parametrize("n,k", [(16, 32), (37, 96), (300, 416), (33, 160)])
 def test_repack_roundtrip_bit_exact(fmt, n, k):
     banner("repack", fmt, n, k)
@@ -42,7 +42,7 @@ def _gemv(fmt, data, scale, x, m):
 
 @pytest.mark.parametrize("m", [1, 3, 16, 17, 32])
 @pytest.mark.parametrize("n,k", [(16, 32), (37, 96), (300, 416), (1000, 2048), (64, 14336)])
-@pytest.mark.parametrize("fmt", ["q4", "q8", "f32"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "fp8", "f32"])
 def test_gemv_matches_oracle(fmt, n, k, m):
     banner("gemv", fmt, n, k, m)
     data, scale = synth.weight(n, k, fmt, 0.02, 0, f"g{n}x{k}", DEV)
@@ -53,18 +53,25 @@ def test_gemv_matches_oracle(fmt, n, k, m):
 
 
 @pytest.mark.parametrize("m", [1, 5, 32])
-@pytest.mark.parametrize("fmt", ["q4", "q8"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "fp8"])
 def test_gemv_integer_exact(fmt, m):
     # Power-of-two scales and small integer inputs: every partial sum is exact
     # in fp32 as well as in the oracle's fp64, so the results must be equal.
+    # FP8: scale 1 and codes with exponents 6..9 (|value| in [0.5, 16), 4
+    # significant bits) keep every sum within fp32's 24 bits.
     banner("gemv exact", fmt, m)
     n, k = 70, 640
     g = np.random.default_rng(11)
     scale = torch.from_numpy(POW2_SCALES[g.integers(0, 5, size=(n, k // 32))].view(np.int16)).to(DEV)
     if fmt == "q4":
         data = torch.from_numpy(g.integers(0, 256, size=(n, k // 2), dtype=np.uint8)).to(DEV)
-    else:
+    elif fmt == "q8":
         data = torch.from_numpy(g.integers(-127, 128, size=(n, k), dtype=np.int8)).to(DEV)
+    else:
+        codes = np.array([s << 7 | e << 3 | f for s in (0, 1) for e in range(6, 10) for f in range(8)],
+                         np.uint8)
+        data = torch.from_numpy(codes[g.integers(0, codes.size, size=(n, k))]).to(DEV)
+        scale = torch.full((n, k // 32), 0x3C00, dtype=torch.int16, device=DEV)
     x = torch.from_numpy(g.integers(-8, 9, size=(m, k)).astype(np.float32)).to(DEV)
     y = _gemv(fmt, data, scale, x, m)
     ref = oracle.gemv(fmt, data, scale, n, k, host(x))
@@ -87,6 +94,7 @@ FULL_SHAPES = [
     ("q4", 151936, 1536),
     ("q4", 6144, 4096), ("q4", 4096, 4096), ("q4", 28672, 4096), ("q4", 4096, 14336),
     ("q4", 128256, 4096),
+    ("fp8", 151936, 896), ("fp8", 128256, 4096), ("fp8", 4096, 14336),
 ]
 
 
