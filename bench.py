@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--only-m1", action="store_true", help="run only the M=1 line")
     ap.add_argument("--m1-steps", type=int, default=256)
     ap.add_argument("--m1-ctx", type=int, default=512, help="context tokens of the M=1 line")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 1.5B-shaped M sweep")
     ap.add_argument("--fd-only", action="store_true",
                     help="run only the flash-decode launches (layer-sized synthetic cache at the "
                          "workload's lengths) and a plain copy of known size, for counter runs")
@@ -198,6 +199,30 @@ def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps):
                        f"workload ({sec:.1f} s; fp64, {threads} OpenMP threads)")
 
 
+def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32)):
+    """The 1.5B-shaped Q4 decoder over a synthetic 1024-row KV context per
+    sequence: greedy decode tok/s at each batch size M (one graph per M)."""
+    import synth
+    S = synth.QWEN25_15B_Q4
+    m_max = max(ms)
+    W, dd = build_decoder(S, m_max, S.max_len)
+    lengths = synth.context_lengths(S, m_max)
+    fill_kv_context(S, dd, lengths)
+    first = synth.first_tokens(S, m_max).tolist()
+    wbytes = dd.weight_bytes()
+    out = dict(workload=f"{S.name}: 1024-row context, {steps} greedy steps per M, one graph per step",
+               weight_bytes=wbytes)
+    for m in ms:
+        sec, _, _ = timed_greedy(dd, S, m, first[:m], lengths[:m], steps, 2)
+        kv = sum(S.n_layers * 2 * S.n_kv_heads * (L + i + 1) * S.head_dim * 4
+                 for L in lengths[:m] for i in range(steps)) / steps
+        out[f"m{m}"] = dict(tok_s=m * steps / sec, ms_per_step=1e3 * sec / steps,
+                            hbm_frac=(wbytes + kv) * steps / sec / 1e9 / HBM_PEAK_GBS)
+    del dd, W
+    torch.cuda.empty_cache()
+    return out
+
+
 def fp8_gemv_line(reps=20):
     """The FP8 (E4M3) block format on the weights-once GEMV at the LM-head shape
     of the 8B-shaped decoder (128256 x 4096): rra_batched_gemv (activation
@@ -319,6 +344,8 @@ def main():
         log(f"m1 {m1}")
     fp8 = fp8_gemv_line()
     log(f"fp8 gemv {fp8}")
+    sweep = None if args.no_sweep else m_sweep_line()
+    log(f"m sweep {sweep}")
 
     out = {
         "metric": "decode tok/s at M=1 and M=32; weight+KV stream HBM GB/s as % of peak",
@@ -352,6 +379,7 @@ def main():
         },
         "m1": m1,
         "fp8_gemv": fp8,
+        "m_sweep": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

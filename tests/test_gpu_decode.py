@@ -288,6 +288,32 @@ def test_qwen15b_q4_batch4_context1024():
         tok = o["tok"].tolist()
 
 
+@pytest.mark.parametrize("m", [1, 32])
+def test_qwen15b_q4_m_sweep_ends(m):
+    # The 1.5B-shaped Q4 decoder at the ends of its batch sweep, 1024-row
+    # synthetic contexts, one captured graph; the oracle checks up to two
+    # sampled sequences.
+    S = synth.QWEN25_15B_Q4
+    banner("decode", S.name, "m", m)
+    W = synth.decoder_weights(S, seed=0, device=DEV)
+    run = Run(S, W, m, S.max_len)
+    sample = [0] if m == 1 else [5, 31]
+    orc = oracle.DecoderOracle(S, W, len(sample), S.max_len)
+    lens = synth.context_lengths(S, m)
+    run.fill_context(lens, orc, sample)
+    tok = synth.first_tokens(S, m).tolist()
+    for step in range(2):
+        pos = [L + step for L in lens]
+        ids, hid, logits = run.step(tok, pos, flags=rra.RRA_GRAPH)
+        xs = host(W.embed[torch.as_tensor([tok[i] for i in sample], device=DEV)])
+        o = orc.step(xs, [pos[i] for i in sample])
+        compare_step(([ids[i] for i in sample], hid[sample], logits[sample]), o, f"step {step}")
+        new = list(ids)
+        for j, i in enumerate(sample):
+            new[i] = int(o["tok"][j])
+        tok = new
+
+
 def test_llama8b_q4_batch32_graph_sampled_sequences():
     # Full 32-layer Q4 decoder, 32 sequences at positions in [2048, 4096], one
     # captured graph; the oracle checks two sampled sequences.
