@@ -231,7 +231,8 @@ typedef struct rra_model_desc {
     const float *out_gamma;        /* device [hidden] */
     rra_weight lm_head;            /* [vocab][hidden] */
     const float *embed;            /* device [vocab][hidden] fp32, or NULL (needed for RRA_STEP_GATHER) */
-    int32_t attn_chunk;            /* flash-decode rows per split, 0 = library choice */
+    int32_t attn_chunk;            /* flash-decode rows per split; 0 = chosen by the library
+                                      for each step from its m, nkv and max_len */
 } rra_model_desc;
 
 typedef struct rra_model rra_model;

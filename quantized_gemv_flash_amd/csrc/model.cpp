@@ -169,7 +169,7 @@ struct GraphEntry {
 struct rra_model {
     rra_model_desc d{};
     std::vector<rra_layer_desc> layers;
-    int chunk = 0;
+    int chunk[RRA_M_MAX + 1] = {};  // flash-decode rows per split, per batch size
     // workspace carve-up
     float *ss = nullptr, *xg = nullptr, *part = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr;
     float *fd = nullptr, *logits = nullptr, *rope = nullptr;
@@ -218,7 +218,19 @@ size_t part_floats(const rra_model_desc &d, const rra_layer_desc &l) {
     return best;
 }
 
-Layout layout_of(const rra_model_desc &d, int chunk) {
+// Flash-decode chunk used for a step of m sequences.
+int chunk_for(const rra_model_desc &d, int m) {
+    return fd_choose_chunk(m, d.n_kv_heads, d.max_len, d.attn_chunk);
+}
+
+size_t fd_floats(const rra_model_desc &d) {
+    size_t best = 0;
+    for (int m = 1; m <= d.m_max; ++m)
+        best = std::max(best, fd_partials_floats(m, d.n_heads, d.head_dim, d.max_len, chunk_for(d, m)));
+    return best;
+}
+
+Layout layout_of(const rra_model_desc &d) {
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -237,7 +249,7 @@ Layout layout_of(const rra_model_desc &d, int chunk) {
     L.lens = take(4 * M);
     L.attn = take(4 * M * d.n_heads * d.head_dim);
     L.act = take(4 * M * d.intermediate);
-    L.fd = take(4 * fd_partials_floats((int)M, d.n_heads, d.head_dim, d.max_len, chunk));
+    L.fd = take(4 * fd_floats(d));
     L.logits = take(4 * M * (size_t)d.vocab);
     L.argmax = take(argmax_ws_bytes((int)M, d.vocab));
     L.rope = take(4 * (size_t)d.max_len * d.head_dim);
@@ -332,7 +344,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, fl
                                 s));
         const FragOut fo_o = image_for(M, L.wo, m);
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
-                                    d.max_len, M->chunk, M->fd, s, &fo_o));
+                                    d.max_len, M->chunk[m], M->fd, s, &fo_o));
         const GemvPlan &po = M->plan_o[m];
         RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part, (size_t)m * H, s));
         RRA_TRY(launch_residual_ss(M->part, po.split, (size_t)m * H, x, M->ss, L.ffn_gamma, M->xg, m,
@@ -360,8 +372,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, fl
 
 extern "C" size_t rra_model_workspace_bytes(const rra_model_desc *d) {
     if (validate_desc(d) != RRA_OK) return 0;
-    const int chunk = fd_choose_chunk(d->m_max, d->n_kv_heads, d->max_len, d->attn_chunk);
-    return layout_of(*d, chunk).total;
+    return layout_of(*d).total;
 }
 
 extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t ws_bytes,
@@ -371,8 +382,7 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     *out = nullptr;
     RRA_TRY(validate_desc(d));
     if (!ws) return fail(RRA_EINVAL, "rra_model_create: null workspace");
-    const int chunk = fd_choose_chunk(d->m_max, d->n_kv_heads, d->max_len, d->attn_chunk);
-    const Layout L = layout_of(*d, chunk);
+    const Layout L = layout_of(*d);
     if (ws_bytes < L.total)
         return fail(RRA_ENOTINIT, "rra_model_create: workspace has %zu bytes, needs %zu", ws_bytes,
                     L.total);
@@ -380,7 +390,6 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     M->d = *d;
     M->layers.assign(d->layers, d->layers + d->n_layers);
     M->d.layers = M->layers.data();
-    M->chunk = chunk;
     char *b = static_cast<char *>(ws);
     M->ss = reinterpret_cast<float *>(b + L.ss);
     M->xg = reinterpret_cast<float *>(b + L.xg);
@@ -396,6 +405,7 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     M->rope = reinterpret_cast<float *>(b + L.rope);
     M->err = reinterpret_cast<uint32_t *>(b + L.err);
     for (int m = 1; m <= d->m_max; ++m) {
+        M->chunk[m] = chunk_for(*d, m);
         const rra_layer_desc &l0 = d->layers[0];
         M->plan_qkv[m] = gemv_plan(l0.wqkv, m);
         M->plan_o[m] = gemv_plan(l0.wo, m);
