@@ -63,12 +63,23 @@ __device__ __forceinline__ uint32_t u32_at(const uint4 &v, int i) {
 // comes from one v_and_or_b32 that drops two nibbles into the mantissas of
 // the fp16 pair 1024 + n (low nibbles) or 1024 + 16 n (high nibbles), and one
 // packed fp16 op that maps it to n - 8 (exact: small integers).
+//
+// The compiler splits (w & mask) | bits into v_and_b32 + v_or_b32 because a
+// VOP3 instruction takes no literal operand on this target; the inline form
+// keeps one instruction by taking the mask from an SGPR and the fp16 exponent
+// bits from a VGPR (one scalar operand per VALU instruction).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(bits));
+    return r;
+}
+
 __device__ __forceinline__ half8_t dequant_q4(uint32_t w) {
-    const uint32_t w8 = w >> 8;
-    const half2_t lo_a = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | 0x64006400u);
-    const half2_t hi_a = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | 0x64006400u);
-    const half2_t lo_b = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | 0x64006400u);
-    const half2_t hi_b = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | 0x64006400u);
+    const uint32_t w8 = w >> 8, e = 0x64006400u;
+    const half2_t lo_a = __builtin_bit_cast(half2_t, and_or(w, 0x000F000Fu, e));
+    const half2_t hi_a = __builtin_bit_cast(half2_t, and_or(w, 0x00F000F0u, e));
+    const half2_t lo_b = __builtin_bit_cast(half2_t, and_or(w8, 0x000F000Fu, e));
+    const half2_t hi_b = __builtin_bit_cast(half2_t, and_or(w8, 0x00F000F0u, e));
     const half2_t k1032 = {(_Float16)1032.f, (_Float16)1032.f};
     const half2_t r16 = {(_Float16)0.0625f, (_Float16)0.0625f};
     const half2_t k72 = {(_Float16)-72.f, (_Float16)-72.f};
@@ -155,18 +166,22 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int FMT, int CT, int RPW>
+template <int FMT, int CT, int RPW, int NW>
 struct QGemv {
     using F = TileFmt<FMT>;
     static constexpr int NB = F::NB, TB = F::TB;
-    static constexpr int FRAG = NB * CT * 2;       // 1 KiB image fragments per K tile
-    static constexpr int SB = TB - 1024;           // scale bytes per tile
-    static constexpr int SCH = 4 * RPW * SB / 16;  // 16-byte scale pieces per K tile
-    static constexpr int XB = FRAG * 1024;         // image bytes per K tile
-    static constexpr int XDW = FRAG / 4;           // image DMAs per wave per K tile
-    static constexpr int SCW = (SCH + 63) / 64;    // waves that DMA one scale piece each
-    static constexpr int SCB = SCW * 1024;         // scale bytes per LDS buffer
-    static_assert(FRAG % 4 == 0 && SCW <= 4, "DMA split over the 4 waves");
+    static constexpr int FRAG = NB * CT * 2;        // 1 KiB image fragments per K tile
+    static constexpr int SB = TB - 1024;            // scale bytes per tile
+    static constexpr int SCH = NW * RPW * SB / 16;  // 16-byte scale pieces per K tile
+    static constexpr int XB = FRAG * 1024;          // image bytes per K tile
+    static constexpr int XDW = (FRAG + NW - 1) / NW;  // image DMAs per wave per K tile
+    static constexpr int SCW = (SCH + 63) / 64;     // waves that DMA one scale piece each
+    static constexpr int SCB = SCW * 1024;          // scale bytes per LDS buffer
+    static_assert(SCW <= NW, "scale DMA split over the waves");
+    // fragment wave + NW * j exists (every wave has XDW when NW divides FRAG)
+    __device__ __forceinline__ bool has_frag(int j) const {
+        return FRAG % NW == 0 || wave + NW * j < FRAG;
+    }
     typedef uint4 Ring[RPW];
     typedef floatx4 Acc[RPW][CT];
 
@@ -180,8 +195,8 @@ struct QGemv {
         const int kt = min(kt_begin + c, kt_end - 1);
 #pragma unroll
         for (int j = 0; j < XDW; ++j) {
-            const int f = wave + 4 * j;
-            dma16(ximg + ((size_t)kt * FRAG + f) * 1024 + lane * 16, xd + f * 1024);
+            const int f = wave + NW * j;
+            if (has_frag(j)) dma16(ximg + ((size_t)kt * FRAG + f) * 1024 + lane * 16, xd + f * 1024);
         }
         if (wave < SCW) {  // piece e -> (row tile, piece)
             const int e = min(wave * 64 + lane, SCH - 1);
@@ -221,7 +236,7 @@ struct QGemv {
     __device__ __forceinline__ void stage_at(const Cursor &k, uint32_t xd, uint32_t sd) const {
 #pragma unroll
         for (int j = 0; j < XDW; ++j)
-            dma16(k.x + (size_t)4 * j * 1024, xd + (uint32_t)(wave + 4 * j) * 1024);
+            if (has_frag(j)) dma16(k.x + (size_t)NW * j * 1024, xd + (uint32_t)(wave + NW * j) * 1024);
         if (wave < SCW) dma16(k.s, sd + (uint32_t)wave * 1024);
     }
     __device__ __forceinline__ void issue_at(const Cursor &k, Ring &q) const {
@@ -295,6 +310,13 @@ struct QGemv {
                 }
             }
         }
+        // The tile's accumulator updates stay here: left free, the compiler
+        // sinks them past the step's barrier, keeping every MFMA result of the
+        // tile live (registers) and leaving the matrix unit idle meanwhile.
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int cc = 0; cc < CT; ++cc) asm volatile("" : "+v"(acc[r][cc]));
     }
 
     // One pipeline iteration: DMA of the next tile (cursor kn) into xw/sw and
@@ -374,7 +396,7 @@ struct QGemv {
         g = lane >> 4;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         n_rt = (N + 15) >> 4;
-        rt_wg = blockIdx.x * 4 * RPW;
+        rt_wg = blockIdx.x * NW * RPW;
         rt0 = rt_wg + wave * RPW;
         nkt = nkt_;
         kt_begin = blockIdx.y * kt_per_split;
@@ -382,20 +404,22 @@ struct QGemv {
     }
 };
 
-// Grid (row blocks of 64*RPW rows, K splits); 256 threads = 4 waves; wave w
-// owns row tiles [(blockIdx.x*4 + w)*RPW, +RPW).  The split's K tiles are
+// Grid (row blocks of 16*NW*RPW rows, K splits); NW waves; wave w owns row
+// tiles [(blockIdx.x*NW + w)*RPW, +RPW).  All NW waves share each staged
+// activation tile, so more waves per workgroup move fewer image bytes per
+// weight byte.  The split's K tiles are
 // processed in a two-stage software pipeline (QGemv::step): while tile c is
 // computed from registers and one LDS buffer, tile c+1's weights load into
 // the other register set and its activation image and scales into the other
 // LDS buffer by LDS-DMA.  Outputs are multiplied by inv[m] (RMSNorm, when
 // nrm.ss is set) and written to out[split][m][n] (split_stride floats apart).
-template <int FMT, int CT, int RPW>
-__global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__ wt,
-                                                     const uint8_t *__restrict__ ximg,
-                                                     float *__restrict__ out, int M, int N, int K,
-                                                     int nkt, int kt_per_split,
-                                                     long long split_stride, NormIn nrm) {
-    using G = QGemv<FMT, CT, RPW>;
+template <int FMT, int CT, int RPW, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_q_kernel(const uint8_t *__restrict__ wt,
+                                                         const uint8_t *__restrict__ ximg,
+                                                         float *__restrict__ out, int M, int N,
+                                                         int K, int nkt, int kt_per_split,
+                                                         long long split_stride, NormIn nrm) {
+    using G = QGemv<FMT, CT, RPW, NW>;
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::XB];
     __shared__ __attribute__((aligned(16))) uint8_t sl[2][G::SCB];
 
@@ -447,13 +471,14 @@ __global__ __launch_bounds__(256) void gemv_q_kernel(const uint8_t *__restrict__
 // tile.  Tiles past the split end are clamped copies, never computed.
 // Because no DMA follows a weight load, the compiler's own count of the
 // loads in flight matches the hardware's and it adds no waits.
-template <int FMT, int CT, int RPW, int NT>
-__global__ __launch_bounds__(256) void gemv_q_short_kernel(const uint8_t *__restrict__ wt,
-                                                           const uint8_t *__restrict__ ximg,
-                                                           float *__restrict__ out, int M, int N,
-                                                           int K, int nkt, int kt_per_split,
-                                                           long long split_stride, NormIn nrm) {
-    using G = QGemv<FMT, CT, RPW>;
+template <int FMT, int CT, int RPW, int NW, int NT>
+__global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__restrict__ wt,
+                                                               const uint8_t *__restrict__ ximg,
+                                                               float *__restrict__ out, int M,
+                                                               int N, int K, int nkt,
+                                                               int kt_per_split,
+                                                               long long split_stride, NormIn nrm) {
+    using G = QGemv<FMT, CT, RPW, NW>;
     __shared__ __attribute__((aligned(16))) uint8_t xs[NT][G::XB];
     __shared__ __attribute__((aligned(16))) uint8_t sl[NT][G::SCB];
 
@@ -662,24 +687,24 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ tiled, uint8_t *__rest
     }
 }
 
-template <int FMT, int CT, int RPW>
+template <int FMT, int CT, int RPW, int NW>
 rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m, float *out,
                     size_t stride, const NormIn &nrm, hipStream_t s) {
     const int n_rt = (int)cdiv(w.n, 16);
     const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
-    dim3 grid((unsigned)cdiv(n_rt, 4 * RPW), (unsigned)p.split);
+    dim3 grid((unsigned)cdiv(n_rt, NW * RPW), (unsigned)p.split), block(64 * NW);
     const auto *wd = static_cast<const uint8_t *>(w.data);
     if (p.kt_per_split <= 2) {
-        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, 2>), grid, dim3(256), 0, s, wd, img,
+        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, NW, 2>), grid, block, 0, s, wd, img,
                            out, m, (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
         return check_launch("gemv_q_short_kernel");
     }
     if (p.kt_per_split <= 4) {
-        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, 4>), grid, dim3(256), 0, s, wd, img,
+        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, NW, 4>), grid, block, 0, s, wd, img,
                            out, m, (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
         return check_launch("gemv_q_short_kernel");
     }
-    hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW>), grid, dim3(256), 0, s, wd, img, out, m,
+    hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW, NW>), grid, block, 0, s, wd, img, out, m,
                        (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
     return check_launch("gemv_q_kernel");
 }
@@ -688,11 +713,15 @@ template <int FMT>
 rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m,
                       float *out, size_t stride, const NormIn &nrm, hipStream_t s) {
     if (m <= 16) {
-        if (p.rpw >= 2) return launch_q<FMT, 1, 2>(w, p, img, m, out, stride, nrm, s);
-        return launch_q<FMT, 1, 1>(w, p, img, m, out, stride, nrm, s);
+        if (p.rpw >= 2) return launch_q<FMT, 1, 2, 4>(w, p, img, m, out, stride, nrm, s);
+        return launch_q<FMT, 1, 1, 4>(w, p, img, m, out, stride, nrm, s);
     }
-    if (p.rpw >= 2) return launch_q<FMT, 2, 2>(w, p, img, m, out, stride, nrm, s);
-    return launch_q<FMT, 2, 1>(w, p, img, m, out, stride, nrm, s);
+    if (p.nw == 8) {
+        if (p.rpw >= 2) return launch_q<FMT, 2, 2, 8>(w, p, img, m, out, stride, nrm, s);
+        return launch_q<FMT, 2, 1, 8>(w, p, img, m, out, stride, nrm, s);
+    }
+    if (p.rpw >= 2) return launch_q<FMT, 2, 2, 4>(w, p, img, m, out, stride, nrm, s);
+    return launch_q<FMT, 2, 1, 4>(w, p, img, m, out, stride, nrm, s);
 }
 
 }  // namespace
@@ -705,7 +734,12 @@ GemvPlan gemv_plan(const rra_weight &w, int m) {
     // Row tiles per wave: 2 (fewer activation bytes per weight byte), or 1
     // when that leaves fewer than 128 row blocks.
     p.rpw = cdiv(n_rt, 8) >= 128 ? 2 : 1;
-    const int n_rb = (int)cdiv(n_rt, 4 * p.rpw);
+    // 8 waves per workgroup (one activation tile shared by twice the rows:
+    // half the image bytes per weight byte) where that still leaves at least
+    // 256 workgroups, i.e. LM-head-sized N; used at m > 16, where the image
+    // has two column tiles.  Each output is computed the same way either way.
+    p.nw = cdiv(n_rt, 8 * p.rpw) >= 256 ? 8 : 4;
+    const int n_rb = (int)cdiv(n_rt, p.nw * p.rpw);
     // K splits: a power of two giving about 768 workgroups (3 per compute
     // unit).  The plan depends on the weight shape only, never on m, so a
     // sequence's result is bit-identical whatever batch it is computed in.

@@ -49,11 +49,12 @@ rra_status validate_weight(const rra_weight *w, const char *what, bool need_tile
 
 // ------------------------------------------------------------------ GEMV
 // How one GEMV is spread over the chip: `split` K-splits, each writing
-// partial sums [split][m][n]; `rpw` row tiles per wave (256-thread groups of
-// 4 waves).
+// partial sums [split][m][n]; workgroups of `nw` waves, each wave owning
+// `rpw` row tiles.
 struct GemvPlan {
     int split = 1;
-    int rpw = 1;
+    int rpw = 1;  // row tiles (16 rows) per wave
+    int nw = 4;   // waves per workgroup sharing one activation tile
     int kt_per_split = 1;
 };
 GemvPlan gemv_plan(const rra_weight &w, int m);
