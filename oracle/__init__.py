@@ -253,7 +253,12 @@ class DecoderOracle:
     def _mv(self, w, n, k, x):
         return gemv(self.fmt, w[0], w[1], n, k, x)
 
-    def layer(self, l: int, x: np.ndarray, pos: Sequence[int]) -> np.ndarray:
+    def layer(self, l: int, x: np.ndarray, pos: Sequence[int],
+              slots: Optional[Sequence[int]] = None) -> np.ndarray:
+        """Row i sits at position pos[i] of the oracle's sequence slots[i]
+        (default i).  Rows are taken in order, each writing its K/V row and then
+        attending to rows [0, pos[i]] of its sequence, so rows that share a
+        sequence at consecutive positions attend causally (a prefill)."""
         S, Lw = self.s, self.layers[l]
         M, H = x.shape
         nq, nkv, hd, I = S.n_heads, S.n_kv_heads, S.head_dim, S.intermediate
@@ -265,23 +270,34 @@ class DecoderOracle:
             k = qkv[i, nq * hd:(nq + nkv) * hd].reshape(nkv, hd)
             v = qkv[i, (nq + nkv) * hd:].reshape(nkv, hd)
             p = int(pos[i])
+            c = i if slots is None else int(slots[i])
             q, k = rope(q, p, S.rope_theta), rope(k, p, S.rope_theta)
-            self.kc[l][i, :, p] = k
-            self.vc[l][i, :, p] = v
-            attn[i] = attention(q, self.kc[l][i], self.vc[l][i], p + 1).reshape(-1)
+            self.kc[l][c, :, p] = k
+            self.vc[l][c, :, p] = v
+            attn[i] = attention(q, self.kc[l][c], self.vc[l][c], p + 1).reshape(-1)
         x = x + self._mv(Lw["wo"], H, nq * hd, attn)
         u = rmsnorm(x, Lw["ffn_gamma"], S.rms_eps)
         gu = self._mv(Lw["wgu"], 2 * I, H, u)
         a = swiglu(gu[:, :I], gu[:, I:])
         return x + self._mv(Lw["wd"], H, I, a)
 
-    def step(self, x, pos: Sequence[int]):
+    def step(self, x, pos: Sequence[int], slots: Optional[Sequence[int]] = None):
         """One decode step for the oracle's sequences.  x [n][H] (embedding rows),
-        pos [n].  Returns dict(hidden [n][H], logits [n][V], tok [n], gap [n])."""
+        pos [n], slots [n] (sequence of each row, default row i -> sequence i).
+        Returns dict(hidden [n][H], logits [n][V], tok [n], gap [n])."""
         x = np.asarray(_np(x), np.float64).reshape(len(pos), self.s.hidden)
         for l in range(len(self.layers)):
-            x = self.layer(l, x, pos)
+            x = self.layer(l, x, pos, slots)
         u = rmsnorm(x, self.out_gamma, self.s.rms_eps)
         logits = gemv(self.lm_fmt, self.lm_head[0], self.lm_head[1], self.s.vocab, self.s.hidden, u)
         tok, gap = argmax(logits)
         return dict(hidden=x, logits=logits, tok=tok, gap=gap)
+
+    def prefill(self, seq: int, x, start: int):
+        """Prompt ingestion ([head_dim] tensor_core_attention: causal
+        attention over the prompt): the T embedding rows x [T][H] at positions
+        start .. start+T-1 of sequence `seq`, every layer over all T rows, row t
+        attending to rows [0, start + t] of the sequence.  Returns step()'s dict
+        for the T rows; the last row's tok is the next greedy token."""
+        T = np.asarray(_np(x)).reshape(-1, self.s.hidden).shape[0]
+        return self.step(x, [start + t for t in range(T)], [seq] * T)

@@ -380,3 +380,81 @@ def test_decoder_oracle_batched_equals_separate_sequences():
         one = oracle.DecoderOracle(S, wts, 1, S.max_len).step(x[i:i + 1], pos[i:i + 1])
         assert np.array_equal(one["logits"][0], both["logits"][i])
         assert np.array_equal(one["hidden"][0], both["hidden"][i])
+
+
+def _torch_llama_prefill(shape, wts, xs, start, ctx):
+    """Prompt ingestion written independently in matrix form: all T rows of a
+    layer at once, RoPE as a complex rotation at positions start..start+T-1,
+    and attention as torch sdpa over [context rows; prompt rows] with an
+    explicit causal mask (row t sees keys j <= start + t)."""
+    S = shape
+    nq, nkv, hd, I, H = S.n_heads, S.n_kv_heads, S.head_dim, S.intermediate, S.hidden
+    half = hd // 2
+    freq = torch.tensor(S.rope_theta, dtype=torch.float64) ** (
+        -torch.arange(half, dtype=torch.float64) * 2.0 / hd)
+    x = torch.as_tensor(xs, dtype=torch.float64).clone()
+    T = x.shape[0]
+    pos = torch.arange(start, start + T, dtype=torch.float64)
+
+    def rot(z):  # z [T][heads][hd]
+        c = torch.complex(z[..., :half], z[..., half:]) * torch.polar(
+            torch.ones(T, 1, half, dtype=torch.float64), pos[:, None, None] * freq)
+        return torch.cat([c.real, c.imag], -1)
+
+    W = lambda t: t[0].to(torch.float64)
+    mask = torch.arange(start + T)[None, :] <= (start + torch.arange(T))[:, None]
+    ks, vs = [], []
+    for l, lw in enumerate(wts.layers):
+        u = F.rms_norm(x, (H,), lw.attn_gamma.double(), eps=S.rms_eps)
+        qkv = u @ W(lw.wqkv).T
+        q = rot(qkv[:, :nq * hd].view(T, nq, hd))
+        k = rot(qkv[:, nq * hd:(nq + nkv) * hd].view(T, nkv, hd))
+        v = qkv[:, (nq + nkv) * hd:].view(T, nkv, hd)
+        K = torch.cat([ctx[l][0], k.transpose(0, 1)], 1)  # [nkv][start+T][hd]
+        V = torch.cat([ctx[l][1], v.transpose(0, 1)], 1)
+        ks.append(K)
+        vs.append(V)
+        o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], K[None], V[None],
+                                           attn_mask=mask, enable_gqa=True)
+        x = x + o[0].transpose(0, 1).reshape(T, nq * hd) @ W(lw.wo).T
+        u = F.rms_norm(x, (H,), lw.ffn_gamma.double(), eps=S.rms_eps)
+        gu = u @ W(lw.wgu).T
+        x = x + (F.silu(gu[:, :I]) * gu[:, I:]) @ W(lw.wd).T
+    u = F.rms_norm(x, (H,), wts.out_gamma.double(), eps=S.rms_eps)
+    return x, u @ W(wts.lm_head).T, ks, vs
+
+
+@pytest.mark.parametrize("start", [0, 5])
+def test_prefill_oracle_matches_masked_matrix_form(start):
+    S = synth.TINY_LLAMA_F32
+    wts = synth.decoder_weights(S, seed=3, gamma="random")
+    T, seq = 7, 1
+    ctx = [(synth.normal((S.n_kv_heads, start, S.head_dim), 1.0, 3, f"pf_k{l}").double(),
+            synth.normal((S.n_kv_heads, start, S.head_dim), 1.0, 3, f"pf_v{l}").double())
+           for l in range(S.n_layers)]
+    orc = oracle.DecoderOracle(S, wts, 2, S.max_len)
+    for l in range(S.n_layers):
+        orc.set_context(l, seq, ctx[l][0], ctx[l][1])
+    toks = synth.uniform_int((T,), 0, S.vocab - 1, 3, "pf_tok")
+    x = wts.embed[toks].double().numpy()
+    got = orc.prefill(seq, x, start)
+    hid, logits, ks, vs = _torch_llama_prefill(S, wts, x, start, ctx)
+    np.testing.assert_allclose(got["hidden"], hid.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(got["logits"], logits.numpy(), rtol=1e-10, atol=1e-12)
+    for l in range(S.n_layers):
+        np.testing.assert_allclose(orc.kc[l][seq, :, :start + T], ks[l].numpy(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(orc.vc[l][seq, :, :start + T], vs[l].numpy(), rtol=1e-12, atol=1e-13)
+        assert not orc.kc[l][0].any() and not orc.vc[l][0].any()  # the other slot is untouched
+
+
+def test_prefill_oracle_equals_one_token_steps():
+    S = synth.TINY_LLAMA_F32
+    wts = synth.decoder_weights(S, seed=4)
+    toks = synth.uniform_int((6,), 0, S.vocab - 1, 4, "pf_tok2")
+    x = wts.embed[toks].double().numpy()
+    a = oracle.DecoderOracle(S, wts, 1, S.max_len).prefill(0, x, 2)
+    b = oracle.DecoderOracle(S, wts, 1, S.max_len)
+    for t in range(6):
+        one = b.step(x[t:t + 1], [2 + t])
+        assert np.array_equal(one["hidden"][0], a["hidden"][t])
+        assert np.array_equal(one["logits"][0], a["logits"][t])
