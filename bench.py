@@ -218,9 +218,30 @@ def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32)):
                  for L in lengths[:m] for i in range(steps)) / steps
         out[f"m{m}"] = dict(tok_s=m * steps / sec, ms_per_step=1e3 * sec / steps,
                             hbm_frac=(wbytes + kv) * steps / sec / 1e9 / HBM_PEAK_GBS)
+    out["prefill"] = prefill_line(S, dd, 1024)
     del dd, W
     torch.cuda.empty_cache()
     return out
+
+
+def prefill_line(S, dd, n_tokens, reps=3):
+    """Prompt ingestion (rra_prefill) of n_tokens seeded token ids into cache
+    slot 0 from position 0, in chunks of the model's prefill rows (its m_max):
+    each chunk is one pass of the decode step over all layers."""
+    import synth
+    toks = synth.uniform_int((n_tokens,), 0, S.vocab - 1, 0, "bench_prompt").to("cuda", torch.int32)
+    nt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dd.model.rra_prefill(toks, n_tokens, 0, 0, next_tok=nt)  # warm-up
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        dd.model.rra_prefill(toks, n_tokens, 0, 0, next_tok=nt)
+    ev1.record()
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3 / reps
+    return dict(tokens=n_tokens, rows_per_chunk=dd.model.m_max, ms=1e3 * sec,
+                tok_s=n_tokens / sec)
 
 
 def fp8_gemv_line(reps=20):
@@ -337,6 +358,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(S, W, dd, lengths, first, 8, 4)
         log(f"cpu baseline {cpu}")
+    prefill = prefill_line(S, dd, 512)  # overwrites slot 0's cache: after everything above
+    log(f"prefill {prefill}")
     del dd, W
     torch.cuda.empty_cache()
     if not args.no_m1:
@@ -379,6 +402,7 @@ def main():
         },
         "m1": m1,
         "fp8_gemv": fp8,
+        "prefill": dict(workload=f"{S.name}: 512 prompt tokens into one slot", **prefill),
         "m_sweep": sweep,
         "cpu_baseline": cpu,
     }

@@ -233,6 +233,8 @@ typedef struct rra_model_desc {
     const float *embed;            /* device [vocab][hidden] fp32, or NULL (needed for RRA_STEP_GATHER) */
     int32_t attn_chunk;            /* flash-decode rows per split; 0 = chosen by the library
                                       for each step from its m, nkv and max_len */
+    int32_t prefill_rows;          /* prompt tokens per rra_prefill chunk, 0..32 (0 = m_max);
+                                      the workspace holds max(m_max, prefill_rows) rows */
 } rra_model_desc;
 
 typedef struct rra_model rra_model;
@@ -281,6 +283,31 @@ rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t ws_bytes, 
 rra_status rra_decode_step(rra_model *mdl, float *x, uint32_t *pos, uint32_t *tok,
                            uint32_t *tok_host, float *logits, int32_t m, int32_t flags,
                            hipStream_t s);
+
+/* Prefill (context ingestion; [head_dim] tensor_core_attention: causal
+ * attention of every prompt token to itself and the tokens before it).
+ * Runs the n_tokens prompt tokens of cache slot `seq` through the model at
+ * positions start .. start + n_tokens - 1: every layer's K/V rows for those
+ * positions are written into the slot's cache, each token attending to cache
+ * rows [0, its position] -- the rows already there (a context ingested
+ * earlier) and the prompt tokens before it -- exactly as the same tokens fed
+ * one at a time through rra_decode_step would.  The tokens go through in
+ * chunks of prefill_rows: each chunk is one decode-step pass whose rows are
+ * the chunk's tokens (weights streamed once per chunk), all mapped to slot
+ * `seq`.  Only the last token reaches the output norm, LM head and argmax.
+ * tokens   : device uint32 [n_tokens], ids < vocab.
+ * seq      : cache slot in [0, m_max).  Other slots are not touched.
+ * start    : position of tokens[0]; start + n_tokens <= max_len (else
+ *            RRA_EINVAL, nothing enqueued).
+ * next_tok : device uint32 [1] or NULL: the greedy id after the last token
+ *            (the first token a decode step for this slot then consumes at
+ *            position start + n_tokens).
+ * logits   : device fp32 [vocab] or NULL: the last token's logits.
+ * Needs the model's embedding table.  Enqueued on s without a sync and
+ * without graph capture; it uses the model's workspace, so calls on one model
+ * (prefill or decode) must be ordered on one stream. */
+rra_status rra_prefill(rra_model *mdl, const uint32_t *tokens, int32_t n_tokens, int32_t seq,
+                       uint32_t start, uint32_t *next_tok, float *logits, hipStream_t s);
 
 /* Waits for stream s and reports (and clears) a device-side error: RRA_EINVAL
  * if a step saw a position >= max_len since the last check. */

@@ -4,7 +4,7 @@ Argument marshalling only: every function forwards to the C ABI declared in
 ``include/rra.h`` under the same name, passing torch tensors' device
 addresses and the current HIP stream.  All computation runs in librra's HIP
 kernels; there is no fallback.  Importing this package fails if librra.so has
-not been built (``python -m quantized_gemv_flash_amd.build``).
+not been built (``python quantized_gemv_flash_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -51,12 +51,12 @@ class rra_model_desc(ctypes.Structure):
                 ("vocab", c_int32), ("rms_eps", c_float), ("rope_theta", c_double),
                 ("max_len", c_int32), ("m_max", c_int32), ("layers", POINTER(rra_layer_desc)),
                 ("out_gamma", c_void_p), ("lm_head", rra_weight), ("embed", c_void_p),
-                ("attn_chunk", c_int32)]
+                ("attn_chunk", c_int32), ("prefill_rows", c_int32)]
 
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_gemv_flash_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python quantized_gemv_flash_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     P, S, I, U = c_void_p, c_size_t, c_int32, c_uint32
     W = POINTER(rra_weight)
@@ -82,6 +82,7 @@ def _load() -> ctypes.CDLL:
         "rra_model_workspace_bytes": ([POINTER(rra_model_desc)], S),
         "rra_model_create": ([POINTER(rra_model_desc), P, S, P, POINTER(c_void_p)], I),
         "rra_decode_step": ([P, P, P, P, P, P, I, I, P], I),
+        "rra_prefill": ([P, P, I, I, U, P, P, P], I),
         "rra_model_check": ([P, P], I),
         "rra_graph_stats": ([P, POINTER(c_uint64), POINTER(c_uint64), POINTER(c_uint32)], I),
         "rra_model_destroy": ([P], None),
@@ -240,7 +241,7 @@ class Model:
     def __init__(self, *, n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab,
                  rms_eps, rope_theta, max_len, m_max, layers: Sequence[dict], out_gamma,
                  lm_head: Weight, embed: Optional[torch.Tensor] = None, attn_chunk: int = 0,
-                 stream=None):
+                 prefill_rows: int = 0, stream=None):
         self._keep = [layers, out_gamma, lm_head, embed]
         arr = (rra_layer_desc * n_layers)()
         for i, l in enumerate(layers):
@@ -252,7 +253,7 @@ class Model:
             n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab, rms_eps,
             rope_theta, max_len, m_max, ctypes.cast(arr, POINTER(rra_layer_desc)),
             out_gamma.data_ptr(), lm_head.c, embed.data_ptr() if embed is not None else None,
-            attn_chunk)
+            attn_chunk, prefill_rows)
         nbytes = lib.rra_model_workspace_bytes(ctypes.byref(self.desc))
         if nbytes == 0:
             # re-run creation on a null workspace to surface the validation message
@@ -272,6 +273,14 @@ class Model:
         _check("rra_decode_step", lib.rra_decode_step(
             self.handle, _p(x), _p(pos), _p(tok), host, _p(logits), m, flags, _stream(stream)))
         return list(host) if host is not None else None
+
+    def rra_prefill(self, tokens, n_tokens: int, seq: int, start: int, next_tok=None,
+                    logits=None, stream=None):
+        """Ingests n_tokens prompt tokens (device uint32) into cache slot seq at
+        positions start...; the last token's greedy id / logits go to next_tok /
+        logits when given."""
+        _check("rra_prefill", lib.rra_prefill(self.handle, _p(tokens), n_tokens, seq, start,
+                                              _p(next_tok), _p(logits), _stream(stream)))
 
     def rra_model_check(self, stream=None):
         _check("rra_model_check", lib.rra_model_check(self.handle, _stream(stream)))

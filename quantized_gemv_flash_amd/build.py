@@ -1,7 +1,8 @@
 """Builds librra.so (HIP, gfx950) in-tree from csrc/.
 
 Each source is compiled to an object under _build/ in parallel, then linked.
-Usage: python -m quantized_gemv_flash_amd.build
+Usage: python quantized_gemv_flash_amd/build.py [--force]  (a plain script: importing
+the package would load the library it builds)
 """
 from __future__ import annotations
 

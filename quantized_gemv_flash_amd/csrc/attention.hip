@@ -60,8 +60,9 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict
 template <int HD, int G>
 __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
-    const uint32_t *__restrict__ seq_len, float *__restrict__ part_o,
-    float *__restrict__ part_lse, int nq, int nkv, int max_len, int chunk, int nc_max) {
+    const uint32_t *__restrict__ seq_len, const uint32_t *__restrict__ slot_seq,
+    float *__restrict__ part_o, float *__restrict__ part_lse, int nq, int nkv, int max_len,
+    int chunk, int nc_max) {
     constexpr int GP = (G + 3) & ~3;  // probabilities stored key-major, G padded to 4
     const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
     const int L = (int)min(seq_len[m], (uint32_t)max_len);
@@ -75,7 +76,8 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float *stat = red + 4 * G * HD;   // [G] max, [G] sum
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t row0 = ((size_t)m * nkv + g) * max_len + t0;
+    const size_t cs = slot_seq ? slot_seq[m] : (uint32_t)m;  // cache slot of query row m
+    const size_t row0 = (cs * nkv + g) * max_len + t0;
     const float *K = kc + row0 * HD;
     const float *V = vc + row0 * HD;
 
@@ -282,22 +284,25 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
 
 template <int HD, int G>
 rra_status launch_chunk(const float *q, const float *kc, const float *vc, const uint32_t *lens,
-                        float *po, float *pl, int m, int nq, int nkv, int max_len, int chunk,
-                        int nc_max, hipStream_t s) {
+                        const uint32_t *slot_seq, float *po, float *pl, int m, int nq, int nkv,
+                        int max_len, int chunk, int nc_max, hipStream_t s) {
     constexpr int GP = (G + 3) & ~3;
     const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * G);
     hipLaunchKernelGGL((fd_chunk_kernel<HD, G>), dim3(nc_max, nkv, m), dim3(256), shm, s, q, kc,
-                       vc, lens, po, pl, nq, nkv, max_len, chunk, nc_max);
+                       vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max);
     return check_launch("fd_chunk_kernel");
 }
 
 template <int HD>
 rra_status launch_chunk_hd(int G, const float *q, const float *kc, const float *vc,
-                           const uint32_t *lens, float *po, float *pl, int m, int nq, int nkv,
-                           int max_len, int chunk, int nc_max, hipStream_t s) {
+                           const uint32_t *lens, const uint32_t *slot_seq, float *po, float *pl,
+                           int m, int nq, int nkv, int max_len, int chunk, int nc_max,
+                           hipStream_t s) {
     switch (G) {
 #define RRA_G(gv) \
-    case gv: return launch_chunk<HD, gv>(q, kc, vc, lens, po, pl, m, nq, nkv, max_len, chunk, nc_max, s);
+    case gv:                                                                               \
+        return launch_chunk<HD, gv>(q, kc, vc, lens, slot_seq, po, pl, m, nq, nkv, max_len, chunk, \
+                                    nc_max, s);
         RRA_G(1) RRA_G(2) RRA_G(3) RRA_G(4) RRA_G(5) RRA_G(6) RRA_G(7) RRA_G(8)
 #undef RRA_G
         default: return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", G);
@@ -336,18 +341,18 @@ rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
-                               const FragOut *fo) {
+                               const FragOut *fo, const uint32_t *slot_seq) {
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
     const int nc_max = (int)cdiv(max_len, chunk);
     float *po = part;
     float *pl = part + (size_t)m * nq * nc_max * hd;
     if (hd == 128)
-        RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, po, pl, m, nq, nkv, max_len,
-                                     chunk, nc_max, s));
+        RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
+                                     max_len, chunk, nc_max, s));
     else
-        RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, po, pl, m, nq, nkv, max_len,
-                                    chunk, nc_max, s));
+        RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
+                                    max_len, chunk, nc_max, s));
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,
                            out, nq, max_len, chunk, nc_max, img);

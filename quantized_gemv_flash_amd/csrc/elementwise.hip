@@ -147,8 +147,10 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
                                 const uint32_t *__restrict__ pos, const float *__restrict__ table,
                                 float *__restrict__ q_out, float *__restrict__ kc,
                                 float *__restrict__ vc, uint32_t *__restrict__ seq_len,
-                                uint32_t *__restrict__ err, int nq, int nkv, int hd, int max_len) {
+                                uint32_t *__restrict__ err, const uint32_t *__restrict__ slot_seq,
+                                int nq, int nkv, int hd, int max_len) {
     const int m = blockIdx.x, head = blockIdx.y, j = threadIdx.x, half = hd >> 1;
+    const size_t cs_row = slot_seq ? slot_seq[m] : (uint32_t)m;  // cache slot of row m
     const int nrow = (nq + 2 * nkv) * hd;
     const uint32_t p = pos[m];
     const bool ok = p < (uint32_t)max_len;  // also false for an empty slot (RRA_POS_NONE)
@@ -168,7 +170,7 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
     } else if (ok) {
         const bool is_k = head < nq + nkv;
         const int g = is_k ? head - nq : head - nq - nkv;
-        float *dst = (is_k ? kc : vc) + (((size_t)m * nkv + g) * max_len + p) * hd;
+        float *dst = (is_k ? kc : vc) + ((cs_row * nkv + g) * max_len + p) * hd;
         dst[j] = a;
         dst[j + half] = c;
     }
@@ -332,10 +334,10 @@ rra_status launch_residual_ss(const float *part, int split, size_t split_stride,
 rra_status launch_qkv_post(const float *part, int split, size_t split_stride, const uint32_t *pos,
                            const float *table, float *q_out, float *k_cache, float *v_cache,
                            uint32_t *seq_len, uint32_t *err, int m, int nq, int nkv, int hd,
-                           int max_len, hipStream_t s) {
+                           int max_len, const uint32_t *slot_seq, hipStream_t s) {
     hipLaunchKernelGGL(qkv_post_kernel, dim3(m, nq + 2 * nkv), dim3(hd / 2), 0, s, part, split,
                        (long long)split_stride, pos, table, q_out, k_cache, v_cache, seq_len, err,
-                       nq, nkv, hd, max_len);
+                       slot_seq, nq, nkv, hd, max_len);
     return check_launch("qkv_post_kernel");
 }
 
@@ -360,6 +362,22 @@ rra_status launch_swiglu_reduce(const float *part, int split, size_t split_strid
     hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)cdiv(groups, 256), m), dim3(256), 0, s,
                        part, split, (long long)split_stride, act, inter, fo);
     return check_launch("swiglu_reduce_kernel");
+}
+
+__global__ void prefill_rows_kernel(uint32_t *pos, uint32_t *slot_seq, uint32_t base,
+                                    uint32_t seq, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        pos[i] = base + (uint32_t)i;
+        slot_seq[i] = seq;
+    }
+}
+
+rra_status launch_prefill_rows(uint32_t *pos, uint32_t *slot_seq, uint32_t base, uint32_t seq,
+                               int n, hipStream_t s) {
+    hipLaunchKernelGGL(prefill_rows_kernel, dim3((unsigned)cdiv(n, 64)), dim3(64), 0, s, pos,
+                       slot_seq, base, seq, n);
+    return check_launch("prefill_rows_kernel");
 }
 
 rra_status launch_embed_gather(const float *embed, const uint32_t *tok, const uint32_t *pos,

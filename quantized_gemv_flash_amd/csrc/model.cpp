@@ -176,6 +176,11 @@ struct rra_model {
     uint32_t *lens = nullptr, *err = nullptr;
     void *argmax_ws = nullptr;
     uint8_t *img = nullptr;  // activation image of the next Q8/Q4 GEMV
+    int rows = 0;            // batch rows the workspace holds: max(m_max, prefill rows)
+    int prefill_rows = 0;    // prompt tokens per prefill chunk
+    // prefill chunk state: x rows, positions, cache slot per row, token ids
+    float *px = nullptr;
+    uint32_t *ppos = nullptr, *pseq = nullptr, *ptok = nullptr;
     // per-M plans (index m)
     GemvPlan plan_qkv[RRA_M_MAX + 1], plan_o[RRA_M_MAX + 1], plan_gu[RRA_M_MAX + 1],
         plan_d[RRA_M_MAX + 1], plan_lm[RRA_M_MAX + 1];
@@ -187,12 +192,16 @@ struct rra_model {
 namespace {
 
 struct Layout {
-    size_t ss, xg, img, part, q, lens, attn, act, fd, logits, argmax, rope, err, total;
+    size_t ss, xg, img, part, q, lens, attn, act, fd, logits, argmax, rope, err, px, pidx, total;
 };
+
+// Rows of one prefill chunk, and the batch rows the workspace is laid out for.
+int prefill_rows_of(const rra_model_desc &d) { return d.prefill_rows ? d.prefill_rows : d.m_max; }
+int rows_of(const rra_model_desc &d) { return std::max(d.m_max, prefill_rows_of(d)); }
 
 // Largest activation image any GEMV of the model reads (0 if all are fp32).
 size_t image_bytes(const rra_model_desc &d) {
-    const int ct = frag_ct(d.m_max);
+    const int ct = frag_ct(rows_of(d));
     size_t best = 0;
     auto need = [&](const rra_weight &w) {
         if (w.fmt != RRA_F32) best = std::max(best, frag_image_bytes(w.fmt, ct, w.k));
@@ -208,7 +217,7 @@ size_t image_bytes(const rra_model_desc &d) {
 
 size_t part_floats(const rra_model_desc &d, const rra_layer_desc &l) {
     size_t best = 0;
-    for (int m = 1; m <= d.m_max; ++m) {
+    for (int m = 1; m <= rows_of(d); ++m) {
         const rra_weight *ws[4] = {&l.wqkv, &l.wo, &l.wgu, &l.wd};
         for (const rra_weight *w : ws) {
             const GemvPlan p = gemv_plan(*w, m);
@@ -225,7 +234,7 @@ int chunk_for(const rra_model_desc &d, int m) {
 
 size_t fd_floats(const rra_model_desc &d) {
     size_t best = 0;
-    for (int m = 1; m <= d.m_max; ++m)
+    for (int m = 1; m <= rows_of(d); ++m)
         best = std::max(best, fd_partials_floats(m, d.n_heads, d.head_dim, d.max_len, chunk_for(d, m)));
     return best;
 }
@@ -238,7 +247,7 @@ Layout layout_of(const rra_model_desc &d) {
         off = align_up(off + bytes, 256);
         return at;
     };
-    const size_t M = (size_t)d.m_max;
+    const size_t M = (size_t)rows_of(d);
     size_t partf = 0;
     for (int i = 0; i < d.n_layers; ++i) partf = std::max(partf, part_floats(d, d.layers[i]));
     L.ss = take(4 * M * ss_parts(d.hidden));
@@ -254,6 +263,8 @@ Layout layout_of(const rra_model_desc &d) {
     L.argmax = take(argmax_ws_bytes((int)M, d.vocab));
     L.rope = take(4 * (size_t)d.max_len * d.head_dim);
     L.err = take(256);
+    L.px = take(4 * M * d.hidden);
+    L.pidx = take(3 * 4 * M);
     L.total = off;
     return L;
 }
@@ -280,6 +291,8 @@ rra_status validate_desc(const rra_model_desc *d) {
         return fail(RRA_EINVAL, "model: hidden and intermediate must be multiples of 8");
     if (d->m_max < 1 || d->m_max > RRA_M_MAX)
         return fail(RRA_EINVAL, "model: m_max=%d not in 1..32", d->m_max);
+    if (d->prefill_rows < 0 || d->prefill_rows > RRA_M_MAX)
+        return fail(RRA_EINVAL, "model: prefill_rows=%d not in 0..32", d->prefill_rows);
     if (d->max_len < 1) return fail(RRA_EINVAL, "model: max_len=%d", d->max_len);
     if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.0))
         return fail(RRA_EINVAL, "model: bad rms_eps or rope_theta");
@@ -316,15 +329,22 @@ const void *gemv_input(const rra_model *M, const rra_weight &w, const float *row
     return w.fmt == RRA_F32 ? static_cast<const void *>(rows) : M->img;
 }
 
-// Every launch of one decode step, in stream order.
-rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, float *logits,
-                        int m, int flags, hipStream_t s) {
+// Internal step flag: stop after the last layer (no LM head, no argmax).
+constexpr int kStepNoHead = 1 << 16;
+
+// Every launch of one decode step, in stream order.  Row i reads token
+// tok_in[i] (under RRA_STEP_GATHER), sits at position pos[i] and uses cache
+// slot slot_seq[i] (slot i when slot_seq is null); the greedy ids go to
+// tok_out.
+rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *tok_in,
+                        uint32_t *tok_out, float *logits, int m, int flags,
+                        const uint32_t *slot_seq, hipStream_t s) {
     const rra_model_desc &d = M->d;
     const int H = d.hidden, nq = d.n_heads, nkv = d.n_kv_heads, hd = d.head_dim,
               I = d.intermediate;
     const int nqkv = (nq + 2 * nkv) * hd;
     if (flags & RRA_STEP_GATHER)
-        RRA_TRY(launch_embed_gather(d.embed, tok, pos, x, m, H, d.vocab, s));
+        RRA_TRY(launch_embed_gather(d.embed, tok_in, pos, x, m, H, d.vocab, s));
     const int np = ss_parts(H);
     const NormIn nrm{M->ss, np, d.rms_eps};
     // RMSNorm is formed inside each consuming GEMV from per-chunk sums of
@@ -341,10 +361,10 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, fl
                             s, &nrm));
         RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
                                 L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd, d.max_len,
-                                s));
+                                slot_seq, s));
         const FragOut fo_o = image_for(M, L.wo, m);
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
-                                    d.max_len, M->chunk[m], M->fd, s, &fo_o));
+                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq));
         const GemvPlan &po = M->plan_o[m];
         RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part, (size_t)m * H, s));
         RRA_TRY(launch_residual_ss(M->part, po.split, (size_t)m * H, x, M->ss, L.ffn_gamma, M->xg, m,
@@ -363,9 +383,11 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, uint32_t *tok, fl
         RRA_TRY(launch_residual_ss(M->part, pd.split, (size_t)m * H, x, M->ss, next_gamma, M->xg,
                                    m, H, image_for(M, next_w, m), s));
     }
+    if (flags & kStepNoHead) return RRA_OK;
     RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits, 0, s,
                         &nrm));
-    return launch_argmax(logits, tok, m, d.vocab, M->argmax_ws, pos, (flags & RRA_STEP_ADVANCE) != 0, s);
+    return launch_argmax(logits, tok_out, m, d.vocab, M->argmax_ws, pos,
+                         (flags & RRA_STEP_ADVANCE) != 0, s);
 }
 
 }  // namespace
@@ -404,7 +426,13 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     M->argmax_ws = b + L.argmax;
     M->rope = reinterpret_cast<float *>(b + L.rope);
     M->err = reinterpret_cast<uint32_t *>(b + L.err);
-    for (int m = 1; m <= d->m_max; ++m) {
+    M->px = reinterpret_cast<float *>(b + L.px);
+    M->rows = rows_of(*d);
+    M->prefill_rows = prefill_rows_of(*d);
+    M->ppos = reinterpret_cast<uint32_t *>(b + L.pidx);
+    M->pseq = M->ppos + M->rows;
+    M->ptok = M->pseq + M->rows;
+    for (int m = 1; m <= M->rows; ++m) {
         M->chunk[m] = chunk_for(*d, m);
         const rra_layer_desc &l0 = d->layers[0];
         M->plan_qkv[m] = gemv_plan(l0.wqkv, m);
@@ -469,7 +497,7 @@ static rra_status capture_and_launch(rra_model *M, const GraphKey &key, float *x
     // failed capture cannot poison other threads' work.  End the capture
     // whatever happened, so the stream always leaves capture mode.
     RRA_TRY_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-    const rra_status body = enqueue_step(M, x, pos, tok, logits, m, flags, s);
+    const rra_status body = enqueue_step(M, x, pos, tok, tok, logits, m, flags, nullptr, s);
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(s, &graph);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -535,17 +563,53 @@ extern "C" rra_status rra_decode_step(rra_model *M, float *x, uint32_t *pos, uin
             const rra_status st = capture_and_launch(M, key, x, pos, tok, lg, m, flags, s);
             if (st != RRA_OK) {
                 clear_error();
-                const rra_status eager = enqueue_step(M, x, pos, tok, lg, m, flags, s);
+                const rra_status eager = enqueue_step(M, x, pos, tok, tok, lg, m, flags, nullptr, s);
                 if (eager != RRA_OK) return fail(RRA_ECAPTURE, "capture and eager step failed: %s",
                                                  rra_last_error());
             }
         }
     } else {
-        RRA_TRY(enqueue_step(M, x, pos, tok, lg, m, flags, s));
+        RRA_TRY(enqueue_step(M, x, pos, tok, tok, lg, m, flags, nullptr, s));
     }
     if (tok_host) {
         RRA_TRY_HIP(hipMemcpyAsync(tok_host, tok, sizeof(uint32_t) * m, hipMemcpyDeviceToHost, s));
         RRA_TRY_HIP(hipStreamSynchronize(s));
     }
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_prefill(rra_model *M, const uint32_t *tokens, int32_t n_tokens,
+                                  int32_t seq, uint32_t start, uint32_t *next_tok, float *logits,
+                                  hipStream_t s) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_prefill: null model");
+    const rra_model_desc &d = M->d;
+    if (!tokens || n_tokens < 1) return fail(RRA_EINVAL, "rra_prefill: no tokens");
+    if (seq < 0 || seq >= d.m_max)
+        return fail(RRA_EINVAL, "rra_prefill: seq=%d not in 0..m_max-1=%d", seq, d.m_max - 1);
+    if (!d.embed) return fail(RRA_EINVAL, "rra_prefill: the model has no embedding table");
+    if ((int64_t)start + n_tokens > d.max_len)
+        return fail(RRA_EINVAL, "rra_prefill: positions %u..%lld exceed max_len=%d", start,
+                    (long long)start + n_tokens - 1, d.max_len);
+    // Chunks of up to prefill_rows tokens, each one step whose rows are the
+    // chunk's tokens at consecutive positions, all in cache slot `seq`: a
+    // step writes every row's K/V before attention reads the cache, so row i
+    // attends to the cache rows before it and to rows 0..i of its own chunk.
+    const int R = M->prefill_rows;
+    int n_last = 0;
+    for (int c0 = 0; c0 < n_tokens; c0 += R) {
+        const int n = std::min(R, n_tokens - c0);
+        const bool last = c0 + n == n_tokens;
+        RRA_TRY(launch_prefill_rows(M->ppos, M->pseq, start + (uint32_t)c0, (uint32_t)seq, n, s));
+        RRA_TRY(enqueue_step(M, M->px, M->ppos, tokens + c0, M->ptok, M->logits, n,
+                             RRA_STEP_GATHER | (last ? 0 : kStepNoHead), M->pseq, s));
+        n_last = n;
+    }
+    if (next_tok)
+        RRA_TRY_HIP(hipMemcpyAsync(next_tok, M->ptok + (n_last - 1), sizeof(uint32_t),
+                                   hipMemcpyDeviceToDevice, s));
+    if (logits)
+        RRA_TRY_HIP(hipMemcpyAsync(logits, M->logits + (size_t)(n_last - 1) * d.vocab,
+                                   sizeof(float) * d.vocab, hipMemcpyDeviceToDevice, s));
     return RRA_OK;
 }

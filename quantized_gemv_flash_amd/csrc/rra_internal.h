@@ -94,10 +94,11 @@ size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk);
 rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
                              float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
                              int max_len, hipStream_t s);
+// Row i of q attends to cache slot slot_seq[i] (slot i when slot_seq is null).
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
-                               const FragOut *fo = nullptr);
+                               const FragOut *fo = nullptr, const uint32_t *slot_seq = nullptr);
 
 // ------------------------------------------------------------------ elementwise
 rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m, int h,
@@ -124,16 +125,20 @@ rra_status launch_residual_ss(const float *part, int split, size_t split_stride,
                               const FragOut &fo, hipStream_t s);
 inline int ss_parts(int h) { return (int)cdiv(h, 2048); }
 // qkv = sum_s part[s]; rope(q, k) at pos; q -> q_out [m][nq][hd]; k, v rows
-// scattered into the caches at pos; seq_len[i] = min(pos[i] + 1, max_len);
-// pos >= max_len sets *err.
+// scattered into the caches at pos, in cache slot slot_seq[i] (slot i when
+// slot_seq is null); seq_len[i] = min(pos[i] + 1, max_len); pos >= max_len
+// sets *err.
 rra_status launch_qkv_post(const float *part, int split, size_t split_stride, const uint32_t *pos,
                            const float *table, float *q_out, float *k_cache, float *v_cache,
                            uint32_t *seq_len, uint32_t *err, int m, int nq, int nkv, int hd,
-                           int max_len, hipStream_t s);
+                           int max_len, const uint32_t *slot_seq, hipStream_t s);
 // act[i][j] = silu(sum_s part[s][i][j]) * sum_s part[s][i][inter + j], and
 // its activation image for the down GEMV.
 rra_status launch_swiglu_reduce(const float *part, int split, size_t split_stride, float *act,
                                 int m, int inter, const FragOut &fo, hipStream_t s);
+// pos[i] = base + i, slot_seq[i] = seq for i < n (one prefill chunk).
+rra_status launch_prefill_rows(uint32_t *pos, uint32_t *slot_seq, uint32_t base, uint32_t seq,
+                               int n, hipStream_t s);
 // x[i] = embed[tok[i]] for every slot whose pos is not RRA_POS_NONE.
 rra_status launch_embed_gather(const float *embed, const uint32_t *tok, const uint32_t *pos,
                                float *x, int m, int h, int vocab, hipStream_t s);

@@ -33,7 +33,7 @@ class DeviceDecoder:
 
 
 def load_decoder(shape, weights, m_max: int, max_len: int, attn_chunk: int = 0,
-                 drop_planar: bool = False, stream=None) -> DeviceDecoder:
+                 drop_planar: bool = False, prefill_rows: int = 0, stream=None) -> DeviceDecoder:
     """`shape` has the decoder dimensions (n_layers, hidden, n_heads, n_kv_heads,
     head_dim, intermediate, vocab, fmt, rms_eps, rope_theta); `weights` has
     .layers (each with wqkv, wo, wgu, wd as (data, scale) pairs, attn_gamma,
@@ -63,5 +63,6 @@ def load_decoder(shape, weights, m_max: int, max_len: int, attn_chunk: int = 0,
                   n_kv_heads=S.n_kv_heads, head_dim=S.head_dim, intermediate=S.intermediate,
                   vocab=S.vocab, rms_eps=S.rms_eps, rope_theta=S.rope_theta, max_len=max_len,
                   m_max=m_max, layers=layers, out_gamma=weights.out_gamma, lm_head=lm,
-                  embed=weights.embed, attn_chunk=attn_chunk, stream=stream)
+                  embed=weights.embed, attn_chunk=attn_chunk, prefill_rows=prefill_rows,
+                  stream=stream)
     return DeviceDecoder(model, kcs, vcs, keep, lm, weights.embed)
