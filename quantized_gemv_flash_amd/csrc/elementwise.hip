@@ -17,42 +17,28 @@
 namespace rra {
 namespace {
 
-// Sum over the `split` K-split planes of a GEMV result (stride floats
-// apart), in plane order.  Up to 8 planes are loaded at once (clamped
-// addresses, unconditional loads), so the latency is paid once per 8 planes,
-// not once per plane.
-__device__ __forceinline__ float sum_splits(const float *__restrict__ p, int split,
-                                           long long stride) {
-    float acc = 0.f;
+// Sums over the `split` K-split planes of a GEMV result (stride floats
+// apart), in plane order, of two columns at once (p and q).  Up to 8 planes
+// are loaded at once (clamped addresses, unconditional loads), so the latency
+// is paid once per 8 planes, not once per plane.
+__device__ __forceinline__ void sum_splits2(const float *__restrict__ p, const float *__restrict__ q,
+                                            int split, long long stride, float &a, float &c) {
+    a = 0.f;
+    c = 0.f;
     for (int s0 = 0; s0 < split; s0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = p[(size_t)min(s0 + j, split - 1) * stride];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc += (s0 + j < split) ? v[j] : 0.f;
-    }
-    return acc;
-}
-
-// Same over 4 consecutive columns (16-byte loads).
-__device__ __forceinline__ float4 sum_splits4(const float *__restrict__ p, int split,
-                                              long long stride) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < split; s0 += 8) {
-        float4 v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = *reinterpret_cast<const float4 *>(p + (size_t)min(s0 + j, split - 1) * stride);
+        float u[8], w[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const bool in = s0 + j < split;
-            acc.x += in ? v[j].x : 0.f;
-            acc.y += in ? v[j].y : 0.f;
-            acc.z += in ? v[j].z : 0.f;
-            acc.w += in ? v[j].w : 0.f;
+            const size_t off = (size_t)min(s0 + j, split - 1) * stride;
+            u[j] = p[off];
+            w[j] = q[off];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            a += (s0 + j < split) ? u[j] : 0.f;
+            c += (s0 + j < split) ? w[j] : 0.f;
         }
     }
-    return acc;
 }
 
 __device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
@@ -64,6 +50,64 @@ __device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
 __device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// Split sum of NV 8-column vectors (p[v] .. p[v] + 8) shared by the four
+// waves of a 256-thread block: lane g of every wave works on the same group,
+// wave q adds planes q, q + 4, q + 8, ... (8 / NV planes in flight per
+// thread), and wave 0 then adds the other waves' sums in wave order (a fixed
+// order: the result does not depend on timing).  All 256 threads must call
+// it (it synchronises the block); the total is valid in wave 0.  `red` is
+// 3 * 64 * NV * 8 floats of shared memory.
+template <int NV>
+__device__ __forceinline__ void group_split_sum(const float *const (&p)[NV], bool active,
+                                                int split, long long stride,
+                                                float (&acc)[NV][8], float *red) {
+    const int gl = threadIdx.x & 63, q = threadIdx.x >> 6;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[v][e] = 0.f;
+    if (active) {
+        constexpr int UN = 8 / NV;
+        for (int s0 = q; s0 < split; s0 += 4 * UN) {
+            float4 a[UN][NV][2];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const size_t off = (size_t)min(s0 + 4 * u, split - 1) * stride;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    a[u][v][0] = *reinterpret_cast<const float4 *>(p[v] + off);
+                    a[u][v][1] = *reinterpret_cast<const float4 *>(p[v] + off + 4);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                if (s0 + 4 * u >= split) continue;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    acc[v][0] += a[u][v][0].x; acc[v][1] += a[u][v][0].y;
+                    acc[v][2] += a[u][v][0].z; acc[v][3] += a[u][v][0].w;
+                    acc[v][4] += a[u][v][1].x; acc[v][5] += a[u][v][1].y;
+                    acc[v][6] += a[u][v][1].z; acc[v][7] += a[u][v][1].w;
+                }
+            }
+        }
+    }
+    if (q > 0) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[(((q - 1) * 64 + gl) * NV + v) * 8 + e] = acc[v][e];
+    }
+    __syncthreads();
+    if (q == 0) {
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[v][e] += red[((r * 64 + gl) * NV + v) * 8 + e];
+    }
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -98,11 +142,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x,
     for (int i = threadIdx.x; i < h; i += blockDim.x) o[i] = xr[i] * inv * gamma[i];
 }
 
-// Grid (ceil(h / 2048), m), 256 threads, one 8-column group per thread:
-// x[m][c] += sum_s part[s][m][c] (split may be 0: x unchanged); the chunk's
-// sum of squares of the updated row -> ss[m * nchunks + chunk]; xg = x * gamma
-// (fp32) and, when fo.img is set, its GEMV activation image (zeros for the
-// groups in [h, kpad)).  The next GEMV forms RMSNorm from ss (NormIn).
+// Grid (ceil(h / 512), m), 256 threads: 64 groups of 8 columns per block,
+// the four waves sharing each group's split sum (group_split_sum), wave 0
+// finishing it: x[m][c] += sum_s part[s][m][c] (split may be 0: x unchanged);
+// the block's sum of squares of the updated row -> ss[m * nblocks + block];
+// xg = x * gamma (fp32) and, when fo.img is set, its GEMV activation image
+// (zeros for the groups in [h, kpad)).  The next GEMV forms RMSNorm from ss
+// (NormIn).
 __global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restrict__ part, int split,
                                                           long long split_stride,
                                                           float *__restrict__ x,
@@ -110,33 +156,37 @@ __global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restric
                                                           const float *__restrict__ gamma,
                                                           float *__restrict__ xg, int h,
                                                           FragOut fo) {
+    __shared__ float red[3 * 64 * 8];
     __shared__ float sh[4];
     const int ch = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
-    const int k0 = (ch * 256 + threadIdx.x) * 8;
+    const int k0 = (ch * 64 + (threadIdx.x & 63)) * 8;
     const size_t base = (size_t)m * h + k0;
+    float acc[1][8];
+    const float *const pp[1] = {split > 0 ? part + base : nullptr};
+    group_split_sum<1>(pp, split > 0 && k0 < h, split, split_stride, acc, red);
     float sq = 0.f;
-    if (k0 < h) {
-        float v[8];
-        load8(x + base, v);
-        if (split > 0) {
-            const float4 a = sum_splits4(part + base, split, split_stride);
-            const float4 b = sum_splits4(part + base + 4, split, split_stride);
-            v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-            v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
-            store8(x + base, v);
-        }
-        float gv[8];
-        load8(gamma + k0, gv);
+    if (threadIdx.x < 64) {
+        if (k0 < h) {
+            float v[8];
+            load8(x + base, v);
+            if (split > 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sq = fmaf(v[e], v[e], sq);
-            gv[e] *= v[e];
+                for (int e = 0; e < 8; ++e) v[e] += acc[0][e];
+                store8(x + base, v);
+            }
+            float gv[8];
+            load8(gamma + k0, gv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sq = fmaf(v[e], v[e], sq);
+                gv[e] *= v[e];
+            }
+            store8(xg + base, gv);
+            if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, gv);
+        } else if (fo.img && k0 < fo.kpad) {
+            const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, z);
         }
-        store8(xg + base, gv);
-        if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, gv);
-    } else if (fo.img && k0 < fo.kpad) {
-        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, z);
     }
     sq = block_sum(sq, sh);
     if (threadIdx.x == 0) ss[(size_t)m * nch + ch] = sq;
@@ -155,8 +205,8 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
     const uint32_t p = pos[m];
     const bool ok = p < (uint32_t)max_len;  // also false for an empty slot (RRA_POS_NONE)
     const size_t b = (size_t)m * nrow + (size_t)head * hd;
-    float a = sum_splits(part + b + j, split, split_stride);
-    float c = sum_splits(part + b + j + half, split, split_stride);
+    float a, c;
+    sum_splits2(part + b + j, part + b + j + half, split, split_stride, a, c);
     if (head < nq + nkv && ok) {
         const float cs = table[((size_t)p * half + j) * 2], sn = table[((size_t)p * half + j) * 2 + 1];
         const float ra = a * cs - c * sn, rc = a * sn + c * cs;
@@ -203,25 +253,26 @@ __global__ void swiglu_kernel(const float *gate, const float *up, float *out, in
     out[i] = silu(gate[m * gate_stride + j]) * up[m * up_stride + j];
 }
 
-// act[m][j] = silu(sum_s part[s][m][j]) * sum_s part[s][m][inter + j], one
-// 8-column group per thread; also the down GEMV's activation image.
-// Grid (ceil(kpad / 8 / 256), m).
-__global__ void swiglu_reduce_kernel(const float *__restrict__ part, int split,
-                                     long long split_stride, float *__restrict__ act, int inter,
-                                     FragOut fo) {
+// act[m][j] = silu(sum_s part[s][m][j]) * sum_s part[s][m][inter + j], and
+// its activation image for the down GEMV.  Grid (ceil(max(inter, kpad) / 512),
+// m), 256 threads: 64 groups of 8 columns per block, the four waves sharing
+// each group's gate and up split sums (group_split_sum), wave 0 finishing.
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float *__restrict__ part,
+                                                            int split, long long split_stride,
+                                                            float *__restrict__ act, int inter,
+                                                            FragOut fo) {
+    __shared__ float red[3 * 64 * 16];
     const int m = blockIdx.y;
-    const int k0 = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    const int k0 = (blockIdx.x * 64 + (threadIdx.x & 63)) * 8;
+    const size_t gi = (size_t)m * 2 * inter + k0, ui = gi + inter;
+    float acc[2][8];
+    const float *const pp[2] = {part + gi, part + ui};
+    group_split_sum<2>(pp, k0 < inter, split, split_stride, acc, red);
+    if (threadIdx.x >= 64) return;
     if (k0 < inter) {
-        const size_t gi = (size_t)m * 2 * inter + k0, ui = gi + inter;
         float v[8];
-        const float4 g0 = sum_splits4(part + gi, split, split_stride);
-        const float4 g1 = sum_splits4(part + gi + 4, split, split_stride);
-        const float4 u0 = sum_splits4(part + ui, split, split_stride);
-        const float4 u1 = sum_splits4(part + ui + 4, split, split_stride);
-        v[0] = silu(g0.x) * u0.x; v[1] = silu(g0.y) * u0.y;
-        v[2] = silu(g0.z) * u0.z; v[3] = silu(g0.w) * u0.w;
-        v[4] = silu(g1.x) * u1.x; v[5] = silu(g1.y) * u1.y;
-        v[6] = silu(g1.z) * u1.z; v[7] = silu(g1.w) * u1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = silu(acc[0][e]) * acc[1][e];
         store8(act + (size_t)m * inter + k0, v);
         if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, v);
     } else if (fo.img && k0 < fo.kpad) {
@@ -359,7 +410,7 @@ rra_status launch_swiglu(const float *gate, const float *up, float *out, int m, 
 rra_status launch_swiglu_reduce(const float *part, int split, size_t split_stride, float *act,
                                 int m, int inter, const FragOut &fo, hipStream_t s) {
     const int groups = (int)cdiv(std::max(inter, fo.img ? fo.kpad : inter), 8);
-    hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)cdiv(groups, 256), m), dim3(256), 0, s,
+    hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)cdiv(groups, 64), m), dim3(256), 0, s,
                        part, split, (long long)split_stride, act, inter, fo);
     return check_launch("swiglu_reduce_kernel");
 }

@@ -338,7 +338,7 @@ struct QGemv {
 
     // RMSNorm inputs: the first SSP partial sums of squares of this lane's
     // columns, loaded early (clamped, fixed count) and summed after a wait.
-    static constexpr int SSP = 4;
+    static constexpr int SSP = 8;
     __device__ __forceinline__ void load_ss(const NormIn &nrm, int M, float (&sv)[CT][SSP]) const {
         if (!nrm.ss) return;
 #pragma unroll

@@ -116,14 +116,14 @@ rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void 
 void rope_table_host(float *table, int max_len, int hd, double theta);
 
 // Fused epilogues used by the decode step.
-// x[i] += sum_s part[s][i] (split may be 0); per 2048-column chunk c the sum
+// x[i] += sum_s part[s][i] (split may be 0); per 512-column chunk c the sum
 // of squares of the updated row, ss[i * ss_parts(h) + c]; and xg = x * gamma,
 // the input of the next RMSNorm-fused GEMV (fp32, and its image if fo.img).
 // h % 8 == 0.
 rra_status launch_residual_ss(const float *part, int split, size_t split_stride, float *x,
                               float *ss, const float *gamma, float *xg, int m, int h,
                               const FragOut &fo, hipStream_t s);
-inline int ss_parts(int h) { return (int)cdiv(h, 2048); }
+inline int ss_parts(int h) { return (int)cdiv(h, 512); }
 // qkv = sum_s part[s]; rope(q, k) at pos; q -> q_out [m][nq][hd]; k, v rows
 // scattered into the caches at pos, in cache slot slot_seq[i] (slot i when
 // slot_seq is null); seq_len[i] = min(pos[i] + 1, max_len); pos >= max_len
