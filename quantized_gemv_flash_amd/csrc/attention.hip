@@ -132,6 +132,20 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             }
         }
     }
+    // ---- values, first round: requested now, in flight during the softmax.
+    // hd/4 lanes per row, rows r0 + 4 KPW u of each round of RS rows; rows
+    // past n are clamped loads, never used.
+    constexpr int LPK = HD / 4, KPW = 64 / LPK, UV = 8, RS = 4 * KPW * UV;
+    const int d4 = lane % LPK, r0 = wave * KPW + lane / LPK;
+    float4 vb[UV];
+    auto vload = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int t = min(base + r0 + u * 4 * KPW, n - 1);
+            vb[u] = *reinterpret_cast<const float4 *>(V + (size_t)t * HD + 4 * d4);
+        }
+    };
+    vload(0);
     __syncthreads();
 
     // ---- per-head max, exponentials, sum
@@ -153,19 +167,19 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     }
     __syncthreads();
 
-    // ---- probability-weighted values: hd/4 lanes per row, 8 rows per lane in flight
-    constexpr int LPK = HD / 4, KPW = 64 / LPK, UV = 8;
-    const int d4 = lane % LPK, kslot = lane / LPK;
+    // ---- probability-weighted values: each round's rows are loaded one round
+    // ahead (the first before the softmax), so a round's loads overlap the
+    // previous round's arithmetic.
+    const int kslot = lane / LPK;
     float4 o[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) o[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int tb = wave * KPW + kslot; tb < n; tb += 4 * KPW * UV) {
+    for (int base = 0; base < n; base += RS) {
         float4 v[UV];
 #pragma unroll
-        for (int u = 0; u < UV; ++u) {
-            const int t = min(tb + u * 4 * KPW, n - 1);  // clamped; rows past n are skipped
-            v[u] = *reinterpret_cast<const float4 *>(V + (size_t)t * HD + 4 * d4);
-        }
+        for (int u = 0; u < UV; ++u) v[u] = vb[u];
+        if (base + RS < n) vload(base + RS);  // uniform over the workgroup
+        const int tb = base + r0;
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int t = tb + u * 4 * KPW;
