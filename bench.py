@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--m1-steps", type=int, default=256)
     ap.add_argument("--m1-ctx", type=int, default=512, help="context tokens of the M=1 line")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 1.5B-shaped M sweep")
+    ap.add_argument("--main-only", action="store_true",
+                    help="only the M=32 step and the flash-decode roofline (no M=1, FP8, "
+                         "prefill or sweep lines), for profiling")
     ap.add_argument("--fd-only", action="store_true",
                     help="run only the flash-decode launches (layer-sized synthetic cache at the "
                          "workload's lengths) and a plain copy of known size, for counter runs")
@@ -358,16 +361,16 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(S, W, dd, lengths, first, 8, 4)
         log(f"cpu baseline {cpu}")
-    prefill = prefill_line(S, dd, 512)  # overwrites slot 0's cache: after everything above
+    prefill = None if args.main_only else prefill_line(S, dd, 512)  # overwrites slot 0's cache
     log(f"prefill {prefill}")
     del dd, W
     torch.cuda.empty_cache()
-    if not args.no_m1:
+    if not (args.no_m1 or args.main_only):
         m1 = m1_line(args.m1_steps, args.m1_ctx)
         log(f"m1 {m1}")
-    fp8 = fp8_gemv_line()
+    fp8 = None if args.main_only else fp8_gemv_line()
     log(f"fp8 gemv {fp8}")
-    sweep = None if args.no_sweep else m_sweep_line()
+    sweep = None if (args.no_sweep or args.main_only) else m_sweep_line()
     log(f"m sweep {sweep}")
 
     out = {
@@ -402,7 +405,7 @@ def main():
         },
         "m1": m1,
         "fp8_gemv": fp8,
-        "prefill": dict(workload=f"{S.name}: 512 prompt tokens into one slot", **prefill),
+        "prefill": prefill and dict(workload=f"{S.name}: 512 prompt tokens into one slot", **prefill),
         "m_sweep": sweep,
         "cpu_baseline": cpu,
     }
