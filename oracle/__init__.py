@@ -41,8 +41,8 @@ _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "oracle.c")
 _LIB = os.path.join(_DIR, "liboracle.so")
 
-F32, Q8, Q4, FP8 = 0, 1, 2, 3
-_FMT = {"f32": F32, "q8": Q8, "q4": Q4, "fp8": FP8}
+F32, Q8, Q4, FP8, Q6K = 0, 1, 2, 3, 4
+_FMT = {"f32": F32, "q8": Q8, "q4": Q4, "fp8": FP8, "q6k": Q6K}
 
 
 def build(force: bool = False) -> str:

@@ -17,7 +17,9 @@
  * fp16 scale per block, value = scale*q; Q4: 32 unsigned 4-bit values and one
  * fp16 scale, value = scale*(q-8)).  FP8 (the pages' other weight precision,
  * [batched_forward] LM-head notes) is 32 OCP FP8 E4M3 values and one fp16
- * scale per block, value = scale*e4m3(q).
+ * scale per block, value = scale*e4m3(q).  Q6K (the 6-bit K-quant those notes
+ * also name; its block layout is not on the pages) is read as the K-quant
+ * family's 6-bit format, see orc_dequant_row.
  */
 #include <math.h>
 #include <stdint.h>
@@ -28,7 +30,11 @@
 #define ORC_Q8 1
 #define ORC_Q4 2
 #define ORC_FP8 3
+#define ORC_Q6K 4
 #define ORC_QBLOCK 32
+#define ORC_Q6K_SUPER 256
+#define ORC_Q6K_CODE_BYTES 192
+#define ORC_Q6K_SCALE_BYTES 18
 
 /* IEEE 754 binary16 -> binary64, from the bit fields: sign, 5-bit exponent
  * (bias 15), 10-bit fraction; exponent 0 encodes subnormals 2^-14 * f/1024,
@@ -70,10 +76,36 @@ double orc_e4m3_to_f64(uint8_t c) {
  *   Q8 : data is int8[n][k], scale is fp16[n][k/32]; w = scale * q;
  *   Q4 : data is uint8[n][k/2] (byte j: element 2j low nibble, 2j+1 high
  *        nibble), scale fp16[n][k/32]; w = scale * (q - 8);
- *   FP8: data is E4M3 codes uint8[n][k], scale fp16[n][k/32]; w = scale * e4m3(q). */
+ *   FP8: data is E4M3 codes uint8[n][k], scale fp16[n][k/32]; w = scale * e4m3(q);
+ *   Q6K: the 6-bit K-quant the pages name for LM heads: super-blocks of 256
+ *        values, each of 16 sub-blocks of 16 values with a signed int8 scale
+ *        sc, and one fp16 scale d per super-block; 6-bit codes q in 0..63;
+ *        w = d * sc[sub-block] * (q - 32).  data is uint8[n][k/256][192]: 128
+ *        bytes of the codes' low 4 bits (byte j: element 2j low nibble, 2j+1
+ *        high nibble), then 64 bytes of their high 2 bits (byte j: element
+ *        4j + e at bits 2e, 2e+1); scale is uint8[n][k/256][18]: the 16
+ *        sub-scales, then d (fp16, low byte first). */
 void orc_dequant_row(int fmt, const void *data, const uint16_t *scale, int64_t k,
                      int64_t row, double *out) {
     int64_t nb = k / ORC_QBLOCK;
+    if (fmt == ORC_Q6K) {
+        const int64_t nsb = k / ORC_Q6K_SUPER;
+        const uint8_t *codes = (const uint8_t *)data + row * nsb * ORC_Q6K_CODE_BYTES;
+        const uint8_t *recs = (const uint8_t *)scale + row * nsb * ORC_Q6K_SCALE_BYTES;
+        for (int64_t sb = 0; sb < nsb; ++sb) {
+            const uint8_t *lo = codes + sb * ORC_Q6K_CODE_BYTES, *hi = lo + 128;
+            const uint8_t *rec = recs + sb * ORC_Q6K_SCALE_BYTES;
+            double d = orc_f16_to_f64((uint16_t)(rec[16] | (rec[17] << 8)));
+            for (int i = 0; i < ORC_Q6K_SUPER; ++i) {
+                int low = (i % 2 == 0) ? (lo[i / 2] & 0xF) : (lo[i / 2] >> 4);
+                int high = (hi[i / 4] >> (2 * (i % 4))) & 3;
+                int q = low | (high << 4);
+                double sc = (double)(int8_t)rec[i / 16];
+                out[sb * ORC_Q6K_SUPER + i] = d * sc * (double)(q - 32);
+            }
+        }
+        return;
+    }
     if (fmt == ORC_F32) {
         const float *w = (const float *)data + row * k;
         for (int64_t i = 0; i < k; ++i) out[i] = (double)w[i];

@@ -39,7 +39,7 @@ class Decoder:
     head_dim: int
     intermediate: int
     vocab: int
-    fmt: str  # "f32" | "q8" | "q4" | "fp8"
+    fmt: str  # "f32" | "q8" | "q4" | "fp8" (and "q6k" for an LM head)
     rms_eps: float = 1e-6
     rope_theta: float = 1e4
     weight_std: float = 0.02
@@ -211,6 +211,46 @@ def quantize_q4(w: torch.Tensor):
     return packed.contiguous(), s16.view(torch.int16).contiguous()
 
 
+Q6K_SUPER = 256
+
+
+def quantize_q6k(w: torch.Tensor):
+    """fp32 [N][K] -> (codes uint8 [N][K/256*192], scale records uint8
+    [N][K/256*18]) in the 6-bit K-quant layout (see the oracle's dequant).
+
+    Per sub-block of 16: s = maxabs/31.5; per super-block of 256: d = max s /
+    126.5, stored as fp16 (round to nearest even; the margin below 127 absorbs
+    that rounding); sub-scale sc = min(ceil(s / d), 127) with the stored d, so
+    the step d*sc >= s and |w| / (d sc) <= 31.5; q = clamp(rint(w / (d sc)) + 32,
+    0, 63).  A sub-block whose sc is 0 gets every q = 32; an all-zero
+    super-block gets d = 0.
+    """
+    n, k = w.shape
+    assert k % Q6K_SUPER == 0, "Q6K needs K to be a multiple of 256"
+    nsb = k // Q6K_SUPER
+    b = w.reshape(n, nsb, 16, 16)
+    s = b.abs().amax(dim=3) / 31.5                       # [n][nsb][16]
+    d16 = (s.amax(dim=2) / 126.5).to(torch.float16)      # [n][nsb]
+    d = d16.to(torch.float32).unsqueeze(2)
+    sc = torch.where(d > 0, torch.ceil(s / torch.where(d > 0, d, torch.ones_like(d))),
+                     torch.zeros_like(s)).clamp_(0, 127)
+    step = (d * sc).unsqueeze(3)                           # [n][nsb][16][1]
+    safe = torch.where(step > 0, step, torch.ones_like(step))
+    q = torch.where(step > 0, torch.round(b / safe), torch.zeros_like(b)) + 32
+    q = q.clamp_(0, 63).to(torch.uint8).reshape(n, nsb, Q6K_SUPER)
+    low = q & 0xF
+    lo = low[:, :, 0::2] | (low[:, :, 1::2] << 4)         # [n][nsb][128]
+    high = q >> 4
+    hi = (high[:, :, 0::4] | (high[:, :, 1::4] << 2) | (high[:, :, 2::4] << 4)
+          | (high[:, :, 3::4] << 6))                      # [n][nsb][64]
+    codes = torch.cat([lo, hi], dim=2).reshape(n, nsb * 192)
+    dbytes = d16.view(torch.int16).unsqueeze(2)
+    dlo = (dbytes & 0xFF).to(torch.uint8)
+    dhi = ((dbytes >> 8) & 0xFF).to(torch.uint8)
+    rec = torch.cat([sc.to(torch.uint8), dlo, dhi], dim=2).reshape(n, nsb * 18)
+    return codes.contiguous(), rec.contiguous()
+
+
 def quantize(w: torch.Tensor, fmt: str):
     """Returns (data, scale-or-None) in the planar layout for `fmt`."""
     if fmt == "f32":
@@ -221,6 +261,8 @@ def quantize(w: torch.Tensor, fmt: str):
         return quantize_q4(w)
     if fmt == "fp8":
         return quantize_fp8(w)
+    if fmt == "q6k":
+        return quantize_q6k(w)
     raise ValueError(f"unknown weight format {fmt!r}")
 
 

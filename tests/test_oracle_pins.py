@@ -88,6 +88,53 @@ def _brute_row_fp8(row_bytes: bytes, scales, k):
             for i, c in enumerate(row_bytes)]
 
 
+def _brute_row_q6k(codes: bytes, recs: bytes, k):
+    # The 6-bit code of element i: low 4 bits are nibble i of the super-block's
+    # first 128 bytes read as one little-endian integer, high 2 bits are 2-bit
+    # field i of its last 64 bytes read the same way; value = d * sc * (q - 32)
+    # with sc the signed byte i // 16 of the record and d its fp16 tail.
+    out = []
+    for sb in range(k // 256):
+        c = codes[sb * 192:(sb + 1) * 192]
+        r = recs[sb * 18:(sb + 1) * 18]
+        lo, hi = int.from_bytes(c[:128], "little"), int.from_bytes(c[128:], "little")
+        d = Fraction(np.frombuffer(r[16:18], np.float16).item())
+        for i in range(256):
+            q = ((lo >> (4 * i)) & 0xF) | (((hi >> (2 * i)) & 0x3) << 4)
+            sc = struct.unpack("b", r[i // 16:i // 16 + 1])[0]
+            out.append(d * sc * (q - 32))
+    return out
+
+
+def _pack_q6k_superblock(q, sc, d_bits):
+    # Bytes of one super-block from 256 codes (0..63), 16 signed sub-scales and
+    # the fp16 bits of d, packed bit by bit (no vector tricks).
+    lo = sum((qi & 0xF) << (4 * i) for i, qi in enumerate(q)).to_bytes(128, "little")
+    hi = sum((qi >> 4) << (2 * i) for i, qi in enumerate(q)).to_bytes(64, "little")
+    rec = struct.pack("16b", *sc) + struct.pack("<H", d_bits)
+    return lo + hi, rec
+
+
+def test_q6k_worked_example():
+    # One row, K = 256.  d = 0.5 (fp16 0x3800); sub-block j has scale sc[j];
+    # code q of element i is chosen so each value is easy to check by hand:
+    # element 0 (sub-block 0, sc = 1): q = 63 -> 0.5 * 1 * 31 = 15.5
+    # element 1 (sc = 1): q = 0 -> 0.5 * 1 * -32 = -16
+    # element 16 (sub-block 1, sc = -2): q = 33 -> 0.5 * -2 * 1 = -1
+    # element 255 (sub-block 15, sc = 127): q = 48 -> 0.5 * 127 * 16 = 1016
+    # element 200 (sub-block 12, sc = -128): q = 31 -> 0.5 * -128 * -1 = 64
+    # every other element: q = 32 -> 0.
+    q = [32] * 256
+    q[0], q[1], q[16], q[255], q[200] = 63, 0, 33, 48, 31
+    sc = [1, -2] + [0] * 10 + [-128, 0, 0, 127]
+    codes, rec = _pack_q6k_superblock(q, sc, 0x3800)
+    got = oracle.dequant("q6k", np.frombuffer(codes, np.uint8).reshape(1, 192),
+                         np.frombuffer(rec, np.uint8).reshape(1, 18), 1, 256, [0])[0]
+    want = np.zeros(256)
+    want[[0, 1, 16, 255, 200]] = [15.5, -16.0, -1.0, 1016.0, 64.0]
+    assert np.array_equal(got, want)
+
+
 def test_e4m3_decode_matches_torch_for_every_code():
     codes = torch.arange(256, dtype=torch.uint8)
     ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -112,12 +159,12 @@ def test_fp8_worked_example():
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q8", "fp8"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "fp8", "q6k"])
 def test_gemv_integer_exact_brute_force(fmt):
     # Power-of-two scales and small-integer x make every partial sum exact in
     # fp64, so the oracle must equal exact rational arithmetic bit for bit.
     rng = np.random.default_rng(7)
-    n, k, m = 5, 96, 3
+    n, k, m = 5, (512 if fmt == "q6k" else 96), 3
     scales = (np.array([0x3C00, 0x3800, 0x4000, 0x3400, 0x2C00], np.uint16)[
         rng.integers(0, 5, size=(n, k // 32))]).astype(np.uint16)
     if fmt == "q4":
@@ -126,10 +173,20 @@ def test_gemv_integer_exact_brute_force(fmt):
     elif fmt == "q8":
         data = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
         rows = [_brute_row_q8(data[r].tobytes(), scales[r], k) for r in range(n)]
-    else:
+    elif fmt == "fp8":
         codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)  # no NaN
         data = codes[rng.integers(0, codes.size, size=(n, k))]
         rows = [_brute_row_fp8(data[r].tobytes(), scales[r], k) for r in range(n)]
+    else:
+        nsb = k // 256
+        data = rng.integers(0, 256, size=(n, nsb * 192), dtype=np.uint8)
+        scales = np.zeros((n, nsb * 18), np.uint8)
+        for r in range(n):
+            for sb in range(nsb):
+                scales[r, sb * 18:sb * 18 + 16] = rng.integers(-128, 128, 16).astype(np.int8).view(np.uint8)
+                d = np.array([[0x3C00, 0x3800, 0x4000, 0x2C00][rng.integers(0, 4)]], np.uint16)
+                scales[r, sb * 18 + 16:sb * 18 + 18] = d.view(np.uint8)
+        rows = [_brute_row_q6k(data[r].tobytes(), scales[r].tobytes(), k) for r in range(n)]
     x = rng.integers(-9, 10, size=(m, k)).astype(np.float64)
     y = oracle.gemv(fmt, data, scales, n, k, x)
     for mi in range(m):
@@ -168,6 +225,14 @@ def test_quantiser_roundtrip_is_close():
         deq = oracle.dequant(fmt, d, s, 8, 64, range(8))
         step = np.repeat(s.numpy().view(np.float16).astype(np.float64), 32, axis=1)
         assert np.all(np.abs(deq - w.numpy()) <= 0.5 * step * (1 + 1e-3) + 1e-9)
+    # Q6K: within half a step d * sc of each sub-block of 16.
+    w2 = synth.normal((4, 512), 0.02, 0, "pin_quant6")
+    d, r = synth.quantize(w2, "q6k")
+    deq = oracle.dequant("q6k", d, r, 4, 512, range(4))
+    rec = r.numpy().reshape(4, 2, 18)
+    dd = rec[:, :, 16:18].copy().view(np.float16).astype(np.float64)      # [4][2][1]
+    step = np.repeat((dd * rec[:, :, :16].view(np.int8)).reshape(4, 32), 16, axis=1)
+    assert np.all(np.abs(deq - w2.numpy()) <= 0.5 * step * (1 + 1e-3) + 1e-9)
     # FP8: within half a unit in the last place of E4M3 (3 fraction bits, so a
     # relative 2^-4), or half the subnormal step (2^-10) times the scale.
     d, s = synth.quantize(w, "fp8")
