@@ -247,24 +247,32 @@ def prefill_line(S, dd, n_tokens, reps=3):
                 tok_s=n_tokens / sec)
 
 
-def fp8_gemv_line(reps=20):
-    """The FP8 (E4M3) block format on the weights-once GEMV at the LM-head shape
-    of the 8B-shaped decoder (128256 x 4096): rra_batched_gemv (activation
-    image + GEMV) timed with HIP events at M = 1 and 32."""
+LM_HEAD_FORMATS = {
+    # format: (description, weight bytes per value)
+    "fp8": ("fp8 (E4M3 + fp16 scale per 32)", 34 / 32),
+    "q6k": ("q6k (6-bit codes, int8 scale per 16, fp16 scale per 256)", 210 / 256),
+}
+
+
+def lm_head_gemv_line(fmt, reps=20):
+    """A further block format on the weights-once GEMV at the LM-head shape of
+    the 8B-shaped decoder (128256 x 4096): rra_batched_gemv (activation image +
+    GEMV) timed with HIP events at M = 1 and 32."""
     import synth
     import quantized_gemv_flash_amd as rra
     n, k = 128256, 4096
-    data, scale = synth.weight(n, k, "fp8", 0.02, 0, "bench_fp8_lm", "cuda")
-    w = rra.device_weight(data, scale, "fp8")
+    data, scale = synth.weight(n, k, fmt, 0.02, 0, f"bench_{fmt}_lm", "cuda")
+    w = rra.device_weight(data, scale, fmt)
     del data, scale
-    wbytes = n * k * 34 / 32  # codes + one fp16 scale per 32
-    res = dict(shape=f"{n}x{k} fp8 (E4M3 + fp16 scale per 32)", weight_bytes=wbytes)
+    desc, per_value = LM_HEAD_FORMATS[fmt]
+    wbytes = n * k * per_value
+    res = dict(shape=f"{n}x{k} {desc}", weight_bytes=wbytes)
     for m in (1, 32):
         x = torch.randn((m, k), device="cuda")
         y = torch.empty((m, n), device="cuda")
         ws = torch.empty(max(4, rra.rra_batched_gemv_workspace_bytes(w, m)), dtype=torch.uint8,
                          device="cuda")
-        for _ in range(3):
+        for _ in range(10):
             rra.rra_batched_gemv(w, x, y, m, ws)
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -368,8 +376,10 @@ def main():
     if not (args.no_m1 or args.main_only):
         m1 = m1_line(args.m1_steps, args.m1_ctx)
         log(f"m1 {m1}")
-    fp8 = None if args.main_only else fp8_gemv_line()
+    fp8 = None if args.main_only else lm_head_gemv_line("fp8")
     log(f"fp8 gemv {fp8}")
+    q6k = None if args.main_only else lm_head_gemv_line("q6k")
+    log(f"q6k gemv {q6k}")
     sweep = None if (args.no_sweep or args.main_only) else m_sweep_line()
     log(f"m sweep {sweep}")
 
@@ -405,6 +415,7 @@ def main():
         },
         "m1": m1,
         "fp8_gemv": fp8,
+        "q6k_gemv": q6k,
         "prefill": prefill and dict(workload=f"{S.name}: 512 prompt tokens into one slot", **prefill),
         "m_sweep": sweep,
         "cpu_baseline": cpu,

@@ -50,7 +50,8 @@ typedef enum rra_status {
     RRA_ECAPTURE = 4  /* graph capture failed and the eager fallback failed too */
 } rra_status;
 
-/* Weight formats.  Blocks are 32 consecutive elements along K of one row.
+/* Weight formats.  Blocks are 32 consecutive elements along K of one row
+ * (Q6K: super-blocks of 256).
  *   RRA_F32: fp32 weights.
  *   RRA_Q8 : 32 int8 values q and one fp16 scale per block; w = scale * q.
  *   RRA_Q4 : 32 unsigned 4-bit values q and one fp16 scale per block;
@@ -60,29 +61,48 @@ typedef enum rra_status {
  *            scale per block; w = scale * e4m3(q).  The pages run the LM head
  *            in FP8 ([batched_forward] batched_output_norm_lm_head_argmax);
  *            here it is one more block format of the same weights-once GEMV,
- *            usable for any matrix. */
-typedef enum rra_wfmt { RRA_F32 = 0, RRA_Q8 = 1, RRA_Q4 = 2, RRA_FP8 = 3 } rra_wfmt;
+ *            usable for any matrix.
+ *   RRA_Q6K: the 6-bit K-quant the pages name for LM heads (its block
+ *            layout is not on the pages; read as the K-quant family's 6-bit
+ *            format): super-blocks of 256 values along K, each of 16
+ *            sub-blocks of 16 with a signed int8 scale sc, and one fp16 scale d
+ *            per super-block; 6-bit codes q in 0..63; w = d * sc * (q - 32).
+ *            k must be a multiple of 256. */
+typedef enum rra_wfmt {
+    RRA_F32 = 0,
+    RRA_Q8 = 1,
+    RRA_Q4 = 2,
+    RRA_FP8 = 3,
+    RRA_Q6K = 4
+} rra_wfmt;
 
 /* Storage layouts.
  *   RRA_PLANAR: F32 float[n][k]; Q8 data int8[n][k]; FP8 data uint8 codes
  *     [n][k]; Q4 data uint8[n][k/2] where byte j of a row holds element 2j in
  *     its low nibble and element 2j+1 in its high nibble; scales fp16 bit
- *     patterns [n][k/32].
- *   RRA_TILED (Q8/Q4/FP8): the layout the GEMV streams.  Rows are grouped in
- *     tiles of 16 and K in tiles of 128 (Q4) or 64 (Q8, FP8), one tile = 1 KiB
- *     of quantised values followed by its scales (128 B for Q4, 64 B else); the
- *     scales live inside `data` and `scale` is NULL.  Rows are padded to a
- *     multiple of 16 and K to a multiple of the K tile with zero-valued
- *     blocks.  Produced by rra_repack_weight; rra_tiled_bytes gives its size. */
+ *     patterns [n][k/32].  Q6K data uint8[n][k/256][192]: per super-block 128
+ *     bytes of the codes' low 4 bits (byte j: element 2j low nibble, 2j+1 high
+ *     nibble), then 64 bytes of their high 2 bits (byte j: element 4j + e at
+ *     bits 2e, 2e+1); Q6K `scale` points to uint8[n][k/256][18] records: the
+ *     16 sub-scales, then d (fp16, low byte first).
+ *   RRA_TILED (Q8/Q4/FP8/Q6K): the layout the GEMV streams.  Rows are grouped
+ *     in tiles of 16 and K in tiles of 128 (Q4, Q6K) or 64 (Q8, FP8), one tile
+ *     = 1 KiB of quantised values (Q6K: their low 4 bits, then 512 B of their
+ *     high 2 bits) followed by its scales (128 B for Q4, 64 B for Q8/FP8; Q6K:
+ *     128 B of sub-scales and the 16 rows' d); the scales live inside `data`
+ *     and `scale` is NULL.  Rows are padded to a multiple of 16 and K to a
+ *     multiple of the K tile with zero-valued blocks.  Produced by
+ *     rra_repack_weight; rra_tiled_bytes gives its size. */
 typedef enum rra_wlayout { RRA_PLANAR = 0, RRA_TILED = 1 } rra_wlayout;
 
 /* A weight matrix W [n][k] (n outputs, k inputs); y = W x. */
 typedef struct rra_weight {
     int32_t fmt;           /* rra_wfmt */
     int32_t layout;        /* rra_wlayout; RRA_F32 must be RRA_PLANAR */
-    int64_t n, k;          /* k % 32 == 0 for Q8/Q4 */
+    int64_t n, k;          /* k % 32 == 0 for Q8/Q4/FP8, k % 256 == 0 for Q6K */
     const void *data;      /* device, see the layouts above */
-    const uint16_t *scale; /* device fp16 bits [n][k/32] (planar Q8/Q4), else NULL */
+    const uint16_t *scale; /* device: planar Q8/Q4/FP8 fp16 bits [n][k/32], planar
+                              Q6K byte records (above); tiled and F32: NULL */
 } rra_weight;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -93,19 +113,20 @@ int32_t rra_version(void);
 
 /* ------------------------------------------------------------------ layout */
 
-/* Bytes of the RRA_TILED form of an [n][k] weight of format fmt (Q8/Q4);
+/* Bytes of the RRA_TILED form of an [n][k] weight of format fmt (Q8/Q4/FP8/Q6K);
  * 0 for an invalid shape or format. */
 size_t rra_tiled_bytes(int32_t fmt, int64_t n, int64_t k);
 
-/* Converts a planar Q8/Q4 weight into the tiled layout at `tiled` (device,
- * tiled_bytes >= rra_tiled_bytes) and fills *out (host) with its descriptor.
- * Bit-exact: no value is changed, only moved.  EINVAL on F32, on a non-planar
- * input, on k % 32 != 0 or on a short buffer. */
+/* Converts a planar Q8/Q4/FP8/Q6K weight into the tiled layout at `tiled`
+ * (device, tiled_bytes >= rra_tiled_bytes) and fills *out (host) with its
+ * descriptor.  Bit-exact: no value is changed, only moved.  EINVAL on F32, on
+ * a non-planar input, on k % 32 != 0 (Q6K: k % 256) or on a short buffer. */
 rra_status rra_repack_weight(const rra_weight *planar, void *tiled, size_t tiled_bytes,
                              rra_weight *out, hipStream_t s);
 
-/* Inverse of rra_repack_weight: writes the planar data (device, Q8 int8[n][k]
- * or Q4 uint8[n][k/2]) and scales (device fp16 bits [n][k/32]). */
+/* Inverse of rra_repack_weight: writes the planar data and scales (device,
+ * the RRA_PLANAR layout of the weight's format; for Q6K `scale` receives the
+ * byte records). */
 rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uint16_t *scale,
                              hipStream_t s);
 

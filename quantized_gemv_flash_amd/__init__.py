@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librra.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rra.h")
 
 RRA_OK, RRA_EINVAL, RRA_ENOTINIT, RRA_EHIP, RRA_ECAPTURE = 0, 1, 2, 3, 4
-RRA_F32, RRA_Q8, RRA_Q4, RRA_FP8 = 0, 1, 2, 3
+RRA_F32, RRA_Q8, RRA_Q4, RRA_FP8, RRA_Q6K = 0, 1, 2, 3, 4
 RRA_PLANAR, RRA_TILED = 0, 1
 RRA_GRAPH, RRA_STEP_GATHER, RRA_STEP_ADVANCE = 1, 2, 4
 RRA_POS_NONE = 0xFFFFFFFF  # empty batch slot; -1 in an int32 position tensor
 POS_NONE_I32 = -1
-FMT = {"f32": RRA_F32, "q8": RRA_Q8, "q4": RRA_Q4, "fp8": RRA_FP8}
+FMT = {"f32": RRA_F32, "q8": RRA_Q8, "q4": RRA_Q4, "fp8": RRA_FP8, "q6k": RRA_Q6K}
 
 
 class RraError(RuntimeError):
@@ -164,9 +164,10 @@ def rra_unpack_weight(tiled: Weight, data: torch.Tensor, scale: torch.Tensor, st
 
 def device_weight(data: torch.Tensor, scale: Optional[torch.Tensor], fmt: str, stream=None) -> Weight:
     """A GEMV-ready weight from planar tensors already on the device: F32 as is,
-    Q8/Q4/FP8 repacked into the tiled layout."""
+    Q8/Q4/FP8/Q6K repacked into the tiled layout."""
     n = data.shape[0]
-    k = data.shape[1] * (2 if fmt == "q4" else 1)
+    k = data.shape[1] * 2 if fmt == "q4" else (data.shape[1] // 192 * 256 if fmt == "q6k"
+                                                else data.shape[1])
     w = Weight(fmt, n, k, data, scale)
     return w if fmt == "f32" else rra_repack_weight(w, stream)
 

@@ -6,13 +6,14 @@
 // GEMV workgroup converting x again, the producer of a GEMV input writes it
 // once in the exact layout the GEMV copies into LDS:
 //
-//   per K tile kt (KT = 128 for Q4, 64 for Q8; NB = KT / 32 blocks), for
+//   per K tile kt (KT = 128 for Q4 and Q6K, 64 for Q8 and FP8; NB = KT / 32
+//   blocks), for
 //   block b, column tile c (16 sequences), part h (0 = hi, 1 = lo): a 1 KiB
 //   fragment of 64 slots x 16 bytes at
 //       ((((kt * NB + b) * CT + c) * 2 + h) * 1024 + slot * 16;
 //   slot frag_slot(j, r, b) holds the 8 fp16 values of sequence 16c + r,
 //   elements kt*KT + 32b + 8j + [0..8) in the order the weight operand uses
-//   (Q4: 0,4,1,5,2,6,3,7; Q8: 0..7).
+//   (Q4 and Q6K: 0,4,1,5,2,6,3,7; Q8 and FP8: 0..7).
 //
 // CT = 1 for M <= 16 sequences, 2 for M <= 32.  Elements k >= K up to the K
 // tile end must be written as zeros.
@@ -68,7 +69,7 @@ __device__ __forceinline__ void write_frag8(uint8_t *img, int ct, int m, int k0,
 
 __device__ __forceinline__ void write_frag8_fmt(int fmt, uint8_t *img, int ct, int m, int k0,
                                                 const float (&v)[8]) {
-    if (fmt == RRA_Q4)
+    if (fmt == RRA_Q4 || fmt == RRA_Q6K)
         write_frag8<RRA_Q4>(img, ct, m, k0, v);
     else
         write_frag8<RRA_Q8>(img, ct, m, k0, v);

@@ -35,16 +35,25 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int FMT>
 struct TileFmt;
+// KT columns, NB blocks of 32, TB bytes per tile, scales at byte SO of a tile,
+// IMG = the activation image layout the format reads (frag.h).
 template <>
 struct TileFmt<RRA_Q4> {
-    static constexpr int KT = 128, NB = 4, TB = 1024 + 128;
+    static constexpr int KT = 128, NB = 4, TB = 1024 + 128, SO = 1024, IMG = RRA_Q4;
 };
 template <>
 struct TileFmt<RRA_Q8> {
-    static constexpr int KT = 64, NB = 2, TB = 1024 + 64;
+    static constexpr int KT = 64, NB = 2, TB = 1024 + 64, SO = 1024, IMG = RRA_Q8;
 };
 template <>
 struct TileFmt<RRA_FP8> : TileFmt<RRA_Q8> {};  // one byte per value, same tiles
+// Q6K: 1 KiB of low 4 bits, 512 B of high 2 bits, then 128 B of int8
+// sub-scales ([lane half j/2][row][block]) and the 16 rows' fp16 d.  A K tile
+// is half a 256-value super-block, so d repeats in the two tiles of one.
+template <>
+struct TileFmt<RRA_Q6K> {
+    static constexpr int KT = 128, NB = 4, TB = 1024 + 512 + 128 + 32, SO = 1536, IMG = RRA_Q4;
+};
 
 __device__ __forceinline__ uint32_t pk_sub(uint32_t p, float c) {
     half2_t h = __builtin_bit_cast(half2_t, p);
@@ -112,6 +121,42 @@ __device__ __forceinline__ half8_t dequant_fp8(uint32_t d0, uint32_t d1) {
     return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Q6K: elements 0..7 of a group (low 4 bits n in one dword, as Q4; high 2
+// bits t at bits 2e of h16) with sub-scale sc -> two fp16 operands whose sum
+// is sc * (q - 32), q = 16 t + n, in Q4's order [0, 4, 1, 5, 2, 6, 3, 7]:
+//   a2 = sc * n            (|.| <= 128 * 15 < 2048: exact in fp16)
+//   a1 = 16 sc (t - 2)     (|.| <= 4096, a multiple of 16: exact)
+// Nibbles land in fp16 mantissas as 1024 + n (low) or 1024 + 16 n (high).
+// Low: (x - 1024) * sc.  High: one fused multiply-add (1024 + 16 n) sc/16 -
+// 64 sc, a single rounding of an exactly representable value (the same form
+// for the low nibbles would need the constant 1024 sc, past fp16's range for
+// |sc| > 63).  For a1 the 2-bit fields of elements e and e + 4 are brought 16
+// bits apart (h16 | h16 << 8), dropped into the mantissas of 1024 + t, then
+// (x - 1026) * 16 sc.
+__device__ __forceinline__ void dequant_q6k(uint32_t nib, uint32_t h16, _Float16 sc, half8_t &a1,
+                                            half8_t &a2) {
+    const half2_t s2 = {sc, sc};
+    const half2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+    const half2_t s_16 = s2 * half2_t{(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2_t s_64 = s2 * half2_t{(_Float16)-64.f, (_Float16)-64.f};
+    const half2_t s_t = s2 * half2_t{(_Float16)16.f, (_Float16)16.f};
+    const uint32_t e = 0x64006400u, w8 = nib >> 8;
+    const half2_t p04 = (__builtin_bit_cast(half2_t, and_or(nib, 0x000F000Fu, e)) - k1024) * s2;
+    const half2_t p15 = __builtin_elementwise_fma(
+        __builtin_bit_cast(half2_t, and_or(nib, 0x00F000F0u, e)), s_16, s_64);
+    const half2_t p26 = (__builtin_bit_cast(half2_t, and_or(w8, 0x000F000Fu, e)) - k1024) * s2;
+    const half2_t p37 = __builtin_elementwise_fma(
+        __builtin_bit_cast(half2_t, and_or(w8, 0x00F000F0u, e)), s_16, s_64);
+    a2 = half8_t{p04[0], p04[1], p15[0], p15[1], p26[0], p26[1], p37[0], p37[1]};
+    const uint32_t y = h16 | (h16 << 8);
+    const half2_t k1026 = {(_Float16)1026.f, (_Float16)1026.f};
+    const half2_t t0 = (__builtin_bit_cast(half2_t, and_or(y, 0x00030003u, e)) - k1026) * s_t;
+    const half2_t t1 = (__builtin_bit_cast(half2_t, and_or(y >> 2, 0x00030003u, e)) - k1026) * s_t;
+    const half2_t t2 = (__builtin_bit_cast(half2_t, and_or(y >> 4, 0x00030003u, e)) - k1026) * s_t;
+    const half2_t t3 = (__builtin_bit_cast(half2_t, and_or(y >> 6, 0x00030003u, e)) - k1026) * s_t;
+    a1 = half8_t{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+}
+
 // Q8: two dwords = int8 elements 0..7 of a group -> fp16 q in element order.
 __device__ __forceinline__ half8_t dequant_q8(uint32_t d0, uint32_t d1) {
     const uint32_t u0 = d0 ^ 0x80808080u, u1 = d1 ^ 0x80808080u;  // q + 128
@@ -171,7 +216,9 @@ struct QGemv {
     using F = TileFmt<FMT>;
     static constexpr int NB = F::NB, TB = F::TB;
     static constexpr int FRAG = NB * CT * 2;        // 1 KiB image fragments per K tile
-    static constexpr int SB = TB - 1024;            // scale bytes per tile
+    static constexpr int SB = TB - F::SO;           // scale bytes per tile
+    static constexpr bool Q6 = FMT == RRA_Q6K;      // high-bit plane, sub-scales
+    static constexpr int WL = Q6 ? 2 : 1;           // weight loads per row tile
     static constexpr int SCH = NW * RPW * SB / 16;  // 16-byte scale pieces per K tile
     static constexpr int XB = FRAG * 1024;          // image bytes per K tile
     static constexpr int XDW = (FRAG + NW - 1) / NW;  // image DMAs per wave per K tile
@@ -182,7 +229,10 @@ struct QGemv {
     __device__ __forceinline__ bool has_frag(int j) const {
         return FRAG % NW == 0 || wave + NW * j < FRAG;
     }
-    typedef uint4 Ring[RPW];
+    struct Ring {
+        uint4 q[RPW];  // this lane's 16 B of each row tile (Q6K: the low 4 bits)
+        uint2 h[RPW];  // Q6K: this lane's 8 B of the high 2-bit plane
+    };
     typedef floatx4 Acc[RPW][CT];
 
     const uint8_t *wt, *ximg;
@@ -202,7 +252,7 @@ struct QGemv {
             const int e = min(wave * 64 + lane, SCH - 1);
             const int piece = e % (SB / 16), rr = e / (SB / 16);
             const int rt = min(rt_wg + rr, n_rt - 1);
-            dma16(wt + ((size_t)rt * nkt + kt) * TB + 1024 + piece * 16, sd + wave * 1024);
+            dma16(wt + ((size_t)rt * nkt + kt) * TB + F::SO + piece * 16, sd + wave * 1024);
         }
     }
 
@@ -220,7 +270,7 @@ struct QGemv {
         k.x = ximg + ((size_t)kt * FRAG + wave) * 1024 + lane * 16;
         const int e = min(wave * 64 + lane, SCH - 1);
         const int rts = min(rt_wg + e / (SB / 16), n_rt - 1);
-        k.s = wt + ((size_t)rts * nkt + kt) * TB + 1024 + (e % (SB / 16)) * 16;
+        k.s = wt + ((size_t)rts * nkt + kt) * TB + F::SO + (e % (SB / 16)) * 16;
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
             k.w[r] = wt + ((size_t)min(rt0 + r, n_rt - 1) * nkt + kt) * TB + lane * 16;
@@ -241,7 +291,10 @@ struct QGemv {
     }
     __device__ __forceinline__ void issue_at(const Cursor &k, Ring &q) const {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) q[r] = *reinterpret_cast<const uint4 *>(k.w[r]);
+        for (int r = 0; r < RPW; ++r) {
+            q.q[r] = *reinterpret_cast<const uint4 *>(k.w[r]);
+            if (Q6) q.h[r] = *reinterpret_cast<const uint2 *>(k.w[r] + 1024 - 8 * lane);
+        }
     }
 
     // Quantised values of K tile kt_begin + c for this wave's row tiles,
@@ -252,7 +305,9 @@ struct QGemv {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             const int rt = min(rt0 + r, n_rt - 1);
-            q[r] = *reinterpret_cast<const uint4 *>(wt + ((size_t)rt * nkt + kt) * TB + lane * 16);
+            const uint8_t *t = wt + ((size_t)rt * nkt + kt) * TB;
+            q.q[r] = *reinterpret_cast<const uint4 *>(t + lane * 16);
+            if (Q6) q.h[r] = *reinterpret_cast<const uint2 *>(t + 1024 + lane * 8);
         }
     }
 
@@ -261,6 +316,34 @@ struct QGemv {
     // (never stored).
     __device__ __forceinline__ void compute(const Ring &q, const uint8_t *xs, const uint8_t *ss,
                                             Acc &acc) const {
+        if constexpr (Q6)
+            compute_q6k(q, xs, ss, acc);
+        else
+            compute_blocks(q, xs, ss, acc);
+        // The tile's accumulator updates stay here: left free, the compiler
+        // sinks them past the step's barrier, keeping every MFMA result of the
+        // tile live (registers) and leaving the matrix unit idle meanwhile.
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int cc = 0; cc < CT; ++cc) asm volatile("" : "+v"(acc[r][cc]));
+    }
+
+    // B fragments (hi, lo per column tile) of block b of the staged tile.
+    __device__ __forceinline__ void load_b(const uint8_t *xs, int b, half8_t (&Bh)[CT],
+                                           half8_t (&Bl)[CT]) const {
+        const int slot = frag_slot<F::IMG>(lane >> 4, lane & 15, b);
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) {
+            Bh[cc] = *reinterpret_cast<const half8_t *>(xs + ((b * CT + cc) * 2 + 0) * 1024 + slot * 16);
+            Bl[cc] = *reinterpret_cast<const half8_t *>(xs + ((b * CT + cc) * 2 + 1) * 1024 + slot * 16);
+        }
+    }
+
+    // Q8 / Q4 / FP8: one fp16 scale per (row, block of 32), applied to each
+    // block's MFMA result in fp32.
+    __device__ __forceinline__ void compute_blocks(const Ring &q, const uint8_t *xs,
+                                                   const uint8_t *ss, Acc &acc) const {
         // scales of this wave's row tiles: rows 4g+i, blocks b at (g, i, b)
         _Float16 sh[RPW][4 * NB];
 #pragma unroll
@@ -286,15 +369,10 @@ struct QGemv {
             // all four from being loaded up front, which costs registers)
             asm volatile("" ::: "memory");
             half8_t Bh[CT], Bl[CT];
-            const int slot = frag_slot<FMT>(lane >> 4, lane & 15, b);
-#pragma unroll
-            for (int cc = 0; cc < CT; ++cc) {
-                Bh[cc] = *reinterpret_cast<const half8_t *>(xs + ((b * CT + cc) * 2 + 0) * 1024 + slot * 16);
-                Bl[cc] = *reinterpret_cast<const half8_t *>(xs + ((b * CT + cc) * 2 + 1) * 1024 + slot * 16);
-            }
+            load_b(xs, b, Bh, Bl);
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
-                const uint4 qv = q[r];
+                const uint4 qv = q.q[r];
                 const half8_t a =
                     (FMT == RRA_Q4)    ? dequant_q4(u32_at(qv, b))
                     : (FMT == RRA_FP8) ? dequant_fp8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1))
@@ -310,13 +388,61 @@ struct QGemv {
                 }
             }
         }
-        // The tile's accumulator updates stay here: left free, the compiler
-        // sinks them past the step's barrier, keeping every MFMA result of the
-        // tile live (registers) and leaving the matrix unit idle meanwhile.
+    }
+
+    // Q6K: the int8 sub-scale is folded exactly into the fp16 operands
+    // (dequant_q6k), so the MFMAs accumulate the whole tile and d is applied
+    // once per tile.  Lane (j, r) needs the sub-scale of row r, sub-block
+    // 2b + j/2 of its half super-block: one dword per row tile holds blocks
+    // 0..3; the MFMA result rows 4g + i take d of those rows.
+    __device__ __forceinline__ void compute_q6k(const Ring &q, const uint8_t *xs,
+                                                const uint8_t *ss, Acc &acc) const {
+        uint32_t scw[RPW];
+        _Float16 dv[RPW][4];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const uint8_t *sp = ss + (wave * RPW + r) * SB;
+            scw[r] = *reinterpret_cast<const uint32_t *>(sp + (((lane >> 5) * 16 + (lane & 15)) * 4));
+            const uint2 d2 = *reinterpret_cast<const uint2 *>(sp + 128 + 8 * g);
+            const half2_t d01 = __builtin_bit_cast(half2_t, d2.x), d23 = __builtin_bit_cast(half2_t, d2.y);
+            dv[r][0] = d01[0];
+            dv[r][1] = d01[1];
+            dv[r][2] = d23[0];
+            dv[r][3] = d23[1];
+        }
+        floatx4 tt[RPW][CT];
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
-            for (int cc = 0; cc < CT; ++cc) asm volatile("" : "+v"(acc[r][cc]));
+            for (int cc = 0; cc < CT; ++cc) tt[r][cc] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            asm volatile("" ::: "memory");
+            half8_t Bh[CT], Bl[CT];
+            load_b(xs, b, Bh, Bl);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const uint32_t hw = (b < 2) ? q.h[r].x : q.h[r].y;
+                const uint32_t h16 = (b & 1) ? (hw >> 16) : (hw & 0xFFFFu);
+                const _Float16 sc = (_Float16)(int)(int8_t)(scw[r] >> (8 * b));
+                half8_t a1, a2;
+                dequant_q6k(u32_at(q.q[r], b), h16, sc, a1, a2);
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc) {
+                    floatx4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bh[cc], tt[r][cc], 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bl[cc], t, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bh[cc], t, 0, 0, 0);
+                    tt[r][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bl[cc], t, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[r][cc][i] = fmaf((float)dv[r][i], tt[r][cc][i], acc[r][cc][i]);
     }
 
     // One pipeline iteration: DMA of the next tile (cursor kn) into xw/sw and
@@ -502,7 +628,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__
 #pragma unroll
         for (int cc = 0; cc < CT; ++cc) acc[r][cc] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    wait_vm<NT * RPW>();  // every DMA landed; weight loads may be in flight
+    wait_vm<NT * RPW * G::WL>();  // every DMA landed; weight loads may be in flight
     lds_barrier();
     float sq[CT];
     p.sum_ss(nrm, sv, sq);
@@ -687,6 +813,88 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ tiled, uint8_t *__rest
     }
 }
 
+// Q6K tile (rt, kt) = half (kt & 1) of super-block kt / 2.  Lane (r, j):
+// 16 B of low 4 bits (dword b = the 8 nibbles of elements 32b + 8j + [0, 8) of
+// the half, as the planar bytes hold them) at 16 lane; 8 B of high 2-bit fields
+// (16 bits per block, blocks 0,1 in the first dword, 2,3 in the second) at
+// 1024 + 8 lane.  Sub-scales at 1536: byte ((h * 16 + r) * 4 + b) = sub-block
+// 8 (kt & 1) + 2b + h of row r; d of row r at 1664 + 2r.  Rows >= N are zero.
+__global__ void repack_q6k_kernel(const uint8_t *__restrict__ codes,
+                                  const uint8_t *__restrict__ recs, uint8_t *__restrict__ tiled,
+                                  int N, int K, int nkt) {
+    const long long tile = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int rt = (int)(tile / nkt), kt = (int)(tile % nkt);
+    uint8_t *dst = tiled + tile * TileFmt<RRA_Q6K>::TB;
+    const int nsb = K / 256, sb = kt >> 1, half = kt & 1;
+    const int r = lane & 15, j = lane >> 4;
+    const int row = rt * 16 + r;
+    const bool ok = row < N;
+    const uint8_t *cb = codes + ((size_t)(ok ? row : 0) * nsb + sb) * 192;
+    uint32_t d[4], h[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int e0 = half * 128 + 32 * b + 8 * j;
+        d[b] = ok ? *reinterpret_cast<const uint32_t *>(cb + e0 / 2) : 0u;
+        h[b] = ok ? *reinterpret_cast<const uint16_t *>(cb + 128 + e0 / 4) : 0u;
+    }
+    *reinterpret_cast<uint4 *>(dst + lane * 16) = uint4{d[0], d[1], d[2], d[3]};
+    *reinterpret_cast<uint2 *>(dst + 1024 + lane * 8) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int idx = 2 * lane + t;  // (hh * 16 + rr) * 4 + bb
+        const int hh = idx >> 6, rr = (idx >> 2) & 15, bb = idx & 3;
+        const int srow = rt * 16 + rr;
+        dst[1536 + idx] = srow < N ? recs[((size_t)srow * nsb + sb) * 18 + half * 8 + 2 * bb + hh] : 0;
+    }
+    if (lane < 16) {
+        const int srow = rt * 16 + lane;
+        const uint8_t *rec = recs + ((size_t)(srow < N ? srow : 0) * nsb + sb) * 18;
+        reinterpret_cast<uint16_t *>(dst + 1664)[lane] =
+            srow < N ? (uint16_t)(rec[16] | (rec[17] << 8)) : (uint16_t)0;
+    }
+}
+
+__global__ void unpack_q6k_kernel(const uint8_t *__restrict__ tiled, uint8_t *__restrict__ codes,
+                                  uint8_t *__restrict__ recs, int N, int K, int nkt) {
+    const long long tile = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int rt = (int)(tile / nkt), kt = (int)(tile % nkt);
+    const uint8_t *src = tiled + tile * TileFmt<RRA_Q6K>::TB;
+    const int nsb = K / 256, sb = kt >> 1, half = kt & 1;
+    const int r = lane & 15, j = lane >> 4;
+    const int row = rt * 16 + r;
+    if (row < N) {
+        uint8_t *cb = codes + ((size_t)row * nsb + sb) * 192;
+        const uint4 v = *reinterpret_cast<const uint4 *>(src + lane * 16);
+        const uint2 hv = *reinterpret_cast<const uint2 *>(src + 1024 + lane * 8);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t h[4] = {hv.x & 0xFFFFu, hv.x >> 16, hv.y & 0xFFFFu, hv.y >> 16};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int e0 = half * 128 + 32 * b + 8 * j;
+            *reinterpret_cast<uint32_t *>(cb + e0 / 2) = d[b];
+            *reinterpret_cast<uint16_t *>(cb + 128 + e0 / 4) = (uint16_t)h[b];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int idx = 2 * lane + t;
+        const int hh = idx >> 6, rr = (idx >> 2) & 15, bb = idx & 3;
+        const int srow = rt * 16 + rr;
+        if (srow < N) recs[((size_t)srow * nsb + sb) * 18 + half * 8 + 2 * bb + hh] = src[1536 + idx];
+    }
+    if (lane < 16 && half == 0) {
+        const int srow = rt * 16 + lane;
+        if (srow < N) {
+            const uint16_t dd = reinterpret_cast<const uint16_t *>(src + 1664)[lane];
+            uint8_t *rec = recs + ((size_t)srow * nsb + sb) * 18;
+            rec[16] = (uint8_t)(dd & 0xFF);
+            rec[17] = (uint8_t)(dd >> 8);
+        }
+    }
+}
+
 template <int FMT, int CT, int RPW, int NW>
 rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m, float *out,
                     size_t stride, const NormIn &nrm, hipStream_t s) {
@@ -764,6 +972,7 @@ rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, in
     }
     const auto *img = static_cast<const uint8_t *>(x);
     if (w.fmt == RRA_Q4) return launch_fmt<RRA_Q4>(w, p, img, m, out, stride, n, s);
+    if (w.fmt == RRA_Q6K) return launch_fmt<RRA_Q6K>(w, p, img, m, out, stride, n, s);
     if (w.fmt == RRA_FP8) return launch_fmt<RRA_FP8>(w, p, img, m, out, stride, n, s);
     return launch_fmt<RRA_Q8>(w, p, img, m, out, stride, n, s);
 }
@@ -772,7 +981,7 @@ rra_status launch_x_to_image(const float *x, uint8_t *img, int fmt, int m, int k
     const int kpad = (int)(cdiv(k, tile_k(fmt)) * tile_k(fmt));
     const int ct = frag_ct(m);
     dim3 grid((unsigned)cdiv(kpad / 8, 256), (unsigned)m);
-    if (fmt == RRA_Q4)
+    if (k128_tiles(fmt))
         hipLaunchKernelGGL(x_to_image_kernel<RRA_Q4>, grid, dim3(256), 0, s, x, img, m, k, kpad, ct);
     else
         hipLaunchKernelGGL(x_to_image_kernel<RRA_Q8>, grid, dim3(256), 0, s, x, img, m, k, kpad, ct);
@@ -792,7 +1001,7 @@ rra_status launch_reduce_splits(const float *part, int split, size_t split_strid
 using namespace rra;
 
 extern "C" size_t rra_tiled_bytes(int32_t fmt, int64_t n, int64_t k) {
-    if (!is_quantised(fmt) || n <= 0 || k <= 0 || k % 32) return 0;
+    if (!is_quantised(fmt) || n <= 0 || k <= 0 || k % (fmt == RRA_Q6K ? 256 : 32)) return 0;
     return (size_t)cdiv(n, 16) * (size_t)cdiv(k, tile_k(fmt)) * (size_t)tile_bytes(fmt);
 }
 
@@ -801,7 +1010,7 @@ extern "C" rra_status rra_repack_weight(const rra_weight *planar, void *tiled, s
     clear_error();
     if (!planar || !tiled || !out) return fail(RRA_EINVAL, "rra_repack_weight: null argument");
     if (!is_quantised(planar->fmt))
-        return fail(RRA_EINVAL, "rra_repack_weight: only Q8/Q4/FP8 weights are tiled");
+        return fail(RRA_EINVAL, "rra_repack_weight: only Q8/Q4/FP8/Q6K weights are tiled");
     if (planar->layout != RRA_PLANAR)
         return fail(RRA_EINVAL, "rra_repack_weight: input must be planar");
     RRA_TRY(validate_weight(planar, "rra_repack_weight", false));
@@ -813,7 +1022,11 @@ extern "C" rra_status rra_repack_weight(const rra_weight *planar, void *tiled, s
     const long long tiles = cdiv(planar->n, 16) * (long long)nkt;
     auto q = static_cast<const uint8_t *>(planar->data);
     auto dst = static_cast<uint8_t *>(tiled);
-    if (planar->fmt == RRA_Q4)
+    if (planar->fmt == RRA_Q6K)
+        hipLaunchKernelGGL(repack_q6k_kernel, dim3((unsigned)tiles), dim3(64), 0, s, q,
+                           reinterpret_cast<const uint8_t *>(planar->scale), dst, (int)planar->n,
+                           (int)planar->k, nkt);
+    else if (planar->fmt == RRA_Q4)
         hipLaunchKernelGGL(repack_kernel<RRA_Q4>, dim3((unsigned)tiles), dim3(64), 0, s, q,
                            planar->scale, dst, (int)planar->n, (int)planar->k, nkt);
     else
@@ -832,13 +1045,16 @@ extern "C" rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uin
     clear_error();
     if (!tiled || !data || !scale) return fail(RRA_EINVAL, "rra_unpack_weight: null argument");
     if (!is_quantised(tiled->fmt) || tiled->layout != RRA_TILED)
-        return fail(RRA_EINVAL, "rra_unpack_weight: input must be a tiled Q8/Q4/FP8 weight");
+        return fail(RRA_EINVAL, "rra_unpack_weight: input must be a tiled Q8/Q4/FP8/Q6K weight");
     RRA_TRY(validate_weight(tiled, "rra_unpack_weight", true));
     const int nkt = (int)cdiv(tiled->k, tile_k(tiled->fmt));
     const long long tiles = cdiv(tiled->n, 16) * (long long)nkt;
     auto src = static_cast<const uint8_t *>(tiled->data);
     auto q = static_cast<uint8_t *>(data);
-    if (tiled->fmt == RRA_Q4)
+    if (tiled->fmt == RRA_Q6K)
+        hipLaunchKernelGGL(unpack_q6k_kernel, dim3((unsigned)tiles), dim3(64), 0, s, src, q,
+                           reinterpret_cast<uint8_t *>(scale), (int)tiled->n, (int)tiled->k, nkt);
+    else if (tiled->fmt == RRA_Q4)
         hipLaunchKernelGGL(unpack_kernel<RRA_Q4>, dim3((unsigned)tiles), dim3(64), 0, s, src, q,
                            scale, (int)tiled->n, (int)tiled->k, nkt);
     else

@@ -62,6 +62,9 @@ rra_status validate_weight(const rra_weight *w, const char *what, bool need_tile
         return RRA_OK;
     }
     if (w->k % 32) return fail(RRA_EINVAL, "%s: k=%lld is not a multiple of 32", what, (long long)w->k);
+    if (w->fmt == RRA_Q6K && w->k % 256)
+        return fail(RRA_EINVAL, "%s: Q6K needs k (%lld) to be a multiple of 256", what,
+                    (long long)w->k);
     if (w->layout == RRA_PLANAR) {
         if (need_tiled_q)
             return fail(RRA_EINVAL, "%s: planar quantised weight; convert it with rra_repack_weight",

@@ -36,14 +36,20 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ tiles
-// A tile covers 16 rows and KT columns: 1 KiB of quantised values, then the
-// scales of its 16 rows x NB blocks.
+// A tile covers 16 rows and KT columns: 1 KiB of quantised values (Q6K: the
+// low 4 bits, then 512 B of high 2 bits), then the scales of its 16 rows.
 constexpr int kRowTile = 16;
-// Q8 and FP8 share one tile geometry (one byte per value); Q4 has its own.
-inline bool is_quantised(int fmt) { return fmt == RRA_Q8 || fmt == RRA_Q4 || fmt == RRA_FP8; }
-inline int tile_k(int fmt) { return fmt == RRA_Q4 ? 128 : 64; }
-inline int tile_blocks(int fmt) { return fmt == RRA_Q4 ? 4 : 2; }
-inline int tile_bytes(int fmt) { return fmt == RRA_Q4 ? 1024 + 128 : 1024 + 64; }
+// Q8 and FP8 share one tile geometry (one byte per value); Q4 and Q6K share
+// theirs (128 columns, 4 blocks of 32).
+inline bool is_quantised(int fmt) {
+    return fmt == RRA_Q8 || fmt == RRA_Q4 || fmt == RRA_FP8 || fmt == RRA_Q6K;
+}
+inline bool k128_tiles(int fmt) { return fmt == RRA_Q4 || fmt == RRA_Q6K; }
+inline int tile_k(int fmt) { return k128_tiles(fmt) ? 128 : 64; }
+inline int tile_blocks(int fmt) { return k128_tiles(fmt) ? 4 : 2; }
+inline int tile_bytes(int fmt) {
+    return fmt == RRA_Q6K ? 1024 + 512 + 128 + 32 : fmt == RRA_Q4 ? 1024 + 128 : 1024 + 64;
+}
 
 rra_status validate_weight(const rra_weight *w, const char *what, bool need_tiled_q);
 
@@ -83,7 +89,8 @@ rra_status launch_reduce_splits(const float *part, int split, size_t split_strid
 // Where a producer writes the next GEMV's activation image (frag.h).
 struct FragOut {
     uint8_t *img;  // nullptr: no image (fp32 weights)
-    int fmt;       // the consumer's format: RRA_Q4, or RRA_Q8 / RRA_FP8 (same image)
+    int fmt;       // the consumer's format: RRA_Q4 / RRA_Q6K, or RRA_Q8 / RRA_FP8
+                   // (each pair reads the same image)
     int ct;        // column tiles (1 for m <= 16, 2 otherwise)
     int kpad;      // K rounded up to the K tile; groups in [K, kpad) are zeros
 };

@@ -31,7 +31,9 @@ def assert_close(gpu, ref, rtol=RTOL, atol=ATOL, what="", row_scale=False):
     if row_scale:
         mag = np.maximum(mag, np.sqrt(np.mean(r * r, axis=-1, keepdims=True)))
     bound = atol + rtol * mag
-    bad = err > bound
+    bad = ~(err <= bound)  # a NaN or inf on either side is a failure
+    if np.isnan(r).any():
+        raise AssertionError(f"{what}: the oracle's values hold NaN")
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; worst at "
