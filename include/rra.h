@@ -175,8 +175,10 @@ rra_status rra_kv_scatter(const float *k_rows, const float *v_rows, float *k_cac
  * seq_len : device uint32 [m]; values are clamped to max_len; a sequence with
  *       seq_len 0 leaves its out rows untouched.
  * hd in {64, 128}; nq % nkv == 0; nq / nkv <= 8.
- * chunk : rows per split, a multiple of 32 in [32, 1024], or 0 to let the
- *       library choose from (m, nkv, max_len).
+ * chunk : at most this many rows per split, a multiple of 32 in [32, 1024],
+ *       or 0 to let the library choose from (m, nkv, max_len).  The rows of a
+ *       sequence are dealt round-robin to nc = ceil(max_len / chunk) splits
+ *       (split c takes rows c, c + nc, ...); the result is the same softmax. 
  * ws  : device scratch, ws_bytes >= rra_flash_decode_workspace_bytes(...) with
  *       the same chunk argument. */
 size_t rra_flash_decode_workspace_bytes(int32_t m, int32_t nq, int32_t nkv, int32_t hd,

@@ -6,15 +6,22 @@
 // pass combines the partials with softmax (log-sum-exp) rescaling.  Q has nq
 // heads; K/V have nkv heads, query head h reading KV head h / (nq / nkv).
 //
-// MI355X design.  One 256-thread workgroup per (chunk, KV head, sequence)
+// MI355X design.  One 256-thread workgroup per (split, KV head, sequence)
 // serves all G = nq/nkv query heads of its KV head, so every cached K/V byte
 // is read from HBM exactly once per step (the pages' kernel runs one 32-lane
 // group per *query* head).  Scores: 8 lanes per cached row, each lane a 128-bit
 // load per 32 columns, dot products for the G heads, 3-step butterfly.  The G
 // score rows of the chunk live in LDS; one wave per head forms max / exp /
 // sum; values: hd/4 lanes per row with 128-bit loads, G accumulators per lane,
-// then a cross-wave sum in LDS.  The grid covers max_len / chunk chunks and a
-// workgroup past seq_len returns at once, so a captured graph stays valid as
+// then a cross-wave sum in LDS.  The grid has nc = ceil(max_len / chunk)
+// splits per (sequence, KV head), and split c takes rows c, c + nc, c + 2nc,
+// ... (at most `chunk` of them) rather than one contiguous chunk: the softmax
+// partials and their log-sum-exp combination hold for any partition of the
+// rows, and with the rows dealt round-robin the nc workgroups of a sequence
+// sweep its cache region together, so the reads in flight stay within a
+// narrow window of HBM (measured on MI355X: 6.0-6.2 TB/s for the bare reads
+// with 8 splits, against 5.4 for contiguous chunks).  A split with no rows
+// (c >= seq_len) returns at once, so a captured graph stays valid as
 // positions advance.
 #include "frag.h"
 #include "rra_internal.h"
@@ -53,7 +60,8 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict
     }
 }
 
-// Partial result of chunk c for query head h of sequence m:
+// Partial result of split c (rows t = c + i nc_max) for query head h of
+// sequence m:
 //   part_o[((m*nq + h)*nc_max + c)*HD + d] = sum_t p_t v_t[d] / l,
 //   part_lse[(m*nq + h)*nc_max + c]      = max_t s_t + ln l,
 // with s_t = <q_h, k_t>/sqrt(HD), p_t = e^(s_t - max), l = sum_t p_t.
@@ -66,9 +74,11 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     constexpr int GP = (G + 3) & ~3;  // probabilities stored key-major, G padded to 4
     const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
     const int L = (int)min(seq_len[m], (uint32_t)max_len);
-    const int t0 = c * chunk;
-    if (t0 >= L) return;
-    const int n = min(chunk, L - t0);
+    if (c >= L) return;
+    // Rows c, c + nc_max, c + 2 nc_max, ... < L (local row i is cache row
+    // c + i nc_max): the nc_max workgroups of one (sequence, KV head) sweep its
+    // cache region together, front to back.
+    const int n = (L - c + nc_max - 1) / nc_max;  // <= chunk
 
     extern __shared__ float smem[];
     float *sc = smem;                 // [chunk][GP] scores, then probabilities
@@ -77,7 +87,8 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t cs = slot_seq ? slot_seq[m] : (uint32_t)m;  // cache slot of query row m
-    const size_t row0 = (cs * nkv + g) * max_len + t0;
+    const size_t row0 = (cs * nkv + g) * max_len + c;
+    const size_t rs = (size_t)nc_max * HD;  // floats between consecutive local rows
     const float *K = kc + row0 * HD;
     const float *V = vc + row0 * HD;
 
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
 #pragma unroll
             for (int i = 0; i < F4; ++i)
-                kv[u][i] = *reinterpret_cast<const float4 *>(K + (size_t)tc * HD + 4 * (e + 8 * i));
+                kv[u][i] = *reinterpret_cast<const float4 *>(K + (size_t)tc * rs + 4 * (e + 8 * i));
         }
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int t = min(base + r0 + u * 4 * KPW, n - 1);
-            vb[u] = *reinterpret_cast<const float4 *>(V + (size_t)t * HD + 4 * d4);
+            vb[u] = *reinterpret_cast<const float4 *>(V + (size_t)t * rs + 4 * d4);
         }
     };
     vload(0);
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
     if (L > 0) {
-        const int nc = (L + chunk - 1) / chunk;
+        const int nc = min(L, nc_max);  // workgroups that had rows
         const float *lse = part_lse + ((size_t)m * nq + h) * nc_max;
         float mx = -INFINITY;
         for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
@@ -327,16 +338,18 @@ rra_status launch_chunk_hd(int G, const float *q, const float *kc, const float *
 
 int fd_choose_chunk(int m, int nkv, int max_len, int chunk) {
     if (chunk > 0) return chunk;
-    // Chunk = the power of two in 64..256 nearest to (cached rows) / 288, so a
-    // short cache still gets about one workgroup per compute unit while a long
-    // one keeps 256-row chunks.  Shorter chunks only add per-workgroup cost
-    // (query load, softmax, partial write) and reduce work; longer ones leave
-    // compute units idle.  Measured on MI355X over M = 1..32 at 0.5B, 1.5B and
-    // 8B-sized KV heads: within 7 % of the best fixed chunk everywhere.
-    const int64_t target = (int64_t)m * nkv * max_len / 288;
-    int c = 64;
-    while (c < 256 && 2 * target > 3 * (int64_t)c) c *= 2;
-    return c;
+    // About one workgroup per 512 cached rows, but at least 256 (one per
+    // compute unit) and at most 2048; the splits per (sequence, KV head) then
+    // give the rows per split, rounded up to a multiple of 32 in 64..1024.
+    // Fewer, longer splits save per-workgroup cost (query load, softmax,
+    // partial write) and reduce work; more keep short caches spread over the
+    // chip.  Measured on MI355X over M = 1..32 at 0.5B, 1.5B and 8B-sized KV
+    // heads: within 5 % of the best fixed split size everywhere.
+    const int64_t pairs = (int64_t)m * nkv;
+    const int64_t wgs = std::min<int64_t>(2048, std::max<int64_t>(256, pairs * max_len / 512));
+    const int64_t nc = std::max<int64_t>(1, wgs / pairs);
+    const int64_t rows = (max_len + nc - 1) / nc;
+    return (int)std::min<int64_t>(1024, std::max<int64_t>(64, (rows + 31) / 32 * 32));
 }
 
 size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk) {

@@ -90,7 +90,7 @@ def test_gemv_requires_workspace():
 def test_flash_decode_sizes_and_validation():
     # chunk chosen from (m, nkv, max_len); partials are m*nq*nc*(hd+1) floats
     c = rra.rra_flash_decode_chunk(32, 8, 8192, 0)
-    assert c in (32, 64, 128, 256, 512)
+    assert c % 32 == 0 and 64 <= c <= 1024
     nc = -(-8192 // c)
     assert rra.rra_flash_decode_workspace_bytes(32, 32, 8, 128, 8192, 0) == 32 * 32 * nc * 129 * 4
     assert rra.rra_flash_decode_workspace_bytes(1, 14, 2, 64, 768, 64) == 14 * 12 * 65 * 4
