@@ -134,17 +134,17 @@ rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uint16_t *scal
  * [batched_forward] forward_batched_to_token_ids: batched GEMV kernels read
  * and dequantise every weight block once for all M inputs.
  *   y[i][r] = sum_c W[r][c] * x[i][c]   for i < m, r < n.
- * w   : F32 planar, or Q8/Q4 tiled (planar Q8/Q4 -> EINVAL, repack first).
- * x   : device fp32 [m][k]; |x| must stay below 65504 for Q8/Q4 (the
+ * w   : F32 planar, or a tiled quantised weight (planar -> EINVAL, repack first).
+ * x   : device fp32 [m][k]; |x| must stay below 65504 for quantised weights (the
  *       activations enter the matrix cores as an fp16 high part plus an fp16
  *       low part).
  * y   : device fp32 [m][n]; must not overlap x.
  * ws  : device scratch, ws_bytes >= rra_batched_gemv_workspace_bytes(w, m),
  *       owned by the caller and reused freely after the call completes on s.
  *       It holds the activations converted once into the matrix-core operand
- *       image (Q8/Q4) and the split-K partial sums (when K is split).  May be
- *       NULL only when that size is 0; otherwise a missing or short ws gives
- *       RRA_ENOTINIT and nothing is launched.
+ *       image (quantised weights) and the split-K partial sums (when K is
+ *       split).  May be NULL only when that size is 0; otherwise a missing or
+ *       short ws gives RRA_ENOTINIT and nothing is launched.
  * Results do not depend on the stream, the call or the run (no atomics). */
 size_t rra_batched_gemv_workspace_bytes(const rra_weight *w, int32_t m);
 rra_status rra_batched_gemv(const rra_weight *w, const float *x, float *y, int32_t m,

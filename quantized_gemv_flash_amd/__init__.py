@@ -146,7 +146,7 @@ def rra_tiled_bytes(fmt: str, n: int, k: int) -> int:
 
 
 def rra_repack_weight(planar: Weight, stream=None) -> Weight:
-    """Planar Q8/Q4 -> tiled copy in a new device tensor."""
+    """Planar quantised weight -> tiled copy in a new device tensor."""
     nbytes = rra_tiled_bytes(planar.fmt, planar.n, planar.k)
     if nbytes == 0:
         raise RraError("rra_repack_weight", RRA_EINVAL, "invalid shape or format")

@@ -1,7 +1,7 @@
 // frag.h -- the activation "B-operand image" shared by the GEMV (consumer) and
 // the kernels that produce GEMV inputs.
 //
-// The Q8/Q4 GEMV multiplies on the matrix cores with the fp32 activation x
+// The quantised GEMV multiplies on the matrix cores with the fp32 activation x
 // split as x = hi + lo (hi = fp16(x), lo = fp16(x - hi)).  Instead of every
 // GEMV workgroup converting x again, the producer of a GEMV input writes it
 // once in the exact layout the GEMV copies into LDS:

@@ -3,14 +3,18 @@
 // [batched_forward] forward_batched_to_token_ids: every weight block is read
 // and dequantised once for all M inputs.
 //
-// Q8/Q4 path (gfx950 matrix cores).  One v_mfma_f32_16x16x32_f16 takes a
-// 16-row x 32-column slab of W -- exactly one quantisation block per row -- and
-// a 32 x 16 slab of X^T (16 sequences).  The quantised values q (Q8) or q - 8
-// (Q4) are small integers, exact in fp16; the block scale is applied in fp32
-// after the block's products, so W is never rounded.  X is fp32 and enters as
+// Quantised path (Q8, Q4, FP8, Q6K; gfx950 matrix cores).  One
+// v_mfma_f32_16x16x32_f16 takes a 16-row x 32-column slab of W -- exactly one
+// quantisation block per row -- and a 32 x 16 slab of X^T (16 sequences).  The
+// dequantised operands are exact in fp16 (Q8 and Q4 values are small integers,
+// E4M3 values are a subset of fp16, a Q6K value is split into two exact
+// parts); the fp16 block scale (Q6K: the super-block scale) is applied in fp32
+// after the products, so W is never rounded.  X is fp32 and enters as
 // x = hi + lo with hi = fp16(x), lo = fp16(x - hi): two MFMAs per slab give
 // ~22 significant bits, i.e. fp32-like dot products (products are exact in the
-// fp32 accumulator: 11-bit x 11-bit mantissas).
+// fp32 accumulator: 11-bit x 11-bit mantissas).  A workgroup of NW waves owns
+// NW * RPW row tiles and one K split; all its waves share each staged
+// activation tile.
 //
 // Data movement.  Weights are pre-tiled (rra_repack_weight): one 16-row x KT
 // tile is 1 KiB of values (each lane of a wave loads 16 contiguous bytes that
@@ -1063,7 +1067,7 @@ extern "C" rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uin
     return check_launch("unpack_kernel");
 }
 
-// Workspace of the public GEMV: the activation image (Q8/Q4), then the
+// Workspace of the public GEMV: the activation image (quantised weights), then the
 // split-K partial sums when K is split.
 static size_t gemv_ws_layout(const rra_weight &w, int m, size_t *part_off) {
     const GemvPlan p = gemv_plan(w, m);

@@ -178,7 +178,7 @@ struct rra_model {
     float *fd = nullptr, *logits = nullptr, *rope = nullptr;
     uint32_t *lens = nullptr, *err = nullptr;
     void *argmax_ws = nullptr;
-    uint8_t *img = nullptr;  // activation image of the next Q8/Q4 GEMV
+    uint8_t *img = nullptr;  // activation image of the next quantised GEMV
     int rows = 0;            // batch rows the workspace holds: max(m_max, prefill rows)
     int prefill_rows = 0;    // prompt tokens per prefill chunk
     // prefill chunk state: x rows, positions, cache slot per row, token ids

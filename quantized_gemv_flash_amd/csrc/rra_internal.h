@@ -75,12 +75,12 @@ struct NormIn {
     float eps;
 };
 // Enqueues the GEMV; the result (or its K-split partial sums) goes to
-// out[split][m][n] with out_split_stride floats between splits.  For Q8/Q4
+// out[split][m][n] with out_split_stride floats between splits.  For quantised
 // weights `x` is the activation image (frag.h) with frag_ct(m) column tiles;
 // for F32 weights it is fp32 [m][k].
 rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, int m, float *out,
                        size_t out_split_stride, hipStream_t s, const NormIn *nrm = nullptr);
-// Converts fp32 x [m][k] into the activation image of a Q8/Q4 GEMV.
+// Converts fp32 x [m][k] into the activation image of a quantised GEMV.
 rra_status launch_x_to_image(const float *x, uint8_t *img, int fmt, int m, int k, hipStream_t s);
 // y[i][r] = sum over `split` partial planes (+ y[i][r] if accumulate).
 rra_status launch_reduce_splits(const float *part, int split, size_t split_stride, float *y,

@@ -1,7 +1,7 @@
 """Places a decoder's weights on the device for librra and creates the model.
 
 Takes planar weights as (data, scale) tensor pairs on the target device (the
-layout of include/rra.h's RRA_PLANAR), repacks the Q8/Q4 ones into the tiled
+layout of include/rra.h's RRA_PLANAR), repacks the quantised ones into the tiled
 GEMV layout with rra_repack_weight, allocates zeroed KV caches
 [m_max][nkv][max_len][hd] per layer, and builds the rra_model descriptor.
 """
