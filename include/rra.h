@@ -266,7 +266,13 @@ typedef struct rra_model rra_model;
 #define RRA_GRAPH 1        /* run as a captured HIP graph (captured on the first
                               call for a given (m, flags, pointers) key, replayed
                               after; [graph] module doc, [batched_forward]
-                              forward_batched_to_token_ids_graphed) */
+                              forward_batched_to_token_ids_graphed).  If the
+                              capture fails it is discarded, the stream leaves
+                              capture mode and the step runs eagerly ([reduces]
+                              try_graph_capture); the environment variable
+                              RRA_FAIL_CAPTURE=1 makes every capture fail, to
+                              test that path.  RRA_VERBOSE=1 logs captures and
+                              fallbacks to stderr. */
 #define RRA_STEP_GATHER 2  /* x[i] = embed[tok[i]] first (tok read as input) */
 #define RRA_STEP_ADVANCE 4 /* pos[i] += 1 after the step */
 

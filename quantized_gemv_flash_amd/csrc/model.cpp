@@ -43,6 +43,14 @@ bool verbose() {
     return v;
 }
 
+// RRA_FAIL_CAPTURE set (and not "0"): every graph capture reports its body as
+// failed, so tests can drive the discard-and-run-eagerly path from the host.
+// Read at each capture (captures are rare), so a test can set and clear it.
+bool capture_failure_requested() {
+    const char *e = getenv("RRA_FAIL_CAPTURE");
+    return e && *e && strcmp(e, "0") != 0;
+}
+
 rra_status check_launch(const char *what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(RRA_EHIP, "launch of %s failed: %s", what, hipGetErrorString(e));
@@ -500,7 +508,9 @@ static rra_status capture_and_launch(rra_model *M, const GraphKey &key, float *x
     // failed capture cannot poison other threads' work.  End the capture
     // whatever happened, so the stream always leaves capture mode.
     RRA_TRY_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-    const rra_status body = enqueue_step(M, x, pos, tok, tok, logits, m, flags, nullptr, s);
+    rra_status body = enqueue_step(M, x, pos, tok, tok, logits, m, flags, nullptr, s);
+    if (body == RRA_OK && capture_failure_requested())
+        body = fail(RRA_ECAPTURE, "capture failure requested by RRA_FAIL_CAPTURE");
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(s, &graph);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

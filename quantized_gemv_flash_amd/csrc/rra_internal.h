@@ -15,6 +15,7 @@ namespace rra {
 rra_status fail(rra_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 bool verbose();
+bool capture_failure_requested();
 
 #define RRA_TRY_HIP(call)                                                               \
     do {                                                                                \

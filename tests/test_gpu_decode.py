@@ -4,6 +4,8 @@ The oracle runs on the same seeded bytes.  Where greedy ids could differ
 (oracle top-2 gap < 1e-3) the GPU is teacher-forced with the oracle's ids, so
 no value computed on the GPU ever enters the oracle.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -78,12 +80,19 @@ def test_tiny_f32_sixteen_greedy_steps():
         tok = o["tok"].tolist()
 
 
-def test_tiny_f32_batched_equals_separate_bitwise():
-    S = synth.TINY_LLAMA_F32
+SMALL_DECODERS = [synth.TINY_LLAMA_F32,
+                  dataclasses.replace(synth.SMALL_LLAMA_FP8, name="small-llama-q8", fmt="q8"),
+                  dataclasses.replace(synth.SMALL_LLAMA_FP8, name="small-llama-q4", fmt="q4"),
+                  synth.SMALL_LLAMA_FP8]
+
+
+@pytest.mark.parametrize("S", SMALL_DECODERS, ids=lambda S: S.name)
+def test_batched_equals_separate_bitwise(S):
+    # M-batched == M separate M=1 runs, bit for bit, in every weight format.
     W = synth.decoder_weights(S, seed=3, device=DEV, gamma="random")
     m = 3
-    both = Run(S, W, m, S.max_len)
-    ones = [Run(S, W, 1, S.max_len) for _ in range(m)]
+    both = Run(S, W, m, 16)
+    ones = [Run(S, W, 1, 16) for _ in range(m)]
     toks = synth.first_tokens(S, m, seed=3).tolist()
     starts = [0, 2, 5]
     for step in range(6):
@@ -96,10 +105,10 @@ def test_tiny_f32_batched_equals_separate_bitwise():
         toks = ids_b
 
 
-def test_graph_replay_equals_eager_bitwise():
-    S = synth.TINY_LLAMA_F32
+@pytest.mark.parametrize("S", SMALL_DECODERS, ids=lambda S: S.name)
+def test_graph_replay_equals_eager_bitwise(S):
     W = synth.decoder_weights(S, seed=1, device=DEV, gamma="random")
-    eager, graph = Run(S, W, 2, S.max_len), Run(S, W, 2, S.max_len)
+    eager, graph = Run(S, W, 2, 16), Run(S, W, 2, 16)
     toks = synth.first_tokens(S, 2, seed=1).tolist()
     steps = 10
     for step in range(steps):
@@ -113,6 +122,29 @@ def test_graph_replay_equals_eager_bitwise():
     for l in range(S.n_layers):
         assert torch.equal(eager.dd.k_caches[l], graph.dd.k_caches[l])
         assert torch.equal(eager.dd.v_caches[l], graph.dd.v_caches[l])
+
+
+def test_capture_failure_discarded_and_step_runs_eagerly(monkeypatch):
+    # A failed capture ([reduces] try_graph_capture): the graph is discarded,
+    # the stream leaves capture mode, the step runs eagerly with the same
+    # results; once captures succeed again the graph is built and replayed.
+    S = synth.TINY_LLAMA_F32
+    W = synth.decoder_weights(S, seed=2, device=DEV, gamma="random")
+    eager, graph = Run(S, W, 2, S.max_len), Run(S, W, 2, S.max_len)
+    toks = synth.first_tokens(S, 2, seed=2).tolist()
+    for step in range(4):
+        if step == 0:
+            monkeypatch.setenv("RRA_FAIL_CAPTURE", "1")
+        if step == 2:
+            monkeypatch.delenv("RRA_FAIL_CAPTURE")
+        a = eager.step(toks, [step, step + 1])
+        b = graph.step(toks, [step, step + 1], flags=rra.RRA_GRAPH)
+        assert torch.cuda.current_stream().query() in (True, False)  # usable, not capturing
+        assert a[0] == b[0] and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+        st = graph.dd.model.rra_graph_stats()
+        assert st["captures"] == (0 if step < 2 else 1)
+        assert st["replays"] == (1 if step == 3 else 0)
+        toks = a[0]
 
 
 def test_device_greedy_loop_gather_advance_in_graph():
