@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librra.so")
 SOURCES = ["gemv.hip", "attention.hip", "elementwise.hip", "model.cpp"]
-HEADERS = [os.path.join(CSRC, h) for h in ("rra_internal.h", "frag.h")] + [os.path.join(INCLUDE, "rra.h")]
+HEADERS = [os.path.join(CSRC, h) for h in ("rra_internal.h", "frag.h", "epilogue.h")] + [
+    os.path.join(INCLUDE, "rra.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

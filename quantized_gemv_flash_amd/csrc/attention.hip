@@ -23,6 +23,7 @@
 // with 8 splits, against 5.4 for contiguous chunks).  A split with no rows
 // (c >= seq_len) returns at once, so a captured graph stays valid as
 // positions advance.
+#include "epilogue.h"
 #include "frag.h"
 #include "rra_internal.h"
 
@@ -30,17 +31,6 @@
 
 namespace rra {
 namespace {
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
 __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict__ k_rows,
                                                          const float *__restrict__ v_rows,
@@ -256,39 +246,11 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
     constexpr int PER = HD / 64;
     const int L = (int)min(seq_len[m], (uint32_t)max_len);
     float acc[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    fd_combine<HD>(part_o, part_lse, m, h, nq, nc_max, L, lane, acc);
     if (L > 0) {
-        const int nc = min(L, nc_max);  // workgroups that had rows
-        const float *lse = part_lse + ((size_t)m * nq + h) * nc_max;
-        float mx = -INFINITY;
-        for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
-        mx = wave_max(mx);
-        float wsum = 0.f;
-        for (int c = lane; c < nc; c += 64) wsum += expf(lse[c] - mx);
-        wsum = wave_sum(wsum);
-        // chunks 8 at a time, every load issued before any is used
-        const float *po = part_o + ((size_t)m * nq + h) * nc_max * HD;
-        for (int c0 = 0; c0 < nc; c0 += 8) {
-            float v[8][PER], w[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int cj = min(c0 + j, nc - 1);
-                w[j] = (c0 + j < nc) ? expf(lse[cj] - mx) : 0.f;
-#pragma unroll
-                for (int i = 0; i < PER; ++i) v[j][i] = po[(size_t)cj * HD + lane + 64 * i];
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int i = 0; i < PER; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
-        }
         float *o = out + ((size_t)m * nq + h) * HD;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            acc[j] /= wsum;
-            o[lane + 64 * j] = acc[j];
-        }
+        for (int j = 0; j < PER; ++j) o[lane + 64 * j] = acc[j];
     }
     if (!fo.img) return;
 #pragma unroll
@@ -368,18 +330,19 @@ rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
-                               const FragOut *fo, const uint32_t *slot_seq) {
+                               const FragOut *fo, const uint32_t *slot_seq, bool reduce) {
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
     const int nc_max = (int)cdiv(max_len, chunk);
     float *po = part;
-    float *pl = part + (size_t)m * nq * nc_max * hd;
+    float *pl = const_cast<float *>(fd_part_lse(part, m, nq, hd, nc_max));
     if (hd == 128)
         RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
                                      max_len, chunk, nc_max, s));
     else
         RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
                                     max_len, chunk, nc_max, s));
+    if (!reduce) return RRA_OK;
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,
                            out, nq, max_len, chunk, nc_max, img);

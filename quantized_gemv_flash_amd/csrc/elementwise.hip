@@ -9,6 +9,7 @@
 //   SwiGLU   silu(gate) * up, silu(z) = z / (1 + e^-z)
 //   argmax   lowest index among the maximal logits ([reduces] gpu_argmax:
 //            block-level (max, index) pairs, then a final reduce)
+#include "epilogue.h"
 #include "frag.h"
 #include "rra_internal.h"
 
@@ -50,70 +51,6 @@ __device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
 __device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-
-// Split sum of NV 8-column vectors (p[v] .. p[v] + 8) shared by the four
-// waves of a 256-thread block: lane g of every wave works on the same group,
-// wave q adds planes q, q + 4, q + 8, ... (8 / NV planes in flight per
-// thread), and wave 0 then adds the other waves' sums in wave order (a fixed
-// order: the result does not depend on timing).  All 256 threads must call
-// it (it synchronises the block); the total is valid in wave 0.  `red` is
-// 3 * 64 * NV * 8 floats of shared memory.
-template <int NV>
-__device__ __forceinline__ void group_split_sum(const float *const (&p)[NV], bool active,
-                                                int split, long long stride,
-                                                float (&acc)[NV][8], float *red) {
-    const int gl = threadIdx.x & 63, q = threadIdx.x >> 6;
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[v][e] = 0.f;
-    if (active) {
-        constexpr int UN = 8 / NV;
-        for (int s0 = q; s0 < split; s0 += 4 * UN) {
-            float4 a[UN][NV][2];
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const size_t off = (size_t)min(s0 + 4 * u, split - 1) * stride;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    a[u][v][0] = *reinterpret_cast<const float4 *>(p[v] + off);
-                    a[u][v][1] = *reinterpret_cast<const float4 *>(p[v] + off + 4);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                if (s0 + 4 * u >= split) continue;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    acc[v][0] += a[u][v][0].x; acc[v][1] += a[u][v][0].y;
-                    acc[v][2] += a[u][v][0].z; acc[v][3] += a[u][v][0].w;
-                    acc[v][4] += a[u][v][1].x; acc[v][5] += a[u][v][1].y;
-                    acc[v][6] += a[u][v][1].z; acc[v][7] += a[u][v][1].w;
-                }
-            }
-        }
-    }
-    if (q > 0) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[(((q - 1) * 64 + gl) * NV + v) * 8 + e] = acc[v][e];
-    }
-    __syncthreads();
-    if (q == 0) {
-        for (int r = 0; r < 3; ++r)
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[v][e] += red[((r * 64 + gl) * NV + v) * 8 + e];
-    }
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
 }
 
 // Sum over a 256-thread block; every thread gets the result.
@@ -242,8 +179,6 @@ __global__ void rope_kernel(float *__restrict__ z, const uint32_t *__restrict__ 
     zr[j] = a * cs - c * sn;
     zr[j + half] = a * sn + c * cs;
 }
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __global__ void swiglu_kernel(const float *gate, const float *up, float *out, int n,
                               long long gate_stride, long long up_stride, long long total) {

@@ -1,0 +1,148 @@
+// epilogue.h -- reductions shared by the step's epilogue kernels and by the
+// GEMV prologues that stand in for them at small batch sizes.  Both callers
+// run the same functions with the same thread mapping, so a value is computed
+// by the same operations in the same order whichever kernel produces it (a
+// sequence's result does not depend on the batch it is in).
+#pragma once
+
+#include "rra_internal.h"
+
+namespace rra {
+namespace {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Split sum of NV 8-column vectors (p[v] .. p[v] + 8) shared by the four
+// waves of a 256-thread block: lane g of every wave works on the same group,
+// wave q adds planes q, q + 4, q + 8, ... (8 / NV planes in flight per
+// thread), and wave 0 then adds the other waves' sums in wave order (a fixed
+// order: the result does not depend on timing).  All 256 threads must call
+// it (it synchronises the block); the total is valid in wave 0.  `red` is
+// 3 * 64 * NV * 8 floats of shared memory.
+template <int NV>
+__device__ __forceinline__ void group_split_sum(const float *const (&p)[NV], bool active,
+                                                int split, long long stride,
+                                                float (&acc)[NV][8], float *red) {
+    const int gl = threadIdx.x & 63, q = threadIdx.x >> 6;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[v][e] = 0.f;
+    if (active) {
+        constexpr int UN = 8 / NV;
+        for (int s0 = q; s0 < split; s0 += 4 * UN) {
+            float4 a[UN][NV][2];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const size_t off = (size_t)min(s0 + 4 * u, split - 1) * stride;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    a[u][v][0] = *reinterpret_cast<const float4 *>(p[v] + off);
+                    a[u][v][1] = *reinterpret_cast<const float4 *>(p[v] + off + 4);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                if (s0 + 4 * u >= split) continue;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    acc[v][0] += a[u][v][0].x; acc[v][1] += a[u][v][0].y;
+                    acc[v][2] += a[u][v][0].z; acc[v][3] += a[u][v][0].w;
+                    acc[v][4] += a[u][v][1].x; acc[v][5] += a[u][v][1].y;
+                    acc[v][6] += a[u][v][1].z; acc[v][7] += a[u][v][1].w;
+                }
+            }
+        }
+    }
+    if (q > 0) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[(((q - 1) * 64 + gl) * NV + v) * 8 + e] = acc[v][e];
+    }
+    __syncthreads();
+    if (q == 0) {
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[v][e] += red[((r * 64 + gl) * NV + v) * 8 + e];
+    }
+}
+
+// [head_dim] flash_decoding_attention_into, second pass: the output of query
+// head h of sequence m from its splits' partials (part_o normalised outputs,
+// part_lse log-sum-exps; the first min(L, nc_max) splits hold rows):
+// sum_c e^(lse_c - max) o_c / sum_c e^(lse_c - max).  One wave; lane holds
+// columns lane + 64 j in acc[j].  L == 0 leaves acc at 0.
+template <int HD>
+__device__ __forceinline__ void fd_combine(const float *__restrict__ part_o,
+                                           const float *__restrict__ part_lse, int m, int h,
+                                           int nq, int nc_max, int L, int lane,
+                                           float (&acc)[HD / 64]) {
+    constexpr int PER = HD / 64;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    if (L <= 0) return;
+    const int nc = min(L, nc_max);  // splits that had rows
+    const float *lse = part_lse + ((size_t)m * nq + h) * nc_max;
+    const float *po = part_o + ((size_t)m * nq + h) * nc_max * HD;
+    // Every load that does not depend on another is issued first: this
+    // lane's lse (split `lane`; up to 64 splits stay in registers and are
+    // read back by shuffles) and the first 16 splits' outputs.
+    const float l0 = lse[min(lane, nc - 1)];
+    float v0[8][PER], v1[8][PER];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            v0[j][i] = po[(size_t)min(j, nc - 1) * HD + lane + 64 * i];
+            v1[j][i] = po[(size_t)min(8 + j, nc - 1) * HD + lane + 64 * i];
+        }
+    float mx = lane < nc ? l0 : -INFINITY;
+    for (int c = lane + 64; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
+    mx = wave_max(mx);
+    float wsum = lane < nc ? expf(l0 - mx) : 0.f;
+    for (int c = lane + 64; c < nc; c += 64) wsum += expf(lse[c] - mx);
+    wsum = wave_sum(wsum);
+    // splits 8 at a time, in split order
+    auto add8 = [&](int c0, const float (&v)[8][PER]) {
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cj = min(c0 + j, nc - 1);
+            const float lc = cj < 64 ? __shfl(l0, cj, 64) : lse[cj];
+            w[j] = (c0 + j < nc) ? expf(lc - mx) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
+    };
+    add8(0, v0);
+    if (nc > 8) add8(8, v1);
+    for (int c0 = 16; c0 < nc; c0 += 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                v0[j][i] = po[(size_t)min(c0 + j, nc - 1) * HD + lane + 64 * i];
+        add8(c0, v0);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] /= wsum;
+}
+
+}  // namespace
+}  // namespace rra

@@ -52,19 +52,28 @@ __device__ __forceinline__ void split8(const float (&v)[8], half8_t &hi, half8_t
     }
 }
 
+// Writes the group x[m][kk .. kk+8) of one K tile (kk = column within the
+// tile, a multiple of 8) into that tile's image at `tile` (global memory or
+// LDS: one tile is NB * ct * 2 KiB), with `ct` column tiles.
+template <int FMT>
+__device__ __forceinline__ void write_frag8_tile(uint8_t *tile, int ct, int m, int kk,
+                                                 const float (&v)[8]) {
+    const int b = kk >> 5, j = (kk & 31) >> 3;
+    half8_t hi, lo;
+    split8<FMT>(v, hi, lo);
+    const int base = ((b * ct + (m >> 4)) * 2) * 1024 + frag_slot<FMT>(j, m & 15, b) * 16;
+    *reinterpret_cast<half8_t *>(tile + base) = hi;
+    *reinterpret_cast<half8_t *>(tile + base + 1024) = lo;
+}
+
 // Writes the group x[m][k0 .. k0+8) (k0 % 8 == 0) into an image with `ct`
 // column tiles.
 template <int FMT>
 __device__ __forceinline__ void write_frag8(uint8_t *img, int ct, int m, int k0,
                                             const float (&v)[8]) {
     constexpr int KT = (FMT == RRA_Q4) ? 128 : 64, NB = KT / 32;
-    const int kt = k0 / KT, kk = k0 - kt * KT, b = kk >> 5, j = (kk & 31) >> 3;
-    half8_t hi, lo;
-    split8<FMT>(v, hi, lo);
-    const size_t base = ((((size_t)kt * NB + b) * ct + (m >> 4)) * 2) * 1024 +
-                        (size_t)frag_slot<FMT>(j, m & 15, b) * 16;
-    *reinterpret_cast<half8_t *>(img + base) = hi;
-    *reinterpret_cast<half8_t *>(img + base + 1024) = lo;
+    const int kt = k0 / KT;
+    write_frag8_tile<FMT>(img + (size_t)kt * NB * ct * 2 * 1024, ct, m, k0 - kt * KT, v);
 }
 
 __device__ __forceinline__ void write_frag8_fmt(int fmt, uint8_t *img, int ct, int m, int k0,

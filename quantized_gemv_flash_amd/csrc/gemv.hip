@@ -28,6 +28,7 @@
 //
 // F32 path: plain wave-per-row FMA GEMV (fp32 weights are only used by small
 // models, where it is latency-bound).
+#include "epilogue.h"
 #include "frag.h"
 #include "rra_internal.h"
 
@@ -252,6 +253,11 @@ struct QGemv {
             const int f = wave + NW * j;
             if (has_frag(j)) dma16(ximg + ((size_t)kt * FRAG + f) * 1024 + lane * 16, xd + f * 1024);
         }
+        stage_scales(c, sd);
+    }
+    // The scales part of stage() alone.
+    __device__ __forceinline__ void stage_scales(int c, uint8_t *sd) const {
+        const int kt = min(kt_begin + c, kt_end - 1);
         if (wave < SCW) {  // piece e -> (row tile, piece)
             const int e = min(wave * 64 + lane, SCH - 1);
             const int piece = e % (SB / 16), rr = e / (SB / 16);
@@ -601,16 +607,89 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_kernel(const uint8_t *__restri
 // tile.  Tiles past the split end are clamped copies, never computed.
 // Because no DMA follows a weight load, the compiler's own count of the
 // loads in flight matches the hardware's and it adds no waits.
-template <int FMT, int CT, int RPW, int NW, int NT>
+// Prologues (GemvPrologue): the image of K tiles kt_begin + t (t < nch) of
+// this workgroup's split, built in LDS (xs[t]) for rows m < M, one column
+// tile (M <= 16), four waves.  PRO: kProSwiglu, or kProAttn + HD.
+template <int IMG, int KT, int XB>
+__device__ __forceinline__ void prologue_swiglu(const GemvPrologue &pro, int M, int kt_begin,
+                                                int nch, uint8_t (*xs)[XB], float *red) {
+    // groups of 8 columns: gidx = (m * nch + t) * (KT / 8) + kk
+    constexpr int GPT = KT / 8;
+    const int total = M * nch * GPT, inter = pro.n;
+    for (int g0 = 0; g0 < total; g0 += 64) {
+        const int gidx = g0 + (threadIdx.x & 63);
+        const bool valid = gidx < total;
+        const int gc = valid ? gidx : 0;
+        const int kk = gc % GPT, t = (gc / GPT) % nch, m = gc / (GPT * nch);
+        const int k0 = (kt_begin + t) * KT + 8 * kk;
+        const size_t gi = (size_t)m * 2 * inter + k0;
+        float acc[2][8];
+        const float *const pp[2] = {pro.part + gi, pro.part + gi + inter};
+        group_split_sum<2>(pp, valid && k0 < inter, pro.split, pro.stride, acc, red);
+        if (threadIdx.x < 64 && valid) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = k0 < inter ? silu(acc[0][e]) * acc[1][e] : 0.f;
+            write_frag8_tile<IMG>(xs[t], 1, m, 8 * kk, v);
+        }
+        __syncthreads();  // `red` is reused by the next pass
+    }
+}
+
+template <int IMG, int KT, int XB, int HD>
+__device__ __forceinline__ void prologue_attn(const GemvPrologue &pro, int M, int kt_begin,
+                                              int nch, uint8_t (*xs)[XB], float *so) {
+    // heads overlapping columns [kt_begin KT, (kt_begin + nch) KT), one wave
+    // per (sequence, head) pair; so = 4 waves x HD floats.
+    constexpr int PER = HD / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int k_lo = kt_begin * KT, k_hi = (kt_begin + nch) * KT, nqhd = pro.n * HD;
+    const int h_lo = k_lo / HD, h_hi = min(pro.n, (k_hi + HD - 1) / HD);
+    const int pairs = M * max(0, h_hi - h_lo);
+    float *sw = so + wave * HD;
+    for (int pidx = wave; pidx < pairs; pidx += 4) {
+        const int m = pidx / (h_hi - h_lo), h = h_lo + pidx % (h_hi - h_lo);
+        const int L = (int)min(pro.seq_len[m], (uint32_t)pro.max_len);
+        float acc[PER];
+        fd_combine<HD>(pro.part, pro.lse, m, h, pro.n, pro.nc_max, L, lane, acc);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) sw[lane + 64 * j] = acc[j];
+        __builtin_amdgcn_wave_barrier();
+        if (lane < HD / 8) {
+            const int k0 = h * HD + lane * 8;
+            if (k0 >= k_lo && k0 < k_hi) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = sw[lane * 8 + e];
+                write_frag8_tile<IMG>(xs[k0 / KT - kt_begin], 1, m, k0 % KT, v);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    // zeros for the groups in [nq hd, kpad)
+    for (int gidx = threadIdx.x; gidx < M * nch * (KT / 8); gidx += blockDim.x) {
+        const int kk = gidx % (KT / 8), t = (gidx / (KT / 8)) % nch, m = gidx / (nch * (KT / 8));
+        if ((kt_begin + t) * KT + 8 * kk >= nqhd) {
+            const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            write_frag8_tile<IMG>(xs[t], 1, m, 8 * kk, z);
+        }
+    }
+}
+
+template <int FMT, int CT, int RPW, int NW, int NT, int PRO = 0>
 __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__restrict__ wt,
                                                                const uint8_t *__restrict__ ximg,
                                                                float *__restrict__ out, int M,
                                                                int N, int K, int nkt,
                                                                int kt_per_split,
-                                                               long long split_stride, NormIn nrm) {
+                                                               long long split_stride, NormIn nrm,
+                                                               GemvPrologue pro) {
     using G = QGemv<FMT, CT, RPW, NW>;
+    static_assert(PRO == 0 || (CT == 1 && NW == 4), "prologues build one column tile, 4 waves");
     __shared__ __attribute__((aligned(16))) uint8_t xs[NT][G::XB];
     __shared__ __attribute__((aligned(16))) uint8_t sl[NT][G::SCB];
+    constexpr int RED = PRO == kProSwiglu ? 3 * 64 * 16 : PRO >= kProAttn ? 4 * 128 : 1;
+    __shared__ float red[RED];
 
     G p;
     p.init(wt, ximg, N, nkt, kt_per_split);
@@ -619,7 +698,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__
     float sv[CT][G::SSP];
     p.load_ss(nrm, M, sv);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) p.stage(t, xs[t], sl[t]);
+    for (int t = 0; t < NT; ++t) {
+        if (PRO == 0)
+            p.stage(t, xs[t], sl[t]);
+        else
+            p.stage_scales(t, sl[t]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     typename G::Ring q[NT];
 #pragma unroll
@@ -632,6 +716,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__
 #pragma unroll
         for (int cc = 0; cc < CT; ++cc) acc[r][cc] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (PRO == kProSwiglu)
+        prologue_swiglu<TileFmt<FMT>::IMG, TileFmt<FMT>::KT, G::XB>(pro, M, p.kt_begin, nch, xs, red);
+    else if constexpr (PRO == kProAttn)
+        prologue_attn<TileFmt<FMT>::IMG, TileFmt<FMT>::KT, G::XB, 64>(pro, M, p.kt_begin, nch, xs, red);
+    else if constexpr (PRO == kProAttn + 1)
+        prologue_attn<TileFmt<FMT>::IMG, TileFmt<FMT>::KT, G::XB, 128>(pro, M, p.kt_begin, nch, xs, red);
     wait_vm<NT * RPW * G::WL>();  // every DMA landed; weight loads may be in flight
     lds_barrier();
     float sq[CT];
@@ -899,23 +989,47 @@ __global__ void unpack_q6k_kernel(const uint8_t *__restrict__ tiled, uint8_t *__
     }
 }
 
+template <int FMT, int CT, int RPW, int NW, int NT>
+rra_status launch_short(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m,
+                        float *out, size_t stride, const NormIn &nrm, const GemvPrologue &pro,
+                        dim3 grid, int nkt, hipStream_t s) {
+    const auto *wd = static_cast<const uint8_t *>(w.data);
+#define RRA_SHORT(PRO)                                                                         \
+    hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, NW, NT, PRO>), grid, dim3(64 * NW), 0, \
+                       s, wd, img, out, m, (int)w.n, (int)w.k, nkt, p.kt_per_split,           \
+                       (long long)stride, nrm, pro)
+    if constexpr (CT == 1 && NW == 4) {
+        const int hd = pro.kind == kProAttn ? (int)(w.k / pro.n) : 0;
+        if (pro.kind == kProSwiglu)
+            RRA_SHORT(kProSwiglu);
+        else if (pro.kind == kProAttn && hd == 64)
+            RRA_SHORT(kProAttn);
+        else if (pro.kind == kProAttn && hd == 128)
+            RRA_SHORT(kProAttn + 1);
+        else if (pro.kind != kProNone)
+            return fail(RRA_EINVAL, "gemv prologue: unsupported kind %d (hd %d)", pro.kind, hd);
+        else
+            RRA_SHORT(kProNone);
+    } else {
+        if (pro.kind != kProNone) return fail(RRA_EINVAL, "gemv prologue: m > 16");
+        RRA_SHORT(kProNone);
+    }
+#undef RRA_SHORT
+    return check_launch("gemv_q_short_kernel");
+}
+
 template <int FMT, int CT, int RPW, int NW>
 rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m, float *out,
-                    size_t stride, const NormIn &nrm, hipStream_t s) {
+                    size_t stride, const NormIn &nrm, const GemvPrologue &pro, hipStream_t s) {
     const int n_rt = (int)cdiv(w.n, 16);
     const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
     dim3 grid((unsigned)cdiv(n_rt, NW * RPW), (unsigned)p.split), block(64 * NW);
     const auto *wd = static_cast<const uint8_t *>(w.data);
-    if (p.kt_per_split <= 2) {
-        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, NW, 2>), grid, block, 0, s, wd, img,
-                           out, m, (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
-        return check_launch("gemv_q_short_kernel");
-    }
-    if (p.kt_per_split <= 4) {
-        hipLaunchKernelGGL((gemv_q_short_kernel<FMT, CT, RPW, NW, 4>), grid, block, 0, s, wd, img,
-                           out, m, (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
-        return check_launch("gemv_q_short_kernel");
-    }
+    if (p.kt_per_split <= 2)
+        return launch_short<FMT, CT, RPW, NW, 2>(w, p, img, m, out, stride, nrm, pro, grid, nkt, s);
+    if (p.kt_per_split <= 4)
+        return launch_short<FMT, CT, RPW, NW, 4>(w, p, img, m, out, stride, nrm, pro, grid, nkt, s);
+    if (pro.kind != kProNone) return fail(RRA_EINVAL, "gemv prologue: split longer than 4 tiles");
     hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW, NW>), grid, block, 0, s, wd, img, out, m,
                        (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
     return check_launch("gemv_q_kernel");
@@ -923,17 +1037,18 @@ rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, 
 
 template <int FMT>
 rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m,
-                      float *out, size_t stride, const NormIn &nrm, hipStream_t s) {
+                      float *out, size_t stride, const NormIn &nrm, const GemvPrologue &pro,
+                      hipStream_t s) {
     if (m <= 16) {
-        if (p.rpw >= 2) return launch_q<FMT, 1, 2, 4>(w, p, img, m, out, stride, nrm, s);
-        return launch_q<FMT, 1, 1, 4>(w, p, img, m, out, stride, nrm, s);
+        if (p.rpw >= 2) return launch_q<FMT, 1, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
+        return launch_q<FMT, 1, 1, 4>(w, p, img, m, out, stride, nrm, pro, s);
     }
     if (p.nw == 8) {
-        if (p.rpw >= 2) return launch_q<FMT, 2, 2, 8>(w, p, img, m, out, stride, nrm, s);
-        return launch_q<FMT, 2, 1, 8>(w, p, img, m, out, stride, nrm, s);
+        if (p.rpw >= 2) return launch_q<FMT, 2, 2, 8>(w, p, img, m, out, stride, nrm, pro, s);
+        return launch_q<FMT, 2, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
     }
-    if (p.rpw >= 2) return launch_q<FMT, 2, 2, 4>(w, p, img, m, out, stride, nrm, s);
-    return launch_q<FMT, 2, 1, 4>(w, p, img, m, out, stride, nrm, s);
+    if (p.rpw >= 2) return launch_q<FMT, 2, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
+    return launch_q<FMT, 2, 1, 4>(w, p, img, m, out, stride, nrm, pro, s);
 }
 
 }  // namespace
@@ -963,10 +1078,18 @@ GemvPlan gemv_plan(const rra_weight &w, int m) {
     return p;
 }
 
+bool gemv_takes_prologue(const rra_weight &w, const GemvPlan &p, int m) {
+    return is_quantised(w.fmt) && m <= 4 && p.kt_per_split <= 4;
+}
+
 rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, int m, float *out,
-                       size_t stride, hipStream_t s, const NormIn *nrm) {
+                       size_t stride, hipStream_t s, const NormIn *nrm, const GemvPrologue *pro) {
     const NormIn none{nullptr, 0, 0.f};
     const NormIn &n = nrm ? *nrm : none;
+    const GemvPrologue no_pro{kProNone, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
+    const GemvPrologue &pr = pro ? *pro : no_pro;
+    if (pr.kind != kProNone && !gemv_takes_prologue(w, p, m))
+        return fail(RRA_EINVAL, "gemv prologue: needs a quantised weight, m <= 4 and short splits");
     if (w.fmt == RRA_F32) {
         dim3 grid((unsigned)cdiv(w.n, 4));
         hipLaunchKernelGGL(gemv_f32_kernel, grid, dim3(256), 0, s,
@@ -975,10 +1098,10 @@ rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, in
         return check_launch("gemv_f32_kernel");
     }
     const auto *img = static_cast<const uint8_t *>(x);
-    if (w.fmt == RRA_Q4) return launch_fmt<RRA_Q4>(w, p, img, m, out, stride, n, s);
-    if (w.fmt == RRA_Q6K) return launch_fmt<RRA_Q6K>(w, p, img, m, out, stride, n, s);
-    if (w.fmt == RRA_FP8) return launch_fmt<RRA_FP8>(w, p, img, m, out, stride, n, s);
-    return launch_fmt<RRA_Q8>(w, p, img, m, out, stride, n, s);
+    if (w.fmt == RRA_Q4) return launch_fmt<RRA_Q4>(w, p, img, m, out, stride, n, pr, s);
+    if (w.fmt == RRA_Q6K) return launch_fmt<RRA_Q6K>(w, p, img, m, out, stride, n, pr, s);
+    if (w.fmt == RRA_FP8) return launch_fmt<RRA_FP8>(w, p, img, m, out, stride, n, pr, s);
+    return launch_fmt<RRA_Q8>(w, p, img, m, out, stride, n, pr, s);
 }
 
 rra_status launch_x_to_image(const float *x, uint8_t *img, int fmt, int m, int k, hipStream_t s) {

@@ -183,6 +183,7 @@ struct rra_model {
     int chunk[RRA_M_MAX + 1] = {};  // flash-decode rows per split, per batch size
     // workspace carve-up
     float *ss = nullptr, *xg = nullptr, *part = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr;
+    float *part_d = nullptr;  // the down GEMV's partials (its prologue may read `part`)
     float *fd = nullptr, *logits = nullptr, *rope = nullptr;
     uint32_t *lens = nullptr, *err = nullptr;
     void *argmax_ws = nullptr;
@@ -203,7 +204,8 @@ struct rra_model {
 namespace {
 
 struct Layout {
-    size_t ss, xg, img, part, q, lens, attn, act, fd, logits, argmax, rope, err, px, pidx, total;
+    size_t ss, xg, img, part, part_d, q, lens, attn, act, fd, logits, argmax, rope, err, px, pidx,
+        total;
 };
 
 // Rows of one prefill chunk, and the batch rows the workspace is laid out for.
@@ -265,6 +267,7 @@ Layout layout_of(const rra_model_desc &d) {
     L.xg = take(4 * M * d.hidden);
     L.img = take(image_bytes(d));
     L.part = take(4 * partf);
+    L.part_d = take(4 * partf);
     L.q = take(4 * M * d.n_heads * d.head_dim);
     L.lens = take(4 * M);
     L.attn = take(4 * M * d.n_heads * d.head_dim);
@@ -373,25 +376,38 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
                                 L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd, d.max_len,
                                 slot_seq, s));
+        // At small m the O GEMV combines the attention partials itself and the
+        // down GEMV forms SwiGLU itself (GemvPrologue): two launches fewer per
+        // layer, with the same arithmetic as the kernels they stand in for.
+        const GemvPlan &po = M->plan_o[m];
+        const bool pro_o = gemv_takes_prologue(L.wo, po, m);
         const FragOut fo_o = image_for(M, L.wo, m);
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
-                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq));
-        const GemvPlan &po = M->plan_o[m];
-        RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part, (size_t)m * H, s));
+                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq, !pro_o));
+        const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
+        const GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
+                              0, 0, nq, nc_max, d.max_len};
+        RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part, (size_t)m * H, s,
+                            nullptr, pro_o ? &pa : nullptr));
         RRA_TRY(launch_residual_ss(M->part, po.split, (size_t)m * H, x, M->ss, L.ffn_gamma, M->xg, m,
                                    H, image_for(M, L.wgu, m), s));
         // feed-forward block
         const GemvPlan &pg = M->plan_gu[m];
         RRA_TRY(launch_gemv(L.wgu, pg, gemv_input(M, L.wgu, M->xg), m, M->part, (size_t)m * 2 * I, s,
                             &nrm));
-        RRA_TRY(launch_swiglu_reduce(M->part, pg.split, (size_t)m * 2 * I, M->act, m, I,
-                                     image_for(M, L.wd, m), s));
         const GemvPlan &pd = M->plan_d[m];
-        RRA_TRY(launch_gemv(L.wd, pd, gemv_input(M, L.wd, M->act), m, M->part, (size_t)m * H, s));
+        const bool pro_d = gemv_takes_prologue(L.wd, pd, m);
+        if (!pro_d)
+            RRA_TRY(launch_swiglu_reduce(M->part, pg.split, (size_t)m * 2 * I, M->act, m, I,
+                                         image_for(M, L.wd, m), s));
+        const GemvPrologue ps{kProSwiglu, M->part, nullptr, nullptr, (long long)m * 2 * I, pg.split,
+                              I, 0, 0};
+        RRA_TRY(launch_gemv(L.wd, pd, gemv_input(M, L.wd, M->act), m, M->part_d, (size_t)m * H, s,
+                            nullptr, pro_d ? &ps : nullptr));
         const bool last = l + 1 == d.n_layers;
         const float *next_gamma = last ? d.out_gamma : M->layers[l + 1].attn_gamma;
         const rra_weight &next_w = last ? d.lm_head : M->layers[l + 1].wqkv;
-        RRA_TRY(launch_residual_ss(M->part, pd.split, (size_t)m * H, x, M->ss, next_gamma, M->xg,
+        RRA_TRY(launch_residual_ss(M->part_d, pd.split, (size_t)m * H, x, M->ss, next_gamma, M->xg,
                                    m, H, image_for(M, next_w, m), s));
     }
     if (flags & kStepNoHead) return RRA_OK;
@@ -428,6 +444,7 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     M->xg = reinterpret_cast<float *>(b + L.xg);
     M->img = reinterpret_cast<uint8_t *>(b + L.img);
     M->part = reinterpret_cast<float *>(b + L.part);
+    M->part_d = reinterpret_cast<float *>(b + L.part_d);
     M->q = reinterpret_cast<float *>(b + L.q);
     M->lens = reinterpret_cast<uint32_t *>(b + L.lens);
     M->attn = reinterpret_cast<float *>(b + L.attn);

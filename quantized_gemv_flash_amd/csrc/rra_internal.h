@@ -75,12 +75,32 @@ struct NormIn {
     int nparts;
     float eps;
 };
+// A quantised GEMV's input formed inside the GEMV (small batches, short
+// splits): instead of copying a finished activation image, each workgroup
+// builds the image of its own K range from the producing step's partial
+// results, with the same arithmetic as the kernel that would otherwise write
+// the image (epilogue.h), so the result is bit-identical either way.
+enum GemvPrologueKind { kProNone = 0, kProSwiglu = 1, kProAttn = 2 };
+struct GemvPrologue {
+    int kind;                 // GemvPrologueKind
+    const float *part;        // SwiGLU: gate/up split partials [split][m][2 n]; attention: part_o
+    const float *lse;         // attention: part_lse
+    const uint32_t *seq_len;  // attention: per-sequence lengths (clamped to max_len)
+    long long stride;         // SwiGLU: floats between split planes
+    int split;                // SwiGLU: split planes
+    int n;                    // SwiGLU: intermediate size; attention: query heads
+    int nc_max, max_len;      // attention
+};
+// Whether a GEMV of this plan can take a prologue (short splits, m <= 4).
+bool gemv_takes_prologue(const rra_weight &w, const GemvPlan &p, int m);
+
 // Enqueues the GEMV; the result (or its K-split partial sums) goes to
 // out[split][m][n] with out_split_stride floats between splits.  For quantised
 // weights `x` is the activation image (frag.h) with frag_ct(m) column tiles;
 // for F32 weights it is fp32 [m][k].
 rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, int m, float *out,
-                       size_t out_split_stride, hipStream_t s, const NormIn *nrm = nullptr);
+                       size_t out_split_stride, hipStream_t s, const NormIn *nrm = nullptr,
+                       const GemvPrologue *pro = nullptr);
 // Converts fp32 x [m][k] into the activation image of a quantised GEMV.
 rra_status launch_x_to_image(const float *x, uint8_t *img, int fmt, int m, int k, hipStream_t s);
 // y[i][r] = sum over `split` partial planes (+ y[i][r] if accumulate).
@@ -103,10 +123,17 @@ rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_
                              float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
                              int max_len, hipStream_t s);
 // Row i of q attends to cache slot slot_seq[i] (slot i when slot_seq is null).
+// reduce = false launches the split kernel only (the O GEMV then combines the
+// partials in its prologue).
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
-                               const FragOut *fo = nullptr, const uint32_t *slot_seq = nullptr);
+                               const FragOut *fo = nullptr, const uint32_t *slot_seq = nullptr,
+                               bool reduce = true);
+// Where rra_flash_decode's partials live in `part` (m sequences, nq heads).
+inline const float *fd_part_lse(const float *part, int m, int nq, int hd, int nc_max) {
+    return part + (size_t)m * nq * nc_max * hd;
+}
 
 // ------------------------------------------------------------------ elementwise
 rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m, int h,

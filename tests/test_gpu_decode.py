@@ -86,15 +86,17 @@ SMALL_DECODERS = [synth.TINY_LLAMA_F32,
                   synth.SMALL_LLAMA_FP8]
 
 
+@pytest.mark.parametrize("m", [3, 6])
 @pytest.mark.parametrize("S", SMALL_DECODERS, ids=lambda S: S.name)
-def test_batched_equals_separate_bitwise(S):
+def test_batched_equals_separate_bitwise(S, m):
     # M-batched == M separate M=1 runs, bit for bit, in every weight format.
+    # At m <= 4 the O and down GEMVs form their inputs in a prologue; m = 6
+    # takes the separate epilogue kernels against M=1's prologues.
     W = synth.decoder_weights(S, seed=3, device=DEV, gamma="random")
-    m = 3
     both = Run(S, W, m, 16)
     ones = [Run(S, W, 1, 16) for _ in range(m)]
     toks = synth.first_tokens(S, m, seed=3).tolist()
-    starts = [0, 2, 5]
+    starts = [0, 2, 5, 1, 3, 4][:m]
     for step in range(6):
         pos = [s + step for s in starts]
         ids_b, hid_b, lg_b = both.step(toks, pos)
