@@ -11,8 +11,10 @@ A step is one decode token for all 32 sequences; tok/s = M * steps / time.
 Also reported: the M = 1 line (Qwen2.5-0.5B-shaped Q8 decoder after a
 512-token teacher-forced context, 256 greedy steps), the HBM roofline of the
 dominant kernel (split-K flash decoding, timed alone with HIP events on the
-stream it runs on), the FP8 block format on the GEMV at the LM-head shape, and
-the CPU oracle's speed on a bounded sample.
+stream it runs on), the FP8 and Q6K block formats on the GEMV at the LM-head
+shape, prompt ingestion, an M sweep of the 1.5B-shaped decoder, the standalone
+attention workload at every split size, a practical HBM ceiling, and the CPU
+oracle's speed on a bounded sample.
 
 Prints one JSON line.
 """
@@ -38,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fd-reps", type=int, default=20)
     ap.add_argument("--only-m1", action="store_true", help="run only the M=1 line")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="run only the standalone flash-decode line and the HBM ceiling")
     ap.add_argument("--m1-steps", type=int, default=256)
     ap.add_argument("--m1-ctx", type=int, default=512, help="context tokens of the M=1 line")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 1.5B-shaped M sweep")
@@ -126,6 +130,72 @@ def flash_decode_roofline(S, dd, lens, reps):
     sec = ev0.elapsed_time(ev1) / 1e3 / reps
     kv_bytes = sum(2 * nkv * L * hd * 4 for L in lens)  # K and V rows read once
     return sec, kv_bytes, chunk
+
+
+def flash_decode_line(reps=20):
+    """The standalone attention workload (32 sequences, 32 Q / 8 KV heads, hd
+    128, lengths uniform in [1, 8192], an 8192-row cache): rra_flash_decode at
+    each fixed chunk size and at the library's own choice, timed with HIP
+    events, against the K+V bytes read once."""
+    import synth
+    import quantized_gemv_flash_amd as rra
+    a = synth.FLASH_DECODE_M32
+    q, kc, vc, _, _, lens = synth.attention_inputs(a, seed=0, device="cuda")
+    L = lens.tolist()
+    seq = lens.to(device="cuda", dtype=torch.int32)
+    out = torch.empty_like(q)
+    kv_bytes = sum(2 * a.n_kv_heads * l * a.head_dim * 4 for l in L)
+    res = dict(workload=f"{a.name}: M={a.m}, {a.n_heads}/{a.n_kv_heads} heads, hd {a.head_dim}, "
+                        f"lengths U[1,{a.max_len}], max_len {a.max_len}",
+               algorithmic_bytes=kv_bytes, chunks={})
+    for chunk in list(a.chunks) + [0]:
+        ws = torch.empty(rra.rra_flash_decode_workspace_bytes(a.m, a.n_heads, a.n_kv_heads,
+                                                              a.head_dim, a.max_len, chunk),
+                         dtype=torch.uint8, device="cuda")
+        args = (q, kc, vc, seq, out, a.m, a.n_heads, a.n_kv_heads, a.head_dim, a.max_len, chunk, ws)
+        for _ in range(3):
+            rra.rra_flash_decode(*args)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            rra.rra_flash_decode(*args)
+        ev1.record()
+        torch.cuda.synchronize()
+        sec = ev0.elapsed_time(ev1) / 1e3 / reps
+        used = chunk or rra.rra_flash_decode_chunk(a.m, a.n_kv_heads, a.max_len, 0)
+        key = str(chunk) if chunk else f"auto ({used})"
+        res["chunks"][key] = dict(us=sec * 1e6, gbs=kv_bytes / sec / 1e9,
+                                  hbm_frac=kv_bytes / sec / 1e9 / HBM_PEAK_GBS)
+        del ws
+    del q, kc, vc, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def hbm_ceiling_line(nbytes=1 << 32, reps=10):
+    """Practical HBM ceilings on the same GPU, with PyTorch's own kernels: a
+    device-to-device copy (read + write counted) and a full reduction (read)."""
+    src = torch.empty(nbytes // 4, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("sum", lambda: src.sum(), nbytes)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        sec = ev0.elapsed_time(ev1) / 1e3 / reps
+        res[f"{name}_gbs"] = moved / sec / 1e9
+    res["bytes"] = nbytes
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
 
 
 def fd_only(S, steps, reps):
@@ -333,6 +403,10 @@ def main():
     if args.only_m1:
         print(json.dumps({"m1": m1_line(args.m1_steps, args.m1_ctx)}), flush=True)
         return
+    if args.only_attention:
+        print(json.dumps({"flash_decode": flash_decode_line(), "hbm_ceiling": hbm_ceiling_line()}),
+              flush=True)
+        return
     if args.fd_only:
         print(json.dumps({"fd_only": fd_only(synth.LLAMA3_8B_Q4, args.steps, args.fd_reps)}),
               flush=True)
@@ -382,6 +456,10 @@ def main():
     log(f"q6k gemv {q6k}")
     sweep = None if (args.no_sweep or args.main_only) else m_sweep_line()
     log(f"m sweep {sweep}")
+    fd_c = None if args.main_only else flash_decode_line()
+    log(f"flash decode chunks {fd_c}")
+    ceil = None if args.main_only else hbm_ceiling_line()
+    log(f"hbm ceiling {ceil}")
 
     out = {
         "metric": "decode tok/s at M=1 and M=32; weight+KV stream HBM GB/s as % of peak",
@@ -418,6 +496,8 @@ def main():
         "q6k_gemv": q6k,
         "prefill": prefill and dict(workload=f"{S.name}: 512 prompt tokens into one slot", **prefill),
         "m_sweep": sweep,
+        "flash_decode": fd_c,
+        "hbm_ceiling": ceil,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

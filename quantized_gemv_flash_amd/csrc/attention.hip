@@ -55,14 +55,22 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict
 //   part_o[((m*nq + h)*nc_max + c)*HD + d] = sum_t p_t v_t[d] / l,
 //   part_lse[(m*nq + h)*nc_max + c]      = max_t s_t + ln l,
 // with s_t = <q_h, k_t>/sqrt(HD), p_t = e^(s_t - max), l = sum_t p_t.
+//
+// A workgroup serves G query heads of KV head g = blockIdx.y / hs: the KV
+// head's nq/nkv = G hs query heads are dealt to hs workgroups.  hs = 1 reads
+// every KV byte once (bandwidth-bound grids); hs > 1 shortens each
+// workgroup's work where the grid is small and latency-bound (the other
+// workgroups' K/V reads are cache hits).  A head's arithmetic is the same
+// whatever G and hs are.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
     const uint32_t *__restrict__ seq_len, const uint32_t *__restrict__ slot_seq,
     float *__restrict__ part_o, float *__restrict__ part_lse, int nq, int nkv, int max_len,
-    int chunk, int nc_max) {
+    int chunk, int nc_max, int hs) {
     constexpr int GP = (G + 3) & ~3;  // probabilities stored key-major, G padded to 4
-    const int c = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
+    const int c = blockIdx.x, g = blockIdx.y / hs, m = blockIdx.z;
+    const int hq0 = blockIdx.y * G;  // first query head: g G hs + (blockIdx.y mod hs) G
     const int L = (int)min(seq_len[m], (uint32_t)max_len);
     if (c >= L) return;
     // Rows c, c + nc_max, c + 2 nc_max, ... < L (local row i is cache row
@@ -75,7 +83,8 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float *red = smem + GP * chunk;   // [4 waves][G][HD]
     float *stat = red + 4 * G * HD;   // [G] max, [G] sum
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t cs = slot_seq ? slot_seq[m] : (uint32_t)m;  // cache slot of query row m
     const size_t row0 = (cs * nkv + g) * max_len + c;
     const size_t rs = (size_t)nc_max * HD;  // floats between consecutive local rows
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float4 qr[G][F4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float *qh = q + ((size_t)m * nq + g * G + h) * HD;
+        const float *qh = q + ((size_t)m * nq + hq0 + h) * HD;
 #pragma unroll
         for (int i = 0; i < F4; ++i) {
             float4 v = *reinterpret_cast<const float4 *>(qh + 4 * (e + 8 * i));
@@ -103,6 +112,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             tt[u] = base + u * 32 + wave * 8 + ks;
+            if (base + u * 32 + wave * 8 >= n) break;  // wave-uniform: no rows left
             const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
 #pragma unroll
             for (int i = 0; i < F4; ++i)
@@ -110,6 +120,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
         }
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
+            if (base + u * 32 + wave * 8 >= n) break;
             float s[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -225,10 +236,10 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
         const int h = idx / HD, d = idx - h * HD;
         const float v = red[(0 * G + h) * HD + d] + red[(1 * G + h) * HD + d] +
                         red[(2 * G + h) * HD + d] + red[(3 * G + h) * HD + d];
-        part_o[(((size_t)m * nq + g * G + h) * nc_max + c) * HD + d] = v / stat[G + h];
+        part_o[(((size_t)m * nq + hq0 + h) * nc_max + c) * HD + d] = v / stat[G + h];
     }
     if (tid < G)
-        part_lse[((size_t)m * nq + g * G + tid) * nc_max + c] = stat[tid] + logf(stat[G + tid]);
+        part_lse[((size_t)m * nq + hq0 + tid) * nc_max + c] = stat[tid] + logf(stat[G + tid]);
 }
 
 // out[m][h] = sum_c w_c o~_c / sum_c w_c, w_c = e^(lse_c - max lse), over the
@@ -272,28 +283,43 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
 template <int HD, int G>
 rra_status launch_chunk(const float *q, const float *kc, const float *vc, const uint32_t *lens,
                         const uint32_t *slot_seq, float *po, float *pl, int m, int nq, int nkv,
-                        int max_len, int chunk, int nc_max, hipStream_t s) {
+                        int max_len, int chunk, int nc_max, int hs, hipStream_t s) {
     constexpr int GP = (G + 3) & ~3;
     const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * G);
-    hipLaunchKernelGGL((fd_chunk_kernel<HD, G>), dim3(nc_max, nkv, m), dim3(256), shm, s, q, kc,
-                       vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max);
+    hipLaunchKernelGGL((fd_chunk_kernel<HD, G>), dim3(nc_max, nkv * hs, m), dim3(256), shm, s, q,
+                       kc, vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs);
     return check_launch("fd_chunk_kernel");
 }
 
+// Workgroups per KV head's query-head group: 1 while the grid has at least
+// 256 workgroups (one per compute unit); below that (short caches at small
+// batch, latency-bound) the largest divisor of the group size that keeps the
+// grid within 1024 workgroups.
+int fd_head_split(int group, int m, int nkv, int nc_max) {
+    const int64_t base = (int64_t)nc_max * nkv * m;
+    if (base >= 256) return 1;
+    int hs = 1;
+    for (int d = 2; d <= group; ++d)
+        if (group % d == 0 && base * d <= 1024) hs = d;
+    return hs;
+}
+
 template <int HD>
-rra_status launch_chunk_hd(int G, const float *q, const float *kc, const float *vc,
+rra_status launch_chunk_hd(int group, const float *q, const float *kc, const float *vc,
                            const uint32_t *lens, const uint32_t *slot_seq, float *po, float *pl,
                            int m, int nq, int nkv, int max_len, int chunk, int nc_max,
                            hipStream_t s) {
-    switch (G) {
+    if (group < 1 || group > 8) return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", group);
+    const int hs = fd_head_split(group, m, nkv, nc_max);
+    switch (group / hs) {
 #define RRA_G(gv) \
-    case gv:                                                                               \
+    case gv:                                                                                    \
         return launch_chunk<HD, gv>(q, kc, vc, lens, slot_seq, po, pl, m, nq, nkv, max_len, chunk, \
-                                    nc_max, s);
+                                    nc_max, hs, s);
         RRA_G(1) RRA_G(2) RRA_G(3) RRA_G(4) RRA_G(5) RRA_G(6) RRA_G(7) RRA_G(8)
 #undef RRA_G
-        default: return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", G);
     }
+    return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", group);
 }
 
 }  // namespace

@@ -172,6 +172,24 @@ def test_flash_decode_zero_length_leaves_output():
     assert_close(out[1], oracle.attention(host(q)[1], host(kc)[1], host(vc)[1], 5))
 
 
+@pytest.mark.parametrize("hd,nq,nkv", [(64, 14, 2), (128, 32, 8), (128, 12, 2)])
+def test_flash_decode_head_split_is_bitwise_neutral(hd, nq, nkv):
+    # With a fixed chunk, one sequence alone runs on a small grid, where each
+    # KV head's query heads are dealt to several workgroups; in a batch of 24
+    # the grid is large and one workgroup serves the whole group.  Every head's
+    # arithmetic is the same either way: the outputs must be equal bitwise.
+    m, max_len, chunk = 24, 512, 32
+    banner("fd head split", hd, nq, nkv)
+    a = synth.Attention("t", m, nq, nkv, hd, max_len, 1, max_len, ())
+    q, kc, vc, _, _, lens = synth.attention_inputs(a, seed=7, device=DEV)
+    L = lens.tolist()
+    both = _fd_run(q, kc, vc, L, m, nq, nkv, hd, max_len, chunk)
+    for s in (0, 5, m - 1):
+        one = _fd_run(q[s:s + 1].contiguous(), kc[s:s + 1].contiguous(), vc[s:s + 1].contiguous(),
+                      L[s:s + 1], 1, nq, nkv, hd, max_len, chunk)
+        assert torch.equal(one[0], both[s]), f"seq {s} L={L[s]}"
+
+
 def test_flash_decode_full_size_every_chunk():
     # 32 sequences, 32 Q / 8 KV heads, hd 128, lengths uniform in [1, 8192],
     # cache 8192 rows; the new row is scattered at L-1 first.  Each split-K
