@@ -42,17 +42,6 @@ __device__ __forceinline__ void sum_splits2(const float *__restrict__ p, const f
     }
 }
 
-__device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-__device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-
 // Sum over a 256-thread block; every thread gets the result.
 __device__ __forceinline__ float block_sum(float v, float *sh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -88,7 +77,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x,
 // (NormIn).
 __global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restrict__ part, int split,
                                                           long long split_stride,
-                                                          float *__restrict__ x,
+                                                          const float *x_in, float *x,
                                                           float *__restrict__ ss,
                                                           const float *__restrict__ gamma,
                                                           float *__restrict__ xg, int h,
@@ -104,20 +93,11 @@ __global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restric
     float sq = 0.f;
     if (threadIdx.x < 64) {
         if (k0 < h) {
-            float v[8];
-            load8(x + base, v);
-            if (split > 0) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] += acc[0][e];
-                store8(x + base, v);
-            }
-            float gv[8];
-            load8(gamma + k0, gv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sq = fmaf(v[e], v[e], sq);
-                gv[e] *= v[e];
-            }
+            float v[8], gm[8], gv[8];
+            load8(x_in + base, v);
+            load8(gamma + k0, gm);
+            resid8(v, acc[0], split > 0, gm, gv, sq);
+            if (split > 0 || x_in != x) store8(x + base, v);
             store8(xg + base, gv);
             if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, gv);
         } else if (fo.img && k0 < fo.kpad) {
@@ -207,7 +187,7 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float *__restr
     if (k0 < inter) {
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = silu(acc[0][e]) * acc[1][e];
+        for (int e = 0; e < 8; ++e) v[e] = swiglu1(acc[0][e], acc[1][e]);
         store8(act + (size_t)m * inter + k0, v);
         if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, v);
     } else if (fo.img && k0 < fo.kpad) {
@@ -309,11 +289,11 @@ rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m,
     return check_launch("rmsnorm_kernel");
 }
 
-rra_status launch_residual_ss(const float *part, int split, size_t split_stride, float *x,
-                              float *ss, const float *gamma, float *xg, int m, int h,
+rra_status launch_residual_ss(const float *part, int split, size_t split_stride, const float *x_in,
+                              float *x, float *ss, const float *gamma, float *xg, int m, int h,
                               const FragOut &fo, hipStream_t s) {
     hipLaunchKernelGGL(residual_ss_kernel, dim3((unsigned)ss_parts(h), m), dim3(256), 0, s, part,
-                       split, (long long)split_stride, x, ss, gamma, xg, h, fo);
+                       split, (long long)split_stride, x_in ? x_in : x, x, ss, gamma, xg, h, fo);
     return check_launch("residual_ss_kernel");
 }
 

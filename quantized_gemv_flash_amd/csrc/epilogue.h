@@ -22,6 +22,37 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(g) u, rounded to fp32 (never fused into a consumer's add)
+__device__ __forceinline__ float swiglu1(float g, float u) {
+#pragma clang fp contract(off)
+    return silu(g) * u;
+}
+
+__device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// One lane's 8 columns of the residual step: v = x + acc (acc the split sum
+// of the block's output, when add), sq += v^2 in column order, gv = gamma v.
+__device__ __forceinline__ void resid8(float (&v)[8], const float (&acc)[8], bool add,
+                                       const float (&gamma)[8], float (&gv)[8], float &sq) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (add) v[e] += acc[e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        sq = fmaf(v[e], v[e], sq);
+        gv[e] = gamma[e] * v[e];
+    }
+}
 
 // Split sum of NV 8-column vectors (p[v] .. p[v] + 8) shared by the four
 // waves of a 256-thread block: lane g of every wave works on the same group,

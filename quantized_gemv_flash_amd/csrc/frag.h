@@ -41,8 +41,12 @@ __device__ __forceinline__ int frag_slot(int j, int r, int b) {
 }
 
 // Splits 8 consecutive fp32 activations (k order) into hi/lo fp16 operands.
+// Contraction is off: the producer's product (gamma x, silu(g) u, ...) must
+// be rounded to fp32 before the subtraction, whichever kernel inlines this,
+// so that every producer of an image writes the same bits.
 template <int FMT>
 __device__ __forceinline__ void split8(const float (&v)[8], half8_t &hi, half8_t &lo) {
+#pragma clang fp contract(off)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int src = (FMT == RRA_Q4) ? (e >> 1) + 4 * (e & 1) : e;

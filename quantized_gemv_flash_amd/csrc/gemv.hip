@@ -629,7 +629,7 @@ __device__ __forceinline__ void prologue_swiglu(const GemvPrologue &pro, int M, 
         if (threadIdx.x < 64 && valid) {
             float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = k0 < inter ? silu(acc[0][e]) * acc[1][e] : 0.f;
+            for (int e = 0; e < 8; ++e) v[e] = k0 < inter ? swiglu1(acc[0][e], acc[1][e]) : 0.f;
             write_frag8_tile<IMG>(xs[t], 1, m, 8 * kk, v);
         }
         __syncthreads();  // `red` is reused by the next pass
@@ -676,6 +676,78 @@ __device__ __forceinline__ void prologue_attn(const GemvPrologue &pro, int M, in
     }
 }
 
+// The residual step for rows m < M (residual_ss_kernel's work, with its
+// thread mapping and order of operations): for each (row, 512-column chunk)
+// pair, lane g of the four waves holds columns chunk*512 + 8g .. + 7, the
+// waves share the split sum (group_split_sum), and wave 0 forms
+// x_out = x_in + sum, the chunk's sum of squares (a wave sum, as the block sum
+// of the separate kernel: the other waves add zeros) and x_out * gamma, whose
+// columns in this split's K tiles go to the image.  tsum[m] = the sum over
+// the row's chunks, in chunk order.  parts: M * ceil(n/512) floats.
+template <int IMG, int KT, int XB>
+__device__ __forceinline__ void prologue_resid(const GemvPrologue &pro, int M, int kt_begin,
+                                               int nch, uint8_t (*xs)[XB], float *red,
+                                               float *parts, float *tsum) {
+    const int H = pro.n, np = ss_parts(H), pairs = M * np;
+    const int lane = threadIdx.x & 63;
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+    const int k_lo = kt_begin * KT, k_hi = (kt_begin + nch) * KT;
+    for (int p0 = 0; p0 < pairs; p0 += 2) {
+        int k0[2];
+        size_t base[2];
+        const float *pp[2];
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int pidx = min(p0 + v, pairs - 1), m = pidx / np, ch = pidx % np;
+            k0[v] = ch * 512 + lane * 8;
+            base[v] = (size_t)m * H + (k0[v] < H ? k0[v] : 0);  // clamped: never used
+            pp[v] = pro.part + base[v];
+        }
+        float xv[2][8], gm[2][8];
+        if (threadIdx.x < 64) {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                load8(pro.x_in + base[v], xv[v]);
+                load8(pro.gamma + (k0[v] < H ? k0[v] : 0), gm[v]);
+            }
+        }
+        float acc[2][8];
+        group_split_sum<2>(pp, true, pro.split, pro.stride, acc, red);
+        if (threadIdx.x < 64) {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int pidx = p0 + v;
+                if (pidx >= pairs) break;
+                const int m = pidx / np;
+                float sq = 0.f;
+                if (k0[v] < H) {
+                    float gv[8];
+                    resid8(xv[v], acc[v], true, gm[v], gv, sq);
+                    if (writer) store8(pro.x_out + base[v], xv[v]);
+                    if (k0[v] >= k_lo && k0[v] < k_hi)
+                        write_frag8_tile<IMG>(xs[k0[v] / KT - kt_begin], 1, m, k0[v] % KT, gv);
+                }
+                sq = wave_sum(sq);
+                if (lane == 0) parts[pidx] = 0.f + sq;
+            }
+        }
+        __syncthreads();  // `red` is reused by the next pass; parts complete
+    }
+    if ((int)threadIdx.x < M) {
+        float t = 0.f;
+        for (int c = 0; c < np; ++c) t += parts[threadIdx.x * np + c];
+        tsum[threadIdx.x] = t;
+    }
+    // zeros for the groups in [H, kpad)
+    for (int gidx = threadIdx.x; gidx < M * nch * (KT / 8); gidx += blockDim.x) {
+        const int kk = gidx % (KT / 8), t = (gidx / (KT / 8)) % nch, m = gidx / (nch * (KT / 8));
+        if ((kt_begin + t) * KT + 8 * kk >= H) {
+            const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            write_frag8_tile<IMG>(xs[t], 1, m, 8 * kk, z);
+        }
+    }
+}
+
 template <int FMT, int CT, int RPW, int NW, int NT, int PRO = 0>
 __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__restrict__ wt,
                                                                const uint8_t *__restrict__ ximg,
@@ -688,7 +760,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__
     static_assert(PRO == 0 || (CT == 1 && NW == 4), "prologues build one column tile, 4 waves");
     __shared__ __attribute__((aligned(16))) uint8_t xs[NT][G::XB];
     __shared__ __attribute__((aligned(16))) uint8_t sl[NT][G::SCB];
-    constexpr int RED = PRO == kProSwiglu ? 3 * 64 * 16 : PRO >= kProAttn ? 4 * 128 : 1;
+    constexpr int RED = PRO == kProSwiglu ? 3 * 64 * 16
+                        : PRO == kProResid ? 3 * 64 * 16 + 4 * 8 + 4
+                        : PRO >= kProAttn  ? 4 * 128
+                                           : 1;
     __shared__ float red[RED];
 
     G p;
@@ -722,10 +797,21 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__
         prologue_attn<TileFmt<FMT>::IMG, TileFmt<FMT>::KT, G::XB, 64>(pro, M, p.kt_begin, nch, xs, red);
     else if constexpr (PRO == kProAttn + 1)
         prologue_attn<TileFmt<FMT>::IMG, TileFmt<FMT>::KT, G::XB, 128>(pro, M, p.kt_begin, nch, xs, red);
+    else if constexpr (PRO == kProResid)
+        prologue_resid<TileFmt<FMT>::IMG, TileFmt<FMT>::KT, G::XB>(pro, M, p.kt_begin, nch, xs, red,
+                                                                   red + 3 * 64 * 16,
+                                                                   red + 3 * 64 * 16 + 4 * 8);
     wait_vm<NT * RPW * G::WL>();  // every DMA landed; weight loads may be in flight
     lds_barrier();
     float sq[CT];
     p.sum_ss(nrm, sv, sq);
+    if constexpr (PRO == kProResid) {
+        // the norm from the prologue's sums (one total per row, no more parts)
+        const float *tsum = red + 3 * 64 * 16 + 4 * 8;
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) sq[cc] = tsum[min(16 * cc + (p.lane & 15), M - 1)];
+        nrm = NormIn{tsum, 1, pro.eps};
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         if (t < nch) p.compute(q[t], xs[t], sl[t], acc);
@@ -1006,6 +1092,8 @@ rra_status launch_short(const rra_weight &w, const GemvPlan &p, const uint8_t *i
             RRA_SHORT(kProAttn);
         else if (pro.kind == kProAttn && hd == 128)
             RRA_SHORT(kProAttn + 1);
+        else if (pro.kind == kProResid)
+            RRA_SHORT(kProResid);
         else if (pro.kind != kProNone)
             return fail(RRA_EINVAL, "gemv prologue: unsupported kind %d (hd %d)", pro.kind, hd);
         else
@@ -1080,6 +1168,13 @@ GemvPlan gemv_plan(const rra_weight &w, int m) {
 
 bool gemv_takes_prologue(const rra_weight &w, const GemvPlan &p, int m) {
     return is_quantised(w.fmt) && m <= 4 && p.kt_per_split <= 4;
+}
+
+bool gemv_takes_resid_prologue(const rra_weight &w, const GemvPlan &p, int m, int planes) {
+    // every workgroup reads planes x m x K floats: at most 64 (row, chunk,
+    // plane) triples of 512 columns, about two memory round trips
+    return gemv_takes_prologue(w, p, m) && m * ss_parts((int)w.k) <= 32 &&
+           (int64_t)planes * m * ss_parts((int)w.k) <= 64;
 }
 
 rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, int m, float *out,

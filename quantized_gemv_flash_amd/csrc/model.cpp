@@ -183,7 +183,9 @@ struct rra_model {
     int chunk[RRA_M_MAX + 1] = {};  // flash-decode rows per split, per batch size
     // workspace carve-up
     float *ss = nullptr, *xg = nullptr, *part = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr;
-    float *part_d = nullptr;  // the down GEMV's partials (its prologue may read `part`)
+    float *part_d = nullptr;  // the O and down GEMVs' partials (the next GEMV's prologue may read
+                              // them while writing `part`)
+    float *xalt = nullptr;    // the residual stream's second buffer (residual prologues)
     float *fd = nullptr, *logits = nullptr, *rope = nullptr;
     uint32_t *lens = nullptr, *err = nullptr;
     void *argmax_ws = nullptr;
@@ -205,7 +207,7 @@ namespace {
 
 struct Layout {
     size_t ss, xg, img, part, part_d, q, lens, attn, act, fd, logits, argmax, rope, err, px, pidx,
-        total;
+        xalt, total;
 };
 
 // Rows of one prefill chunk, and the batch rows the workspace is laid out for.
@@ -279,6 +281,7 @@ Layout layout_of(const rra_model_desc &d) {
     L.err = take(256);
     L.px = take(4 * M * d.hidden);
     L.pidx = take(3 * 4 * M);
+    L.xalt = take(4 * M * d.hidden);
     L.total = off;
     return L;
 }
@@ -365,14 +368,32 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
     // squares of x; the first ones come from the step input.  Each producer
     // also writes the next GEMV's activation image.
     const rra_layer_desc &L0 = M->layers[0];
-    RRA_TRY(launch_residual_ss(nullptr, 0, 0, x, M->ss, L0.attn_gamma, M->xg, m, H,
+    RRA_TRY(launch_residual_ss(nullptr, 0, 0, x, x, M->ss, L0.attn_gamma, M->xg, m, H,
                                image_for(M, L0.wqkv, m), s));
+    // The residual stream lives in x or in M->xalt.  At small m an
+    // RMSNorm-fused GEMV can do the residual step itself (kProResid): it reads
+    // the stream and the previous GEMV's partials and one of its workgroups
+    // writes the new stream to the other buffer.  The last residual step
+    // always writes x.
+    float *xc = x;
+    auto other = [&](const float *p) { return p == x ? M->xalt : x; };
+    auto resid_pro = [&](const float *planes, int split, const float *gamma) {
+        GemvPrologue r{kProResid, planes, nullptr, nullptr, (long long)m * H, split, H, 0, 0};
+        r.x_in = xc;
+        r.x_out = other(xc);
+        r.gamma = gamma;
+        r.eps = d.rms_eps;
+        xc = r.x_out;
+        return r;
+    };
+    GemvPrologue pr_qkv{kProNone, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
     for (int l = 0; l < d.n_layers; ++l) {
         const rra_layer_desc &L = M->layers[l];
         // attention block
         const GemvPlan &pq = M->plan_qkv[m];
+        const bool rq = pr_qkv.kind == kProResid;
         RRA_TRY(launch_gemv(L.wqkv, pq, gemv_input(M, L.wqkv, M->xg), m, M->part, (size_t)m * nqkv,
-                            s, &nrm));
+                            s, rq ? nullptr : &nrm, rq ? &pr_qkv : nullptr));
         RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
                                 L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd, d.max_len,
                                 slot_seq, s));
@@ -387,14 +408,20 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
         const GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
                               0, 0, nq, nc_max, d.max_len};
-        RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part, (size_t)m * H, s,
+        RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part_d, (size_t)m * H, s,
                             nullptr, pro_o ? &pa : nullptr));
-        RRA_TRY(launch_residual_ss(M->part, po.split, (size_t)m * H, x, M->ss, L.ffn_gamma, M->xg, m,
-                                   H, image_for(M, L.wgu, m), s));
         // feed-forward block
         const GemvPlan &pg = M->plan_gu[m];
-        RRA_TRY(launch_gemv(L.wgu, pg, gemv_input(M, L.wgu, M->xg), m, M->part, (size_t)m * 2 * I, s,
-                            &nrm));
+        if (gemv_takes_resid_prologue(L.wgu, pg, m, po.split)) {
+            const GemvPrologue rg = resid_pro(M->part_d, po.split, L.ffn_gamma);
+            RRA_TRY(launch_gemv(L.wgu, pg, gemv_input(M, L.wgu, M->xg), m, M->part,
+                                (size_t)m * 2 * I, s, nullptr, &rg));
+        } else {
+            RRA_TRY(launch_residual_ss(M->part_d, po.split, (size_t)m * H, xc, xc, M->ss,
+                                       L.ffn_gamma, M->xg, m, H, image_for(M, L.wgu, m), s));
+            RRA_TRY(launch_gemv(L.wgu, pg, gemv_input(M, L.wgu, M->xg), m, M->part,
+                                (size_t)m * 2 * I, s, &nrm));
+        }
         const GemvPlan &pd = M->plan_d[m];
         const bool pro_d = gemv_takes_prologue(L.wd, pd, m);
         if (!pro_d)
@@ -405,10 +432,17 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         RRA_TRY(launch_gemv(L.wd, pd, gemv_input(M, L.wd, M->act), m, M->part_d, (size_t)m * H, s,
                             nullptr, pro_d ? &ps : nullptr));
         const bool last = l + 1 == d.n_layers;
-        const float *next_gamma = last ? d.out_gamma : M->layers[l + 1].attn_gamma;
-        const rra_weight &next_w = last ? d.lm_head : M->layers[l + 1].wqkv;
-        RRA_TRY(launch_residual_ss(M->part_d, pd.split, (size_t)m * H, x, M->ss, next_gamma, M->xg,
-                                   m, H, image_for(M, next_w, m), s));
+        pr_qkv.kind = kProNone;
+        if (!last && gemv_takes_resid_prologue(M->layers[l + 1].wqkv, pq, m, pd.split)) {
+            pr_qkv = resid_pro(M->part_d, pd.split, M->layers[l + 1].attn_gamma);
+        } else {
+            const float *next_gamma = last ? d.out_gamma : M->layers[l + 1].attn_gamma;
+            const rra_weight &next_w = last ? d.lm_head : M->layers[l + 1].wqkv;
+            float *x_out = last ? x : xc;
+            RRA_TRY(launch_residual_ss(M->part_d, pd.split, (size_t)m * H, xc, x_out, M->ss,
+                                       next_gamma, M->xg, m, H, image_for(M, next_w, m), s));
+            xc = x_out;
+        }
     }
     if (flags & kStepNoHead) return RRA_OK;
     RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits, 0, s,
@@ -455,6 +489,7 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     M->rope = reinterpret_cast<float *>(b + L.rope);
     M->err = reinterpret_cast<uint32_t *>(b + L.err);
     M->px = reinterpret_cast<float *>(b + L.px);
+    M->xalt = reinterpret_cast<float *>(b + L.xalt);
     M->rows = rows_of(*d);
     M->prefill_rows = prefill_rows_of(*d);
     M->ppos = reinterpret_cast<uint32_t *>(b + L.pidx);

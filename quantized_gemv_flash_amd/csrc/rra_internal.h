@@ -80,19 +80,32 @@ struct NormIn {
 // builds the image of its own K range from the producing step's partial
 // results, with the same arithmetic as the kernel that would otherwise write
 // the image (epilogue.h), so the result is bit-identical either way.
-enum GemvPrologueKind { kProNone = 0, kProSwiglu = 1, kProAttn = 2 };
+// kProResid: the residual step before an RMSNorm-fused GEMV (residual_ss):
+// x_out = x_in + sum of the previous GEMV's split planes, the sums of squares
+// of x_out (the norm is then applied from them, not from NormIn), and the
+// image of x_out * gamma; x_out is written by one workgroup and must not
+// alias x_in.
+enum GemvPrologueKind { kProNone = 0, kProSwiglu = 1, kProAttn = 2, kProResid = 4 };
 struct GemvPrologue {
     int kind;                 // GemvPrologueKind
-    const float *part;        // SwiGLU: gate/up split partials [split][m][2 n]; attention: part_o
+    const float *part;        // SwiGLU: gate/up split partials [split][m][2 n]; attention: part_o;
+                              // residual: the previous GEMV's partials [split][m][n]
     const float *lse;         // attention: part_lse
     const uint32_t *seq_len;  // attention: per-sequence lengths (clamped to max_len)
-    long long stride;         // SwiGLU: floats between split planes
-    int split;                // SwiGLU: split planes
-    int n;                    // SwiGLU: intermediate size; attention: query heads
+    long long stride;         // SwiGLU, residual: floats between split planes
+    int split;                // SwiGLU, residual: split planes
+    int n;                    // SwiGLU: intermediate size; attention: query heads; residual: hidden
     int nc_max, max_len;      // attention
+    const float *x_in = nullptr;   // residual
+    float *x_out = nullptr;        // residual
+    const float *gamma = nullptr;  // residual
+    float eps = 0.f;               // residual
 };
 // Whether a GEMV of this plan can take a prologue (short splits, m <= 4).
 bool gemv_takes_prologue(const rra_weight &w, const GemvPlan &p, int m);
+// Whether it can take the residual prologue: besides the above, few enough
+// split planes to read (each workgroup reads every plane of the whole rows).
+bool gemv_takes_resid_prologue(const rra_weight &w, const GemvPlan &p, int m, int planes);
 
 // Enqueues the GEMV; the result (or its K-split partial sums) goes to
 // out[split][m][n] with out_split_stride floats between splits.  For quantised
@@ -151,14 +164,15 @@ rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void 
 void rope_table_host(float *table, int max_len, int hd, double theta);
 
 // Fused epilogues used by the decode step.
-// x[i] += sum_s part[s][i] (split may be 0); per 512-column chunk c the sum
+// x[i] = x_in[i] + sum_s part[s][i] (x_in null: x itself; split may be 0);
+// per 512-column chunk c the sum
 // of squares of the updated row, ss[i * ss_parts(h) + c]; and xg = x * gamma,
 // the input of the next RMSNorm-fused GEMV (fp32, and its image if fo.img).
 // h % 8 == 0.
-rra_status launch_residual_ss(const float *part, int split, size_t split_stride, float *x,
-                              float *ss, const float *gamma, float *xg, int m, int h,
+rra_status launch_residual_ss(const float *part, int split, size_t split_stride, const float *x_in,
+                              float *x, float *ss, const float *gamma, float *xg, int m, int h,
                               const FragOut &fo, hipStream_t s);
-inline int ss_parts(int h) { return (int)cdiv(h, 512); }
+__host__ __device__ inline int ss_parts(int h) { return (h + 511) / 512; }
 // qkv = sum_s part[s]; rope(q, k) at pos; q -> q_out [m][nq][hd]; k, v rows
 // scattered into the caches at pos, in cache slot slot_seq[i] (slot i when
 // slot_seq is null); seq_len[i] = min(pos[i] + 1, max_len); pos >= max_len
