@@ -106,6 +106,27 @@ def fill_kv_context(S, dd, lengths, seed=0):
             del k, v
 
 
+def graph_time(fn, reps):
+    """Seconds per call of fn (enqueue-only, on the current stream), timed as
+    one replay of a HIP graph holding `reps` calls, so that the time is the
+    kernels' own and not the gaps between eager launches."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    del g
+    return ev0.elapsed_time(ev1) / 1e3 / reps
+
+
 def flash_decode_roofline(S, dd, lens, reps):
     """Times rra_flash_decode (split-K chunk kernel + its reduce) alone on
     layer 0's cache at the step's sequence lengths."""
@@ -119,15 +140,7 @@ def flash_decode_roofline(S, dd, lens, reps):
     ws = torch.empty(rra.rra_flash_decode_workspace_bytes(m, nq, nkv, hd, max_len, 0),
                      dtype=torch.uint8, device="cuda")
     args = (q, dd.k_caches[0], dd.v_caches[0], seq, out, m, nq, nkv, hd, max_len, 0, ws)
-    rra.rra_flash_decode(*args)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(reps):
-        rra.rra_flash_decode(*args)
-    ev1.record()
-    torch.cuda.synchronize()
-    sec = ev0.elapsed_time(ev1) / 1e3 / reps
+    sec = graph_time(lambda: rra.rra_flash_decode(*args), reps)
     kv_bytes = sum(2 * nkv * L * hd * 4 for L in lens)  # K and V rows read once
     return sec, kv_bytes, chunk
 
@@ -153,16 +166,7 @@ def flash_decode_line(reps=20):
                                                               a.head_dim, a.max_len, chunk),
                          dtype=torch.uint8, device="cuda")
         args = (q, kc, vc, seq, out, a.m, a.n_heads, a.n_kv_heads, a.head_dim, a.max_len, chunk, ws)
-        for _ in range(3):
-            rra.rra_flash_decode(*args)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(reps):
-            rra.rra_flash_decode(*args)
-        ev1.record()
-        torch.cuda.synchronize()
-        sec = ev0.elapsed_time(ev1) / 1e3 / reps
+        sec = graph_time(lambda: rra.rra_flash_decode(*args), reps)
         used = chunk or rra.rra_flash_decode_chunk(a.m, a.n_kv_heads, a.max_len, 0)
         key = str(chunk) if chunk else f"auto ({used})"
         res["chunks"][key] = dict(us=sec * 1e6, gbs=kv_bytes / sec / 1e9,
@@ -174,13 +178,15 @@ def flash_decode_line(reps=20):
 
 
 def hbm_ceiling_line(nbytes=1 << 32, reps=10):
-    """Practical HBM ceilings on the same GPU, with PyTorch's own kernels: a
-    device-to-device copy (read + write counted) and a full reduction (read)."""
+    """Practical HBM ceilings on the same GPU: the library's plain streaming
+    read (rra_hbm_read, 128-bit loads; the best of a few grid sizes) and, for
+    comparison, PyTorch's device-to-device copy (read + write counted)."""
+    import quantized_gemv_flash_amd as rra
     src = torch.empty(nbytes // 4, device="cuda").uniform_()
     dst = torch.empty_like(src)
-    res = {}
-    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
-                            ("sum", lambda: src.sum(), nbytes)):
+    sums = torch.empty(32768, device="cuda")
+
+    def timed(fn):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -190,10 +196,15 @@ def hbm_ceiling_line(nbytes=1 << 32, reps=10):
             fn()
         ev1.record()
         torch.cuda.synchronize()
-        sec = ev0.elapsed_time(ev1) / 1e3 / reps
-        res[f"{name}_gbs"] = moved / sec / 1e9
-    res["bytes"] = nbytes
-    del src, dst
+        return ev0.elapsed_time(ev1) / 1e3 / reps
+
+    by_grid = {b: nbytes / timed(lambda: rra.rra_hbm_read(src, sums, b)) / 1e9
+               for b in (2048, 8192, 16384, 32768)}
+    best = max(by_grid, key=by_grid.get)
+    res = dict(read_gbs=by_grid[best], read_hbm_frac=by_grid[best] / HBM_PEAK_GBS,
+               read_workgroups=best, read_gbs_by_workgroups=by_grid,
+               torch_copy_gbs=2 * nbytes / timed(lambda: dst.copy_(src)) / 1e9, bytes=nbytes)
+    del src, dst, sums
     torch.cuda.empty_cache()
     return res
 

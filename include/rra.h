@@ -217,6 +217,15 @@ rra_status rra_rope(float *z, const uint32_t *pos, const float *table, int32_t m
 rra_status rra_swiglu(const float *gate, const float *up, float *out, int32_t m, int32_t n,
                       hipStream_t s);
 
+/* Measurement aid, not a step of the decode path: a plain streaming read of
+ * `bytes` bytes at `buf` (device memory, 16-byte aligned, bytes a non-zero
+ * multiple of 16) by `blocks` 256-thread workgroups (1 .. 2^20) with 128-bit
+ * loads, the practical HBM ceiling that the kernels' rates are compared
+ * with.  sums: device fp32 [blocks], written with the sum of the fp32 values
+ * each workgroup read (the buffer is read as floats).  Asynchronous on s;
+ * argument errors return RRA_EINVAL without launching. */
+rra_status rra_hbm_read(const void *buf, size_t bytes, float *sums, int32_t blocks, hipStream_t s);
+
 /* Greedy argmax (a14; [reduces] gpu_argmax / batched_gpu_argmax: block-level
  * (max, index) pairs, then a final reduce, for all M rows with no host sync):
  * tok[i] = the lowest index among the maximal logits[i][*].  NaN logits are

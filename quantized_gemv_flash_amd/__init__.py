@@ -79,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "rra_swiglu": ([P, P, P, I, I, P], I),
         "rra_argmax_workspace_bytes": ([I, I], S),
         "rra_argmax": ([P, P, I, I, P, S, P], I),
+        "rra_hbm_read": ([P, S, P, I, P], I),
         "rra_model_workspace_bytes": ([POINTER(rra_model_desc)], S),
         "rra_model_create": ([POINTER(rra_model_desc), P, S, P, POINTER(c_void_p)], I),
         "rra_decode_step": ([P, P, P, P, P, P, I, I, P], I),
@@ -230,6 +231,16 @@ def rra_argmax_workspace_bytes(m, v) -> int:
 def rra_argmax(logits, tok, m, v, ws, stream=None):
     _check("rra_argmax", lib.rra_argmax(_p(logits), _p(tok), m, v, _p(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rra_hbm_read(buf, sums, blocks=None, stream=None):
+    """Streaming read of the whole of `buf` (a device tensor); sums: device
+    fp32 tensor of at least `blocks` elements (default: all of it)."""
+    blocks = sums.numel() if blocks is None else blocks
+    if sums.numel() < blocks:
+        raise RraError(f"rra_hbm_read: sums holds {sums.numel()} floats, needs {blocks}")
+    _check("rra_hbm_read", lib.rra_hbm_read(_p(buf), buf.numel() * buf.element_size(), _p(sums),
+                                            blocks, _stream(stream)))
 
 
 # ---------------------------------------------------------------- decode step

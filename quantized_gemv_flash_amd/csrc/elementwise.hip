@@ -281,6 +281,31 @@ __global__ __launch_bounds__(256) void argmax_pass2_kernel(const float *__restri
     }
 }
 
+// Plain streaming read of n4 16-byte words: grid-stride, eight independent
+// 128-bit loads in flight per thread; each block writes the fp32 sum of the
+// values it read (so the reads cannot be dropped, and the result is checkable).
+__global__ __launch_bounds__(256) void hbm_read_kernel(const float4 *__restrict__ p, size_t n4,
+                                                       float *__restrict__ sums) {
+    constexpr int U = 8;
+    __shared__ float sh[4];
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    float acc = 0.f;
+    for (; i + (U - 1) * stride < n4; i += U * stride) {
+        float4 a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc += (a[u].x + a[u].y) + (a[u].z + a[u].w);
+    }
+    for (; i < n4; i += stride) {
+        const float4 a = p[i];
+        acc += (a.x + a.y) + (a.z + a.w);
+    }
+    acc = block_sum(acc, sh);
+    if (threadIdx.x == 0) sums[blockIdx.x] = acc;
+}
+
 }  // namespace
 
 rra_status launch_rmsnorm(const float *x, const float *gamma, float *out, int m, int h, float eps,
@@ -378,6 +403,12 @@ void rope_table_host(float *table, int max_len, int hd, double theta) {
             table[((size_t)p * half + j) * 2] = (float)std::cos(ang);
             table[((size_t)p * half + j) * 2 + 1] = (float)std::sin(ang);
         }
+}
+
+rra_status launch_hbm_read(const void *buf, size_t bytes, float *sums, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL(hbm_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const float4 *>(buf), bytes / 16, sums);
+    return check_launch("hbm_read_kernel");
 }
 
 }  // namespace rra

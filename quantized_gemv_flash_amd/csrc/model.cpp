@@ -161,6 +161,18 @@ extern "C" rra_status rra_argmax(const float *logits, uint32_t *tok, int32_t m, 
     return launch_argmax(logits, tok, m, v, ws, nullptr, false, s);
 }
 
+extern "C" rra_status rra_hbm_read(const void *buf, size_t bytes, float *sums, int32_t blocks,
+                                   hipStream_t s) {
+    clear_error();
+    if (!buf || !sums) return fail(RRA_EINVAL, "rra_hbm_read: null argument");
+    if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+        return fail(RRA_EINVAL, "rra_hbm_read: %zu bytes at %p: need a non-zero multiple of 16, "
+                    "16-byte aligned", bytes, buf);
+    if (blocks < 1 || blocks > (1 << 20))
+        return fail(RRA_EINVAL, "rra_hbm_read: blocks=%d not in 1..2^20", blocks);
+    return launch_hbm_read(buf, bytes, sums, blocks, s);
+}
+
 // ---------------------------------------------------------------- model
 struct GraphKey {
     int32_t m, flags;

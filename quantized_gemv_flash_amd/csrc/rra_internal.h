@@ -188,6 +188,9 @@ rra_status launch_swiglu_reduce(const float *part, int split, size_t split_strid
 // pos[i] = base + i, slot_seq[i] = seq for i < n (one prefill chunk).
 rra_status launch_prefill_rows(uint32_t *pos, uint32_t *slot_seq, uint32_t base, uint32_t seq,
                                int n, hipStream_t s);
+// Streaming read of `bytes` (a multiple of 16) with `blocks` workgroups;
+// sums[b] = the fp32 sum of the values block b read.
+rra_status launch_hbm_read(const void *buf, size_t bytes, float *sums, int blocks, hipStream_t s);
 // x[i] = embed[tok[i]] for every slot whose pos is not RRA_POS_NONE.
 rra_status launch_embed_gather(const float *embed, const uint32_t *tok, const uint32_t *pos,
                                float *x, int m, int h, int vocab, hipStream_t s);

@@ -211,6 +211,29 @@ def test_flash_decode_full_size_every_chunk():
         assert_close(out, ref, what=f"fd full chunk={chunk}")
 
 
+# ---------------------------------------------------------------- HBM read probe
+@pytest.mark.parametrize("n,blocks", [(4, 1), (1000, 3), (1 << 20, 37), ((1 << 20) + 12, 256)])
+def test_hbm_read_reads_every_value(n, blocks):
+    # Small integers: every block sum and the total are exact in fp32.
+    g = torch.Generator(device="cpu").manual_seed(n)
+    buf = torch.randint(-3, 4, (n,), generator=g).to(torch.float32)
+    sums = torch.full((blocks,), float("nan"), device=DEV)
+    rra.rra_hbm_read(buf.to(DEV), sums)
+    torch.cuda.synchronize()
+    assert host(sums).astype(np.float64).sum() == float(buf.double().sum())
+
+
+def test_hbm_read_rejects_bad_arguments():
+    sums = torch.zeros(4, device=DEV)
+    buf = torch.zeros(8, device=DEV)
+    with pytest.raises(rra.RraError, match="multiple of 16"):
+        rra.rra_hbm_read(buf[:3], sums)
+    with pytest.raises(rra.RraError, match="multiple of 16"):
+        rra.rra_hbm_read(buf[1:5], sums)
+    with pytest.raises(rra.RraError, match="blocks=0"):
+        rra.rra_hbm_read(buf, sums, blocks=0)
+
+
 # ---------------------------------------------------------------- elementwise
 @pytest.mark.parametrize("m,h", [(1, 256), (3, 896), (32, 4096), (2, 4100)])
 def test_rmsnorm(m, h):
