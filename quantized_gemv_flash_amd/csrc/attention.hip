@@ -62,16 +62,38 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict
 // workgroup's work where the grid is small and latency-bound (the other
 // workgroups' K/V reads are cache hits).  A head's arithmetic is the same
 // whatever G and hs are.
-template <int HD, int G>
+//
+// QF: the QKV GEMV's split planes stand in for q and seq_len (QkvIn).  The
+// workgroup owning row pos (c = pos mod nc_max) forms the new K/V row in LDS,
+// takes it in place of the cache row (which its loads still read: the values
+// it writes there are the same), and the first of the hs workgroups of its
+// KV head writes it to the cache.  The arithmetic is qkv_post_kernel's
+// (sum_splits2, rope_pair), so the results equal the unfused path bitwise.
+template <int HD, int G, bool QF>
 __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
     const uint32_t *__restrict__ seq_len, const uint32_t *__restrict__ slot_seq,
     float *__restrict__ part_o, float *__restrict__ part_lse, int nq, int nkv, int max_len,
-    int chunk, int nc_max, int hs) {
+    int chunk, int nc_max, int hs, QkvIn qi) {
     constexpr int GP = (G + 3) & ~3;  // probabilities stored key-major, G padded to 4
     const int c = blockIdx.x, g = blockIdx.y / hs, m = blockIdx.z;
     const int hq0 = blockIdx.y * G;  // first query head: g G hs + (blockIdx.y mod hs) G
-    const int L = (int)min(seq_len[m], (uint32_t)max_len);
+    uint32_t p = 0;
+    bool ok = false;
+    int L;
+    if constexpr (QF) {
+        p = qi.pos[m];
+        ok = p < (uint32_t)max_len;  // false for an empty slot (RRA_POS_NONE) too
+        // an empty slot attends to nothing; any other bad position is an error
+        const uint32_t lr = ok ? p + 1 : (p == RRA_POS_NONE ? 0u : (uint32_t)max_len);
+        if (c == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+            qi.seq_len[m] = lr;
+            if (!ok && p != RRA_POS_NONE) qi.err[0] = 1u;
+        }
+        L = (int)min(lr, (uint32_t)max_len);
+    } else {
+        L = (int)min(seq_len[m], (uint32_t)max_len);
+    }
     if (c >= L) return;
     // Rows c, c + nc_max, c + 2 nc_max, ... < L (local row i is cache row
     // c + i nc_max): the nc_max workgroups of one (sequence, KV head) sweep its
@@ -82,6 +104,36 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float *sc = smem;                 // [chunk][GP] scores, then probabilities
     float *red = smem + GP * chunk;   // [4 waves][G][HD]
     float *stat = red + 4 * G * HD;   // [G] max, [G] sum
+    float *qs = stat + 2 * G;         // QF: [G][HD] queries, then [HD] new K, [HD] new V
+    float *kn = qs + G * HD, *vn = kn + HD;
+    // QF: the new row's local index in this split, or -1
+    const int tp = (QF && ok && (int)(p % (uint32_t)nc_max) == c) ? (int)(p / (uint32_t)nc_max) : -1;
+    if constexpr (QF) {
+        constexpr int HALF = HD / 2;
+        const int nrow = (nq + 2 * nkv) * HD;
+        const int npairs = (G + (tp >= 0 ? 2 : 0)) * HALF;
+        for (int idx = threadIdx.x; idx < npairs; idx += blockDim.x) {
+            const int hh = idx / HALF, j = idx % HALF;
+            const int head = hh < G ? hq0 + hh : hh == G ? nq + g : nq + nkv + g;
+            const size_t b = (size_t)m * nrow + (size_t)head * HD;
+            float a, cc;
+            sum_splits2(qi.part + b + j, qi.part + b + j + HALF, qi.split, qi.stride, a, cc);
+            if (hh <= G && ok)
+                rope_pair(a, cc, qi.table[((size_t)p * HALF + j) * 2],
+                          qi.table[((size_t)p * HALF + j) * 2 + 1]);
+            float *dst = qs + hh * HD;  // qs rows, then kn, vn
+            dst[j] = a;
+            dst[j + HALF] = cc;
+        }
+        __syncthreads();
+        if (tp >= 0 && blockIdx.y % hs == 0) {
+            const size_t at = (((size_t)m * nkv + g) * max_len + p) * HD;
+            for (int d = threadIdx.x; d < HD; d += blockDim.x) {
+                qi.k_cache[at + d] = kn[d];
+                qi.v_cache[at + d] = vn[d];
+            }
+        }
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -99,7 +151,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float4 qr[G][F4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float *qh = q + ((size_t)m * nq + hq0 + h) * HD;
+        const float *qh = QF ? qs + h * HD : q + ((size_t)m * nq + hq0 + h) * HD;
 #pragma unroll
         for (int i = 0; i < F4; ++i) {
             float4 v = *reinterpret_cast<const float4 *>(qh + 4 * (e + 8 * i));
@@ -117,6 +169,11 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
 #pragma unroll
             for (int i = 0; i < F4; ++i)
                 kv[u][i] = *reinterpret_cast<const float4 *>(K + (size_t)tc * rs + 4 * (e + 8 * i));
+            if (QF && tt[u] == tp) {
+#pragma unroll
+                for (int i = 0; i < F4; ++i)
+                    kv[u][i] = *reinterpret_cast<const float4 *>(kn + 4 * (e + 8 * i));
+            }
         }
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
@@ -155,6 +212,8 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
         for (int u = 0; u < UV; ++u) {
             const int t = min(base + r0 + u * 4 * KPW, n - 1);
             vb[u] = *reinterpret_cast<const float4 *>(V + (size_t)t * rs + 4 * d4);
+            if (QF && base + r0 + u * 4 * KPW == tp)
+                vb[u] = *reinterpret_cast<const float4 *>(vn + 4 * d4);
         }
     };
     vload(0);
@@ -283,11 +342,18 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
 template <int HD, int G>
 rra_status launch_chunk(const float *q, const float *kc, const float *vc, const uint32_t *lens,
                         const uint32_t *slot_seq, float *po, float *pl, int m, int nq, int nkv,
-                        int max_len, int chunk, int nc_max, int hs, hipStream_t s) {
+                        int max_len, int chunk, int nc_max, int hs, const QkvIn *qi,
+                        hipStream_t s) {
     constexpr int GP = (G + 3) & ~3;
-    const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * G);
-    hipLaunchKernelGGL((fd_chunk_kernel<HD, G>), dim3(nc_max, nkv * hs, m), dim3(256), shm, s, q,
-                       kc, vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs);
+    const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * G +
+                                        (qi ? (size_t)(G + 2) * HD : 0));
+    const dim3 grid(nc_max, nkv * hs, m);
+    if (qi)
+        hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), shm, s, q, kc, vc, lens,
+                           slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, *qi);
+    else
+        hipLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), shm, s, q, kc, vc,
+                           lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, QkvIn{});
     return check_launch("fd_chunk_kernel");
 }
 
@@ -308,14 +374,14 @@ template <int HD>
 rra_status launch_chunk_hd(int group, const float *q, const float *kc, const float *vc,
                            const uint32_t *lens, const uint32_t *slot_seq, float *po, float *pl,
                            int m, int nq, int nkv, int max_len, int chunk, int nc_max,
-                           hipStream_t s) {
+                           const QkvIn *qi, hipStream_t s) {
     if (group < 1 || group > 8) return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", group);
     const int hs = fd_head_split(group, m, nkv, nc_max);
     switch (group / hs) {
 #define RRA_G(gv) \
     case gv:                                                                                    \
         return launch_chunk<HD, gv>(q, kc, vc, lens, slot_seq, po, pl, m, nq, nkv, max_len, chunk, \
-                                    nc_max, hs, s);
+                                    nc_max, hs, qi, s);
         RRA_G(1) RRA_G(2) RRA_G(3) RRA_G(4) RRA_G(5) RRA_G(6) RRA_G(7) RRA_G(8)
 #undef RRA_G
     }
@@ -327,14 +393,16 @@ rra_status launch_chunk_hd(int group, const float *q, const float *kc, const flo
 int fd_choose_chunk(int m, int nkv, int max_len, int chunk) {
     if (chunk > 0) return chunk;
     // About one workgroup per 512 cached rows, but at least 256 (one per
-    // compute unit) and at most 2048; the splits per (sequence, KV head) then
+    // compute unit) and at most 4096; the splits per (sequence, KV head) then
     // give the rows per split, rounded up to a multiple of 32 in 64..1024.
     // Fewer, longer splits save per-workgroup cost (query load, softmax,
     // partial write) and reduce work; more keep short caches spread over the
     // chip.  Measured on MI355X over M = 1..32 at 0.5B, 1.5B and 8B-sized KV
-    // heads: within 5 % of the best fixed split size everywhere.
+    // heads: within 5 % of the best fixed split size everywhere (8B, M = 32:
+    // the best of 128..1024 rows); with an 8192-row cache at M = 32 (32/8
+    // heads) 512-row splits take 195-199 us against 204-206 at 1024.
     const int64_t pairs = (int64_t)m * nkv;
-    const int64_t wgs = std::min<int64_t>(2048, std::max<int64_t>(256, pairs * max_len / 512));
+    const int64_t wgs = std::min<int64_t>(4096, std::max<int64_t>(256, pairs * max_len / 512));
     const int64_t nc = std::max<int64_t>(1, wgs / pairs);
     const int64_t rows = (max_len + nc - 1) / nc;
     return (int)std::min<int64_t>(1024, std::max<int64_t>(64, (rows + 31) / 32 * 32));
@@ -356,7 +424,9 @@ rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
-                               const FragOut *fo, const uint32_t *slot_seq, bool reduce) {
+                               const FragOut *fo, const uint32_t *slot_seq, bool reduce,
+                               const QkvIn *qi) {
+    if (qi && slot_seq) return fail(RRA_EINVAL, "flash decode: fused QKV input needs no slot map");
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
     const int nc_max = (int)cdiv(max_len, chunk);
@@ -364,10 +434,10 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
     float *pl = const_cast<float *>(fd_part_lse(part, m, nq, hd, nc_max));
     if (hd == 128)
         RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                     max_len, chunk, nc_max, s));
+                                     max_len, chunk, nc_max, qi, s));
     else
         RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                    max_len, chunk, nc_max, s));
+                                    max_len, chunk, nc_max, qi, s));
     if (!reduce) return RRA_OK;
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,

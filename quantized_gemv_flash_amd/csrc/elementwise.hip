@@ -22,26 +22,6 @@ namespace {
 // apart), in plane order, of two columns at once (p and q).  Up to 8 planes
 // are loaded at once (clamped addresses, unconditional loads), so the latency
 // is paid once per 8 planes, not once per plane.
-__device__ __forceinline__ void sum_splits2(const float *__restrict__ p, const float *__restrict__ q,
-                                            int split, long long stride, float &a, float &c) {
-    a = 0.f;
-    c = 0.f;
-    for (int s0 = 0; s0 < split; s0 += 8) {
-        float u[8], w[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const size_t off = (size_t)min(s0 + j, split - 1) * stride;
-            u[j] = p[off];
-            w[j] = q[off];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            a += (s0 + j < split) ? u[j] : 0.f;
-            c += (s0 + j < split) ? w[j] : 0.f;
-        }
-    }
-}
-
 // Sum over a 256-thread block; every thread gets the result.
 __device__ __forceinline__ float block_sum(float v, float *sh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -124,12 +104,8 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
     const size_t b = (size_t)m * nrow + (size_t)head * hd;
     float a, c;
     sum_splits2(part + b + j, part + b + j + half, split, split_stride, a, c);
-    if (head < nq + nkv && ok) {
-        const float cs = table[((size_t)p * half + j) * 2], sn = table[((size_t)p * half + j) * 2 + 1];
-        const float ra = a * cs - c * sn, rc = a * sn + c * cs;
-        a = ra;
-        c = rc;
-    }
+    if (head < nq + nkv && ok)
+        rope_pair(a, c, table[((size_t)p * half + j) * 2], table[((size_t)p * half + j) * 2 + 1]);
     if (head < nq) {
         float *qo = q_out + ((size_t)m * nq + head) * hd;
         qo[j] = a;
@@ -155,9 +131,10 @@ __global__ void rope_kernel(float *__restrict__ z, const uint32_t *__restrict__ 
     if (p >= (uint32_t)max_len) return;
     float *zr = z + ((size_t)m * n_heads + head) * hd;
     const float cs = table[((size_t)p * half + j) * 2], sn = table[((size_t)p * half + j) * 2 + 1];
-    const float a = zr[j], c = zr[j + half];
-    zr[j] = a * cs - c * sn;
-    zr[j + half] = a * sn + c * cs;
+    float a = zr[j], c = zr[j + half];
+    rope_pair(a, c, cs, sn);
+    zr[j] = a;
+    zr[j + half] = c;
 }
 
 __global__ void swiglu_kernel(const float *gate, const float *up, float *out, int n,

@@ -28,6 +28,35 @@ __device__ __forceinline__ float swiglu1(float g, float u) {
     return silu(g) * u;
 }
 
+// a = sum_s p[s * stride], c = sum_s q[s * stride], in split order.
+__device__ __forceinline__ void sum_splits2(const float *__restrict__ p, const float *__restrict__ q,
+                                            int split, long long stride, float &a, float &c) {
+    a = 0.f;
+    c = 0.f;
+    for (int s0 = 0; s0 < split; s0 += 8) {
+        float u[8], w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const size_t off = (size_t)min(s0 + j, split - 1) * stride;
+            u[j] = p[off];
+            w[j] = q[off];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            a += (s0 + j < split) ? u[j] : 0.f;
+            c += (s0 + j < split) ? w[j] : 0.f;
+        }
+    }
+}
+
+// RoPE of the pair (a, c) by (cos, sin): (a cos - c sin, a sin + c cos),
+// with explicit FMAs so that every kernel computes the same bits.
+__device__ __forceinline__ void rope_pair(float &a, float &c, float cs, float sn) {
+    const float ra = fmaf(a, cs, -(c * sn)), rc = fmaf(a, sn, c * cs);
+    a = ra;
+    c = rc;
+}
+
 __device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
     const float4 b = *reinterpret_cast<const float4 *>(p + 4);

@@ -406,9 +406,15 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         const bool rq = pr_qkv.kind == kProResid;
         RRA_TRY(launch_gemv(L.wqkv, pq, gemv_input(M, L.wqkv, M->xg), m, M->part, (size_t)m * nqkv,
                             s, rq ? nullptr : &nrm, rq ? &pr_qkv : nullptr));
-        RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
-                                L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd, d.max_len,
-                                slot_seq, s));
+        // At small m flash decode takes the QKV partials itself (QkvIn: sum,
+        // RoPE, the new K/V row, seq_len); otherwise qkv_post does that work.
+        const bool fuse_qkv = m <= 4 && !slot_seq;
+        const QkvIn qi{M->part, pq.split, (long long)m * nqkv, pos, M->rope,
+                       L.k_cache, L.v_cache, M->lens, M->err};
+        if (!fuse_qkv)
+            RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
+                                    L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd,
+                                    d.max_len, slot_seq, s));
         // At small m the O GEMV combines the attention partials itself and the
         // down GEMV forms SwiGLU itself (GemvPrologue): two launches fewer per
         // layer, with the same arithmetic as the kernels they stand in for.
@@ -416,7 +422,8 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         const bool pro_o = gemv_takes_prologue(L.wo, po, m);
         const FragOut fo_o = image_for(M, L.wo, m);
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
-                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq, !pro_o));
+                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq, !pro_o,
+                                    fuse_qkv ? &qi : nullptr));
         const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
         const GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
                               0, 0, nq, nc_max, d.max_len};

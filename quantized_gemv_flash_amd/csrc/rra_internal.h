@@ -135,14 +135,30 @@ size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk);
 rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
                              float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
                              int max_len, hipStream_t s);
+// The QKV GEMV's output taken by flash decode itself (qkv_post's work, at
+// small batch in the decode step): the split kernel sums the split planes of
+// its query heads and applies RoPE at pos; the workgroup that holds row pos
+// of a sequence forms the new K/V row (summed, K roped), uses it in place of
+// the cache row and writes it to the cache; one workgroup per sequence
+// writes seq_len (and err), with qkv_post's rules.
+struct QkvIn {
+    const float *part = nullptr;  // [split][m][(nq + 2 nkv) hd]
+    int split = 0;
+    long long stride = 0;         // floats between split planes
+    const uint32_t *pos = nullptr;
+    const float *table = nullptr;  // RoPE table [max_len][hd/2][2]
+    float *k_cache = nullptr, *v_cache = nullptr;  // written at row pos
+    uint32_t *seq_len = nullptr, *err = nullptr;
+};
 // Row i of q attends to cache slot slot_seq[i] (slot i when slot_seq is null).
 // reduce = false launches the split kernel only (the O GEMV then combines the
-// partials in its prologue).
+// partials in its prologue).  With qi, q and seq_len are ignored (the split
+// kernel forms them; slot_seq must be null).
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
                                const FragOut *fo = nullptr, const uint32_t *slot_seq = nullptr,
-                               bool reduce = true);
+                               bool reduce = true, const QkvIn *qi = nullptr);
 // Where rra_flash_decode's partials live in `part` (m sequences, nq heads).
 inline const float *fd_part_lse(const float *part, int m, int nq, int hd, int nc_max) {
     return part + (size_t)m * nq * nc_max * hd;
