@@ -32,6 +32,15 @@
 namespace rra {
 namespace {
 
+// 128-bit load marked nontemporal (the cached K/V rows are read once per
+// step, so they should not displace reused lines).  On MI355X this lifts the
+// chunk kernel's K/V stream from about 5.5 to 6.05 TB/s.
+typedef float rra_f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ldnt(const float *p) {
+    const rra_f4v v = __builtin_nontemporal_load(reinterpret_cast<const rra_f4v *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict__ k_rows,
                                                          const float *__restrict__ v_rows,
                                                          float *__restrict__ kc,
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
 #pragma unroll
             for (int i = 0; i < F4; ++i)
-                kv[u][i] = *reinterpret_cast<const float4 *>(K + (size_t)tc * rs + 4 * (e + 8 * i));
+                kv[u][i] = ldnt(K + (size_t)tc * rs + 4 * (e + 8 * i));
             if (QF && tt[u] == tp) {
 #pragma unroll
                 for (int i = 0; i < F4; ++i)
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int t = min(base + r0 + u * 4 * KPW, n - 1);
-            vb[u] = *reinterpret_cast<const float4 *>(V + (size_t)t * rs + 4 * d4);
+            vb[u] = ldnt(V + (size_t)t * rs + 4 * d4);
             if (QF && base + r0 + u * 4 * KPW == tp)
                 vb[u] = *reinterpret_cast<const float4 *>(vn + 4 * d4);
         }

@@ -259,8 +259,10 @@ __global__ __launch_bounds__(256) void argmax_pass2_kernel(const float *__restri
 }
 
 // Plain streaming read of n4 16-byte words: grid-stride, eight independent
-// 128-bit loads in flight per thread; each block writes the fp32 sum of the
-// values it read (so the reads cannot be dropped, and the result is checkable).
+// 128-bit loads in flight per thread, marked nontemporal as the decode step's
+// weight and K/V streams are; each block writes the fp32 sum of the values it
+// read (so the reads cannot be dropped, and the result is checkable).
+typedef float rra_f4v __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void hbm_read_kernel(const float4 *__restrict__ p, size_t n4,
                                                        float *__restrict__ sums) {
     constexpr int U = 8;
@@ -271,7 +273,11 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const float4 *__restrict_
     for (; i + (U - 1) * stride < n4; i += U * stride) {
         float4 a[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) a[u] = p[i + u * stride];
+        for (int u = 0; u < U; ++u) {
+            const rra_f4v v =
+                __builtin_nontemporal_load(reinterpret_cast<const rra_f4v *>(p + i + u * stride));
+            a[u] = make_float4(v.x, v.y, v.z, v.w);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) acc += (a[u].x + a[u].y) + (a[u].z + a[u].w);
     }
