@@ -338,7 +338,7 @@ LM_HEAD_FORMATS = {
 def lm_head_gemv_line(fmt, reps=20):
     """A further block format on the weights-once GEMV at the LM-head shape of
     the 8B-shaped decoder (128256 x 4096): rra_batched_gemv (activation image +
-    GEMV) timed with HIP events at M = 1 and 32."""
+    GEMV) timed with HIP events around graph replays at M = 1 and 32."""
     import synth
     import quantized_gemv_flash_amd as rra
     n, k = 128256, 4096
@@ -353,16 +353,10 @@ def lm_head_gemv_line(fmt, reps=20):
         y = torch.empty((m, n), device="cuda")
         ws = torch.empty(max(4, rra.rra_batched_gemv_workspace_bytes(w, m)), dtype=torch.uint8,
                          device="cuda")
-        for _ in range(10):
-            rra.rra_batched_gemv(w, x, y, m, ws)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(reps):
-            rra.rra_batched_gemv(w, x, y, m, ws)
-        ev1.record()
-        torch.cuda.synchronize()
-        sec = ev0.elapsed_time(ev1) / 1e3 / reps
+        # median of three graph replays of `reps` calls (eager launches let
+        # host-side gaps into the event time)
+        sec = sorted(graph_time(lambda: rra.rra_batched_gemv(w, x, y, m, ws), reps)
+                     for _ in range(3))[1]
         res[f"m{m}_us"] = sec * 1e6
         res[f"m{m}_gbs"] = wbytes / sec / 1e9
         res[f"m{m}_hbm_frac"] = wbytes / sec / 1e9 / HBM_PEAK_GBS
