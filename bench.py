@@ -145,6 +145,39 @@ def flash_decode_roofline(S, dd, lens, reps):
     return sec, kv_bytes, chunk
 
 
+def flash_decode_in_step(S, dd, m, first_tok, start_pos, steps):
+    """Flash decode's chunk kernel timed inside the decode step: the same
+    greedy steps from the same start, run eagerly, with a pair of HIP events
+    per layer recorded on the step's stream around each layer's split-K chunk
+    kernel (rra_model_set_attention_events).  Returns (seconds and algorithmic K/V
+    bytes summed over every layer of every step, the final positions)."""
+    import quantized_gemv_flash_amd as rra
+    dev = "cuda"
+    cur = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * S.n_layers)]
+    for e in evs:
+        e.record(cur)  # creates the event
+    x = torch.empty((m, S.hidden), device=dev)
+    pos = torch.as_tensor(start_pos, dtype=torch.int32, device=dev)
+    tok = torch.as_tensor(first_tok, dtype=torch.int32, device=dev)
+    logits = torch.empty((m, S.vocab), device=dev)
+    flags = rra.RRA_STEP_GATHER | rra.RRA_STEP_ADVANCE
+    dd.model.rra_model_set_attention_events(evs)
+    sec = nbytes = 0.0
+    try:
+        for i in range(steps):
+            dd.model.rra_decode_step(x, pos, tok, m, flags=flags, logits=logits)
+            torch.cuda.synchronize()
+            sec += sum(evs[2 * l].elapsed_time(evs[2 * l + 1]) for l in range(S.n_layers)) / 1e3
+            # rows read this step: every cached row up to and including position start + i
+            nbytes += S.n_layers * sum(2 * S.n_kv_heads * (L + i + 1) * S.head_dim * 4
+                                       for L in start_pos)
+    finally:
+        dd.model.rra_model_set_attention_events(None)
+    dd.model.rra_model_check()
+    return sec, nbytes, pos.tolist()
+
+
 def flash_decode_line(reps=20):
     """The standalone attention workload (32 sequences, 32 Q / 8 KV heads, hd
     128, lengths uniform in [1, 8192], an 8192-row cache): rra_flash_decode at
@@ -243,9 +276,10 @@ ATTENTION_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quanti
 
 
 def counter_traffic():
-    """HBM bytes per rra_flash_decode launch from the committed counter runs
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None
-    once the attention source has changed since they were taken."""
+    """HBM bytes per chunk-kernel launch from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings) and the
+    algorithmic bytes of that launch, or (None, None) once the attention
+    source has changed since they were taken."""
     import hashlib
     try:
         with open(COUNTERS) as f:
@@ -253,10 +287,10 @@ def counter_traffic():
         rec = json.loads(line[len("traffic_json: "):])
         with open(ATTENTION_SRC, "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != rec["attention_hip_sha256"]:
-                return None
-        return float(rec["traffic_bytes_per_launch"])
+                return None, None
+        return float(rec["traffic_bytes_per_launch"]), float(rec["algorithmic_bytes"])
     except (OSError, IndexError, ValueError, KeyError):
-        return None
+        return None, None
 
 
 def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps):
@@ -439,9 +473,17 @@ def main():
                   for L in lengths for i in range(steps)) / steps
     step_gbs = (wbytes + kv_read) / (sec / steps) / 1e9
 
-    fd_sec, fd_bytes, chunk = flash_decode_roofline(S, dd, [p for p in final_pos], args.fd_reps)
+    # the dominant kernel, timed inside the same steps (rerun eagerly with
+    # events around it), and rra_flash_decode alone on layer 0's cache
+    fd_total, fd_total_bytes, pos_ev = flash_decode_in_step(S, dd, m, first, lengths, steps)
+    assert pos_ev == final_pos
+    launches = S.n_layers * steps
+    fd_sec, fd_bytes = fd_total / launches, fd_total_bytes / launches  # per launch
     fd_gbs = fd_bytes / fd_sec / 1e9
-    log(f"flash decode: {fd_sec * 1e6:.1f} us, {fd_gbs:.0f} GB/s (chunk {chunk})")
+    fd_alone, alone_bytes, chunk = flash_decode_roofline(S, dd, [p for p in final_pos],
+                                                         args.fd_reps)
+    log(f"flash decode in the step: {fd_sec * 1e6:.1f} us, {fd_gbs:.0f} GB/s (chunk {chunk}); "
+        f"alone {fd_alone * 1e6:.1f} us")
 
     m1 = None
     cpu = None
@@ -466,6 +508,7 @@ def main():
     ceil = None if args.main_only else hbm_ceiling_line()
     log(f"hbm ceiling {ceil}")
 
+    traffic, traffic_alg = counter_traffic()
     out = {
         "metric": "decode tok/s at M=1 and M=32; weight+KV stream HBM GB/s as % of peak",
         "value": tok_s,
@@ -489,12 +532,21 @@ def main():
         "weight_kv_gbs": step_gbs,
         "weight_kv_hbm_frac": step_gbs / HBM_PEAK_GBS,
         "roofline": {
-            "kernel": "rra_flash_decode (fd_chunk_kernel + fd_reduce_kernel), layer-0 cache, "
-                      f"M={m}, chunk {chunk}",
+            "kernel": "fd_chunk_kernel (flash-decode split-K chunks), every layer of the "
+                      f"{steps} timed steps, M={m}, chunk {chunk}",
             "bound": "hbm", "achieved": fd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": fd_gbs / HBM_PEAK_GBS, "traffic": counter_traffic(),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-scaled)",
+            "frac": fd_gbs / HBM_PEAK_GBS, "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-scaled) "
+                            "at the final lengths, whose algorithmic bytes are "
+                            "traffic_algorithmic_bytes",
+            "traffic_algorithmic_bytes": traffic_alg,
             "avg_us": fd_sec * 1e6, "algorithmic_bytes": fd_bytes,
+            "timing": "HIP events on the step's stream around each layer's chunk kernel, the "
+                      "same steps rerun eagerly; bytes and time summed over layers and steps",
+            "alone_us": fd_alone * 1e6,
+            "alone_gbs": alone_bytes / fd_alone / 1e9,
+            "alone": "rra_flash_decode (chunk kernel + combine) on layer 0's cache at the final "
+                     "lengths, 20 launches in one graph replay",
         },
         "m1": m1,
         "fp8_gemv": fp8,

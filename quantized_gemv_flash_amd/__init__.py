@@ -86,6 +86,7 @@ def _load() -> ctypes.CDLL:
         "rra_prefill": ([P, P, I, I, U, P, P, P], I),
         "rra_model_check": ([P, P], I),
         "rra_graph_stats": ([P, POINTER(c_uint64), POINTER(c_uint64), POINTER(c_uint32)], I),
+        "rra_model_set_attention_events": ([P, P, I], I),
         "rra_model_destroy": ([P], None),
     }
     for name, (args, res) in sig.items():
@@ -302,6 +303,19 @@ class Model:
         _check("rra_graph_stats", lib.rra_graph_stats(self.handle, ctypes.byref(c), ctypes.byref(r),
                                                       ctypes.byref(k)))
         return dict(captures=c.value, replays=r.value, kernels=k.value)
+
+    def rra_model_set_attention_events(self, events=None):
+        """events: None (stop) or 2 x n_layers torch.cuda.Event(enable_timing=True),
+        each already recorded once (so that it exists); kept alive here."""
+        if not events:
+            self._attn_events = None
+            _check("rra_model_set_attention_events",
+                   lib.rra_model_set_attention_events(self.handle, None, 0))
+            return
+        handles = (c_void_p * len(events))(*[e.cuda_event for e in events])
+        self._attn_events = (list(events), handles)
+        _check("rra_model_set_attention_events",
+               lib.rra_model_set_attention_events(self.handle, handles, len(events)))
 
     def close(self):
         if getattr(self, "handle", None):

@@ -409,12 +409,16 @@ int fd_choose_chunk(int m, int nkv, int max_len, int chunk) {
     // Fewer, longer splits save per-workgroup cost (query load, softmax,
     // partial write) and reduce work; more keep short caches spread over the
     // chip.  Measured on MI355X over M = 1..32 at 0.5B, 1.5B and 8B-sized KV
-    // heads: within 5 % of the best fixed split size everywhere (8B, M = 32:
-    // the best of 128..1024 rows); with an 8192-row cache at M = 32 (32/8
-    // heads) 512-row splits take 195-199 us against 204-206 at 1024.
+    // heads: within 5 % of the best fixed split size everywhere.  Once the
+    // grid has 1024 workgroups (four resident per compute unit) a sequence
+    // gets at most 5 splits: more only add per-workgroup cost.  8B-shaped
+    // layer at M = 32 (lengths 2112..4160, 8 KV heads): 5 splits 134-136 us,
+    // 8 splits 140-141 us; an 8192-row cache (lengths U[1, 8192], 8 KV heads):
+    // 8 and 16 splits within 1 % (183-187 us).
     const int64_t pairs = (int64_t)m * nkv;
     const int64_t wgs = std::min<int64_t>(4096, std::max<int64_t>(256, pairs * max_len / 512));
-    const int64_t nc = std::max<int64_t>(1, wgs / pairs);
+    const int64_t nc = std::max<int64_t>(
+        1, std::min<int64_t>(wgs / pairs, std::max<int64_t>(5, (1024 + pairs - 1) / pairs)));
     const int64_t rows = (max_len + nc - 1) / nc;
     return (int)std::min<int64_t>(1024, std::max<int64_t>(64, (rows + 31) / 32 * 32));
 }
@@ -436,7 +440,7 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
                                const FragOut *fo, const uint32_t *slot_seq, bool reduce,
-                               const QkvIn *qi) {
+                               const QkvIn *qi, hipEvent_t chunk_done) {
     if (qi && slot_seq) return fail(RRA_EINVAL, "flash decode: fused QKV input needs no slot map");
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
@@ -449,6 +453,8 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
     else
         RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
                                     max_len, chunk, nc_max, qi, s));
+    // measurement hook: an event recorded between the chunk kernel and the combine
+    if (chunk_done) RRA_TRY_HIP(hipEventRecord(chunk_done, s));
     if (!reduce) return RRA_OK;
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,

@@ -211,6 +211,9 @@ struct rra_model {
     GemvPlan plan_qkv[RRA_M_MAX + 1], plan_o[RRA_M_MAX + 1], plan_gu[RRA_M_MAX + 1],
         plan_d[RRA_M_MAX + 1], plan_lm[RRA_M_MAX + 1];
     std::vector<GraphEntry> graphs;
+    // attention timing: a pair of caller-owned events per layer recorded
+    // around that layer's flash decode in eager steps (empty: none)
+    std::vector<hipEvent_t> attn_events;
     uint64_t captures = 0, replays = 0;
     uint32_t last_kernels = 0;
 };
@@ -421,9 +424,14 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         const GemvPlan &po = M->plan_o[m];
         const bool pro_o = gemv_takes_prologue(L.wo, po, m);
         const FragOut fo_o = image_for(M, L.wo, m);
+        // (eager steps only: an event record captured into a graph does not
+        // wait for the kernels before it, so it would time nothing)
+        const bool timed = !M->attn_events.empty() && !slot_seq && !(flags & RRA_GRAPH);
+        if (timed) RRA_TRY_HIP(hipEventRecord(M->attn_events[2 * l], s));
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
                                     d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq, !pro_o,
-                                    fuse_qkv ? &qi : nullptr));
+                                    fuse_qkv ? &qi : nullptr,
+                                    timed ? M->attn_events[2 * l + 1] : nullptr));
         const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
         const GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
                               0, 0, nq, nc_max, d.max_len};
@@ -659,6 +667,24 @@ extern "C" rra_status rra_decode_step(rra_model *M, float *x, uint32_t *pos, uin
         RRA_TRY_HIP(hipMemcpyAsync(tok_host, tok, sizeof(uint32_t) * m, hipMemcpyDeviceToHost, s));
         RRA_TRY_HIP(hipStreamSynchronize(s));
     }
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_model_set_attention_events(rra_model *M, void *const *events,
+                                                     int32_t n) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_model_set_attention_events: null model");
+    if (!events || n == 0) {
+        M->attn_events.clear();
+        return RRA_OK;
+    }
+    if (n != 2 * M->d.n_layers)
+        return fail(RRA_EINVAL, "rra_model_set_attention_events: n=%d, need 2 x %d layers", n,
+                    M->d.n_layers);
+    for (int32_t i = 0; i < n; ++i)
+        if (!events[i]) return fail(RRA_EINVAL, "rra_model_set_attention_events: null event %d", i);
+    M->attn_events.assign(reinterpret_cast<const hipEvent_t *>(events),
+                          reinterpret_cast<const hipEvent_t *>(events) + n);
     return RRA_OK;
 }
 

@@ -126,6 +126,43 @@ def test_graph_replay_equals_eager_bitwise(S):
         assert torch.equal(eager.dd.v_caches[l], graph.dd.v_caches[l])
 
 
+@pytest.mark.parametrize("m", [2, 6])  # flash decode taking the QKV partials (m <= 4) or not
+def test_attention_events_time_each_layer_and_change_nothing(m):
+    # rra_model_set_attention_events: eager steps with the per-layer event
+    # records give the same ids, logits, hidden state and caches bitwise as
+    # steps without them, and every layer's interval is a positive time; a
+    # graph step records nothing and still matches.
+    S = SMALL_DECODERS[2]  # quantised (Q4): the GEMV prologues and split planes are in play
+    W = synth.decoder_weights(S, seed=3, device=DEV, gamma="random")
+    plain, timed = Run(S, W, m, 16), Run(S, W, m, 16)
+    cur = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * S.n_layers)]
+    for e in evs:
+        e.record(cur)
+    timed.dd.model.rra_model_set_attention_events(evs)
+    toks = synth.first_tokens(S, m, seed=3).tolist()
+    for step in range(4):
+        pos = [step + i for i in range(m)]
+        a = plain.step(toks, pos)
+        b = timed.step(toks, pos)
+        assert a[0] == b[0] and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+        toks = a[0]
+        torch.cuda.synchronize()
+        ms = [evs[2 * l].elapsed_time(evs[2 * l + 1]) for l in range(S.n_layers)]
+        assert all(0.0 < t < 1000.0 for t in ms), ms
+    pos = [4 + i for i in range(m)]
+    a = plain.step(toks, pos)
+    b = timed.step(toks, pos, flags=rra.RRA_GRAPH)
+    assert a[0] == b[0] and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    for l in range(S.n_layers):
+        assert torch.equal(plain.dd.k_caches[l], timed.dd.k_caches[l])
+        assert torch.equal(plain.dd.v_caches[l], timed.dd.v_caches[l])
+    timed.dd.model.rra_model_set_attention_events(None)
+    with pytest.raises(rra.RraError) as e:
+        timed.dd.model.rra_model_set_attention_events(evs[:-1])
+    assert e.value.status == rra.RRA_EINVAL
+
+
 def test_capture_failure_discarded_and_step_runs_eagerly(monkeypatch):
     # A failed capture ([reduces] try_graph_capture): the graph is discarded,
     # the stream leaves capture mode, the step runs eagerly with the same

@@ -139,3 +139,9 @@ def test_model_descriptor_validation():
 def test_decode_step_rejects_null_model():
     st = rra.lib.rra_decode_step(None, None, None, None, None, None, 1, 0, None)
     assert st == rra.RRA_ENOTINIT
+
+
+def test_attention_events_need_a_model():
+    # rra_model_set_attention_events on no model: RRA_ENOTINIT, no GPU call
+    assert rra.lib.rra_model_set_attention_events(None, None, 0) == rra.RRA_ENOTINIT
+    assert b"null model" in rra.lib.rra_last_error()
