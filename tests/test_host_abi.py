@@ -145,3 +145,17 @@ def test_attention_events_need_a_model():
     # rra_model_set_attention_events on no model: RRA_ENOTINIT, no GPU call
     assert rra.lib.rra_model_set_attention_events(None, None, 0) == rra.RRA_ENOTINIT
     assert b"null model" in rra.lib.rra_last_error()
+
+
+@pytest.mark.parametrize("m,nkv,max_len,splits", [
+    (32, 8, 4160, 5),    # 8B-shaped, M=32: 1280 workgroups, capped at 5 splits per sequence
+    (32, 8, 8192, 8),    # 8192-row cache: 1024-row splits (the row cap) give 8
+    (16, 8, 4160, 8),    # 1040 workgroups at 8 splits: the cap is max(5, 1024 / 128) = 8
+    (1, 2, 768, 12),     # small grids: at least 256 workgroups, 64-row splits
+    (32, 2, 1152, 4),    # 1.5B-shaped, M=32
+])
+def test_flash_decode_split_choice(m, nkv, max_len, splits):
+    c = rra.rra_flash_decode_chunk(m, nkv, max_len, 0)
+    assert c % 32 == 0 and 64 <= c <= 1024
+    assert -(-max_len // c) == splits
+    assert rra.rra_flash_decode_chunk(m, nkv, max_len, 96) == 96  # an explicit size is kept
