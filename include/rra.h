@@ -357,15 +357,16 @@ rra_status rra_model_check(rra_model *mdl, hipStream_t s);
 rra_status rra_graph_stats(const rra_model *mdl, uint64_t *captures, uint64_t *replays,
                            uint32_t *kernels);
 
-/* Attention timing, for measurement ([reduces] batched_gpu_argmax times the
- * step's parts with events on the launch stream).  events: n = 2 x n_layers
+/* Attention timing, for measurement ([reduces] forward_graphed_replay_to_token_id
+ * splits a decode step's time into sub-phases on request; this times the
+ * step's dominant kernel on the device).  events: n = 2 x n_layers
  * hipEvent_t handles created by the caller with timing enabled, or NULL / n = 0
  * to stop.  Every eager decode step (flags without RRA_GRAPH) enqueued
- * afterwards records events[2l] on its stream just before layer l's split-K
- * flash-decode chunk kernel and events[2l + 1] right after it (before the
- * combine), so after the step hipEventElapsedTime(events[2l], events[2l + 1])
- * is that layer's chunk-kernel time inside the step.  Graph steps record nothing: an event record captured
- * into a graph does not wait for the kernels before it.  Prefill records
+ * afterwards launches layer l's split-K flash-decode chunk kernel with
+ * hipExtLaunchKernel's event pair (events[2l], events[2l + 1]): the runtime
+ * stamps them at that kernel's own start and end, so after the step
+ * hipEventElapsedTime(events[2l], events[2l + 1]) is that layer's chunk-kernel
+ * time inside the step.  Graph steps record nothing.  Prefill records
  * nothing.  The events stay the caller's and must outlive the steps that
  * record them.  Errors: RRA_ENOTINIT for a null model, RRA_EINVAL for a wrong
  * n or a null event. */

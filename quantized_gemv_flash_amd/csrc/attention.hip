@@ -27,6 +27,8 @@
 #include "frag.h"
 #include "rra_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 namespace rra {
@@ -354,17 +356,30 @@ template <int HD, int G>
 rra_status launch_chunk(const float *q, const float *kc, const float *vc, const uint32_t *lens,
                         const uint32_t *slot_seq, float *po, float *pl, int m, int nq, int nkv,
                         int max_len, int chunk, int nc_max, int hs, const QkvIn *qi,
-                        hipStream_t s) {
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int GP = (G + 3) & ~3;
     const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * G +
                                         (qi ? (size_t)(G + 2) * HD : 0));
     const dim3 grid(nc_max, nkv * hs, m);
-    if (qi)
+    const QkvIn qa = qi ? *qi : QkvIn{};
+    // Timed launches (ev0/ev1 set) go through hipExtLaunchKernel, whose event
+    // pair is stamped at the kernel's own start and end.
+    if (ev0 || ev1) {
+        if (qi)
+            hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), (uint32_t)shm, s,
+                                  ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
+                                  max_len, chunk, nc_max, hs, qa);
+        else
+            hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), (uint32_t)shm,
+                                  s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
+                                  max_len, chunk, nc_max, hs, qa);
+    } else if (qi) {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), shm, s, q, kc, vc, lens,
-                           slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, *qi);
-    else
+                           slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
+    } else {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), shm, s, q, kc, vc,
-                           lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, QkvIn{});
+                           lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
+    }
     return check_launch("fd_chunk_kernel");
 }
 
@@ -385,14 +400,14 @@ template <int HD>
 rra_status launch_chunk_hd(int group, const float *q, const float *kc, const float *vc,
                            const uint32_t *lens, const uint32_t *slot_seq, float *po, float *pl,
                            int m, int nq, int nkv, int max_len, int chunk, int nc_max,
-                           const QkvIn *qi, hipStream_t s) {
+                           const QkvIn *qi, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (group < 1 || group > 8) return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", group);
     const int hs = fd_head_split(group, m, nkv, nc_max);
     switch (group / hs) {
 #define RRA_G(gv) \
     case gv:                                                                                    \
         return launch_chunk<HD, gv>(q, kc, vc, lens, slot_seq, po, pl, m, nq, nkv, max_len, chunk, \
-                                    nc_max, hs, qi, s);
+                                    nc_max, hs, qi, s, ev0, ev1);
         RRA_G(1) RRA_G(2) RRA_G(3) RRA_G(4) RRA_G(5) RRA_G(6) RRA_G(7) RRA_G(8)
 #undef RRA_G
     }
@@ -440,7 +455,7 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
                                const FragOut *fo, const uint32_t *slot_seq, bool reduce,
-                               const QkvIn *qi, hipEvent_t chunk_done) {
+                               const QkvIn *qi, hipEvent_t chunk_start, hipEvent_t chunk_stop) {
     if (qi && slot_seq) return fail(RRA_EINVAL, "flash decode: fused QKV input needs no slot map");
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
@@ -449,12 +464,10 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
     float *pl = const_cast<float *>(fd_part_lse(part, m, nq, hd, nc_max));
     if (hd == 128)
         RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                     max_len, chunk, nc_max, qi, s));
+                                     max_len, chunk, nc_max, qi, s, chunk_start, chunk_stop));
     else
         RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                    max_len, chunk, nc_max, qi, s));
-    // measurement hook: an event recorded between the chunk kernel and the combine
-    if (chunk_done) RRA_TRY_HIP(hipEventRecord(chunk_done, s));
+                                    max_len, chunk, nc_max, qi, s, chunk_start, chunk_stop));
     if (!reduce) return RRA_OK;
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,

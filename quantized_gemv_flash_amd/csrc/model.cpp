@@ -424,13 +424,12 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         const GemvPlan &po = M->plan_o[m];
         const bool pro_o = gemv_takes_prologue(L.wo, po, m);
         const FragOut fo_o = image_for(M, L.wo, m);
-        // (eager steps only: an event record captured into a graph does not
-        // wait for the kernels before it, so it would time nothing)
+        // (eager steps only: the timed launch is not one a graph captures)
         const bool timed = !M->attn_events.empty() && !slot_seq && !(flags & RRA_GRAPH);
-        if (timed) RRA_TRY_HIP(hipEventRecord(M->attn_events[2 * l], s));
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
                                     d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq, !pro_o,
                                     fuse_qkv ? &qi : nullptr,
+                                    timed ? M->attn_events[2 * l] : nullptr,
                                     timed ? M->attn_events[2 * l + 1] : nullptr));
         const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
         const GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,

@@ -159,7 +159,7 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
                                const FragOut *fo = nullptr, const uint32_t *slot_seq = nullptr,
                                bool reduce = true, const QkvIn *qi = nullptr,
-                               hipEvent_t chunk_done = nullptr);
+                               hipEvent_t chunk_start = nullptr, hipEvent_t chunk_stop = nullptr);
 // Where rra_flash_decode's partials live in `part` (m sequences, nq heads).
 inline const float *fd_part_lse(const float *part, int m, int nq, int hd, int nc_max) {
     return part + (size_t)m * nq * nc_max * hd;
