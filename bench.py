@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--main-only", action="store_true",
                     help="only the M=32 step and the flash-decode roofline (no M=1, FP8, "
                          "prefill or sweep lines), for profiling")
+    ap.add_argument("--gemv-only", action="store_true",
+                    help="only the gate/up-shaped Q4 GEMV (28672 x 4096) at M=32 and M=1, "
+                         "for counter runs")
     ap.add_argument("--fd-only", action="store_true",
                     help="run only the flash-decode launches (layer-sized synthetic cache at the "
                          "workload's lengths) and a plain copy of known size, for counter runs")
@@ -268,6 +271,27 @@ def fd_only(S, steps, reps):
     return dict(fd_us=sec * 1e6, fd_bytes=nbytes, chunk=chunk, copy_bytes=COPY_BYTES)
 
 
+def gemv_only(n=28672, k=4096, reps=5):
+    """The 8B-shaped gate/up GEMV (Q4, 28672 x 4096) alone: rra_batched_gemv at
+    M = 32, then M = 1, `reps` eager calls each (for counter runs)."""
+    import synth
+    import quantized_gemv_flash_amd as rra
+    data, scale = synth.weight(n, k, "q4", 0.02, 0, "bench_gemv_gu", "cuda")
+    w = rra.device_weight(data, scale, "q4")
+    del data, scale
+    res = {}
+    for m in (32, 1):
+        x = torch.randn((m, k), device="cuda")
+        y = torch.empty((m, n), device="cuda")
+        ws = torch.empty(max(4, rra.rra_batched_gemv_workspace_bytes(w, m)), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(reps):
+            rra.rra_batched_gemv(w, x, y, m, ws)
+        torch.cuda.synchronize()
+        res[f"m{m}_us"] = graph_time(lambda: rra.rra_batched_gemv(w, x, y, m, ws), 20) * 1e6
+    return dict(shape=f"{n}x{k} q4", weight_bytes=n * k * 18 // 32, **res)
+
+
 COPY_BYTES = 1 << 30
 COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         "flash_decode_llama3_8b_m32.md")
@@ -445,6 +469,9 @@ def main():
     if args.only_attention:
         print(json.dumps({"flash_decode": flash_decode_line(), "hbm_ceiling": hbm_ceiling_line()}),
               flush=True)
+        return
+    if args.gemv_only:
+        print(json.dumps({"gemv_only": gemv_only()}), flush=True)
         return
     if args.fd_only:
         print(json.dumps({"fd_only": fd_only(synth.LLAMA3_8B_Q4, args.steps, args.fd_reps)}),
