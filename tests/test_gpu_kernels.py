@@ -211,6 +211,27 @@ def test_flash_decode_full_size_every_chunk():
         assert_close(out, ref, what=f"fd full chunk={chunk}")
 
 
+def test_flash_decode_llama8b_shape_split_cap():
+    # The 8B-shaped decode step's attention launch: 32 sequences, 32 Q / 8 KV
+    # heads, hd 128, a 4160-row cache, where the library's choice is 5 splits of
+    # <= 832 rows (the split cap).  Lengths straddle the split and row-count
+    # boundaries; the library's choice and the 8-split size both must equal
+    # unsplit softmax attention.
+    m, nq, nkv, hd, max_len = 32, 32, 8, 128, 4160
+    banner("fd 8b shape", m, nq, nkv, hd, max_len)
+    assert rra.rra_flash_decode_chunk(m, nkv, max_len, 0) == 832
+    a = synth.Attention("t", m, nq, nkv, hd, max_len, 1, max_len, ())
+    q, kc, vc, _, _, lens = synth.attention_inputs(a, seed=11, device=DEV)
+    edge = [1, 2, 4, 5, 6, 831, 832, 833, 1664, 1665, 4159, 4160]
+    L = edge + [int(v) for v in lens.tolist()[len(edge):]]
+    hq = host(q)
+    ref = np.stack([oracle.attention(hq[s], host(kc[s, :, :L[s]]), host(vc[s, :, :L[s]]), L[s])
+                    for s in range(m)])
+    for chunk in (0, 544):
+        out = _fd_run(q, kc, vc, L, m, nq, nkv, hd, max_len, chunk)
+        assert_close(out, ref, what=f"fd 8b shape chunk={chunk}")
+
+
 # ---------------------------------------------------------------- HBM read probe
 @pytest.mark.parametrize("n,blocks", [(4, 1), (1000, 3), (1 << 20, 37), ((1 << 20) + 12, 256)])
 def test_hbm_read_reads_every_value(n, blocks):
