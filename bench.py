@@ -151,8 +151,9 @@ def flash_decode_roofline(S, dd, lens, reps):
 def flash_decode_in_step(S, dd, m, first_tok, start_pos, steps):
     """Flash decode's chunk kernel timed inside the decode step: the same
     greedy steps from the same start, run eagerly, with a pair of HIP events
-    per layer recorded on the step's stream around each layer's split-K chunk
-    kernel (rra_model_set_attention_events).  Returns (seconds and algorithmic K/V
+    per layer that the runtime stamps at the start and end of that layer's
+    split-K chunk kernel on the step's stream (rra_model_set_attention_events,
+    hipExtLaunchKernel).  Returns (seconds and algorithmic K/V
     bytes summed over every layer of every step, the final positions)."""
     import quantized_gemv_flash_amd as rra
     dev = "cuda"
@@ -500,8 +501,8 @@ def main():
                   for L in lengths for i in range(steps)) / steps
     step_gbs = (wbytes + kv_read) / (sec / steps) / 1e9
 
-    # the dominant kernel, timed inside the same steps (rerun eagerly with
-    # events around it), and rra_flash_decode alone on layer 0's cache
+    # the dominant kernel, timed inside the same steps (rerun eagerly, its
+    # launches carrying an event pair), and rra_flash_decode alone on layer 0's cache
     fd_total, fd_total_bytes, pos_ev = flash_decode_in_step(S, dd, m, first, lengths, steps)
     assert pos_ev == final_pos
     launches = S.n_layers * steps

@@ -211,8 +211,9 @@ struct rra_model {
     GemvPlan plan_qkv[RRA_M_MAX + 1], plan_o[RRA_M_MAX + 1], plan_gu[RRA_M_MAX + 1],
         plan_d[RRA_M_MAX + 1], plan_lm[RRA_M_MAX + 1];
     std::vector<GraphEntry> graphs;
-    // attention timing: a pair of caller-owned events per layer recorded
-    // around that layer's flash decode in eager steps (empty: none)
+    // attention timing: a pair of caller-owned events per layer, stamped at the
+    // start and end of that layer's flash-decode chunk kernel in eager steps
+    // (empty: none)
     std::vector<hipEvent_t> attn_events;
     uint64_t captures = 0, replays = 0;
     uint32_t last_kernels = 0;
