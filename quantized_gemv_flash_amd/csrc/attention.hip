@@ -119,6 +119,26 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float *kn = qs + G * HD, *vn = kn + HD;
     // QF: the new row's local index in this split, or -1
     const int tp = (QF && ok && (int)(p % (uint32_t)nc_max) == c) ? (int)(p / (uint32_t)nc_max) : -1;
+    // QF: the first round's K rows (see the score loop) do not depend on the
+    // query, so they are requested before the QKV partials are summed: one
+    // memory round trip instead of two before the first scores.
+    constexpr int F4 = HD / 32;  // 128-bit loads per lane per row
+    constexpr int UK = 2;        // rows per lane per score round (see below)
+    float4 kv0[UK][F4];
+    if constexpr (QF) {
+        const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
+        const size_t cs0 = slot_seq ? slot_seq[m] : (uint32_t)m;
+        const float *K0 = kc + ((cs0 * nkv + g) * max_len + c) * HD;
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            if (u * 32 + wv * 8 >= n) break;  // wave-uniform: no rows left
+            const int tc = min(u * 32 + wv * 8 + ks0, n - 1);
+#pragma unroll
+            for (int i = 0; i < F4; ++i)
+                kv0[u][i] = ldnt(K0 + (size_t)tc * nc_max * HD + 4 * (e0 + 8 * i));
+        }
+    }
     if constexpr (QF) {
         constexpr int HALF = HD / 2;
         const int nrow = (nq + 2 * nkv) * HD;
@@ -157,8 +177,6 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     // ---- scores: 8 lanes per cached row, UK rows per lane per round.  UK = 2
     // keeps the kernel at 117 VGPRs (4 waves per SIMD; UK = 4 needs 152, 3
     // waves): on MI355X 1-2 % faster at 512-row splits, 16 % at 32-row ones.
-    constexpr int F4 = HD / 32;  // 128-bit loads per lane per row
-    constexpr int UK = 2;
     const int e = lane & 7, ks = lane >> 3;
     const float qscale = 1.0f / sqrtf((float)HD);
     float4 qr[G][F4];
@@ -179,9 +197,14 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             tt[u] = base + u * 32 + wave * 8 + ks;
             if (base + u * 32 + wave * 8 >= n) break;  // wave-uniform: no rows left
             const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
+            if (QF && base == 0) {
 #pragma unroll
-            for (int i = 0; i < F4; ++i)
-                kv[u][i] = ldnt(K + (size_t)tc * rs + 4 * (e + 8 * i));
+                for (int i = 0; i < F4; ++i) kv[u][i] = kv0[u][i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < F4; ++i)
+                    kv[u][i] = ldnt(K + (size_t)tc * rs + 4 * (e + 8 * i));
+            }
             if (QF && tt[u] == tp) {
 #pragma unroll
                 for (int i = 0; i < F4; ++i)
