@@ -134,7 +134,10 @@ rra_status rra_unpack_weight(const rra_weight *tiled, void *data, uint16_t *scal
  * [batched_forward] forward_batched_to_token_ids: batched GEMV kernels read
  * and dequantise every weight block once for all M inputs.
  *   y[i][r] = sum_c W[r][c] * x[i][c]   for i < m, r < n.
- * w   : F32 planar, or a tiled quantised weight (planar -> EINVAL, repack first).
+ * w   : F32 planar, or a tiled quantised weight (planar -> EINVAL, repack first:
+ *       the kernel streams only the tiled layout, whose 16-row x K-tile records
+ *       put each lane's bytes in matrix-core operand order; converting on every
+ *       call would move the weights twice).
  * x   : device fp32 [m][k]; |x| must stay below 65504 for quantised weights (the
  *       activations enter the matrix cores as an fp16 high part plus an fp16
  *       low part).
@@ -296,6 +299,9 @@ typedef struct rra_model rra_model;
 #define RRA_POS_NONE 0xFFFFFFFFu
 
 size_t rra_model_workspace_bytes(const rra_model_desc *d);
+/* The same size under the name the decode-step contract uses: the workspace
+ * rra_model_create needs for descriptor d (0 if d is invalid). */
+size_t rra_decode_workspace_bytes(const rra_model_desc *d);
 
 /* Validates d, lays the workspace out (device, ws_bytes >=
  * rra_model_workspace_bytes(d)), fills its RoPE table on stream s (and waits
@@ -311,7 +317,8 @@ rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t ws_bytes, 
  *          are written there and attention covers rows [0, pos]; RRA_POS_NONE
  *          marks an empty slot (see above); any other position >= max_len
  *          writes nothing, and is reported by rra_model_check.
- * tok    : device uint32 [m], out (and in under RRA_STEP_GATHER).
+ * tok    : device uint32 [m], out (and in under RRA_STEP_GATHER, where an id
+ *          >= vocab gathers a zero row and is reported by rra_model_check).
  * tok_host : host uint32 [m] or NULL.  When non-NULL the call waits for the
  *          stream and copies the ids there (the one sync of the step).
  * logits : device fp32 [m][vocab] or NULL (then an internal buffer is used).
@@ -347,8 +354,17 @@ rra_status rra_decode_step(rra_model *mdl, float *x, uint32_t *pos, uint32_t *to
 rra_status rra_prefill(rra_model *mdl, const uint32_t *tokens, int32_t n_tokens, int32_t seq,
                        uint32_t start, uint32_t *next_tok, float *logits, hipStream_t s);
 
-/* Waits for stream s and reports (and clears) a device-side error: RRA_EINVAL
- * if a step saw a position >= max_len since the last check. */
+/* Waits for stream s and reports (and clears) the device-side error word:
+ * RRA_EINVAL, with a message naming each condition, if a step or prefill
+ * since the last check saw
+ *   - a position >= max_len (other than RRA_POS_NONE): nothing was written
+ *     for that sequence;
+ *   - a gathered token id >= vocab (RRA_STEP_GATHER, rra_prefill): a zero row
+ *     was used as its embedding;
+ *   - an activation entering a quantised GEMV with |x| >= 65504 or NaN: its
+ *     fp16 operand parts are not exact there, so that step's results are not
+ *     to be trusted.
+ * These are detected inside the kernels (no fault, no extra sync per step). */
 rra_status rra_model_check(rra_model *mdl, hipStream_t s);
 
 /* Graph counters ([graph] decode_graph_replays: the evidence that decode ran

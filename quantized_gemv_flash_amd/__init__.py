@@ -81,6 +81,7 @@ def _load() -> ctypes.CDLL:
         "rra_argmax": ([P, P, I, I, P, S, P], I),
         "rra_hbm_read": ([P, S, P, I, P], I),
         "rra_model_workspace_bytes": ([POINTER(rra_model_desc)], S),
+        "rra_decode_workspace_bytes": ([POINTER(rra_model_desc)], S),
         "rra_model_create": ([POINTER(rra_model_desc), P, S, P, POINTER(c_void_p)], I),
         "rra_decode_step": ([P, P, P, P, P, P, I, I, P], I),
         "rra_prefill": ([P, P, I, I, U, P, P, P], I),

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
         const uint32_t lr = ok ? p + 1 : (p == RRA_POS_NONE ? 0u : (uint32_t)max_len);
         if (c == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
             qi.seq_len[m] = lr;
-            if (!ok && p != RRA_POS_NONE) qi.err[0] = 1u;
+            if (!ok && p != RRA_POS_NONE) report_error(qi.err, kErrPos);
         }
         L = (int)min(lr, (uint32_t)max_len);
     } else {
@@ -111,11 +111,15 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     // cache region together, front to back.
     const int n = (L - c + nc_max - 1) / nc_max;  // <= chunk
 
-    extern __shared__ float smem[];
+    // LDS regions, each starting on a 16-byte boundary (they are read with
+    // 128-bit loads): GP and HD are multiples of 4 floats, and the statistics
+    // region is padded to 2 GP floats.
+    static_assert(GP % 4 == 0 && HD % 4 == 0, "16-byte aligned LDS regions");
+    extern __shared__ __attribute__((aligned(16))) float smem[];
     float *sc = smem;                 // [chunk][GP] scores, then probabilities
     float *red = smem + GP * chunk;   // [4 waves][G][HD]
-    float *stat = red + 4 * G * HD;   // [G] max, [G] sum
-    float *qs = stat + 2 * G;         // QF: [G][HD] queries, then [HD] new K, [HD] new V
+    float *stat = red + 4 * G * HD;   // [G] max, [G] sum (2 GP floats)
+    float *qs = stat + 2 * GP;        // QF: [G][HD] queries, then [HD] new K, [HD] new V
     float *kn = qs + G * HD, *vn = kn + HD;
     // QF: the new row's local index in this split, or -1
     const int tp = (QF && ok && (int)(p % (uint32_t)nc_max) == c) ? (int)(p / (uint32_t)nc_max) : -1;
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = so[lane * 8 + e];
-        write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, h * HD + lane * 8, v);
+        frag_out8(fo, m, h * HD + lane * 8, v);
     }
     if (h == nq - 1) {
         const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -381,7 +385,7 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
                         int max_len, int chunk, int nc_max, int hs, const QkvIn *qi,
                         hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int GP = (G + 3) & ~3;
-    const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * G +
+    const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * GP +
                                         (qi ? (size_t)(G + 2) * HD : 0));
     const dim3 grid(nc_max, nkv * hs, m);
     const QkvIn qa = qi ? *qi : QkvIn{};

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restric
             resid8(v, acc[0], split > 0, gm, gv, sq);
             if (split > 0 || x_in != x) store8(x + base, v);
             store8(xg + base, gv);
-            if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, gv);
+            if (fo.img) frag_out8(fo, m, k0, gv);
         } else if (fo.img && k0 < fo.kpad) {
             const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, z);
@@ -120,7 +120,7 @@ __global__ void qkv_post_kernel(const float *__restrict__ part, int split, long 
     if (head == 0 && j == 0) {
         // an empty slot attends to nothing; any other bad position is an error
         seq_len[m] = ok ? p + 1 : (p == RRA_POS_NONE ? 0u : (uint32_t)max_len);
-        if (!ok && p != RRA_POS_NONE) err[0] = 1u;
+        if (!ok && p != RRA_POS_NONE) report_error(err, kErrPos);
     }
 }
 
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float *__restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = swiglu1(acc[0][e], acc[1][e]);
         store8(act + (size_t)m * inter + k0, v);
-        if (fo.img) write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, v);
+        if (fo.img) frag_out8(fo, m, k0, v);
     } else if (fo.img && k0 < fo.kpad) {
         const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, z);
@@ -175,13 +175,14 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float *__restr
 
 __global__ void embed_gather_kernel(const float *__restrict__ embed, const uint32_t *__restrict__ tok,
                                     const uint32_t *__restrict__ pos, float *__restrict__ x, int h,
-                                    int vocab) {
+                                    int vocab, uint32_t *__restrict__ err) {
     const int m = blockIdx.x;
     if (pos[m] == RRA_POS_NONE) return;  // empty slot: x row left as it is
     const uint32_t t = tok[m];
     float *xr = x + (size_t)m * h;
-    if (t >= (uint32_t)vocab) {
+    if (t >= (uint32_t)vocab) {  // no read outside the table; reported
         for (int i = threadIdx.x; i < h; i += blockDim.x) xr[i] = 0.f;
+        if (threadIdx.x == 0) report_error(err, kErrToken);
         return;
     }
     const float *er = embed + (size_t)t * h;
@@ -355,8 +356,9 @@ rra_status launch_prefill_rows(uint32_t *pos, uint32_t *slot_seq, uint32_t base,
 }
 
 rra_status launch_embed_gather(const float *embed, const uint32_t *tok, const uint32_t *pos,
-                               float *x, int m, int h, int vocab, hipStream_t s) {
-    hipLaunchKernelGGL(embed_gather_kernel, dim3(m), dim3(256), 0, s, embed, tok, pos, x, h, vocab);
+                               float *x, int m, int h, int vocab, uint32_t *err, hipStream_t s) {
+    hipLaunchKernelGGL(embed_gather_kernel, dim3(m), dim3(256), 0, s, embed, tok, pos, x, h, vocab,
+                       err);
     return check_launch("embed_gather_kernel");
 }
 

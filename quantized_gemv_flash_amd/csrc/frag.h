@@ -43,49 +43,58 @@ __device__ __forceinline__ int frag_slot(int j, int r, int b) {
 // Splits 8 consecutive fp32 activations (k order) into hi/lo fp16 operands.
 // Contraction is off: the producer's product (gamma x, silu(g) u, ...) must
 // be rounded to fp32 before the subtraction, whichever kernel inlines this,
-// so that every producer of an image writes the same bits.
+// so that every producer of an image writes the same bits.  Returns false if
+// a value has |x| >= 65504 (its fp16 high part may not be finite) or is NaN.
 template <int FMT>
-__device__ __forceinline__ void split8(const float (&v)[8], half8_t &hi, half8_t &lo) {
+__device__ __forceinline__ bool split8(const float (&v)[8], half8_t &hi, half8_t &lo) {
 #pragma clang fp contract(off)
+    bool ok = true;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int src = (FMT == RRA_Q4) ? (e >> 1) + 4 * (e & 1) : e;
         const _Float16 h = (_Float16)v[src];
         hi[e] = h;
         lo[e] = (_Float16)(v[src] - (float)h);
+        ok = ok && __builtin_fabsf(v[src]) < 65504.0f;
     }
+    return ok;
 }
 
 // Writes the group x[m][kk .. kk+8) of one K tile (kk = column within the
 // tile, a multiple of 8) into that tile's image at `tile` (global memory or
 // LDS: one tile is NB * ct * 2 KiB), with `ct` column tiles.
+// Returns split8's range check.
 template <int FMT>
-__device__ __forceinline__ void write_frag8_tile(uint8_t *tile, int ct, int m, int kk,
+__device__ __forceinline__ bool write_frag8_tile(uint8_t *tile, int ct, int m, int kk,
                                                  const float (&v)[8]) {
     const int b = kk >> 5, j = (kk & 31) >> 3;
     half8_t hi, lo;
-    split8<FMT>(v, hi, lo);
+    const bool ok = split8<FMT>(v, hi, lo);
     const int base = ((b * ct + (m >> 4)) * 2) * 1024 + frag_slot<FMT>(j, m & 15, b) * 16;
     *reinterpret_cast<half8_t *>(tile + base) = hi;
     *reinterpret_cast<half8_t *>(tile + base + 1024) = lo;
+    return ok;
 }
 
 // Writes the group x[m][k0 .. k0+8) (k0 % 8 == 0) into an image with `ct`
 // column tiles.
 template <int FMT>
-__device__ __forceinline__ void write_frag8(uint8_t *img, int ct, int m, int k0,
+__device__ __forceinline__ bool write_frag8(uint8_t *img, int ct, int m, int k0,
                                             const float (&v)[8]) {
     constexpr int KT = (FMT == RRA_Q4) ? 128 : 64, NB = KT / 32;
     const int kt = k0 / KT;
-    write_frag8_tile<FMT>(img + (size_t)kt * NB * ct * 2 * 1024, ct, m, k0 - kt * KT, v);
+    return write_frag8_tile<FMT>(img + (size_t)kt * NB * ct * 2 * 1024, ct, m, k0 - kt * KT, v);
 }
 
-__device__ __forceinline__ void write_frag8_fmt(int fmt, uint8_t *img, int ct, int m, int k0,
+__device__ __forceinline__ bool write_frag8_fmt(int fmt, uint8_t *img, int ct, int m, int k0,
                                                 const float (&v)[8]) {
-    if (fmt == RRA_Q4 || fmt == RRA_Q6K)
-        write_frag8<RRA_Q4>(img, ct, m, k0, v);
-    else
-        write_frag8<RRA_Q8>(img, ct, m, k0, v);
+    if (fmt == RRA_Q4 || fmt == RRA_Q6K) return write_frag8<RRA_Q4>(img, ct, m, k0, v);
+    return write_frag8<RRA_Q8>(img, ct, m, k0, v);
+}
+
+// A producer's image write of 8 values of row m, reporting kErrRange.
+__device__ __forceinline__ void frag_out8(const FragOut &fo, int m, int k0, const float (&v)[8]) {
+    if (!write_frag8_fmt(fo.fmt, fo.img, fo.ct, m, k0, v)) report_error(fo.err, kErrRange);
 }
 
 }  // namespace rra

@@ -645,7 +645,7 @@ __device__ __forceinline__ void prologue_swiglu(const GemvPrologue &pro, int M, 
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = k0 < inter ? swiglu1(acc[0][e], acc[1][e]) : 0.f;
-            write_frag8_tile<IMG>(xs[t], 1, m, 8 * kk, v);
+            if (!write_frag8_tile<IMG>(xs[t], 1, m, 8 * kk, v)) report_error(pro.err, kErrRange);
         }
         __syncthreads();  // `red` is reused by the next pass
     }
@@ -676,7 +676,8 @@ __device__ __forceinline__ void prologue_attn(const GemvPrologue &pro, int M, in
                 float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = sw[lane * 8 + e];
-                write_frag8_tile<IMG>(xs[k0 / KT - kt_begin], 1, m, k0 % KT, v);
+                if (!write_frag8_tile<IMG>(xs[k0 / KT - kt_begin], 1, m, k0 % KT, v))
+                    report_error(pro.err, kErrRange);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -740,7 +741,8 @@ __device__ __forceinline__ void prologue_resid(const GemvPrologue &pro, int M, i
                     resid8(xv[v], acc[v], true, gm[v], gv, sq);
                     if (writer) store8(pro.x_out + base[v], xv[v]);
                     if (k0[v] >= k_lo && k0[v] < k_hi)
-                        write_frag8_tile<IMG>(xs[k0[v] / KT - kt_begin], 1, m, k0[v] % KT, gv);
+                        if (!write_frag8_tile<IMG>(xs[k0[v] / KT - kt_begin], 1, m, k0[v] % KT, gv))
+                            report_error(pro.err, kErrRange);
                 }
                 sq = wave_sum(sq);
                 if (lane == 0) parts[pidx] = 0.f + sq;
@@ -1346,3 +1348,4 @@ extern "C" rra_status rra_batched_gemv(const rra_weight *w, const float *x, floa
     RRA_TRY(launch_gemv(*w, p, in, m, part, stride, s));
     return launch_reduce_splits(part, p.split, stride, y, m, (int)w->n, s);
 }
+

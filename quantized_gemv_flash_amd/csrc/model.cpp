@@ -356,7 +356,7 @@ rra_status validate_desc(const rra_model_desc *d) {
 FragOut image_for(const rra_model *M, const rra_weight &w, int m) {
     if (w.fmt == RRA_F32) return FragOut{nullptr, 0, 1, 0};
     const int kt = tile_k(w.fmt);
-    return FragOut{M->img, w.fmt, frag_ct(m), (int)(cdiv(w.k, kt) * kt)};
+    return FragOut{M->img, w.fmt, frag_ct(m), (int)(cdiv(w.k, kt) * kt), M->err};
 }
 const void *gemv_input(const rra_model *M, const rra_weight &w, const float *rows) {
     return w.fmt == RRA_F32 ? static_cast<const void *>(rows) : M->img;
@@ -377,7 +377,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
               I = d.intermediate;
     const int nqkv = (nq + 2 * nkv) * hd;
     if (flags & RRA_STEP_GATHER)
-        RRA_TRY(launch_embed_gather(d.embed, tok_in, pos, x, m, H, d.vocab, s));
+        RRA_TRY(launch_embed_gather(d.embed, tok_in, pos, x, m, H, d.vocab, M->err, s));
     const int np = ss_parts(H);
     const NormIn nrm{M->ss, np, d.rms_eps};
     // RMSNorm is formed inside each consuming GEMV from per-chunk sums of
@@ -399,6 +399,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         r.x_out = other(xc);
         r.gamma = gamma;
         r.eps = d.rms_eps;
+        r.err = M->err;
         xc = r.x_out;
         return r;
     };
@@ -433,8 +434,9 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
                                     timed ? M->attn_events[2 * l] : nullptr,
                                     timed ? M->attn_events[2 * l + 1] : nullptr));
         const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
-        const GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
-                              0, 0, nq, nc_max, d.max_len};
+        GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
+                        0, 0, nq, nc_max, d.max_len};
+        pa.err = M->err;
         RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part_d, (size_t)m * H, s,
                             nullptr, pro_o ? &pa : nullptr));
         // feed-forward block
@@ -454,8 +456,9 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         if (!pro_d)
             RRA_TRY(launch_swiglu_reduce(M->part, pg.split, (size_t)m * 2 * I, M->act, m, I,
                                          image_for(M, L.wd, m), s));
-        const GemvPrologue ps{kProSwiglu, M->part, nullptr, nullptr, (long long)m * 2 * I, pg.split,
-                              I, 0, 0};
+        GemvPrologue ps{kProSwiglu, M->part, nullptr, nullptr, (long long)m * 2 * I, pg.split,
+                        I, 0, 0};
+        ps.err = M->err;
         RRA_TRY(launch_gemv(L.wd, pd, gemv_input(M, L.wd, M->act), m, M->part_d, (size_t)m * H, s,
                             nullptr, pro_d ? &ps : nullptr));
         const bool last = l + 1 == d.n_layers;
@@ -483,6 +486,10 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
 extern "C" size_t rra_model_workspace_bytes(const rra_model_desc *d) {
     if (validate_desc(d) != RRA_OK) return 0;
     return layout_of(*d).total;
+}
+
+extern "C" size_t rra_decode_workspace_bytes(const rra_model_desc *d) {
+    return rra_model_workspace_bytes(d);
 }
 
 extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t ws_bytes,
@@ -575,7 +582,13 @@ extern "C" rra_status rra_model_check(rra_model *M, hipStream_t s) {
     if (flag) {
         RRA_TRY_HIP(hipMemcpyAsync(M->err, &zero, sizeof zero, hipMemcpyHostToDevice, s));
         RRA_TRY_HIP(hipStreamSynchronize(s));
-        return fail(RRA_EINVAL, "a decode step saw a position >= max_len (%d)", M->d.max_len);
+        std::string what;
+        auto add = [&](const std::string &t) { what += (what.empty() ? "" : "; ") + t; };
+        if (flag & kErrPos) add("a position >= max_len (" + std::to_string(M->d.max_len) + ")");
+        if (flag & kErrToken) add("a token id >= vocab (" + std::to_string(M->d.vocab) + ")");
+        if (flag & kErrRange)
+            add("a GEMV input element with |x| >= 65504 or NaN (outside the fp16 operand range)");
+        return fail(RRA_EINVAL, "a step saw %s", what.c_str());
     }
     return RRA_OK;
 }

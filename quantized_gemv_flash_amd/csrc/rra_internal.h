@@ -33,6 +33,15 @@ bool capture_failure_requested();
 // Checks the launch status of the kernel just enqueued.
 rra_status check_launch(const char *what);
 
+// Bits of the model's device error word (read and cleared by rra_model_check).
+constexpr uint32_t kErrPos = 1;    // a position >= max_len (nothing written for it)
+constexpr uint32_t kErrToken = 2;  // a gathered token id >= vocab (a zero row was used)
+constexpr uint32_t kErrRange = 4;  // a GEMV input element with |x| >= 65504 or not a number
+// Sets `bit` in *err (no-op for a null err).  A vector-memory atomic: rare path.
+__device__ __forceinline__ void report_error(uint32_t *err, uint32_t bit) {
+    if (err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -100,6 +109,7 @@ struct GemvPrologue {
     float *x_out = nullptr;        // residual
     const float *gamma = nullptr;  // residual
     float eps = 0.f;               // residual
+    uint32_t *err = nullptr;       // error word: kErrRange when an image input leaves fp16's range
 };
 // Whether a GEMV of this plan can take a prologue (short splits, m <= 4).
 bool gemv_takes_prologue(const rra_weight &w, const GemvPlan &p, int m);
@@ -127,6 +137,7 @@ struct FragOut {
                    // (each pair reads the same image)
     int ct;        // column tiles (1 for m <= 16, 2 otherwise)
     int kpad;      // K rounded up to the K tile; groups in [K, kpad) are zeros
+    uint32_t *err = nullptr;  // error word: kErrRange when an input leaves fp16's range
 };
 
 // ------------------------------------------------------------------ attention
@@ -208,8 +219,9 @@ rra_status launch_prefill_rows(uint32_t *pos, uint32_t *slot_seq, uint32_t base,
 // Streaming read of `bytes` (a multiple of 16) with `blocks` workgroups;
 // sums[b] = the fp32 sum of the values block b read.
 rra_status launch_hbm_read(const void *buf, size_t bytes, float *sums, int blocks, hipStream_t s);
-// x[i] = embed[tok[i]] for every slot whose pos is not RRA_POS_NONE.
+// x[i] = embed[tok[i]] for every slot whose pos is not RRA_POS_NONE; a token
+// id >= vocab gives a zero row and sets kErrToken in *err (err may be null).
 rra_status launch_embed_gather(const float *embed, const uint32_t *tok, const uint32_t *pos,
-                               float *x, int m, int h, int vocab, hipStream_t s);
+                               float *x, int m, int h, int vocab, uint32_t *err, hipStream_t s);
 
 }  // namespace rra

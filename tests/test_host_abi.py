@@ -159,3 +159,9 @@ def test_flash_decode_split_choice(m, nkv, max_len, splits):
     assert c % 32 == 0 and 64 <= c <= 1024
     assert -(-max_len // c) == splits
     assert rra.rra_flash_decode_chunk(m, nkv, max_len, 96) == 96  # an explicit size is kept
+
+
+def test_decode_workspace_bytes_is_the_model_workspace_size():
+    # the decode-step contract's name for rra_model_workspace_bytes
+    assert rra.lib.rra_decode_workspace_bytes(None) == 0
+    assert rra.lib.rra_model_workspace_bytes(None) == 0
