@@ -281,23 +281,31 @@ class DecoderOracle:
         a = swiglu(gu[:, :I], gu[:, I:])
         return x + self._mv(Lw["wd"], H, I, a)
 
-    def step(self, x, pos: Sequence[int], slots: Optional[Sequence[int]] = None):
+    def step(self, x, pos: Sequence[int], slots: Optional[Sequence[int]] = None,
+             head: str = "all"):
         """One decode step for the oracle's sequences.  x [n][H] (embedding rows),
         pos [n], slots [n] (sequence of each row, default row i -> sequence i).
-        Returns dict(hidden [n][H], logits [n][V], tok [n], gap [n])."""
+        Returns dict(hidden [n][H], logits [r][V], tok [r], gap [r]) where the
+        r rows taken through the output norm and LM head are every row
+        (head="all") or only the last one (head="last"; the same values for that
+        row, the others are simply not computed)."""
         x = np.asarray(_np(x), np.float64).reshape(len(pos), self.s.hidden)
         for l in range(len(self.layers)):
             x = self.layer(l, x, pos, slots)
-        u = rmsnorm(x, self.out_gamma, self.s.rms_eps)
+        if head not in ("all", "last"):
+            raise ValueError(f"head={head!r}")
+        xh = x if head == "all" else x[-1:]
+        u = rmsnorm(xh, self.out_gamma, self.s.rms_eps)
         logits = gemv(self.lm_fmt, self.lm_head[0], self.lm_head[1], self.s.vocab, self.s.hidden, u)
         tok, gap = argmax(logits)
         return dict(hidden=x, logits=logits, tok=tok, gap=gap)
 
-    def prefill(self, seq: int, x, start: int):
+    def prefill(self, seq: int, x, start: int, head: str = "all"):
         """Prompt ingestion ([head_dim] tensor_core_attention: causal
         attention over the prompt): the T embedding rows x [T][H] at positions
         start .. start+T-1 of sequence `seq`, every layer over all T rows, row t
         attending to rows [0, start + t] of the sequence.  Returns step()'s dict
-        for the T rows; the last row's tok is the next greedy token."""
+        for the T rows (with head="last", logits of the last row only); the
+        last row's tok is the next greedy token."""
         T = np.asarray(_np(x)).reshape(-1, self.s.hidden).shape[0]
-        return self.step(x, [start + t for t in range(T)], [seq] * T)
+        return self.step(x, [start + t for t in range(T)], [seq] * T, head=head)

@@ -2,6 +2,9 @@
 import numpy as np
 import torch
 
+import synth
+from quantized_gemv_flash_amd.loader import load_decoder
+
 DEV = "cuda"
 
 # Tolerances: fp32 attention and hidden outputs rel 1e-4 / abs 1e-5
@@ -58,3 +61,56 @@ def u32(values, device=DEV):
 
 def banner(*parts):
     print("[case]", *parts, flush=True)
+
+
+class Run:
+    """Fixed-address step buffers (graph-safe) for one device decoder."""
+
+    def __init__(self, S, W, m, max_len, attn_chunk=0):
+        self.S, self.W, self.m = S, W, m
+        self.dd = load_decoder(S, W, m_max=m, max_len=max_len, attn_chunk=attn_chunk)
+        self.x = torch.empty((m, S.hidden), device=DEV)
+        self.pos = torch.zeros(m, dtype=torch.int32, device=DEV)
+        self.tok = torch.zeros(m, dtype=torch.int32, device=DEV)
+        self.logits = torch.empty((m, S.vocab), device=DEV)
+
+    def step(self, tokens, positions, flags=0):
+        self.x.copy_(self.W.embed[torch.as_tensor(tokens, device=DEV)])
+        self.pos.copy_(torch.as_tensor(positions, dtype=torch.int32))
+        ids = self.dd.model.rra_decode_step(self.x, self.pos, self.tok, self.m, flags=flags,
+                                            logits=self.logits, tok_host=True)
+        return ids, self.x.clone(), self.logits.clone()
+
+    def fill_context(self, lengths, orc=None, orc_seqs=()):
+        """Synthetic context rows [0, lengths[s]) of every slot, every layer;
+        the sampled slots orc_seqs also go to the oracle (its sequence i is
+        slot orc_seqs[i])."""
+        orc_seqs = list(orc_seqs)
+        for l in range(self.S.n_layers):
+            for s in range(self.m):
+                k, v = synth.kv_context_rows(self.S, l, s, lengths[s], device=DEV)
+                self.dd.k_caches[l][s, :, :lengths[s]] = k
+                self.dd.v_caches[l][s, :, :lengths[s]] = v
+                if orc is not None and s in orc_seqs:
+                    orc.set_context(l, orc_seqs.index(s), k, v)
+
+
+def elementwise_violations(gpu, ref, rtol=RTOL, atol=ATOL):
+    """(count, worst |d| / bound) of the elements outside the elementwise
+    bound |d| <= atol + rtol |ref| (diagnostic beside a row-scaled check)."""
+    g = np.asarray(host(gpu) if hasattr(gpu, "detach") else gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    ratio = np.abs(g - r) / (atol + rtol * np.abs(r))
+    return int((ratio > 1).sum()), float(ratio.max())
+
+
+def compare_step(gpu, orc_out, what):
+    """A whole decode step against the oracle: the residual stream after the
+    last layer (row-scaled tolerance), logits (abs 1e-3), greedy ids."""
+    ids, hid, logits = gpu
+    assert_close(hid, orc_out["hidden"], what=f"{what} hidden", row_scale=True)
+    assert_close(logits, orc_out["logits"], rtol=0.0, atol=LOGIT_ATOL, what=f"{what} logits")
+    assert_tokens(ids, orc_out["tok"], orc_out["gap"], orc_out["logits"], what=f"{what} tokens")
+    n, worst = elementwise_violations(hid, orc_out["hidden"])
+    print(f"[{what}] hidden: {n} elements past the elementwise bound (worst {worst:.3g}x)",
+          flush=True)

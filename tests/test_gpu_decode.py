@@ -13,7 +13,7 @@ import torch
 import oracle
 import quantized_gemv_flash_amd as rra
 import synth
-from gpu_common import DEV, LOGIT_ATOL, assert_close, assert_tokens, banner, host, u32
+from gpu_common import DEV, LOGIT_ATOL, Run, assert_close, assert_tokens, banner, compare_step, host, u32
 from quantized_gemv_flash_amd.loader import load_decoder
 
 pytestmark = pytest.mark.gpu
@@ -28,41 +28,6 @@ def side_stream():
     with torch.cuda.stream(s):
         yield s
     s.synchronize()
-
-
-class Run:
-    """Fixed-address step buffers (graph-safe) for one device decoder."""
-
-    def __init__(self, S, W, m, max_len, attn_chunk=0):
-        self.S, self.W, self.m = S, W, m
-        self.dd = load_decoder(S, W, m_max=m, max_len=max_len, attn_chunk=attn_chunk)
-        self.x = torch.empty((m, S.hidden), device=DEV)
-        self.pos = torch.zeros(m, dtype=torch.int32, device=DEV)
-        self.tok = torch.zeros(m, dtype=torch.int32, device=DEV)
-        self.logits = torch.empty((m, S.vocab), device=DEV)
-
-    def step(self, tokens, positions, flags=0):
-        self.x.copy_(self.W.embed[torch.as_tensor(tokens, device=DEV)])
-        self.pos.copy_(torch.as_tensor(positions, dtype=torch.int32))
-        ids = self.dd.model.rra_decode_step(self.x, self.pos, self.tok, self.m, flags=flags,
-                                            logits=self.logits, tok_host=True)
-        return ids, self.x.clone(), self.logits.clone()
-
-    def fill_context(self, lengths, orc=None, orc_seqs=()):
-        for l in range(self.S.n_layers):
-            for s in range(self.m):
-                k, v = synth.kv_context_rows(self.S, l, s, lengths[s], device=DEV)
-                self.dd.k_caches[l][s, :, :lengths[s]] = k
-                self.dd.v_caches[l][s, :, :lengths[s]] = v
-                if orc is not None and s in orc_seqs:
-                    orc.set_context(l, orc_seqs.index(s), k, v)
-
-
-def compare_step(gpu, orc_out, what):
-    ids, hid, logits = gpu
-    assert_close(hid, orc_out["hidden"], what=f"{what} hidden", row_scale=True)
-    assert_close(logits, orc_out["logits"], rtol=0.0, atol=LOGIT_ATOL, what=f"{what} logits")
-    assert_tokens(ids, orc_out["tok"], orc_out["gap"], orc_out["logits"], what=f"{what} tokens")
 
 
 # ---------------------------------------------------------------- tiny fp32
@@ -322,89 +287,44 @@ def test_fp8_weights_small_decoder(S):
         tok = o["tok"].tolist()
 
 
-def test_qwen05b_q8_context_then_greedy():
-    # Full 24-layer Q8 decoder at M=1: 8 teacher-forced context steps on random
-    # token ids, then 8 greedy steps (the bench runs the 512-token context).
-    S = synth.QWEN25_05B_Q8
-    banner("decode", S.name)
-    W = synth.decoder_weights(S, seed=0, device=DEV)
-    run = Run(S, W, 1, 64)
-    orc = oracle.DecoderOracle(S, W, 1, 64)
-    ctx = synth.context_tokens(S, 1, 8).tolist()[0]
-    tok = [ctx[0]]
-    for step in range(16):
-        if step < 8:
-            tok = [ctx[step]]
-        gpu = run.step(tok, [step])
-        o = orc.step(host(W.embed[torch.as_tensor(tok, device=DEV)]), [step])
-        compare_step(gpu, o, f"step {step}")
-        tok = o["tok"].tolist()
+# ---------------------------------------------------------------- error word
+def test_token_id_past_vocab_is_reported():
+    # Under RRA_STEP_GATHER an id >= vocab gathers a zero row (no read outside
+    # the table) and is reported by rra_model_check; the other sequence's
+    # results are those of a batch without it.
+    S = SMALL_DECODERS[2]
+    W = synth.decoder_weights(S, seed=3, device=DEV, gamma="random")
+    flags = rra.RRA_STEP_GATHER
+    both, one = Run(S, W, 2, 16), Run(S, W, 1, 16)
+    both.tok.copy_(torch.as_tensor([7, S.vocab + 5], dtype=torch.int32))
+    both.pos.copy_(torch.as_tensor([2, 2], dtype=torch.int32))
+    one.tok.copy_(torch.as_tensor([7], dtype=torch.int32))
+    one.pos.copy_(torch.as_tensor([2], dtype=torch.int32))
+    both.dd.model.rra_decode_step(both.x, both.pos, both.tok, 2, flags=flags, logits=both.logits)
+    one.dd.model.rra_decode_step(one.x, one.pos, one.tok, 1, flags=flags, logits=one.logits)
+    with pytest.raises(rra.RraError, match="token id >= vocab"):
+        both.dd.model.rra_model_check()
+    both.dd.model.rra_model_check()  # cleared
+    one.dd.model.rra_model_check()
+    assert torch.equal(both.logits[0], one.logits[0])
 
 
-def test_qwen15b_q4_batch4_context1024():
-    S = synth.QWEN25_15B_Q4
-    banner("decode", S.name)
-    m = 4
-    W = synth.decoder_weights(S, seed=0, device=DEV)
-    run = Run(S, W, m, S.max_len)
-    orc = oracle.DecoderOracle(S, W, m, S.max_len)
-    lens = synth.context_lengths(S, m)
-    run.fill_context(lens, orc, list(range(m)))
-    tok = synth.first_tokens(S, m).tolist()
-    for step in range(2):
-        pos = [L + step for L in lens]
-        gpu = run.step(tok, pos, flags=rra.RRA_GRAPH)
-        o = orc.step(host(W.embed[torch.as_tensor(tok, device=DEV)]), pos)
-        compare_step(gpu, o, f"step {step}")
-        tok = o["tok"].tolist()
-
-
-@pytest.mark.parametrize("m", [1, 32])
-def test_qwen15b_q4_m_sweep_ends(m):
-    # The 1.5B-shaped Q4 decoder at the ends of its batch sweep, 1024-row
-    # synthetic contexts, one captured graph; the oracle checks up to two
-    # sampled sequences.
-    S = synth.QWEN25_15B_Q4
-    banner("decode", S.name, "m", m)
-    W = synth.decoder_weights(S, seed=0, device=DEV)
-    run = Run(S, W, m, S.max_len)
-    sample = [0] if m == 1 else [5, 31]
-    orc = oracle.DecoderOracle(S, W, len(sample), S.max_len)
-    lens = synth.context_lengths(S, m)
-    run.fill_context(lens, orc, sample)
-    tok = synth.first_tokens(S, m).tolist()
-    for step in range(2):
-        pos = [L + step for L in lens]
-        ids, hid, logits = run.step(tok, pos, flags=rra.RRA_GRAPH)
-        xs = host(W.embed[torch.as_tensor([tok[i] for i in sample], device=DEV)])
-        o = orc.step(xs, [pos[i] for i in sample])
-        compare_step(([ids[i] for i in sample], hid[sample], logits[sample]), o, f"step {step}")
-        new = list(ids)
-        for j, i in enumerate(sample):
-            new[i] = int(o["tok"][j])
-        tok = new
-
-
-def test_llama8b_q4_batch32_graph_sampled_sequences():
-    # Full 32-layer Q4 decoder, 32 sequences at positions in [2048, 4096], one
-    # captured graph; the oracle checks two sampled sequences.
-    S = synth.LLAMA3_8B_Q4
-    banner("decode", S.name)
-    m = S.m
-    W = synth.decoder_weights(S, seed=0, device=DEV)
-    run = Run(S, W, m, S.max_len)
-    sample = [0, 29]
-    orc = oracle.DecoderOracle(S, W, len(sample), S.max_len)
-    lens = synth.context_lengths(S, m)
-    run.fill_context(lens, orc, sample)
-    tok = synth.first_tokens(S, m).tolist()
-    for step in range(2):
-        pos = [L + step for L in lens]
-        ids, hid, logits = run.step(tok, pos, flags=rra.RRA_GRAPH)
-        xs = host(W.embed[torch.as_tensor([tok[i] for i in sample], device=DEV)])
-        o = orc.step(xs, [pos[i] for i in sample])
-        compare_step(([ids[i] for i in sample], hid[sample], logits[sample]), o, f"step {step}")
-        for j, i in enumerate(sample):
-            tok[i] = int(o["tok"][j])
-        tok = [tok[i] if i in sample else ids[i] for i in range(m)]
-    assert run.dd.model.rra_graph_stats()["replays"] == 1
+@pytest.mark.parametrize("bad", [1.0e5, float("nan")])
+def test_activation_outside_fp16_range_is_reported(bad):
+    # The quantised GEMV takes its input as fp16 high + low parts: an input
+    # element with |x| >= 65504 (or NaN) is reported by rra_model_check.
+    S = SMALL_DECODERS[2]
+    W = synth.decoder_weights(S, seed=3, device=DEV, gamma="random")
+    run = Run(S, W, 1, 16)
+    run.step([5], [0])
+    run.dd.model.rra_model_check()
+    run.x.copy_(W.embed[5:6])
+    run.x[0, 17] = bad
+    run.pos.fill_(1)
+    run.dd.model.rra_decode_step(run.x, run.pos, run.tok, 1, logits=run.logits)
+    with pytest.raises(rra.RraError, match="65504"):
+        run.dd.model.rra_model_check()
+    for c in run.dd.k_caches + run.dd.v_caches:  # the bad step wrote row 1
+        c.zero_()
+    run.step([5], [0])
+    run.dd.model.rra_model_check()  # cleared, and a normal step reports nothing
