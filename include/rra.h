@@ -153,6 +153,22 @@ size_t rra_batched_gemv_workspace_bytes(const rra_weight *w, int32_t m);
 rra_status rra_batched_gemv(const rra_weight *w, const float *x, float *y, int32_t m,
                             void *ws, size_t ws_bytes, hipStream_t s);
 
+/* rra_batched_gemv for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation with the same kernels, bitwise the same y, with no
+ * workspace argument.  Its scratch is a library-owned static device array of
+ * RRA_GEMV_STATIC_SCRATCH_BYTES (16 MiB) per GPU, held until the process
+ * ends; the call allocates nothing.  A call whose workspace would exceed that
+ * size (rra_batched_gemv_workspace_bytes(w, m) > RRA_GEMV_STATIC_SCRATCH_BYTES)
+ * returns RRA_EINVAL without launching.  All calls on one GPU share the one
+ * array: calls that may overlap on that GPU (different streams without an
+ * ordering between them, or different threads) race on it and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero.
+ * s: the kernels run on s's device, whose copy of the array is used. */
+#define RRA_GEMV_STATIC_SCRATCH_BYTES (16u << 20)
+rra_status rra_batched_gemv_noalloc(const rra_weight *w, const float *x, float *y, int32_t m,
+                                    hipStream_t s);
+
 /* ---------------------------------------------------------- KV scatter (a5)
  * [head_dim] flash_decoding_attention_into, step 1: this token's K and V rows
  * are written into the caches at the sequence's position.

@@ -28,6 +28,8 @@
 //
 // F32 path: plain wave-per-row FMA GEMV (fp32 weights are only used by small
 // models, where it is latency-bound).
+#include <mutex>
+
 #include "epilogue.h"
 #include "frag.h"
 #include "rra_internal.h"
@@ -1349,3 +1351,78 @@ extern "C" rra_status rra_batched_gemv(const rra_weight *w, const float *x, floa
     return launch_reduce_splits(part, p.split, stride, y, m, (int)w->n, s);
 }
 
+// ------------------------------------------------------------ no-allocation GEMV
+// rra_batched_gemv_noalloc: the same kernels as rra_batched_gemv, with the
+// workspace (activation image + split-K partials) in a file-scope device
+// array instead of caller memory.  Each GPU the library runs on holds its own
+// copy of the array until the process ends; its device address is looked up
+// once per device (hipGetSymbolAddress with that device current) and only
+// that address is handed to kernels -- the array's name in host code is a
+// host-side stand-in, not a device pointer.  Every workspace byte a call reads
+// is written earlier in the same call (the image by x_to_image_kernel, each
+// split plane by its GEMV workgroups), so nothing needs clearing between calls.
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)RRA_GEMV_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of stream s (the null stream:
+// the current device).
+rra_status static_scratch(hipStream_t s, uint8_t **out) {
+    int dev = -1;
+    if (s)
+        RRA_TRY_HIP(hipStreamGetDevice(s, &dev));
+    else
+        RRA_TRY_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(RRA_EINVAL, "rra_batched_gemv_noalloc: device %d not in 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        RRA_TRY_HIP(hipGetDevice(&cur));
+        if (cur != dev) RRA_TRY_HIP(hipSetDevice(dev));
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return fail(RRA_EHIP, "rra_batched_gemv_noalloc: hipGetSymbolAddress(scratch) on "
+                        "device %d failed: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return RRA_OK;
+}
+}  // namespace
+
+extern "C" rra_status rra_batched_gemv_noalloc(const rra_weight *w, const float *x, float *y,
+                                               int32_t m, hipStream_t s) {
+    clear_error();
+    if (!w || !x || !y) return fail(RRA_EINVAL, "rra_batched_gemv_noalloc: null argument");
+    if (m < 1 || m > RRA_M_MAX)
+        return fail(RRA_EINVAL, "rra_batched_gemv_noalloc: m=%d not in 1..32", m);
+    RRA_TRY(validate_weight(w, "rra_batched_gemv_noalloc", true));
+    size_t part_off;
+    const size_t need = gemv_ws_layout(*w, m, &part_off);
+    if (need > kStaticScratchBytes)
+        return fail(RRA_EINVAL, "rra_batched_gemv_noalloc: this call needs %zu workspace bytes; "
+                    "the static scratch holds %zu (use rra_batched_gemv)", need,
+                    kStaticScratchBytes);
+    const GemvPlan p = gemv_plan(*w, m);
+    if (need == 0) return launch_gemv(*w, p, x, m, y, 0, s);  // fp32, one split: no scratch
+    uint8_t *ws = nullptr;
+    RRA_TRY(static_scratch(s, &ws));
+    const void *in = x;
+    if (w->fmt != RRA_F32) {
+        RRA_TRY(launch_x_to_image(x, ws, w->fmt, m, (int)w->k, s));
+        in = ws;
+    }
+    if (p.split == 1) return launch_gemv(*w, p, in, m, y, 0, s);
+    float *part = reinterpret_cast<float *>(ws + part_off);
+    const size_t stride = (size_t)m * (size_t)w->n;
+    RRA_TRY(launch_gemv(*w, p, in, m, part, stride, s));
+    return launch_reduce_splits(part, p.split, stride, y, m, (int)w->n, s);
+}
