@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--m1-steps", type=int, default=256)
     ap.add_argument("--m1-ctx", type=int, default=512, help="context tokens of the M=1 line")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 1.5B-shaped M sweep")
+    ap.add_argument("--only-sweep", default="",
+                    help="run only the 1.5B-shaped M sweep at these batch sizes (e.g. 1,8,32), "
+                         "for profiling")
     ap.add_argument("--main-only", action="store_true",
                     help="only the M=32 step and the flash-decode roofline (no M=1, FP8, "
                          "prefill or sweep lines), for profiling")
@@ -130,20 +133,26 @@ def graph_time(fn, reps):
     return ev0.elapsed_time(ev1) / 1e3 / reps
 
 
-def flash_decode_roofline(S, dd, lens, reps):
+def flash_decode_roofline(S, dd, lens, reps, plan=None):
     """Times rra_flash_decode (split-K chunk kernel + its reduce) alone on
-    layer 0's cache at the step's sequence lengths."""
+    layer 0's cache at the step's sequence lengths, with the step's plan
+    (chunk, head split) when given, else the default rule."""
     import quantized_gemv_flash_amd as rra
     m, nq, nkv, hd = len(lens), S.n_heads, S.n_kv_heads, S.head_dim
     max_len = dd.k_caches[0].shape[2]
     q = torch.randn((m, nq, hd), device="cuda")
     out = torch.empty_like(q)
     seq = torch.as_tensor(lens, dtype=torch.int32, device="cuda")
-    chunk = rra.rra_flash_decode_chunk(m, nkv, max_len, 0)
+    chunk = plan[0] if plan else rra.rra_flash_decode_chunk(m, nkv, max_len, 0)
     ws = torch.empty(rra.rra_flash_decode_workspace_bytes(m, nq, nkv, hd, max_len, 0),
                      dtype=torch.uint8, device="cuda")
-    args = (q, dd.k_caches[0], dd.v_caches[0], seq, out, m, nq, nkv, hd, max_len, 0, ws)
-    sec = graph_time(lambda: rra.rra_flash_decode(*args), reps)
+    if plan and plan[1] > 0:
+        args = (q, dd.k_caches[0], dd.v_caches[0], seq, out, m, nq, nkv, hd, max_len, plan[0],
+                plan[1], ws)
+        sec = graph_time(lambda: rra.rra_flash_decode_ex(*args), reps)
+    else:
+        args = (q, dd.k_caches[0], dd.v_caches[0], seq, out, m, nq, nkv, hd, max_len, chunk, ws)
+        sec = graph_time(lambda: rra.rra_flash_decode(*args), reps)
     kv_bytes = sum(2 * nkv * L * hd * 4 for L in lens)  # K and V rows read once
     return sec, kv_bytes, chunk
 
@@ -198,14 +207,16 @@ def flash_decode_line(reps=20):
     res = dict(workload=f"{a.name}: M={a.m}, {a.n_heads}/{a.n_kv_heads} heads, hd {a.head_dim}, "
                         f"lengths U[1,{a.max_len}], max_len {a.max_len}",
                algorithmic_bytes=kv_bytes, chunks={})
+    tuned = None
     for chunk in list(a.chunks) + [0]:
         ws = torch.empty(rra.rra_flash_decode_workspace_bytes(a.m, a.n_heads, a.n_kv_heads,
                                                               a.head_dim, a.max_len, chunk),
                          dtype=torch.uint8, device="cuda")
         args = (q, kc, vc, seq, out, a.m, a.n_heads, a.n_kv_heads, a.head_dim, a.max_len, chunk, ws)
+        if chunk == 0:  # the autotuner's pick, cached for this shape, used by chunk = 0
+            tuned = rra.rra_flash_decode_tune(*args[:10], ws)
         sec = graph_time(lambda: rra.rra_flash_decode(*args), reps)
-        used = chunk or rra.rra_flash_decode_chunk(a.m, a.n_kv_heads, a.max_len, 0)
-        key = str(chunk) if chunk else f"auto ({used})"
+        key = str(chunk) if chunk else f"tuned (chunk {tuned[0]}, head split {tuned[1]})"
         res["chunks"][key] = dict(us=sec * 1e6, gbs=kv_bytes / sec / 1e9,
                                   hbm_frac=kv_bytes / sec / 1e9 / HBM_PEAK_GBS)
         del ws
@@ -342,7 +353,7 @@ def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps):
                        f"workload ({sec:.1f} s; fp64, {threads} OpenMP threads)")
 
 
-def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32)):
+def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True):
     """The 1.5B-shaped Q4 decoder over a synthetic 1024-row KV context per
     sequence: greedy decode tok/s at each batch size M (one graph per M)."""
     import synth
@@ -355,13 +366,16 @@ def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32)):
     wbytes = dd.weight_bytes()
     out = dict(workload=f"{S.name}: 1024-row context, {steps} greedy steps per M, one graph per step",
                weight_bytes=wbytes)
+    plans = dd.model.rra_model_tune_attention(list(ms), [L + steps // 2 for L in lengths])
+    out["attention_plans"] = {f"m{m}": dict(chunk=plans[m][0], head_split=plans[m][1]) for m in ms}
     for m in ms:
         sec, _, _ = timed_greedy(dd, S, m, first[:m], lengths[:m], steps, 2)
         kv = sum(S.n_layers * 2 * S.n_kv_heads * (L + i + 1) * S.head_dim * 4
                  for L in lengths[:m] for i in range(steps)) / steps
         out[f"m{m}"] = dict(tok_s=m * steps / sec, ms_per_step=1e3 * sec / steps,
                             hbm_frac=(wbytes + kv) * steps / sec / 1e9 / HBM_PEAK_GBS)
-    out["prefill"] = prefill_line(S, dd, 1024)
+    if prefill:
+        out["prefill"] = prefill_line(S, dd, 1024)
     del dd, W
     torch.cuda.empty_cache()
     return out
@@ -443,11 +457,13 @@ def m1_line(steps_m1=256, ctx=512):
         dd.model.rra_decode_step(x, pos, tok, 1, flags=rra.RRA_GRAPH, logits=lg)
     torch.cuda.synchronize()
     first = synth.first_tokens(S, 1).tolist()
+    plan = dd.model.rra_model_tune_attention([1], [ctx + steps_m1 // 2])[1]
     sec, _, _ = timed_greedy(dd, S, 1, first, [ctx], steps_m1, 3)
     wbytes = dd.weight_bytes()
     kv_read = sum(S.n_layers * 2 * S.n_kv_heads * (ctx + i + 1) * S.head_dim * 4
                   for i in range(steps_m1)) / steps_m1
     res = dict(workload=f"{S.name} M=1, {ctx}-token context then {steps_m1} greedy steps, one graph",
+               attention_plan=dict(chunk=plan[0], head_split=plan[1]),
                tok_s=steps_m1 / sec, ms_per_step=1e3 * sec / steps_m1,
                weight_kv_gbs=(wbytes + kv_read) * steps_m1 / sec / 1e9)
     res["hbm_frac"] = res["weight_kv_gbs"] / HBM_PEAK_GBS
@@ -464,6 +480,11 @@ def main():
         sys.exit(2)
     import synth
     import quantized_gemv_flash_amd as rra  # noqa: F401  (fails loudly if not built)
+    if args.only_sweep:
+        ms = tuple(int(v) for v in args.only_sweep.split(","))
+        print(json.dumps({"m_sweep": m_sweep_line(steps=args.steps, ms=ms, prefill=False)}),
+              flush=True)
+        return
     if args.only_m1:
         print(json.dumps({"m1": m1_line(args.m1_steps, args.m1_ctx)}), flush=True)
         return
@@ -488,6 +509,10 @@ def main():
     fill_kv_context(S, dd, lengths)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s; weights {dd.weight_bytes() / 1e9:.3f} GB")
+    t0 = time.time()
+    plan = dd.model.rra_model_tune_attention([m], [L + steps // 2 for L in lengths])[m]
+    log(f"flash-decode plan for M={m}: chunk {plan[0]}, head split {plan[1]} "
+        f"(tuned in {time.time() - t0:.1f}s)")
     first = synth.first_tokens(S, m).tolist()
     sec, final_pos, _ = timed_greedy(dd, S, m, first, lengths, steps, args.warmup)
     tok_s = m * steps / sec
@@ -509,9 +534,9 @@ def main():
     fd_sec, fd_bytes = fd_total / launches, fd_total_bytes / launches  # per launch
     fd_gbs = fd_bytes / fd_sec / 1e9
     fd_alone, alone_bytes, chunk = flash_decode_roofline(S, dd, [p for p in final_pos],
-                                                         args.fd_reps)
-    log(f"flash decode in the step: {fd_sec * 1e6:.1f} us, {fd_gbs:.0f} GB/s (chunk {chunk}); "
-        f"alone {fd_alone * 1e6:.1f} us")
+                                                         args.fd_reps, plan)
+    log(f"flash decode in the step: {fd_sec * 1e6:.1f} us, {fd_gbs:.0f} GB/s (chunk {plan[0]}, "
+        f"head split {plan[1]}); alone {fd_alone * 1e6:.1f} us")
 
     m1 = None
     cpu = None
@@ -561,7 +586,8 @@ def main():
         "weight_kv_hbm_frac": step_gbs / HBM_PEAK_GBS,
         "roofline": {
             "kernel": "fd_chunk_kernel (flash-decode split-K chunks), every layer of the "
-                      f"{steps} timed steps, M={m}, chunk {chunk}",
+                      f"{steps} timed steps, M={m}, chunk {plan[0]}, head split {plan[1]} "
+                      "(autotuned)",
             "bound": "hbm", "achieved": fd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": fd_gbs / HBM_PEAK_GBS, "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-scaled) "

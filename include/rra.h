@@ -195,18 +195,54 @@ rra_status rra_kv_scatter(const float *k_rows, const float *v_rows, float *k_cac
  *       seq_len 0 leaves its out rows untouched.
  * hd in {64, 128}; nq % nkv == 0; nq / nkv <= 8.
  * chunk : at most this many rows per split, a multiple of 32 in [32, 1024],
- *       or 0 to let the library choose from (m, nkv, max_len).  The rows of a
- *       sequence are dealt round-robin to nc = ceil(max_len / chunk) splits
- *       (split c takes rows c, c + nc, ...); the result is the same softmax. 
+ *       or 0 for the autotuned choice: the one rra_flash_decode_tune cached for
+ *       this (m, nq, nkv, hd, max_len), else a default rule of (m, nkv,
+ *       max_len) (rra_flash_decode_chunk).  The rows of a sequence are dealt
+ *       round-robin to nc = ceil(max_len / chunk) splits (split c takes rows
+ *       c, c + nc, ...); the result is the same softmax.
  * ws  : device scratch, ws_bytes >= rra_flash_decode_workspace_bytes(...) with
- *       the same chunk argument. */
+ *       the same chunk argument (for chunk 0: enough for every candidate the
+ *       tuner may pick). */
 size_t rra_flash_decode_workspace_bytes(int32_t m, int32_t nq, int32_t nkv, int32_t hd,
                                         int32_t max_len, int32_t chunk);
+/* The default rule's rows per split (chunk 0), or chunk itself. */
 int32_t rra_flash_decode_chunk(int32_t m, int32_t nkv, int32_t max_len, int32_t chunk);
 rra_status rra_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                             const uint32_t *seq_len, float *out, int32_t m, int32_t nq,
                             int32_t nkv, int32_t hd, int32_t max_len, int32_t chunk,
                             void *ws, size_t ws_bytes, hipStream_t s);
+
+/* Split-size autotuning ([head_dim] flash_decoding_attention_into takes its
+ * chunk size from a fixed constant; here it is chosen by timing on the GPU).
+ * A candidate is (chunk, head_split): rows per split as above, and the number
+ * of workgroups that share a KV head's nq/nkv query heads (a divisor of
+ * nq/nkv; head_split 1 reads every K/V byte once, more shorten each
+ * workgroup's work on small, latency-bound grids at the cost of cache-hit
+ * re-reads).  The result is the same softmax for every candidate.
+ *
+ * rra_flash_decode_candidates: writes up to cap candidates for this shape
+ * into chunks[] and head_splits[] (host; either may be NULL) and returns how
+ * many there are (0 for an invalid shape).  The list depends only on the
+ * arguments. */
+int32_t rra_flash_decode_candidates(int32_t m, int32_t nq, int32_t nkv, int32_t max_len,
+                                    int32_t *chunks, int32_t *head_splits, int32_t cap);
+/* rra_flash_decode with an explicit candidate (chunk 32..1024, a multiple of
+ * 32; head_split dividing nq/nkv); ws as for that chunk. */
+rra_status rra_flash_decode_ex(const float *q, const float *k_cache, const float *v_cache,
+                               const uint32_t *seq_len, float *out, int32_t m, int32_t nq,
+                               int32_t nkv, int32_t hd, int32_t max_len, int32_t chunk,
+                               int32_t head_split, void *ws, size_t ws_bytes, hipStream_t s);
+/* Times every candidate on the caller's inputs (synchronous on s; s must not
+ * be capturing a graph; `out` and ws are overwritten), writes the fastest to
+ * *chunk_out / *head_split_out (host, nullable) and caches it process-wide
+ * for this (m, nq, nkv, hd, max_len): later chunk = 0 calls of that shape use
+ * it, so the choice stays fixed (and graph-safe) once made.  ws_bytes >=
+ * rra_flash_decode_workspace_bytes(..., chunk = 0). */
+rra_status rra_flash_decode_tune(const float *q, const float *k_cache, const float *v_cache,
+                                 const uint32_t *seq_len, float *out, int32_t m, int32_t nq,
+                                 int32_t nkv, int32_t hd, int32_t max_len, void *ws,
+                                 size_t ws_bytes, hipStream_t s, int32_t *chunk_out,
+                                 int32_t *head_split_out);
 
 /* ------------------------------------------------------- step kernels
  * Exposed for per-step parity checks; rra_decode_step uses fused forms. */
@@ -369,6 +405,28 @@ rra_status rra_decode_step(rra_model *mdl, float *x, uint32_t *pos, uint32_t *to
  * (prefill or decode) must be ordered on one stream. */
 rra_status rra_prefill(rra_model *mdl, const uint32_t *tokens, int32_t n_tokens, int32_t seq,
                        uint32_t start, uint32_t *next_tok, float *logits, hipStream_t s);
+
+/* The model's flash-decode plan for steps of m sequences (m in 1..
+ * max(m_max, prefill_rows)): rows per split and head split (0: the default
+ * rule, which may split heads on small grids).  Initially the default rule
+ * of (m, n_kv_heads, max_len), or attn_chunk when the descriptor sets one. */
+rra_status rra_model_attention_plan(const rra_model *mdl, int32_t m, int32_t *chunk,
+                                    int32_t *head_split);
+/* Sets that plan (chunk: a multiple of 32 in 32..1024 whose partials fit the
+ * workspace, which holds every tuner candidate; head_split: 0 or a divisor of
+ * n_heads / n_kv_heads).  A change drops the model's captured graphs (they
+ * hold the old grid); the next RRA_GRAPH step captures again. */
+rra_status rra_model_set_attention_plan(rra_model *mdl, int32_t m, int32_t chunk,
+                                        int32_t head_split);
+/* Autotunes the plan for each batch size in ms[0..n_ms) (host; NULL or n_ms
+ * <= 0: every m in 1..m_max): times every rra_flash_decode_candidates pair on
+ * layer 0's caches with sequence lengths lengths[i] (host [m_max], clamped to
+ * max_len; NULL: max_len) and keeps the fastest, as rra_model_set_attention_plan
+ * would.  Synchronous on s, which must not be capturing; it overwrites the
+ * model's workspace (not the caches), so it must not overlap steps of the
+ * model.  The cache contents do not matter for the timing. */
+rra_status rra_model_tune_attention(rra_model *mdl, const int32_t *ms, int32_t n_ms,
+                                    const uint32_t *lengths, hipStream_t s);
 
 /* Waits for stream s and reports (and clears) the device-side error word:
  * RRA_EINVAL, with a message naming each condition, if a step or prefill

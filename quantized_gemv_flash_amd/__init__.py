@@ -74,6 +74,13 @@ def _load() -> ctypes.CDLL:
         "rra_flash_decode_workspace_bytes": ([I, I, I, I, I, I], S),
         "rra_flash_decode_chunk": ([I, I, I, I], I),
         "rra_flash_decode": ([P, P, P, P, P, I, I, I, I, I, I, P, S, P], I),
+        "rra_flash_decode_candidates": ([I, I, I, I, P, P, I], I),
+        "rra_flash_decode_ex": ([P, P, P, P, P, I, I, I, I, I, I, I, P, S, P], I),
+        "rra_flash_decode_tune": ([P, P, P, P, P, I, I, I, I, I, P, S, P, POINTER(c_int32),
+                                   POINTER(c_int32)], I),
+        "rra_model_attention_plan": ([P, I, POINTER(c_int32), POINTER(c_int32)], I),
+        "rra_model_set_attention_plan": ([P, I, I, I], I),
+        "rra_model_tune_attention": ([P, P, I, P, P], I),
         "rra_rmsnorm": ([P, P, P, I, I, c_float, P], I),
         "rra_rope_table": ([P, I, I, c_double, P], I),
         "rra_rope": ([P, P, P, I, I, I, I, P], I),
@@ -214,6 +221,31 @@ def rra_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len,
         _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def rra_flash_decode_candidates(m, nq, nkv, max_len):
+    """[(chunk, head_split), ...] the tuner tries for this shape."""
+    n = lib.rra_flash_decode_candidates(m, nq, nkv, max_len, None, None, 0)
+    ch, hs = (c_int32 * max(n, 1))(), (c_int32 * max(n, 1))()
+    lib.rra_flash_decode_candidates(m, nq, nkv, max_len, ch, hs, n)
+    return [(ch[i], hs[i]) for i in range(n)]
+
+
+def rra_flash_decode_ex(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len, chunk,
+                        head_split, ws, stream=None):
+    _check("rra_flash_decode_ex", lib.rra_flash_decode_ex(
+        _p(q), _p(k_cache), _p(v_cache), _p(seq_len), _p(out), m, nq, nkv, hd, max_len, chunk,
+        head_split, _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rra_flash_decode_tune(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len, ws,
+                          stream=None):
+    """Times every candidate on these inputs; returns the cached (chunk, head_split)."""
+    c, h = c_int32(), c_int32()
+    _check("rra_flash_decode_tune", lib.rra_flash_decode_tune(
+        _p(q), _p(k_cache), _p(v_cache), _p(seq_len), _p(out), m, nq, nkv, hd, max_len, _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream), ctypes.byref(c), ctypes.byref(h)))
+    return c.value, h.value
+
+
 # ---------------------------------------------------------------- step kernels
 def rra_rmsnorm(x, gamma, out, m, h, eps, stream=None):
     _check("rra_rmsnorm", lib.rra_rmsnorm(_p(x), _p(gamma), _p(out), m, h, eps, _stream(stream)))
@@ -301,6 +333,27 @@ class Model:
         logits when given."""
         _check("rra_prefill", lib.rra_prefill(self.handle, _p(tokens), n_tokens, seq, start,
                                               _p(next_tok), _p(logits), _stream(stream)))
+
+    def rra_model_attention_plan(self, m: int):
+        c, h = c_int32(), c_int32()
+        _check("rra_model_attention_plan", lib.rra_model_attention_plan(
+            self.handle, m, ctypes.byref(c), ctypes.byref(h)))
+        return c.value, h.value
+
+    def rra_model_set_attention_plan(self, m: int, chunk: int, head_split: int):
+        _check("rra_model_set_attention_plan",
+               lib.rra_model_set_attention_plan(self.handle, m, chunk, head_split))
+
+    def rra_model_tune_attention(self, ms=None, lengths=None, stream=None):
+        """Times the flash-decode candidates for each batch size in ms (default:
+        1..m_max) at the given per-slot lengths (default: max_len); returns
+        {m: (chunk, head_split)}."""
+        arr = None if not ms else (c_int32 * len(ms))(*ms)
+        lens = None if lengths is None else (c_uint32 * self.m_max)(
+            *[int(v) for v in lengths] + [0] * (self.m_max - len(lengths)))
+        _check("rra_model_tune_attention", lib.rra_model_tune_attention(
+            self.handle, arr, len(ms) if ms else 0, lens, _stream(stream)))
+        return {m: self.rra_model_attention_plan(m) for m in (ms or range(1, self.m_max + 1))}
 
     def rra_model_check(self, stream=None):
         _check("rra_model_check", lib.rra_model_check(self.handle, _stream(stream)))

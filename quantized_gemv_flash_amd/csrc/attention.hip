@@ -30,6 +30,8 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 namespace rra {
 namespace {
@@ -426,10 +428,13 @@ int fd_head_split(int group, int m, int nkv, int nc_max) {
 template <int HD>
 rra_status launch_chunk_hd(int group, const float *q, const float *kc, const float *vc,
                            const uint32_t *lens, const uint32_t *slot_seq, float *po, float *pl,
-                           int m, int nq, int nkv, int max_len, int chunk, int nc_max,
+                           int m, int nq, int nkv, int max_len, int chunk, int nc_max, int hs_want,
                            const QkvIn *qi, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (group < 1 || group > 8) return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", group);
-    const int hs = fd_head_split(group, m, nkv, nc_max);
+    if (hs_want < 0 || (hs_want > 0 && group % hs_want))
+        return fail(RRA_EINVAL, "flash decode: head split %d does not divide the group size %d",
+                    hs_want, group);
+    const int hs = hs_want > 0 ? hs_want : fd_head_split(group, m, nkv, nc_max);
     switch (group / hs) {
 #define RRA_G(gv) \
     case gv:                                                                                    \
@@ -465,6 +470,109 @@ int fd_choose_chunk(int m, int nkv, int max_len, int chunk) {
     return (int)std::min<int64_t>(1024, std::max<int64_t>(64, (rows + 31) / 32 * 32));
 }
 
+int fd_candidates(int m, int nkv, int group, int max_len, int *chunks, int *head_splits, int cap) {
+    // Splits per (sequence, KV head) to try; each gives the rows per split
+    // (rounded up to a multiple of 32, in 32..1024), duplicates dropped.  A
+    // head split hs > 1 (the group's query heads dealt to hs workgroups) is
+    // tried only on grids of fewer than 1024 workgroups, where the kernel is
+    // latency-bound; no candidate has more than 8192 workgroups.
+    static const int kSplits[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16, 20, 24, 28, 32,
+                                  40, 48, 56, 64, 80, 96, 112, 128, 160, 192, 224, 256};
+    int n = 0, last_chunk = 0;
+    for (int nc : kSplits) {
+        const int64_t rows = (max_len + nc - 1) / nc;
+        const int chunk = (int)((rows + 31) / 32 * 32);
+        if (chunk > 1024) continue;
+        if (chunk < 32 || chunk == last_chunk) continue;
+        last_chunk = chunk;
+        const int64_t base = cdiv(max_len, chunk) * (int64_t)nkv * m;
+        if (base > 8192) break;  // the splits only grow from here
+        for (int hs = 1; hs <= group; ++hs) {
+            if (group % hs) continue;
+            if (hs > 1 && (base >= 1024 || base * hs > 4096)) break;
+            if (n < cap && chunks) chunks[n] = chunk;
+            if (n < cap && head_splits) head_splits[n] = hs;
+            ++n;
+        }
+    }
+    return n;
+}
+
+size_t fd_tuned_floats(int m, int nq, int nkv, int hd, int max_len) {
+    int chunks[256];
+    const int n = std::min(256, fd_candidates(m, nkv, std::max(1, nq / std::max(1, nkv)), max_len,
+                                              chunks, nullptr, 256));
+    size_t best = fd_partials_floats(m, nq, hd, max_len, fd_choose_chunk(m, nkv, max_len, 0));
+    for (int i = 0; i < n; ++i) best = std::max(best, fd_partials_floats(m, nq, hd, max_len, chunks[i]));
+    return best;
+}
+
+rra_status fd_time_candidates(const float *q, const float *k_cache, const float *v_cache,
+                              const uint32_t *seq_len, float *out, int m, int nq, int nkv, int hd,
+                              int max_len, float *part, hipStream_t s, int *chunk_out,
+                              int *hs_out, float *us_out) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    RRA_TRY_HIP(hipStreamIsCapturing(s, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(RRA_EINVAL, "flash-decode tuning: the stream is capturing a graph");
+    int chunks[256], hss[256];
+    const int n = std::min(256, fd_candidates(m, nkv, nq / nkv, max_len, chunks, hss, 256));
+    if (n == 0) return fail(RRA_EINVAL, "flash-decode tuning: no candidate for this shape");
+    hipEvent_t e0, e1;
+    RRA_TRY_HIP(hipEventCreate(&e0));
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return fail(RRA_EHIP, "flash-decode tuning: hipEventCreate failed");
+    }
+    std::vector<float> best(n, 1e30f);
+    rra_status st = RRA_OK;
+    // Two rounds over every candidate (the fastest time of each kept), so a
+    // slow moment of the machine does not decide alone; each time is the
+    // mean of `reps` back-to-back launches (chunk kernel + combine).
+    constexpr int reps = 4;
+    for (int round = 0; round < 2 && st == RRA_OK; ++round) {
+        for (int i = 0; i < n && st == RRA_OK; ++i) {
+            st = launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len,
+                                     chunks[i], part, s, nullptr, nullptr, true, nullptr, nullptr,
+                                     nullptr, hss[i]);
+            if (st != RRA_OK) break;
+            if (hipEventRecord(e0, s) != hipSuccess) { st = fail(RRA_EHIP, "hipEventRecord"); break; }
+            for (int r = 0; r < reps && st == RRA_OK; ++r)
+                st = launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd,
+                                         max_len, chunks[i], part, s, nullptr, nullptr, true,
+                                         nullptr, nullptr, nullptr, hss[i]);
+            if (st != RRA_OK) break;
+            float ms = 0.f;
+            if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+                st = fail(RRA_EHIP, "flash-decode tuning: event timing failed");
+                break;
+            }
+            best[i] = std::min(best[i], 1e3f * ms / reps);
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    RRA_TRY(st);
+    // Among the candidates within 3 % of the fastest, the one with the fewest
+    // workgroups: timed alone, neighbouring split counts differ by less than
+    // the run-to-run noise, and between the decode step's GEMVs the grid with
+    // less per-workgroup work (query loads, softmax, partial writes) and fewer
+    // partials holds up better (MI355X, 8B-shaped layer at M=32: 5 splits
+    // 129 us in the step against 136 us for 7, within 1 % of each other alone).
+    int fastest = 0;
+    for (int i = 1; i < n; ++i)
+        if (best[i] < best[fastest]) fastest = i;
+    auto wgs = [&](int i) { return cdiv(max_len, chunks[i]) * (int64_t)hss[i]; };
+    int bi = fastest;
+    for (int i = 0; i < n; ++i)
+        if (best[i] <= 1.03f * best[fastest] && wgs(i) < wgs(bi)) bi = i;
+    *chunk_out = chunks[bi];
+    *hs_out = hss[bi];
+    if (us_out) *us_out = best[bi];
+    return RRA_OK;
+}
+
 size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk) {
     const int nc_max = (int)cdiv(max_len, chunk);
     return (size_t)m * nq * nc_max * (size_t)(hd + 1);
@@ -482,7 +590,8 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
                                const FragOut *fo, const uint32_t *slot_seq, bool reduce,
-                               const QkvIn *qi, hipEvent_t chunk_start, hipEvent_t chunk_stop) {
+                               const QkvIn *qi, hipEvent_t chunk_start, hipEvent_t chunk_stop,
+                               int head_split) {
     if (qi && slot_seq) return fail(RRA_EINVAL, "flash decode: fused QKV input needs no slot map");
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
@@ -491,10 +600,12 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
     float *pl = const_cast<float *>(fd_part_lse(part, m, nq, hd, nc_max));
     if (hd == 128)
         RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                     max_len, chunk, nc_max, qi, s, chunk_start, chunk_stop));
+                                     max_len, chunk, nc_max, head_split, qi, s, chunk_start,
+                                     chunk_stop));
     else
         RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                    max_len, chunk, nc_max, qi, s, chunk_start, chunk_stop));
+                                    max_len, chunk, nc_max, head_split, qi, s, chunk_start,
+                                    chunk_stop));
     if (!reduce) return RRA_OK;
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,
@@ -535,6 +646,35 @@ static rra_status fd_validate(int32_t m, int32_t nq, int32_t nkv, int32_t hd, in
     return RRA_OK;
 }
 
+// Tuned choices of the standalone flash decode (rra_flash_decode_tune), by
+// shape; a chunk = 0 call of that shape uses it.
+namespace {
+struct FdTuned {
+    int m, nq, nkv, hd, max_len, chunk, hs;
+};
+std::mutex g_fd_mu;
+std::vector<FdTuned> g_fd_tuned;
+
+bool fd_lookup(int m, int nq, int nkv, int hd, int max_len, int *chunk, int *hs) {
+    std::lock_guard<std::mutex> lock(g_fd_mu);
+    for (const FdTuned &t : g_fd_tuned)
+        if (t.m == m && t.nq == nq && t.nkv == nkv && t.hd == hd && t.max_len == max_len) {
+            *chunk = t.chunk;
+            *hs = t.hs;
+            return true;
+        }
+    return false;
+}
+}  // namespace
+
+extern "C" int32_t rra_flash_decode_candidates(int32_t m, int32_t nq, int32_t nkv, int32_t max_len,
+                                               int32_t *chunks, int32_t *head_splits, int32_t cap) {
+    if (m < 1 || m > RRA_M_MAX || nkv < 1 || nq < 1 || nq % nkv || nq / nkv > 8 || max_len < 1 ||
+        cap < 0)
+        return 0;
+    return fd_candidates(m, nkv, nq / nkv, max_len, chunks, head_splits, cap);
+}
+
 extern "C" int32_t rra_flash_decode_chunk(int32_t m, int32_t nkv, int32_t max_len, int32_t chunk) {
     return fd_choose_chunk(m, nkv, max_len, chunk);
 }
@@ -545,8 +685,10 @@ extern "C" size_t rra_flash_decode_workspace_bytes(int32_t m, int32_t nq, int32_
         clear_error();
         return 0;
     }
-    const int c = fd_choose_chunk(m, nkv, max_len, chunk);
-    return sizeof(float) * fd_partials_floats(m, nq, hd, max_len, c);
+    // chunk = 0: enough for the default rule and for every candidate the
+    // tuner may pick, so tuning never outgrows a workspace sized before it
+    if (chunk == 0) return sizeof(float) * fd_tuned_floats(m, nq, nkv, hd, max_len);
+    return sizeof(float) * fd_partials_floats(m, nq, hd, max_len, chunk);
 }
 
 extern "C" rra_status rra_flash_decode(const float *q, const float *k_cache, const float *v_cache,
@@ -561,7 +703,71 @@ extern "C" rra_status rra_flash_decode(const float *q, const float *k_cache, con
     if (ws_bytes < need)
         return fail(RRA_ENOTINIT, "rra_flash_decode: workspace has %zu bytes, needs %zu", ws_bytes,
                     need);
-    const int c = fd_choose_chunk(m, nkv, max_len, chunk);
+    int c = fd_choose_chunk(m, nkv, max_len, chunk), hs = 0;
+    if (chunk == 0) {
+        int tc, th;
+        if (fd_lookup(m, nq, nkv, hd, max_len, &tc, &th)) {
+            c = tc;
+            hs = th;
+        }
+    }
     return launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len, c,
-                               static_cast<float *>(ws), s);
+                               static_cast<float *>(ws), s, nullptr, nullptr, true, nullptr,
+                               nullptr, nullptr, hs);
+}
+
+extern "C" rra_status rra_flash_decode_ex(const float *q, const float *k_cache,
+                                          const float *v_cache, const uint32_t *seq_len,
+                                          float *out, int32_t m, int32_t nq, int32_t nkv,
+                                          int32_t hd, int32_t max_len, int32_t chunk,
+                                          int32_t head_split, void *ws, size_t ws_bytes,
+                                          hipStream_t s) {
+    clear_error();
+    if (!q || !k_cache || !v_cache || !seq_len || !out || !ws)
+        return fail(RRA_EINVAL, "rra_flash_decode_ex: null argument");
+    RRA_TRY(fd_validate(m, nq, nkv, hd, max_len, chunk));
+    if (chunk == 0) return fail(RRA_EINVAL, "rra_flash_decode_ex: chunk must be given (32..1024)");
+    if (head_split < 1 || (nq / nkv) % head_split)
+        return fail(RRA_EINVAL, "rra_flash_decode_ex: head_split=%d does not divide nq/nkv=%d",
+                    head_split, nq / nkv);
+    const size_t need = sizeof(float) * fd_partials_floats(m, nq, hd, max_len, chunk);
+    if (ws_bytes < need)
+        return fail(RRA_ENOTINIT, "rra_flash_decode_ex: workspace has %zu bytes, needs %zu",
+                    ws_bytes, need);
+    return launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len, chunk,
+                               static_cast<float *>(ws), s, nullptr, nullptr, true, nullptr,
+                               nullptr, nullptr, head_split);
+}
+
+extern "C" rra_status rra_flash_decode_tune(const float *q, const float *k_cache,
+                                            const float *v_cache, const uint32_t *seq_len,
+                                            float *out, int32_t m, int32_t nq, int32_t nkv,
+                                            int32_t hd, int32_t max_len, void *ws,
+                                            size_t ws_bytes, hipStream_t s, int32_t *chunk_out,
+                                            int32_t *head_split_out) {
+    clear_error();
+    if (!q || !k_cache || !v_cache || !seq_len || !out || !ws)
+        return fail(RRA_EINVAL, "rra_flash_decode_tune: null argument");
+    RRA_TRY(fd_validate(m, nq, nkv, hd, max_len, 0));
+    const size_t need = rra_flash_decode_workspace_bytes(m, nq, nkv, hd, max_len, 0);
+    if (ws_bytes < need)
+        return fail(RRA_ENOTINIT, "rra_flash_decode_tune: workspace has %zu bytes, needs %zu",
+                    ws_bytes, need);
+    int c = 0, hs = 0;
+    RRA_TRY(fd_time_candidates(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len,
+                               static_cast<float *>(ws), s, &c, &hs, nullptr));
+    {
+        std::lock_guard<std::mutex> lock(g_fd_mu);
+        bool found = false;
+        for (FdTuned &t : g_fd_tuned)
+            if (t.m == m && t.nq == nq && t.nkv == nkv && t.hd == hd && t.max_len == max_len) {
+                t.chunk = c;
+                t.hs = hs;
+                found = true;
+            }
+        if (!found) g_fd_tuned.push_back(FdTuned{m, nq, nkv, hd, max_len, c, hs});
+    }
+    if (chunk_out) *chunk_out = c;
+    if (head_split_out) *head_split_out = hs;
+    return RRA_OK;
 }

@@ -193,6 +193,7 @@ struct rra_model {
     rra_model_desc d{};
     std::vector<rra_layer_desc> layers;
     int chunk[RRA_M_MAX + 1] = {};  // flash-decode rows per split, per batch size
+    int hsplit[RRA_M_MAX + 1] = {}; // flash-decode head split per batch size (0: default rule)
     // workspace carve-up
     float *ss = nullptr, *xg = nullptr, *part = nullptr, *q = nullptr, *attn = nullptr, *act = nullptr;
     float *part_d = nullptr;  // the O and down GEMVs' partials (the next GEMV's prologue may read
@@ -263,10 +264,14 @@ int chunk_for(const rra_model_desc &d, int m) {
     return fd_choose_chunk(m, d.n_kv_heads, d.max_len, d.attn_chunk);
 }
 
+// Flash-decode partials: enough for the plan of every batch size, whether
+// the default rule's, a fixed attn_chunk's or any candidate the tuner may pick.
 size_t fd_floats(const rra_model_desc &d) {
     size_t best = 0;
-    for (int m = 1; m <= rows_of(d); ++m)
+    for (int m = 1; m <= rows_of(d); ++m) {
         best = std::max(best, fd_partials_floats(m, d.n_heads, d.head_dim, d.max_len, chunk_for(d, m)));
+        best = std::max(best, fd_tuned_floats(m, d.n_heads, d.n_kv_heads, d.head_dim, d.max_len));
+    }
     return best;
 }
 
@@ -432,7 +437,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
                                     d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq, !pro_o,
                                     fuse_qkv ? &qi : nullptr,
                                     timed ? M->attn_events[2 * l] : nullptr,
-                                    timed ? M->attn_events[2 * l + 1] : nullptr));
+                                    timed ? M->attn_events[2 * l + 1] : nullptr, M->hsplit[m]));
         const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
         GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
                         0, 0, nq, nc_max, d.max_len};
@@ -734,5 +739,81 @@ extern "C" rra_status rra_prefill(rra_model *M, const uint32_t *tokens, int32_t 
     if (logits)
         RRA_TRY_HIP(hipMemcpyAsync(logits, M->logits + (size_t)(n_last - 1) * d.vocab,
                                    sizeof(float) * d.vocab, hipMemcpyDeviceToDevice, s));
+    return RRA_OK;
+}
+
+// ---------------------------------------------------------------- attention plan
+static void drop_graphs(rra_model *M) {
+    for (GraphEntry &g : M->graphs) (void)hipGraphExecDestroy(g.exec);
+    M->graphs.clear();
+}
+
+extern "C" rra_status rra_model_attention_plan(const rra_model *M, int32_t m, int32_t *chunk,
+                                               int32_t *head_split) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_model_attention_plan: null model");
+    if (m < 1 || m > M->rows)
+        return fail(RRA_EINVAL, "rra_model_attention_plan: m=%d not in 1..%d", m, M->rows);
+    if (chunk) *chunk = M->chunk[m];
+    if (head_split) *head_split = M->hsplit[m];
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_model_set_attention_plan(rra_model *M, int32_t m, int32_t chunk,
+                                                   int32_t head_split) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_model_set_attention_plan: null model");
+    const rra_model_desc &d = M->d;
+    if (m < 1 || m > M->rows)
+        return fail(RRA_EINVAL, "rra_model_set_attention_plan: m=%d not in 1..%d", m, M->rows);
+    if (chunk < 32 || chunk > 1024 || chunk % 32)
+        return fail(RRA_EINVAL, "rra_model_set_attention_plan: chunk=%d (a multiple of 32 in "
+                    "32..1024)", chunk);
+    const int group = d.n_heads / d.n_kv_heads;
+    if (head_split < 0 || (head_split > 0 && group % head_split))
+        return fail(RRA_EINVAL, "rra_model_set_attention_plan: head_split=%d does not divide %d",
+                    head_split, group);
+    if (fd_partials_floats(m, d.n_heads, d.head_dim, d.max_len, chunk) > fd_floats(d))
+        return fail(RRA_EINVAL, "rra_model_set_attention_plan: chunk=%d needs more partials than "
+                    "the workspace holds", chunk);
+    if (M->chunk[m] != chunk || M->hsplit[m] != head_split) {
+        M->chunk[m] = chunk;
+        M->hsplit[m] = head_split;
+        drop_graphs(M);  // captured steps baked the old grid in
+    }
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_model_tune_attention(rra_model *M, const int32_t *ms, int32_t n_ms,
+                                               const uint32_t *lengths, hipStream_t s) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_model_tune_attention: null model");
+    const rra_model_desc &d = M->d;
+    std::vector<int> todo;
+    if (!ms || n_ms <= 0) {
+        for (int m = 1; m <= d.m_max; ++m) todo.push_back(m);
+    } else {
+        for (int i = 0; i < n_ms; ++i) {
+            if (ms[i] < 1 || ms[i] > d.m_max)
+                return fail(RRA_EINVAL, "rra_model_tune_attention: m=%d not in 1..%d", ms[i],
+                            d.m_max);
+            todo.push_back(ms[i]);
+        }
+    }
+    // lengths the steps will see (clamped to max_len); default: full caches
+    std::vector<uint32_t> lens(d.m_max, (uint32_t)d.max_len);
+    if (lengths)
+        for (int i = 0; i < d.m_max; ++i) lens[i] = std::min<uint32_t>(lengths[i], d.max_len);
+    RRA_TRY_HIP(hipMemcpyAsync(M->lens, lens.data(), sizeof(uint32_t) * d.m_max,
+                               hipMemcpyHostToDevice, s));
+    RRA_TRY_HIP(hipMemsetAsync(M->q, 0, sizeof(float) * d.m_max * d.n_heads * d.head_dim, s));
+    const rra_layer_desc &L0 = M->layers[0];
+    for (int m : todo) {
+        int c = 0, hs = 0;
+        RRA_TRY(fd_time_candidates(M->q, L0.k_cache, L0.v_cache, M->lens, M->attn, m, d.n_heads,
+                                   d.n_kv_heads, d.head_dim, d.max_len, M->fd, s, &c, &hs, nullptr));
+        RRA_TRY(rra_model_set_attention_plan(M, m, c, hs));
+    }
+    RRA_TRY_HIP(hipStreamSynchronize(s));
     return RRA_OK;
 }

@@ -143,6 +143,18 @@ struct FragOut {
 // ------------------------------------------------------------------ attention
 int fd_choose_chunk(int m, int nkv, int max_len, int chunk);
 size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk);
+// The (rows per split, head split) pairs the flash-decode tuner tries for m
+// sequences, nkv KV heads of `group` query heads each and max_len cache rows;
+// writes up to cap of them and returns their count.
+int fd_candidates(int m, int nkv, int group, int max_len, int *chunks, int *head_splits, int cap);
+// Partial floats enough for the default rule and every candidate.
+size_t fd_tuned_floats(int m, int nq, int nkv, int hd, int max_len);
+// Times every candidate (chunk kernel + combine, synchronously on s) on the
+// given inputs and returns the fastest (and its time in us if us_out).
+rra_status fd_time_candidates(const float *q, const float *k_cache, const float *v_cache,
+                              const uint32_t *seq_len, float *out, int m, int nq, int nkv, int hd,
+                              int max_len, float *part, hipStream_t s, int *chunk_out,
+                              int *hs_out, float *us_out);
 rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
                              float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
                              int max_len, hipStream_t s);
@@ -162,6 +174,8 @@ struct QkvIn {
     uint32_t *seq_len = nullptr, *err = nullptr;
 };
 // Row i of q attends to cache slot slot_seq[i] (slot i when slot_seq is null).
+// head_split: workgroups per KV head's query-head group (a divisor of
+// nq / nkv), or 0 for the default rule (fd_head_split).
 // reduce = false launches the split kernel only (the O GEMV then combines the
 // partials in its prologue).  With qi, q and seq_len are ignored (the split
 // kernel forms them; slot_seq must be null).
@@ -170,7 +184,8 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
                                const FragOut *fo = nullptr, const uint32_t *slot_seq = nullptr,
                                bool reduce = true, const QkvIn *qi = nullptr,
-                               hipEvent_t chunk_start = nullptr, hipEvent_t chunk_stop = nullptr);
+                               hipEvent_t chunk_start = nullptr, hipEvent_t chunk_stop = nullptr,
+                               int head_split = 0);
 // Where rra_flash_decode's partials live in `part` (m sequences, nq heads).
 inline const float *fd_part_lse(const float *part, int m, int nq, int hd, int nc_max) {
     return part + (size_t)m * nq * nc_max * hd;

@@ -11,11 +11,13 @@ DEV = "cuda"
 # (|gpu - oracle| <= 1e-5 + 1e-4 |oracle| per element); logits abs 1e-3; argmax
 # compared unless the oracle's top-2 gap is below 1e-3.
 #
-# The residual stream after many layers (row_scale=True): an element that is
-# ~0 by cancellation of O(10) terms cannot be held to 1e-4 of its own value by
-# any fp32 computation (a plain fp32 dot over 14336 terms already errs by up to
-# ~6e-5), so there "rel 1e-4" is taken against the row's magnitude:
-# |gpu - oracle| <= 1e-5 + 1e-4 max(|oracle|, rms(oracle row)).
+# One exception, the residual stream of the 8B-shaped decoder after its 32
+# layers (row_scale=True): an element that is ~0 by cancellation of terms of
+# size ~15 cannot be held to 1e-4 of its own value by an fp32 computation
+# (tests/test_tolerance_pins.py shows a plain fp32 residual update of that
+# shape breaking the elementwise bound), so there "rel 1e-4" is taken against
+# the row's magnitude: |gpu - oracle| <= 1e-5 + 1e-4 max(|oracle|, rms(row)).
+# Every other comparison uses the elementwise bound.
 RTOL, ATOL = 1e-4, 1e-5
 LOGIT_ATOL = 1e-3
 TIE_GAP = 1e-3
@@ -104,11 +106,12 @@ def elementwise_violations(gpu, ref, rtol=RTOL, atol=ATOL):
     return int((ratio > 1).sum()), float(ratio.max())
 
 
-def compare_step(gpu, orc_out, what):
+def compare_step(gpu, orc_out, what, row_scale=False):
     """A whole decode step against the oracle: the residual stream after the
-    last layer (row-scaled tolerance), logits (abs 1e-3), greedy ids."""
+    last layer (elementwise, or row-scaled where a test says so), logits
+    (abs 1e-3), greedy ids."""
     ids, hid, logits = gpu
-    assert_close(hid, orc_out["hidden"], what=f"{what} hidden", row_scale=True)
+    assert_close(hid, orc_out["hidden"], what=f"{what} hidden", row_scale=row_scale)
     assert_close(logits, orc_out["logits"], rtol=0.0, atol=LOGIT_ATOL, what=f"{what} logits")
     assert_tokens(ids, orc_out["tok"], orc_out["gap"], orc_out["logits"], what=f"{what} tokens")
     n, worst = elementwise_violations(hid, orc_out["hidden"])

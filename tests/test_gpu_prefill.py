@@ -41,9 +41,9 @@ def prompt(S, n, seed, tag):
 def check_cache(dd, orc, slot, rows, what):
     for l in range(len(dd.k_caches)):
         assert_close(dd.k_caches[l][slot, :, :rows], orc.kc[l][slot, :, :rows],
-                     what=f"{what} layer {l} K", row_scale=True)
+                     what=f"{what} layer {l} K")
         assert_close(dd.v_caches[l][slot, :, :rows], orc.vc[l][slot, :, :rows],
-                     what=f"{what} layer {l} V", row_scale=True)
+                     what=f"{what} layer {l} V")
 
 
 def check_last(next_tok, logits, o, what):
@@ -85,7 +85,7 @@ def test_prefill_matches_oracle_then_decode_takes_over(S):
     logits = torch.empty((m_max, S.vocab), device=DEV)
     ids = dd.model.rra_decode_step(x, pos, tok, m_max, logits=logits, tok_host=True)
     od = orc.step(host(W.embed[nxt])[None], [T], [slot])
-    assert_close(x[slot:slot + 1], od["hidden"], what="decode hidden", row_scale=True)
+    assert_close(x[slot:slot + 1], od["hidden"], what="decode hidden")
     assert_close(logits[slot:slot + 1], od["logits"], rtol=0.0, atol=LOGIT_ATOL, what="decode logits")
     assert_tokens([ids[slot]], od["tok"], od["gap"], od["logits"], what="decode token")
     check_cache(dd, orc, slot, T + 1, "after decode")

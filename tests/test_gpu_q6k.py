@@ -127,7 +127,7 @@ def test_q6k_lm_head_small_decoder():
         ids = dd.model.rra_decode_step(x, pos, tok_d, S.m, flags=rra.RRA_GRAPH, logits=logits,
                                        tok_host=True)
         o = orc.step(host(W.embed[torch.as_tensor(tok, device=DEV)]), p)
-        assert_close(x, o["hidden"], what=f"step {step} hidden", row_scale=True)
+        assert_close(x, o["hidden"], what=f"step {step} hidden")
         assert_close(logits, o["logits"], rtol=0.0, atol=LOGIT_ATOL, what=f"step {step} logits")
         assert_tokens(ids, o["tok"], o["gap"], o["logits"], what=f"step {step} tokens")
         tok = o["tok"].tolist()

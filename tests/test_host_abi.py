@@ -91,8 +91,12 @@ def test_flash_decode_sizes_and_validation():
     # chunk chosen from (m, nkv, max_len); partials are m*nq*nc*(hd+1) floats
     c = rra.rra_flash_decode_chunk(32, 8, 8192, 0)
     assert c % 32 == 0 and 64 <= c <= 1024
-    nc = -(-8192 // c)
+    # chunk 0: enough for the default rule and for every tuner candidate (the
+    # smallest candidate rows per split give the most partials)
+    nc = -(-8192 // min([c] + [ch for ch, _ in rra.rra_flash_decode_candidates(32, 32, 8, 8192)]))
     assert rra.rra_flash_decode_workspace_bytes(32, 32, 8, 128, 8192, 0) == 32 * 32 * nc * 129 * 4
+    assert rra.rra_flash_decode_workspace_bytes(32, 32, 8, 128, 8192, c) == \
+        32 * 32 * -(-8192 // c) * 129 * 4
     assert rra.rra_flash_decode_workspace_bytes(1, 14, 2, 64, 768, 64) == 14 * 12 * 65 * 4
     assert rra.rra_flash_decode_workspace_bytes(1, 12, 8, 128, 64, 0) == 0   # nq % nkv
     assert rra.rra_flash_decode_workspace_bytes(1, 8, 1, 96, 64, 0) == 0     # hd
@@ -165,3 +169,24 @@ def test_decode_workspace_bytes_is_the_model_workspace_size():
     # the decode-step contract's name for rra_model_workspace_bytes
     assert rra.lib.rra_decode_workspace_bytes(None) == 0
     assert rra.lib.rra_model_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("m,nq,nkv,max_len", [(32, 32, 8, 4160), (32, 12, 2, 1152), (1, 14, 2, 768),
+                                              (1, 12, 2, 1152), (32, 32, 8, 8192), (7, 8, 8, 33)])
+def test_flash_decode_candidates_are_valid(m, nq, nkv, max_len):
+    # Every (rows per split, head split) the tuner may try: rows a multiple of
+    # 32 in 32..1024 covering max_len in at most 256 splits, distinct, head
+    # splits dividing the group, grids within 8192 workgroups (head splits only
+    # below 1024), and the list is a pure function of the shape.
+    c = rra.rra_flash_decode_candidates(m, nq, nkv, max_len)
+    assert c and c == rra.rra_flash_decode_candidates(m, nq, nkv, max_len)
+    assert len(set(c)) == len(c)
+    group = nq // nkv
+    for chunk, hs in c:
+        assert chunk % 32 == 0 and 32 <= chunk <= 1024
+        nc = -(-max_len // chunk)
+        assert nc <= 256 and group % hs == 0
+        base = nc * nkv * m
+        assert base <= 8192 and (hs == 1 or base * hs <= 4096 and base < 1024)
+    assert any(hs == 1 for _, hs in c)
+    assert rra.rra_flash_decode_candidates(m, nq + 1, nkv, max_len) == [] or (nq + 1) % nkv == 0
