@@ -94,6 +94,54 @@ def timed_greedy(dd, S, m, first_tok, start_pos, steps, warmup):
     return ev0.elapsed_time(ev1) / 1e3, pos.tolist(), tok.tolist()
 
 
+def host_handoff_line(dd, S, m, first_tok, start_pos, steps):
+    """Host-visible tok/s of the same greedy steps when the host receives every
+    step's ids (wall clock from the first enqueue to the last ids in host
+    memory): blocking (rra_decode_step with tok_host: one stream sync per step)
+    against pipelined (rra_decode_step_async into two pinned buffers with a
+    completion event each, the host reading step t's ids while step t+1 runs)."""
+    import quantized_gemv_flash_amd as rra
+    dev = "cuda"
+    x = torch.empty((m, S.hidden), device=dev)
+    pos = torch.empty(m, dtype=torch.int32, device=dev)
+    tok = torch.empty(m, dtype=torch.int32, device=dev)
+    logits = torch.empty((m, S.vocab), device=dev)
+    flags = rra.RRA_GRAPH | rra.RRA_STEP_GATHER | rra.RRA_STEP_ADVANCE
+    start_t = torch.as_tensor(start_pos, dtype=torch.int32, device=dev)
+    first_t = torch.as_tensor(first_tok, dtype=torch.int32, device=dev)
+
+    def rewind():
+        pos.copy_(start_t)
+        tok.copy_(first_t)
+        torch.cuda.synchronize()
+
+    rewind()
+    dd.model.rra_decode_step(x, pos, tok, m, flags=flags, logits=logits)  # capture
+    rewind()
+    t0 = time.perf_counter()
+    blocking = [dd.model.rra_decode_step(x, pos, tok, m, flags=flags, logits=logits, tok_host=True)
+                for _ in range(steps)]
+    t_block = time.perf_counter() - t0
+    bufs = [torch.empty(m, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    evs = [torch.cuda.Event() for _ in range(2)]
+    for e in evs:
+        e.record()
+    rewind()
+    piped = []
+    t0 = time.perf_counter()
+    for t in range(steps + 1):
+        if t < steps:
+            dd.model.rra_decode_step_async(x, pos, tok, bufs[t % 2], evs[t % 2], m, flags=flags,
+                                           logits=logits)
+        if t >= 1:
+            evs[(t - 1) % 2].synchronize()
+            piped.append(bufs[(t - 1) % 2].tolist())
+    t_pipe = time.perf_counter() - t0
+    assert piped == blocking, "pipelined ids differ from the blocking path's"
+    return dict(steps=steps, blocking_tok_s=m * steps / t_block,
+                pipelined_tok_s=m * steps / t_pipe, ids_equal=True)
+
+
 def build_decoder(S, m, max_len, seed=0):
     import synth
     from quantized_gemv_flash_amd.loader import load_decoder
@@ -467,6 +515,7 @@ def m1_line(steps_m1=256, ctx=512):
                tok_s=steps_m1 / sec, ms_per_step=1e3 * sec / steps_m1,
                weight_kv_gbs=(wbytes + kv_read) * steps_m1 / sec / 1e9)
     res["hbm_frac"] = res["weight_kv_gbs"] / HBM_PEAK_GBS
+    res["host_handoff"] = host_handoff_line(dd, S, 1, first, [ctx], steps_m1)
     del dd, W
     torch.cuda.empty_cache()
     return res
@@ -538,6 +587,8 @@ def main():
     log(f"flash decode in the step: {fd_sec * 1e6:.1f} us, {fd_gbs:.0f} GB/s (chunk {plan[0]}, "
         f"head split {plan[1]}); alone {fd_alone * 1e6:.1f} us")
 
+    handoff = host_handoff_line(dd, S, m, first, lengths, steps)
+    log(f"host hand-off {handoff}")
     m1 = None
     cpu = None
     if not args.no_cpu_baseline:
@@ -582,6 +633,7 @@ def main():
             "max_len": max_len,
         },
         "per_sequence_tok_s": tok_s / m,
+        "host_handoff": handoff,
         "weight_kv_gbs": step_gbs,
         "weight_kv_hbm_frac": step_gbs / HBM_PEAK_GBS,
         "roofline": {

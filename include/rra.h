@@ -381,6 +381,23 @@ rra_status rra_decode_step(rra_model *mdl, float *x, uint32_t *pos, uint32_t *to
                            uint32_t *tok_host, float *logits, int32_t m, int32_t flags,
                            hipStream_t s);
 
+/* The decode step with a non-blocking hand-off of its ids ([reduces]
+ * forward_graphed_replay: a completion event recorded after each replay, to
+ * be queried for pipelining): rra_decode_step (tok_host = NULL), then an
+ * asynchronous copy of the m ids into tok_pinned and a record of `done`, all
+ * on s; returns without waiting.  Once `done` has completed
+ * (hipEventQuery / hipEventSynchronize), tok_pinned holds this step's ids.
+ * tok_pinned: page-locked host memory (hipHostMalloc) [m], else RRA_EINVAL;
+ * done: an event created by the caller.  With RRA_STEP_GATHER |
+ * RRA_STEP_ADVANCE the device feeds the ids back itself, so a caller can
+ * enqueue step t+1 before reading step t's ids: with two tok_pinned buffers
+ * and two events used alternately, the host reads one step's ids while the
+ * next step runs.  A buffer must not be reused until its event has completed
+ * and the host has read it. */
+rra_status rra_decode_step_async(rra_model *mdl, float *x, uint32_t *pos, uint32_t *tok,
+                                 uint32_t *tok_pinned, hipEvent_t done, float *logits, int32_t m,
+                                 int32_t flags, hipStream_t s);
+
 /* Prefill (context ingestion; [head_dim] tensor_core_attention: causal
  * attention of every prompt token to itself and the tokens before it).
  * Runs the n_tokens prompt tokens of cache slot `seq` through the model at

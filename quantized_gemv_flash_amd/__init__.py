@@ -92,6 +92,7 @@ def _load() -> ctypes.CDLL:
         "rra_decode_workspace_bytes": ([POINTER(rra_model_desc)], S),
         "rra_model_create": ([POINTER(rra_model_desc), P, S, P, POINTER(c_void_p)], I),
         "rra_decode_step": ([P, P, P, P, P, P, I, I, P], I),
+        "rra_decode_step_async": ([P, P, P, P, P, P, P, I, I, P], I),
         "rra_prefill": ([P, P, I, I, U, P, P, P], I),
         "rra_model_check": ([P, P], I),
         "rra_graph_stats": ([P, POINTER(c_uint64), POINTER(c_uint64), POINTER(c_uint32)], I),
@@ -325,6 +326,16 @@ class Model:
         _check("rra_decode_step", lib.rra_decode_step(
             self.handle, _p(x), _p(pos), _p(tok), host, _p(logits), m, flags, _stream(stream)))
         return list(host) if host is not None else None
+
+    def rra_decode_step_async(self, x, pos, tok, tok_pinned, done, m: int, flags: int = 0,
+                              logits=None, stream=None):
+        """One decode step whose ids are copied asynchronously into tok_pinned (a
+        pinned host int32 tensor of >= m elements) and followed by a record of
+        `done` (a torch.cuda.Event already recorded once, so that it exists);
+        returns at once.  Read tok_pinned after done.synchronize()/query()."""
+        _check("rra_decode_step_async", lib.rra_decode_step_async(
+            self.handle, _p(x), _p(pos), _p(tok), c_void_p(tok_pinned.data_ptr()),
+            c_void_p(done.cuda_event), _p(logits), m, flags, _stream(stream)))
 
     def rra_prefill(self, tokens, n_tokens: int, seq: int, start: int, next_tok=None,
                     logits=None, stream=None):

@@ -688,6 +688,26 @@ extern "C" rra_status rra_decode_step(rra_model *M, float *x, uint32_t *pos, uin
     return RRA_OK;
 }
 
+extern "C" rra_status rra_decode_step_async(rra_model *M, float *x, uint32_t *pos, uint32_t *tok,
+                                            uint32_t *tok_pinned, hipEvent_t done, float *logits,
+                                            int32_t m, int32_t flags, hipStream_t s) {
+    clear_error();
+    if (!tok_pinned || !done)
+        return fail(RRA_EINVAL, "rra_decode_step_async: null tok_pinned or done event");
+    // The copy must not block the host: only page-locked host memory is taken.
+    hipPointerAttribute_t attr{};
+    const hipError_t pe = hipPointerGetAttributes(&attr, tok_pinned);
+    if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(RRA_EINVAL, "rra_decode_step_async: tok_pinned is not page-locked host memory "
+                    "(allocate it with hipHostMalloc)");
+    }
+    RRA_TRY(rra_decode_step(M, x, pos, tok, nullptr, logits, m, flags, s));
+    RRA_TRY_HIP(hipMemcpyAsync(tok_pinned, tok, sizeof(uint32_t) * m, hipMemcpyDeviceToHost, s));
+    RRA_TRY_HIP(hipEventRecord(done, s));
+    return RRA_OK;
+}
+
 extern "C" rra_status rra_model_set_attention_events(rra_model *M, void *const *events,
                                                      int32_t n) {
     clear_error();

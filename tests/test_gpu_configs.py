@@ -213,3 +213,53 @@ def test_fused_qkv_flash_decode_many_rounds():
                 assert_close(run.dd.k_caches[l][i, :, pos[i]], orc.kc[l][i, :, pos[i]],
                              what=f"layer {l} seq {i} new K row")
         tok = o["tok"].tolist()
+
+
+# ---------------------------------------------------------------- non-blocking hand-off
+def test_async_handoff_double_buffered_matches_blocking_and_oracle():
+    # rra_decode_step_async: the device loop (gather + advance in the graph)
+    # with each step's ids copied to one of two pinned host buffers and a
+    # completion event per buffer; the host reads step t's ids while step t+1
+    # runs.  The ids equal the blocking path's (tok_host: one sync per step)
+    # bit for bit, and follow the oracle's greedy stream until its first
+    # near-tie.
+    S = SMALL_Q4
+    banner("async hand-off", S.name)
+    m, steps = 2, S.max_len - 4
+    W = synth.decoder_weights(S, seed=10, device=DEV, gamma="random")
+    first = synth.first_tokens(S, m, seed=10).tolist()
+    start = [0, 3]
+    flags = rra.RRA_GRAPH | rra.RRA_STEP_GATHER | rra.RRA_STEP_ADVANCE
+    blocking, piped = Run(S, W, m, S.max_len), Run(S, W, m, S.max_len)
+    for r in (blocking, piped):
+        r.tok.copy_(torch.as_tensor(first, dtype=torch.int32))
+        r.pos.copy_(torch.as_tensor(start, dtype=torch.int32))
+    want = [blocking.dd.model.rra_decode_step(blocking.x, blocking.pos, blocking.tok, m,
+                                              flags=flags, logits=blocking.logits, tok_host=True)
+            for _ in range(steps)]
+    bufs = [torch.full((m,), -1, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    evs = [torch.cuda.Event() for _ in range(2)]
+    for e in evs:
+        e.record()  # creates the event
+    got = []
+    for t in range(steps + 1):
+        if t < steps:
+            piped.dd.model.rra_decode_step_async(piped.x, piped.pos, piped.tok, bufs[t % 2],
+                                                 evs[t % 2], m, flags=flags, logits=piped.logits)
+        if t >= 1:  # step t-1's ids, read while step t runs
+            evs[(t - 1) % 2].synchronize()
+            got.append(bufs[(t - 1) % 2].tolist())
+    assert got == want
+    orc = oracle.DecoderOracle(S, W, m, S.max_len)
+    tok = list(first)
+    for step in range(steps):
+        o = orc.step(embed_rows(W, tok), [p + step for p in start])
+        if (o["gap"] < TIE_GAP).any():
+            break
+        assert got[step] == o["tok"].tolist(), f"step {step}"
+        tok = got[step]
+    assert step >= 4
+    with pytest.raises(rra.RraError, match="page-locked"):
+        piped.dd.model.rra_decode_step_async(piped.x, piped.pos, piped.tok,
+                                             torch.zeros(m, dtype=torch.int32), evs[0], m,
+                                             flags=flags, logits=piped.logits)
