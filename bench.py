@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--m1-steps", type=int, default=256)
     ap.add_argument("--m1-ctx", type=int, default=512, help="context tokens of the M=1 line")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 1.5B-shaped M sweep")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the 8B-shaped 512-token prefill line, for profiling")
     ap.add_argument("--only-sweep", default="",
                     help="run only the 1.5B-shaped M sweep at these batch sizes (e.g. 1,8,32), "
                          "for profiling")
@@ -431,8 +433,9 @@ def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True):
 
 def prefill_line(S, dd, n_tokens, reps=3):
     """Prompt ingestion (rra_prefill) of n_tokens seeded token ids into cache
-    slot 0 from position 0, in chunks of the model's prefill rows (its m_max):
-    each chunk is one pass of the decode step over all layers."""
+    slot 0 from position 0, in chunks of the model's prefill rows: per chunk
+    and layer, GEMMs that read the weights once for the chunk's rows and a
+    matrix-core causal attention."""
     import synth
     toks = synth.uniform_int((n_tokens,), 0, S.vocab - 1, 0, "bench_prompt").to("cuda", torch.int32)
     nt = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -445,7 +448,7 @@ def prefill_line(S, dd, n_tokens, reps=3):
     ev1.record()
     torch.cuda.synchronize()
     sec = ev0.elapsed_time(ev1) / 1e3 / reps
-    return dict(tokens=n_tokens, rows_per_chunk=dd.model.m_max, ms=1e3 * sec,
+    return dict(tokens=n_tokens, rows_per_chunk=dd.model.prefill_rows, ms=1e3 * sec,
                 tok_s=n_tokens / sec)
 
 
@@ -529,6 +532,11 @@ def main():
         sys.exit(2)
     import synth
     import quantized_gemv_flash_amd as rra  # noqa: F401  (fails loudly if not built)
+    if args.only_prefill:
+        S = synth.LLAMA3_8B_Q4
+        W, dd = build_decoder(S, 1, 1024)
+        print(json.dumps({"prefill": prefill_line(S, dd, 512)}), flush=True)
+        return
     if args.only_sweep:
         ms = tuple(int(v) for v in args.only_sweep.split(","))
         print(json.dumps({"m_sweep": m_sweep_line(steps=args.steps, ms=ms, prefill=False)}),

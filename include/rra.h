@@ -320,7 +320,7 @@ typedef struct rra_model_desc {
     const float *embed;            /* device [vocab][hidden] fp32, or NULL (needed for RRA_STEP_GATHER) */
     int32_t attn_chunk;            /* flash-decode rows per split; 0 = chosen by the library
                                       for each step from its m, nkv and max_len */
-    int32_t prefill_rows;          /* prompt tokens per rra_prefill chunk, 0..32 (0 = m_max);
+    int32_t prefill_rows;          /* prompt tokens per rra_prefill chunk, 0..128 (0 = 128);
                                       the workspace holds max(m_max, prefill_rows) rows */
 } rra_model_desc;
 
@@ -404,11 +404,16 @@ rra_status rra_decode_step_async(rra_model *mdl, float *x, uint32_t *pos, uint32
  * positions start .. start + n_tokens - 1: every layer's K/V rows for those
  * positions are written into the slot's cache, each token attending to cache
  * rows [0, its position] -- the rows already there (a context ingested
- * earlier) and the prompt tokens before it -- exactly as the same tokens fed
- * one at a time through rra_decode_step would.  The tokens go through in
- * chunks of prefill_rows: each chunk is one decode-step pass whose rows are
- * the chunk's tokens (weights streamed once per chunk), all mapped to slot
- * `seq`.  Only the last token reaches the output norm, LM head and argmax.
+ * earlier) and the prompt tokens before it -- the same result as the tokens
+ * fed one at a time through rra_decode_step (up to rounding).  The tokens go
+ * through in chunks of prefill_rows: per chunk and layer, each weight matrix
+ * is streamed once for all of the chunk's rows (a matrix-core GEMM with the
+ * decode GEMV's exact-integer weights and fp16 high + low activation parts),
+ * RoPE is applied and the chunk's K/V rows are written into the slot, and a
+ * matrix-core causal attention (scores and outputs from fp16 high + low
+ * operand parts, fp32 accumulation, online softmax) takes each row over the
+ * slot's rows up to its position.  Only the last token reaches the output
+ * norm, LM head and argmax.
  * tokens   : device uint32 [n_tokens], ids < vocab.
  * seq      : cache slot in [0, m_max).  Other slots are not touched.
  * start    : position of tokens[0]; start + n_tokens <= max_len (else

@@ -318,6 +318,7 @@ class Model:
         _check("rra_model_create", lib.rra_model_create(
             ctypes.byref(self.desc), _p(self.ws), nbytes, _stream(stream), ctypes.byref(self.handle)))
         self.vocab, self.hidden, self.m_max = vocab, hidden, m_max
+        self.prefill_rows = prefill_rows or 128
 
     def rra_decode_step(self, x, pos, tok, m: int, flags: int = 0, logits=None,
                         tok_host: bool = False, stream=None):

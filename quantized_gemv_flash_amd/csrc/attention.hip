@@ -343,6 +343,193 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
         part_lse[((size_t)m * nq + hq0 + tid) * nc_max + c] = stat[tid] + logf(stat[G + tid]);
 }
 
+// Causal attention of a prompt chunk on the matrix cores ([head_dim]
+// tensor_core_attention: the prompt's tokens attend to themselves and the
+// tokens before them, on the tensor cores).  Rows t < n of q sit at
+// positions start + t of one cache slot; row t attends to the slot's cache
+// rows [0, start + t] (the chunk's own K/V rows are already in the cache).
+//
+// One workgroup per (16-row query tile, KV head), one wave per query head of
+// the KV head's group, so the K/V rows are staged once for the G heads.  Keys
+// go in blocks of 32, staged in LDS as fp16 high and low parts laid out as
+// matrix-core B operands.  S = Q K^T and O += P V use
+// v_mfma_f32_16x16x32_f16 with the fp32 operands split x = hi + lo
+// (hi = fp16(x), lo = fp16(x - hi)): each product is taken as hi*hi + hi*lo
+// + lo*hi, which drops only the lo*lo term (relative size 2^-22), so the
+// scores and outputs carry fp32-level error.  The softmax is the online
+// (running max and sum) form: per block, m' = max(m, max s), l' = l e^(m-m')
+// + sum e^(s-m'), O' = O e^(m-m') + P V with P = e^(s-m'); at the end O / l.
+// Keys past a row's position get probability 0; cache rows past the chunk's
+// last position are staged as zeros (never read as data).
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <int HD, int G>
+__global__ __launch_bounds__(64 * G) void prefill_attn_kernel(
+    const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
+    float *__restrict__ out, int n, int nq, int nkv, int max_len, uint32_t start, FragOut fo) {
+    constexpr int DS = HD / 32;  // 32-wide d steps of S = Q K^T
+    constexpr int DT = HD / 16;  // 16-wide d tiles of O
+    constexpr int OS = HD + 4;   // row stride of the output staging (floats)
+    __shared__ __attribute__((aligned(16))) uint8_t kf[2 * DS * 2 * 1024];  // [key tile][d step][part]
+    __shared__ __attribute__((aligned(16))) uint8_t vf[DT * 2 * 1024];      // [d tile][part]
+    __shared__ __attribute__((aligned(16))) _Float16 pf[G][2][16 * 32];     // [wave][part][row][key]
+    __shared__ __attribute__((aligned(16))) float of[G][16 * OS];           // [wave][row][d]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int g = blockIdx.y, h = g * G + wave, t0 = blockIdx.x * 16;
+    const int j = lane >> 4, r = lane & 15;
+    const int last = n - 1;
+    const float *K = kc + (size_t)g * max_len * HD;
+    const float *V = vc + (size_t)g * max_len * HD;
+
+    // Q as A operands: lane (j, r) holds row t0 + r, d = 32 s + 8 j + [0, 8)
+    half8_t qh[DS], ql[DS];
+    {
+        const float *qr = q + ((size_t)min(t0 + r, last) * nq + h) * HD;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+            float v[8];
+            load8(qr + 32 * s + 8 * j, v);
+            split_exact(v, qh[s], ql[s]);
+        }
+    }
+    const float scale = 1.0f / sqrtf((float)HD);
+    float mrow[4], lrow[4];
+    floatx4 o[DT];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        mrow[i] = -INFINITY;
+        lrow[i] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // this lane's rows of S and O: 4 j + i; their positions
+    int prow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) prow[i] = (int)start + min(t0 + 4 * j + i, last);
+    const int kvalid = (int)start + last;            // last cache row holding data
+    const int kmax = (int)start + min(t0 + 15, last);  // last key any row of the tile reads
+    for (int k0 = 0; k0 <= kmax; k0 += 32) {
+        // ---- stage keys k0 .. k0 + 31: K as B[32 d][16 keys] per (key tile, d step),
+        // V as B[32 keys][16 d] per d tile; hi and lo parts
+        for (int it = threadIdx.x; it < 32 * (HD / 8); it += 64 * G) {
+            const int key = it / (HD / 8), dg = it % (HD / 8);  // (key, group of 8 d)
+            float v[8];
+            if (k0 + key <= kvalid) {
+                load8(K + (size_t)(k0 + key) * HD + 8 * dg, v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            }
+            half8_t hi, lo;
+            split_exact(v, hi, lo);
+            const int nt = key >> 4, s = dg >> 2, jj = dg & 3, slot = 16 * jj + (key & 15);
+            uint8_t *f = kf + ((nt * DS + s) * 2) * 1024 + slot * 16;
+            *reinterpret_cast<half8_t *>(f) = hi;
+            *reinterpret_cast<half8_t *>(f + 1024) = lo;
+        }
+        for (int it = threadIdx.x; it < HD * 4; it += 64 * G) {
+            const int d = it % HD, kg = it / HD;  // (d, group of 8 keys)
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = k0 + 8 * kg + e;
+                v[e] = key <= kvalid ? V[(size_t)key * HD + d] : 0.f;
+            }
+            half8_t hi, lo;
+            split_exact(v, hi, lo);
+            const int t = d >> 4, slot = 16 * kg + (d & 15);
+            uint8_t *f = vf + (t * 2) * 1024 + slot * 16;
+            *reinterpret_cast<half8_t *>(f) = hi;
+            *reinterpret_cast<half8_t *>(f + 1024) = lo;
+        }
+        __syncthreads();
+        // ---- S = Q K^T for the two key tiles
+        floatx4 sc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            floatx4 a = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < DS; ++s) {
+                const uint8_t *f = kf + ((nt * DS + s) * 2) * 1024 + lane * 16;
+                const half8_t kh = *reinterpret_cast<const half8_t *>(f);
+                const half8_t kl = *reinterpret_cast<const half8_t *>(f + 1024);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[s], kh, a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[s], kl, a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[s], kh, a, 0, 0, 0);
+            }
+            sc[nt] = a;
+        }
+        // ---- online softmax over this block (rows 4 j + i, keys k0 + 16 nt + r)
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float s0 = sc[0][i] * scale, s1 = sc[1][i] * scale;
+            if (k0 + r > prow[i]) s0 = -INFINITY;
+            if (k0 + 16 + r > prow[i]) s1 = -INFINITY;
+            float mx = fmaxf(s0, s1);
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            const float mn = fmaxf(mrow[i], mx);  // finite: key 0 is in every row's range
+            alpha[i] = expf(mrow[i] - mn);
+            const float p0 = expf(s0 - mn), p1 = expf(s1 - mn);
+            float ps = p0 + p1;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off, 64);
+            lrow[i] = lrow[i] * alpha[i] + ps;
+            mrow[i] = mn;
+            // P into [row][key] fp16 hi / lo (the A operand layout is read back below)
+            const int row = 4 * j + i;
+            const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+            pf[wave][0][row * 32 + r] = h0;
+            pf[wave][1][row * 32 + r] = (_Float16)(p0 - (float)h0);
+            pf[wave][0][row * 32 + 16 + r] = h1;
+            pf[wave][1][row * 32 + 16 + r] = (_Float16)(p1 - (float)h1);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // ---- O = O alpha + P V: A = P[16 rows][32 keys] (lane (j, r): row r, keys 8 j ..)
+        const half8_t ph = *reinterpret_cast<const half8_t *>(&pf[wave][0][r * 32 + 8 * j]);
+        const half8_t pl = *reinterpret_cast<const half8_t *>(&pf[wave][1][r * 32 + 8 * j]);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            floatx4 a = o[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] *= alpha[i];
+            const uint8_t *f = vf + (t * 2) * 1024 + lane * 16;
+            const half8_t vh = *reinterpret_cast<const half8_t *>(f);
+            const half8_t vl = *reinterpret_cast<const half8_t *>(f + 1024);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vh, a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vl, a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vh, a, 0, 0, 0);
+            o[t] = a;
+        }
+        __syncthreads();  // kf, vf and pf are refilled next block
+    }
+    // ---- O / l, through LDS, to the output rows and the O GEMV's image
+    float *os = of[wave];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) os[(4 * j + i) * OS + 16 * t + r] = o[t][i] / lrow[i];
+    __builtin_amdgcn_wave_barrier();
+    for (int it = lane; it < 16 * (HD / 8); it += 64) {
+        const int row = it / (HD / 8), dg = it % (HD / 8), t = t0 + row;
+        if (t > last) continue;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = os[row * OS + 8 * dg + e];
+        store8(out + ((size_t)t * nq + h) * HD + 8 * dg, v);
+        if (fo.img) frag_out8(fo, t, h * HD + 8 * dg, v);
+    }
+    if (fo.img && h == nq - 1) {  // zeros for the groups in [nq hd, kpad) of the tile's rows
+        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int it = lane; it < 16 * 64; it += 64) {
+            const int row = it / 64, k = nq * HD + 8 * (it % 64), t = t0 + row;
+            if (t <= last && k < fo.kpad) frag_out8(fo, t, k, z);
+        }
+    }
+}
+
 // out[m][h] = sum_c w_c o~_c / sum_c w_c, w_c = e^(lse_c - max lse), over the
 // chunks that hold rows of the sequence.  One wave per (head, sequence).  With
 // fo.img set, the head's slice is also written as the output projection's
@@ -576,6 +763,25 @@ rra_status fd_time_candidates(const float *q, const float *k_cache, const float 
 size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk) {
     const int nc_max = (int)cdiv(max_len, chunk);
     return (size_t)m * nq * nc_max * (size_t)(hd + 1);
+}
+
+rra_status launch_prefill_attention(const float *q, const float *k_slot, const float *v_slot,
+                                    float *out, int n, int nq, int nkv, int hd, int max_len,
+                                    uint32_t start, const FragOut *fo, hipStream_t s) {
+    const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
+    const int group = nq / nkv;
+    const dim3 grid((unsigned)cdiv(n, 16), (unsigned)nkv);
+#define RRA_PA(HDV, GV)                                                                       \
+    if (hd == HDV && group == GV) {                                                          \
+        hipLaunchKernelGGL((prefill_attn_kernel<HDV, GV>), grid, dim3(64 * GV), 0, s, q, k_slot, \
+                           v_slot, out, n, nq, nkv, max_len, start, img);                    \
+        return check_launch("prefill_attn_kernel");                                          \
+    }
+    RRA_PA(64, 1) RRA_PA(64, 2) RRA_PA(64, 3) RRA_PA(64, 4) RRA_PA(64, 5) RRA_PA(64, 6)
+    RRA_PA(64, 7) RRA_PA(64, 8) RRA_PA(128, 1) RRA_PA(128, 2) RRA_PA(128, 3) RRA_PA(128, 4)
+    RRA_PA(128, 5) RRA_PA(128, 6) RRA_PA(128, 7) RRA_PA(128, 8)
+#undef RRA_PA
+    return fail(RRA_EINVAL, "prefill attention: hd=%d, group %d", hd, group);
 }
 
 rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,

@@ -15,8 +15,10 @@
 //   elements kt*KT + 32b + 8j + [0..8) in the order the weight operand uses
 //   (Q4 and Q6K: 0,4,1,5,2,6,3,7; Q8 and FP8: 0..7).
 //
-// CT = 1 for M <= 16 sequences, 2 for M <= 32.  Elements k >= K up to the K
-// tile end must be written as zeros.
+// CT = 1 for M <= 16 rows, 2 for M <= 32 (decode steps), 4 for M <= 64 and
+// 8 for M <= 128 (prompt chunks).  Elements k >= K up to the K tile end must
+// be written as zeros; columns past M hold anything (their outputs are never
+// stored, and a column's products never mix with another column's).
 #pragma once
 
 #include "rra_internal.h"
@@ -25,7 +27,7 @@ namespace rra {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-inline int frag_ct(int m) { return m > 16 ? 2 : 1; }
+inline int frag_ct(int m) { return m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8; }
 inline size_t frag_image_bytes(int fmt, int ct, int64_t k) {
     return (size_t)cdiv(k, tile_k(fmt)) * (size_t)tile_blocks(fmt) * (size_t)ct * 2 * 1024;
 }
@@ -63,6 +65,17 @@ __device__ __forceinline__ bool split8(const float (&v)[8], half8_t &hi, half8_t
 // Writes the group x[m][kk .. kk+8) of one K tile (kk = column within the
 // tile, a multiple of 8) into that tile's image at `tile` (global memory or
 // LDS: one tile is NB * ct * 2 KiB), with `ct` column tiles.
+// x = hi + lo for 8 values in their own order (hi = fp16(x), lo = fp16(x - hi)).
+__device__ __forceinline__ void split_exact(const float (&v)[8], half8_t &hi, half8_t &lo) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const _Float16 h = (_Float16)v[e];
+        hi[e] = h;
+        lo[e] = (_Float16)(v[e] - (float)h);
+    }
+}
+
 // Returns split8's range check.
 template <int FMT>
 __device__ __forceinline__ bool write_frag8_tile(uint8_t *tile, int ct, int m, int kk,

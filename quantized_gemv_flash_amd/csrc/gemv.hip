@@ -390,6 +390,41 @@ struct QGemv {
                 for (int e = 0; e < 8; ++e) sh[r][e] = h0[e];
             }
         }
+        if constexpr (CT > 2) {
+            // prompt chunks (4 or 8 column tiles): the dequantised block stays
+            // in registers while the column tiles' B fragments are read one
+            // tile at a time (all of them at once would take 16 CT registers)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                asm volatile("" ::: "memory");
+                half8_t a[RPW];
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                    const uint4 qv = q.q[r];
+                    a[r] = (FMT == RRA_Q4)    ? dequant_q4(u32_at(qv, b))
+                           : (FMT == RRA_FP8) ? dequant_fp8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1))
+                                              : dequant_q8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1));
+                }
+                const int slot = frag_slot<F::IMG>(lane >> 4, lane & 15, b);
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc) {
+                    const half8_t bh = *reinterpret_cast<const half8_t *>(
+                        xs + ((b * CT + cc) * 2 + 0) * 1024 + slot * 16);
+                    const half8_t bl = *reinterpret_cast<const half8_t *>(
+                        xs + ((b * CT + cc) * 2 + 1) * 1024 + slot * 16);
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r) {
+                        floatx4 tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            a[r], bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[r], bl, tt, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[r][cc][i] = fmaf((float)sh[r][i * NB + b], tt[i], acc[r][cc][i]);
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             // one block's B fragments at a time (a compiler memory barrier keeps
@@ -1132,10 +1167,14 @@ rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, 
     const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
     dim3 grid((unsigned)cdiv(n_rt, NW * RPW), (unsigned)p.split), block(64 * NW);
     const auto *wd = static_cast<const uint8_t *>(w.data);
-    if (p.kt_per_split <= 2)
-        return launch_short<FMT, CT, RPW, NW, 2>(w, p, img, m, out, stride, nrm, pro, grid, nkt, s);
-    if (p.kt_per_split <= 4)
-        return launch_short<FMT, CT, RPW, NW, 4>(w, p, img, m, out, stride, nrm, pro, grid, nkt, s);
+    if constexpr (CT <= 2) {  // prompt chunks hold too large an image for NT K tiles in LDS
+        if (p.kt_per_split <= 2)
+            return launch_short<FMT, CT, RPW, NW, 2>(w, p, img, m, out, stride, nrm, pro, grid,
+                                                     nkt, s);
+        if (p.kt_per_split <= 4)
+            return launch_short<FMT, CT, RPW, NW, 4>(w, p, img, m, out, stride, nrm, pro, grid,
+                                                     nkt, s);
+    }
     if (pro.kind != kProNone) return fail(RRA_EINVAL, "gemv prologue: split longer than 4 tiles");
     hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW, NW>), grid, block, 0, s, wd, img, out, m,
                        (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
@@ -1149,6 +1188,11 @@ rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img
     if (m <= 16) {
         if (p.rpw >= 2) return launch_q<FMT, 1, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
         return launch_q<FMT, 1, 1, 4>(w, p, img, m, out, stride, nrm, pro, s);
+    }
+    if (m > 32) {  // prompt chunks: one row tile per wave, 8 waves share the image
+        if (pro.kind != kProNone) return fail(RRA_EINVAL, "gemv prologue: m > 16");
+        if (m <= 64) return launch_q<FMT, 4, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
+        return launch_q<FMT, 8, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
     }
     if (p.nw == 8) {
         if (p.rpw >= 2) return launch_q<FMT, 2, 2, 8>(w, p, img, m, out, stride, nrm, pro, s);
@@ -1190,6 +1234,25 @@ GemvPlan gemv_plan(const rra_weight &w, int m) {
     return p;
 }
 
+GemvPlan gemm_plan(const rra_weight &w) {
+    GemvPlan p;
+    if (w.fmt == RRA_F32) return p;
+    const int n_rt = (int)cdiv(w.n, 16);
+    const int nkt = (int)cdiv(w.k, tile_k(w.fmt));
+    // Prompt chunks (up to 128 rows): compute-bound, one 8-wave workgroup of
+    // 128 output rows per compute unit at a time (its double-buffered image
+    // takes most of the LDS); K splits until the grid covers the chip, each
+    // split at least two K tiles long.
+    p.rpw = 1;
+    p.nw = 8;
+    const int n_rb = (int)cdiv(n_rt, 8);
+    int split = 1;
+    while (split * n_rb < 256 && split * 4 <= nkt) split *= 2;
+    p.kt_per_split = (int)cdiv(nkt, split);
+    p.split = (int)cdiv(nkt, p.kt_per_split);
+    return p;
+}
+
 bool gemv_takes_prologue(const rra_weight &w, const GemvPlan &p, int m) {
     return is_quantised(w.fmt) && m <= 4 && p.kt_per_split <= 4;
 }
@@ -1210,11 +1273,19 @@ rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, in
     if (pr.kind != kProNone && !gemv_takes_prologue(w, p, m))
         return fail(RRA_EINVAL, "gemv prologue: needs a quantised weight, m <= 4 and short splits");
     if (w.fmt == RRA_F32) {
+        // up to 32 rows per launch (one accumulator per row in registers)
         dim3 grid((unsigned)cdiv(w.n, 4));
-        hipLaunchKernelGGL(gemv_f32_kernel, grid, dim3(256), 0, s,
-                           static_cast<const float *>(w.data), static_cast<const float *>(x), out,
-                           m, (int)w.n, (int)w.k, n);
-        return check_launch("gemv_f32_kernel");
+        for (int m0 = 0; m0 < m; m0 += RRA_M_MAX) {
+            NormIn ns = n;
+            if (ns.ss) ns.ss += (size_t)m0 * ns.nparts;
+            hipLaunchKernelGGL(gemv_f32_kernel, grid, dim3(256), 0, s,
+                               static_cast<const float *>(w.data),
+                               static_cast<const float *>(x) + (size_t)m0 * w.k,
+                               out + (size_t)m0 * w.n, std::min(RRA_M_MAX, m - m0), (int)w.n,
+                               (int)w.k, ns);
+            RRA_TRY(check_launch("gemv_f32_kernel"));
+        }
+        return RRA_OK;
     }
     const auto *img = static_cast<const uint8_t *>(x);
     if (w.fmt == RRA_Q4) return launch_fmt<RRA_Q4>(w, p, img, m, out, stride, n, pr, s);

@@ -208,9 +208,10 @@ struct rra_model {
     // prefill chunk state: x rows, positions, cache slot per row, token ids
     float *px = nullptr;
     uint32_t *ppos = nullptr, *pseq = nullptr, *ptok = nullptr;
-    // per-M plans (index m)
+    // per-M plans (index m), and the plans of prompt chunks of more than 32 rows
     GemvPlan plan_qkv[RRA_M_MAX + 1], plan_o[RRA_M_MAX + 1], plan_gu[RRA_M_MAX + 1],
         plan_d[RRA_M_MAX + 1], plan_lm[RRA_M_MAX + 1];
+    GemvPlan pf_qkv, pf_o, pf_gu, pf_d;
     std::vector<GraphEntry> graphs;
     // attention timing: a pair of caller-owned events per layer, stamped at the
     // start and end of that layer's flash-decode chunk kernel in eager steps
@@ -228,7 +229,7 @@ struct Layout {
 };
 
 // Rows of one prefill chunk, and the batch rows the workspace is laid out for.
-int prefill_rows_of(const rra_model_desc &d) { return d.prefill_rows ? d.prefill_rows : d.m_max; }
+int prefill_rows_of(const rra_model_desc &d) { return d.prefill_rows ? d.prefill_rows : kPrefillMax; }
 int rows_of(const rra_model_desc &d) { return std::max(d.m_max, prefill_rows_of(d)); }
 
 // Largest activation image any GEMV of the model reads (0 if all are fp32).
@@ -247,12 +248,17 @@ size_t image_bytes(const rra_model_desc &d) {
     return best;
 }
 
+// The GEMV plan of a step or prompt chunk of m rows.
+GemvPlan plan_for(const rra_weight &w, int m) {
+    return m > RRA_M_MAX ? gemm_plan(w) : gemv_plan(w, m);
+}
+
 size_t part_floats(const rra_model_desc &d, const rra_layer_desc &l) {
     size_t best = 0;
     for (int m = 1; m <= rows_of(d); ++m) {
         const rra_weight *ws[4] = {&l.wqkv, &l.wo, &l.wgu, &l.wd};
         for (const rra_weight *w : ws) {
-            const GemvPlan p = gemv_plan(*w, m);
+            const GemvPlan p = plan_for(*w, m);
             best = std::max(best, (size_t)p.split * (size_t)m * (size_t)w->n);
         }
     }
@@ -268,7 +274,7 @@ int chunk_for(const rra_model_desc &d, int m) {
 // the default rule's, a fixed attn_chunk's or any candidate the tuner may pick.
 size_t fd_floats(const rra_model_desc &d) {
     size_t best = 0;
-    for (int m = 1; m <= rows_of(d); ++m) {
+    for (int m = 1; m <= d.m_max; ++m) {
         best = std::max(best, fd_partials_floats(m, d.n_heads, d.head_dim, d.max_len, chunk_for(d, m)));
         best = std::max(best, fd_tuned_floats(m, d.n_heads, d.n_kv_heads, d.head_dim, d.max_len));
     }
@@ -296,8 +302,8 @@ Layout layout_of(const rra_model_desc &d) {
     L.attn = take(4 * M * d.n_heads * d.head_dim);
     L.act = take(4 * M * d.intermediate);
     L.fd = take(4 * fd_floats(d));
-    L.logits = take(4 * M * (size_t)d.vocab);
-    L.argmax = take(argmax_ws_bytes((int)M, d.vocab));
+    L.logits = take(4 * (size_t)d.m_max * (size_t)d.vocab);  // prompts: the last row only
+    L.argmax = take(argmax_ws_bytes(d.m_max, d.vocab));
     L.rope = take(4 * (size_t)d.max_len * d.head_dim);
     L.err = take(256);
     L.px = take(4 * M * d.hidden);
@@ -329,8 +335,9 @@ rra_status validate_desc(const rra_model_desc *d) {
         return fail(RRA_EINVAL, "model: hidden and intermediate must be multiples of 8");
     if (d->m_max < 1 || d->m_max > RRA_M_MAX)
         return fail(RRA_EINVAL, "model: m_max=%d not in 1..32", d->m_max);
-    if (d->prefill_rows < 0 || d->prefill_rows > RRA_M_MAX)
-        return fail(RRA_EINVAL, "model: prefill_rows=%d not in 0..32", d->prefill_rows);
+    if (d->prefill_rows < 0 || d->prefill_rows > kPrefillMax)
+        return fail(RRA_EINVAL, "model: prefill_rows=%d not in 0..%d", d->prefill_rows,
+                    kPrefillMax);
     if (d->max_len < 1) return fail(RRA_EINVAL, "model: max_len=%d", d->max_len);
     if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.0))
         return fail(RRA_EINVAL, "model: bad rms_eps or rope_theta");
@@ -372,11 +379,9 @@ constexpr int kStepNoHead = 1 << 16;
 
 // Every launch of one decode step, in stream order.  Row i reads token
 // tok_in[i] (under RRA_STEP_GATHER), sits at position pos[i] and uses cache
-// slot slot_seq[i] (slot i when slot_seq is null); the greedy ids go to
-// tok_out.
+// slot i; the greedy ids go to tok_out.
 rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *tok_in,
-                        uint32_t *tok_out, float *logits, int m, int flags,
-                        const uint32_t *slot_seq, hipStream_t s) {
+                        uint32_t *tok_out, float *logits, int m, int flags, hipStream_t s) {
     const rra_model_desc &d = M->d;
     const int H = d.hidden, nq = d.n_heads, nkv = d.n_kv_heads, hd = d.head_dim,
               I = d.intermediate;
@@ -418,13 +423,13 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
                             s, rq ? nullptr : &nrm, rq ? &pr_qkv : nullptr));
         // At small m flash decode takes the QKV partials itself (QkvIn: sum,
         // RoPE, the new K/V row, seq_len); otherwise qkv_post does that work.
-        const bool fuse_qkv = m <= 4 && !slot_seq;
+        const bool fuse_qkv = m <= 4;
         const QkvIn qi{M->part, pq.split, (long long)m * nqkv, pos, M->rope,
                        L.k_cache, L.v_cache, M->lens, M->err};
         if (!fuse_qkv)
             RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
                                     L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd,
-                                    d.max_len, slot_seq, s));
+                                    d.max_len, nullptr, s));
         // At small m the O GEMV combines the attention partials itself and the
         // down GEMV forms SwiGLU itself (GemvPrologue): two launches fewer per
         // layer, with the same arithmetic as the kernels they stand in for.
@@ -432,9 +437,9 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         const bool pro_o = gemv_takes_prologue(L.wo, po, m);
         const FragOut fo_o = image_for(M, L.wo, m);
         // (eager steps only: the timed launch is not one a graph captures)
-        const bool timed = !M->attn_events.empty() && !slot_seq && !(flags & RRA_GRAPH);
+        const bool timed = !M->attn_events.empty() && !(flags & RRA_GRAPH);
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
-                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, slot_seq, !pro_o,
+                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, nullptr, !pro_o,
                                     fuse_qkv ? &qi : nullptr,
                                     timed ? M->attn_events[2 * l] : nullptr,
                                     timed ? M->attn_events[2 * l + 1] : nullptr, M->hsplit[m]));
@@ -486,6 +491,67 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
                          (flags & RRA_STEP_ADVANCE) != 0, s);
 }
 
+// One prompt chunk: tokens[0..n) of cache slot `seq` at positions start ..
+// start + n - 1 ([head_dim] tensor_core_attention: the prompt's causal
+// attention on the tensor cores).  Every layer: the QKV GEMM for all n rows
+// (weights read once), RoPE and the K/V rows written to the slot's cache, the
+// matrix-core causal attention, the O GEMM, the residual step, the gate/up
+// GEMM, SwiGLU, the down GEMM.  With `last`, the last row alone then goes
+// through the output norm, the LM head and the argmax (ids to M->ptok[0],
+// logits to M->logits row 0).
+rra_status enqueue_prompt_chunk(rra_model *M, const uint32_t *tokens, int n, int seq,
+                                uint32_t start, bool last, hipStream_t s) {
+    const rra_model_desc &d = M->d;
+    const int H = d.hidden, nq = d.n_heads, nkv = d.n_kv_heads, hd = d.head_dim,
+              I = d.intermediate;
+    const int nqkv = (nq + 2 * nkv) * hd;
+    auto plan = [&](const GemvPlan &pf, const GemvPlan *pm) { return n > RRA_M_MAX ? pf : pm[n]; };
+    float *x = M->px;
+    RRA_TRY(launch_prefill_rows(M->ppos, M->pseq, start, (uint32_t)seq, n, s));
+    RRA_TRY(launch_embed_gather(d.embed, tokens, M->ppos, x, n, H, d.vocab, M->err, s));
+    const NormIn nrm{M->ss, ss_parts(H), d.rms_eps};
+    const size_t slot = (size_t)seq * nkv * d.max_len * hd;
+    RRA_TRY(launch_residual_ss(nullptr, 0, 0, x, x, M->ss, M->layers[0].attn_gamma, M->xg, n, H,
+                               image_for(M, M->layers[0].wqkv, n), s));
+    for (int l = 0; l < d.n_layers; ++l) {
+        const rra_layer_desc &L = M->layers[l];
+        const GemvPlan pq = plan(M->pf_qkv, M->plan_qkv), po = plan(M->pf_o, M->plan_o),
+                       pg = plan(M->pf_gu, M->plan_gu), pd = plan(M->pf_d, M->plan_d);
+        RRA_TRY(launch_gemv(L.wqkv, pq, gemv_input(M, L.wqkv, M->xg), n, M->part, (size_t)n * nqkv,
+                            s, &nrm));
+        RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)n * nqkv, M->ppos, M->rope, M->q,
+                                L.k_cache, L.v_cache, M->lens, M->err, n, nq, nkv, hd, d.max_len,
+                                M->pseq, s));
+        const FragOut fo_o = image_for(M, L.wo, n);
+        RRA_TRY(launch_prefill_attention(M->q, L.k_cache + slot, L.v_cache + slot, M->attn, n, nq,
+                                         nkv, hd, d.max_len, start, &fo_o, s));
+        RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), n, M->part_d, (size_t)n * H,
+                            s));
+        RRA_TRY(launch_residual_ss(M->part_d, po.split, (size_t)n * H, x, x, M->ss, L.ffn_gamma,
+                                   M->xg, n, H, image_for(M, L.wgu, n), s));
+        RRA_TRY(launch_gemv(L.wgu, pg, gemv_input(M, L.wgu, M->xg), n, M->part, (size_t)n * 2 * I,
+                            s, &nrm));
+        RRA_TRY(launch_swiglu_reduce(M->part, pg.split, (size_t)n * 2 * I, M->act, n, I,
+                                     image_for(M, L.wd, n), s));
+        RRA_TRY(launch_gemv(L.wd, pd, gemv_input(M, L.wd, M->act), n, M->part_d, (size_t)n * H, s));
+        if (l + 1 < d.n_layers) {
+            const rra_layer_desc &Ln = M->layers[l + 1];
+            RRA_TRY(launch_residual_ss(M->part_d, pd.split, (size_t)n * H, x, x, M->ss,
+                                       Ln.attn_gamma, M->xg, n, H, image_for(M, Ln.wqkv, n), s));
+        } else if (last) {
+            // the last row alone: its residual step and the output norm's inputs
+            float *xl = x + (size_t)(n - 1) * H;
+            RRA_TRY(launch_residual_ss(M->part_d + (size_t)(n - 1) * H, pd.split, (size_t)n * H,
+                                       xl, xl, M->ss, d.out_gamma, M->xg, 1, H,
+                                       image_for(M, d.lm_head, 1), s));
+        }
+    }
+    if (!last) return RRA_OK;
+    RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[1], gemv_input(M, d.lm_head, M->xg), 1, M->logits,
+                        0, s, &nrm));
+    return launch_argmax(M->logits, M->ptok, 1, d.vocab, M->argmax_ws, nullptr, false, s);
+}
+
 }  // namespace
 
 extern "C" size_t rra_model_workspace_bytes(const rra_model_desc *d) {
@@ -534,7 +600,7 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
     M->ppos = reinterpret_cast<uint32_t *>(b + L.pidx);
     M->pseq = M->ppos + M->rows;
     M->ptok = M->pseq + M->rows;
-    for (int m = 1; m <= M->rows; ++m) {
+    for (int m = 1; m <= std::min(M->rows, RRA_M_MAX); ++m) {
         M->chunk[m] = chunk_for(*d, m);
         const rra_layer_desc &l0 = d->layers[0];
         M->plan_qkv[m] = gemv_plan(l0.wqkv, m);
@@ -545,6 +611,13 @@ extern "C" rra_status rra_model_create(const rra_model_desc *d, void *ws, size_t
         lm.kt_per_split = d->lm_head.fmt == RRA_F32 ? 1 : (int)cdiv(d->lm_head.k, tile_k(d->lm_head.fmt));
         lm.split = 1;
         M->plan_lm[m] = lm;
+    }
+    {
+        const rra_layer_desc &l0 = d->layers[0];
+        M->pf_qkv = gemm_plan(l0.wqkv);
+        M->pf_o = gemm_plan(l0.wo);
+        M->pf_gu = gemm_plan(l0.wgu);
+        M->pf_d = gemm_plan(l0.wd);
     }
     std::vector<float> table((size_t)d->max_len * d->head_dim);
     rope_table_host(table.data(), d->max_len, d->head_dim, d->rope_theta);
@@ -605,7 +678,7 @@ static rra_status capture_and_launch(rra_model *M, const GraphKey &key, float *x
     // failed capture cannot poison other threads' work.  End the capture
     // whatever happened, so the stream always leaves capture mode.
     RRA_TRY_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-    rra_status body = enqueue_step(M, x, pos, tok, tok, logits, m, flags, nullptr, s);
+    rra_status body = enqueue_step(M, x, pos, tok, tok, logits, m, flags, s);
     if (body == RRA_OK && capture_failure_requested())
         body = fail(RRA_ECAPTURE, "capture failure requested by RRA_FAIL_CAPTURE");
     hipGraph_t graph = nullptr;
@@ -673,13 +746,13 @@ extern "C" rra_status rra_decode_step(rra_model *M, float *x, uint32_t *pos, uin
             const rra_status st = capture_and_launch(M, key, x, pos, tok, lg, m, flags, s);
             if (st != RRA_OK) {
                 clear_error();
-                const rra_status eager = enqueue_step(M, x, pos, tok, tok, lg, m, flags, nullptr, s);
+                const rra_status eager = enqueue_step(M, x, pos, tok, tok, lg, m, flags, s);
                 if (eager != RRA_OK) return fail(RRA_ECAPTURE, "capture and eager step failed: %s",
                                                  rra_last_error());
             }
         }
     } else {
-        RRA_TRY(enqueue_step(M, x, pos, tok, tok, lg, m, flags, nullptr, s));
+        RRA_TRY(enqueue_step(M, x, pos, tok, tok, lg, m, flags, s));
     }
     if (tok_host) {
         RRA_TRY_HIP(hipMemcpyAsync(tok_host, tok, sizeof(uint32_t) * m, hipMemcpyDeviceToHost, s));
@@ -739,26 +812,20 @@ extern "C" rra_status rra_prefill(rra_model *M, const uint32_t *tokens, int32_t 
     if ((int64_t)start + n_tokens > d.max_len)
         return fail(RRA_EINVAL, "rra_prefill: positions %u..%lld exceed max_len=%d", start,
                     (long long)start + n_tokens - 1, d.max_len);
-    // Chunks of up to prefill_rows tokens, each one step whose rows are the
-    // chunk's tokens at consecutive positions, all in cache slot `seq`: a
-    // step writes every row's K/V before attention reads the cache, so row i
-    // attends to the cache rows before it and to rows 0..i of its own chunk.
+    // Chunks of up to prefill_rows tokens; each chunk's GEMMs stream the
+    // weights once for all of its rows, and its attention is causal within
+    // the chunk and over the slot's earlier rows.
     const int R = M->prefill_rows;
-    int n_last = 0;
     for (int c0 = 0; c0 < n_tokens; c0 += R) {
         const int n = std::min(R, n_tokens - c0);
-        const bool last = c0 + n == n_tokens;
-        RRA_TRY(launch_prefill_rows(M->ppos, M->pseq, start + (uint32_t)c0, (uint32_t)seq, n, s));
-        RRA_TRY(enqueue_step(M, M->px, M->ppos, tokens + c0, M->ptok, M->logits, n,
-                             RRA_STEP_GATHER | (last ? 0 : kStepNoHead), M->pseq, s));
-        n_last = n;
+        RRA_TRY(enqueue_prompt_chunk(M, tokens + c0, n, seq, start + (uint32_t)c0,
+                                     c0 + n == n_tokens, s));
     }
     if (next_tok)
-        RRA_TRY_HIP(hipMemcpyAsync(next_tok, M->ptok + (n_last - 1), sizeof(uint32_t),
-                                   hipMemcpyDeviceToDevice, s));
+        RRA_TRY_HIP(hipMemcpyAsync(next_tok, M->ptok, sizeof(uint32_t), hipMemcpyDeviceToDevice, s));
     if (logits)
-        RRA_TRY_HIP(hipMemcpyAsync(logits, M->logits + (size_t)(n_last - 1) * d.vocab,
-                                   sizeof(float) * d.vocab, hipMemcpyDeviceToDevice, s));
+        RRA_TRY_HIP(hipMemcpyAsync(logits, M->logits, sizeof(float) * d.vocab,
+                                   hipMemcpyDeviceToDevice, s));
     return RRA_OK;
 }
 
@@ -772,8 +839,8 @@ extern "C" rra_status rra_model_attention_plan(const rra_model *M, int32_t m, in
                                                int32_t *head_split) {
     clear_error();
     if (!M) return fail(RRA_ENOTINIT, "rra_model_attention_plan: null model");
-    if (m < 1 || m > M->rows)
-        return fail(RRA_EINVAL, "rra_model_attention_plan: m=%d not in 1..%d", m, M->rows);
+    if (m < 1 || m > M->d.m_max)
+        return fail(RRA_EINVAL, "rra_model_attention_plan: m=%d not in 1..%d", m, M->d.m_max);
     if (chunk) *chunk = M->chunk[m];
     if (head_split) *head_split = M->hsplit[m];
     return RRA_OK;
@@ -784,8 +851,8 @@ extern "C" rra_status rra_model_set_attention_plan(rra_model *M, int32_t m, int3
     clear_error();
     if (!M) return fail(RRA_ENOTINIT, "rra_model_set_attention_plan: null model");
     const rra_model_desc &d = M->d;
-    if (m < 1 || m > M->rows)
-        return fail(RRA_EINVAL, "rra_model_set_attention_plan: m=%d not in 1..%d", m, M->rows);
+    if (m < 1 || m > d.m_max)
+        return fail(RRA_EINVAL, "rra_model_set_attention_plan: m=%d not in 1..%d", m, d.m_max);
     if (chunk < 32 || chunk > 1024 || chunk % 32)
         return fail(RRA_EINVAL, "rra_model_set_attention_plan: chunk=%d (a multiple of 32 in "
                     "32..1024)", chunk);

@@ -74,6 +74,10 @@ struct GemvPlan {
     int kt_per_split = 1;
 };
 GemvPlan gemv_plan(const rra_weight &w, int m);
+// The plan of a prompt chunk of 33..128 rows (decode steps use gemv_plan).
+GemvPlan gemm_plan(const rra_weight &w);
+// Rows of one prompt chunk at most (rra_prefill).
+constexpr int kPrefillMax = 128;
 // RMSNorm folded into a GEMV.  The GEMV input holds x[m][k] * gamma[k] (the
 // producer applies gamma) and every output of row m is multiplied by
 // inv[m] = 1 / sqrt(ss[m] / K + eps), ss[m] = sum of the `nparts` partial sums
@@ -186,6 +190,13 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                bool reduce = true, const QkvIn *qi = nullptr,
                                hipEvent_t chunk_start = nullptr, hipEvent_t chunk_stop = nullptr,
                                int head_split = 0);
+// Causal attention of a prompt chunk (matrix cores): q [n][nq][hd] at
+// positions start .. start + n - 1 of one cache slot (k_slot, v_slot: that
+// slot's [nkv][max_len][hd]), row t over the slot's rows [0, start + t];
+// out [n][nq][hd] and, with fo, the O GEMV's activation image.
+rra_status launch_prefill_attention(const float *q, const float *k_slot, const float *v_slot,
+                                    float *out, int n, int nq, int nkv, int hd, int max_len,
+                                    uint32_t start, const FragOut *fo, hipStream_t s);
 // Where rra_flash_decode's partials live in `part` (m sequences, nq heads).
 inline const float *fd_part_lse(const float *part, int m, int nq, int hd, int nc_max) {
     return part + (size_t)m * nq * nc_max * hd;

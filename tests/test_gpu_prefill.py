@@ -1,11 +1,13 @@
 """Parity of prompt ingestion (rra_prefill) with the CPU oracle's prefill.
 
-Prefill runs a sequence's prompt tokens through the model in chunks of
-`prefill_rows` tokens, every chunk one pass of the decode step whose rows all
-map to the sequence's cache slot.  Checked: every layer's K/V cache rows of
-the slot, the last token's logits and greedy id, the other slots untouched,
-ragged last chunks, a second prefill call continuing the first, and a decode
-step taking over from the prefilled cache.
+Prefill runs a sequence's prompt tokens through the model in chunks of up to
+`prefill_rows` (<= 128) tokens: per layer a GEMM that streams the weights
+once for the chunk's rows, RoPE and the chunk's K/V rows into the sequence's
+cache slot, and a matrix-core causal attention over the slot's rows.
+Checked: every layer's K/V cache rows of the slot, the last token's logits
+and greedy id, the other slots untouched, ragged last chunks, a second
+prefill call continuing the first, and a decode step taking over from the
+prefilled cache.
 """
 import dataclasses
 
@@ -110,25 +112,55 @@ def test_prefill_continues_a_context_across_calls():
     check_last(nt, lg, o, "two calls")
 
 
-def test_prefill_chunk_of_one_equals_decode_steps_bitwise():
-    # prefill_rows = 1 makes every chunk a one-row step: the cache must be
-    # bit-identical to feeding the same tokens through rra_decode_step.
-    S = synth.TINY_LLAMA_F32
-    W = synth.decoder_weights(S, seed=2, device=DEV, gamma="random")
-    a = load_decoder(S, W, m_max=1, max_len=16, prefill_rows=1)
-    b = load_decoder(S, W, m_max=1, max_len=16)
-    toks = prompt(S, 9, 2, "prefill3").to(DEV, torch.int32)
-    a.model.rra_prefill(toks, 9, 0, 0)
-    x = torch.empty((1, S.hidden), device=DEV)
-    pos = u32([0])
-    tok = torch.zeros(1, dtype=torch.int32, device=DEV)
-    for t in range(9):
-        tok[0] = toks[t]
-        pos[0] = t
-        b.model.rra_decode_step(x, pos, tok, 1, flags=rra.RRA_STEP_GATHER)
+@pytest.mark.parametrize("S", [synth.TINY_LLAMA_F32, SMALL_Q8, SMALL_Q4, synth.SMALL_LLAMA_FP8],
+                         ids=lambda S: S.name)
+def test_prefill_128_row_chunks_match_oracle(S):
+    # 150 tokens in chunks of 128 + 22 into slot 1 of three (the 128-row GEMMs
+    # and five 32-key blocks of the matrix-core attention), then 60 more from
+    # position 150 in chunks of 60 (a chunk starting past the slot's first
+    # rows), each call's last token's logits and id against the oracle.
+    banner("prefill 128", S.name)
+    max_len, m_max, slot = 256, 3, 1
+    W = synth.decoder_weights(S, seed=4, device=DEV, gamma="random")
+    dd = load_decoder(S, W, m_max=m_max, max_len=max_len, prefill_rows=128)
+    orc = oracle.DecoderOracle(S, W, m_max, max_len)
+    toks = prompt(S, 210, 4, "prefill128")
+    nt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    lg = torch.empty(S.vocab, device=DEV)
+    dd.model.rra_prefill(toks[:150].to(DEV, torch.int32), 150, slot, 0, next_tok=nt, logits=lg)
+    o = orc.prefill(slot, host(W.embed[toks[:150].to(DEV)]), 0, head="last")
     torch.cuda.current_stream().synchronize()
-    for l in range(S.n_layers):
-        assert torch.equal(a.k_caches[l], b.k_caches[l]) and torch.equal(a.v_caches[l], b.v_caches[l])
+    check_cache(dd, orc, slot, 150, "first call")
+    check_last(nt, lg, o, "first call")
+    dd.model.rra_prefill(toks[150:].to(DEV, torch.int32), 60, slot, 150, next_tok=nt, logits=lg)
+    o = orc.prefill(slot, host(W.embed[toks[150:].to(DEV)]), 150, head="last")
+    torch.cuda.current_stream().synchronize()
+    check_cache(dd, orc, slot, 210, "second call")
+    check_last(nt, lg, o, "second call")
+    for other in (0, 2):
+        for l in range(S.n_layers):
+            assert not dd.k_caches[l][other].any() and not dd.v_caches[l][other].any()
+    dd.model.rra_model_check()
+
+
+def test_prefill_chunk_sizes_agree():
+    # The same 70-token prompt in chunks of 1, 16, 33 and 128 rows (the
+    # 1-, 2-, 4- and 8-column-tile GEMMs and their attention tiles): every
+    # cache row and the next token within the tolerance of each other and of
+    # the oracle.
+    S = SMALL_Q4
+    W = synth.decoder_weights(S, seed=2, device=DEV, gamma="random")
+    toks = prompt(S, 70, 2, "prefill3")
+    orc = oracle.DecoderOracle(S, W, 1, 80)
+    o = orc.prefill(0, host(W.embed[toks.to(DEV)]), 0, head="last")
+    for rows in (1, 16, 33, 128):
+        dd = load_decoder(S, W, m_max=1, max_len=80, prefill_rows=rows)
+        nt = torch.zeros(1, dtype=torch.int32, device=DEV)
+        lg = torch.empty(S.vocab, device=DEV)
+        dd.model.rra_prefill(toks.to(DEV, torch.int32), 70, 0, 0, next_tok=nt, logits=lg)
+        torch.cuda.current_stream().synchronize()
+        check_cache(dd, orc, 0, 70, f"rows {rows}")
+        check_last(nt, lg, o, f"rows {rows}")
 
 
 def test_prefill_rejects_bad_arguments_without_enqueueing():
@@ -147,20 +179,22 @@ def test_prefill_rejects_bad_arguments_without_enqueueing():
         assert not dd.k_caches[l].any()
 
 
-def test_qwen15b_q4_prefill_33_tokens_rows32():
-    # The 1.5B-shaped Q4 decoder with 32-row prefill chunks (32 + 1 tokens)
-    # into slot 2 of four.
+@pytest.mark.parametrize("T,rows", [(33, 32), (96, 128)])
+def test_qwen15b_q4_prefill(T, rows):
+    # The 1.5B-shaped Q4 decoder into slot 2 of four: 33 tokens in 32-row
+    # chunks (32 + 1), and a 96-token prompt in one chunk (the 8-column-tile
+    # GEMMs, three 32-key blocks of attention per 16-row tile).
     S = synth.QWEN25_15B_Q4
-    banner("prefill", S.name)
+    banner("prefill", S.name, T, rows)
     W = synth.decoder_weights(S, seed=0, device=DEV)
-    dd = load_decoder(S, W, m_max=4, max_len=64, prefill_rows=32)
-    orc = oracle.DecoderOracle(S, W, 4, 64)
-    T, slot = 33, 2
+    dd = load_decoder(S, W, m_max=4, max_len=128, prefill_rows=rows)
+    orc = oracle.DecoderOracle(S, W, 4, 128)
+    slot = 2
     toks = prompt(S, T, 0, "prefill5")
     nt = torch.zeros(1, dtype=torch.int32, device=DEV)
     lg = torch.empty(S.vocab, device=DEV)
     dd.model.rra_prefill(toks.to(DEV, torch.int32), T, slot, 0, next_tok=nt, logits=lg)
-    o = orc.prefill(slot, host(W.embed[toks.to(DEV)]), 0)
+    o = orc.prefill(slot, host(W.embed[toks.to(DEV)]), 0, head="last")
     torch.cuda.current_stream().synchronize()
     check_cache(dd, orc, slot, T, "1.5B prefill")
     check_last(nt, lg, o, "1.5B prefill")
