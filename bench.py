@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--m1-steps", type=int, default=256)
     ap.add_argument("--m1-ctx", type=int, default=512, help="context tokens of the M=1 line")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 1.5B-shaped M sweep")
+    ap.add_argument("--fixed-plans", action="store_true",
+                    help="flash decode at the library's default split rule instead of autotuned "
+                         "plans (deterministic launch shapes, for counter runs)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the 8B-shaped 512-token prefill line, for profiling")
     ap.add_argument("--only-sweep", default="",
@@ -379,9 +382,10 @@ def counter_traffic():
         return None, None
 
 
-def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps):
+def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps, of_m=32):
     """The oracle, as it stands, on `steps` greedy decode steps of the first
-    `nseq` sequences of the same workload (its own tokens fed back)."""
+    `nseq` sequences of the same workload (its own tokens fed back), from the
+    same cache contents (the GPU's, copied once; setup not timed)."""
     import oracle
     t_setup = time.time()
     orc = oracle.DecoderOracle(S, W, nseq, max(lengths[:nseq]) + steps)
@@ -399,11 +403,11 @@ def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps):
     sec = time.time() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return dict(value=nseq * steps / sec, unit="tok/s", cores=threads, kind="oracle",
-                sample=f"{steps} greedy decode steps of {nseq} of the 32 sequences of the same "
-                       f"workload ({sec:.1f} s; fp64, {threads} OpenMP threads)")
+                sample=f"{steps} greedy decode steps of {nseq} of the {of_m} sequences of the "
+                       f"same workload ({sec:.1f} s; fp64, {threads} OpenMP threads)")
 
 
-def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True):
+def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True, cpu=False):
     """The 1.5B-shaped Q4 decoder over a synthetic 1024-row KV context per
     sequence: greedy decode tok/s at each batch size M (one graph per M)."""
     import synth
@@ -424,6 +428,11 @@ def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True):
                  for L in lengths[:m] for i in range(steps)) / steps
         out[f"m{m}"] = dict(tok_s=m * steps / sec, ms_per_step=1e3 * sec / steps,
                             hbm_frac=(wbytes + kv) * steps / sec / 1e9 / HBM_PEAK_GBS)
+    if cpu:  # the oracle at both ends of the sweep (M=32: a sample of 8 sequences)
+        out["cpu_baseline"] = {
+            "m1": cpu_baseline(S, W, dd, lengths, first, 1, 4, of_m=1),
+            "m32": cpu_baseline(S, W, dd, lengths, first, 8, 4, of_m=32)}
+        log(f"sweep cpu baselines {out['cpu_baseline']}")
     if prefill:
         out["prefill"] = prefill_line(S, dd, 1024)
     del dd, W
@@ -489,7 +498,7 @@ def lm_head_gemv_line(fmt, reps=20):
     return res
 
 
-def m1_line(steps_m1=256, ctx=512):
+def m1_line(steps_m1=256, ctx=512, cpu=False, tune=True):
     import synth
     S = synth.QWEN25_05B_Q8
     W, dd = build_decoder(S, 1, S.max_len)
@@ -508,7 +517,8 @@ def m1_line(steps_m1=256, ctx=512):
         dd.model.rra_decode_step(x, pos, tok, 1, flags=rra.RRA_GRAPH, logits=lg)
     torch.cuda.synchronize()
     first = synth.first_tokens(S, 1).tolist()
-    plan = dd.model.rra_model_tune_attention([1], [ctx + steps_m1 // 2])[1]
+    plan = (dd.model.rra_model_tune_attention([1], [ctx + steps_m1 // 2])[1] if tune
+            else dd.model.rra_model_attention_plan(1))
     sec, _, _ = timed_greedy(dd, S, 1, first, [ctx], steps_m1, 3)
     wbytes = dd.weight_bytes()
     kv_read = sum(S.n_layers * 2 * S.n_kv_heads * (ctx + i + 1) * S.head_dim * 4
@@ -519,6 +529,9 @@ def m1_line(steps_m1=256, ctx=512):
                weight_kv_gbs=(wbytes + kv_read) * steps_m1 / sec / 1e9)
     res["hbm_frac"] = res["weight_kv_gbs"] / HBM_PEAK_GBS
     res["host_handoff"] = host_handoff_line(dd, S, 1, first, [ctx], steps_m1)
+    if cpu:  # the oracle on 8 steps after the same 512-row context (the GPU's cache rows)
+        res["cpu_baseline"] = cpu_baseline(S, W, dd, [ctx], first, 1, 8, of_m=1)
+        log(f"m1 cpu baseline {res['cpu_baseline']}")
     del dd, W
     torch.cuda.empty_cache()
     return res
@@ -543,7 +556,8 @@ def main():
               flush=True)
         return
     if args.only_m1:
-        print(json.dumps({"m1": m1_line(args.m1_steps, args.m1_ctx)}), flush=True)
+        print(json.dumps({"m1": m1_line(args.m1_steps, args.m1_ctx, tune=not args.fixed_plans)}),
+              flush=True)
         return
     if args.only_attention:
         print(json.dumps({"flash_decode": flash_decode_line(), "hbm_ceiling": hbm_ceiling_line()}),
@@ -567,7 +581,10 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s; weights {dd.weight_bytes() / 1e9:.3f} GB")
     t0 = time.time()
-    plan = dd.model.rra_model_tune_attention([m], [L + steps // 2 for L in lengths])[m]
+    if args.fixed_plans:
+        plan = dd.model.rra_model_attention_plan(m)
+    else:
+        plan = dd.model.rra_model_tune_attention([m], [L + steps // 2 for L in lengths])[m]
     log(f"flash-decode plan for M={m}: chunk {plan[0]}, head split {plan[1]} "
         f"(tuned in {time.time() - t0:.1f}s)")
     first = synth.first_tokens(S, m).tolist()
@@ -607,13 +624,14 @@ def main():
     del dd, W
     torch.cuda.empty_cache()
     if not (args.no_m1 or args.main_only):
-        m1 = m1_line(args.m1_steps, args.m1_ctx)
+        m1 = m1_line(args.m1_steps, args.m1_ctx, cpu=not args.no_cpu_baseline)
         log(f"m1 {m1}")
     fp8 = None if args.main_only else lm_head_gemv_line("fp8")
     log(f"fp8 gemv {fp8}")
     q6k = None if args.main_only else lm_head_gemv_line("q6k")
     log(f"q6k gemv {q6k}")
-    sweep = None if (args.no_sweep or args.main_only) else m_sweep_line()
+    sweep = None if (args.no_sweep or args.main_only) else m_sweep_line(
+        cpu=not args.no_cpu_baseline)
     log(f"m sweep {sweep}")
     fd_c = None if args.main_only else flash_decode_line()
     log(f"flash decode chunks {fd_c}")

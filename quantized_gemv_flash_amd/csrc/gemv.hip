@@ -802,6 +802,201 @@ __device__ __forceinline__ void prologue_resid(const GemvPrologue &pro, int M, i
     }
 }
 
+// Prompt-chunk GEMM (up to 128 rows of x, 8 column tiles): the decode
+// GEMV's operand flow with the work split two ways.  8 waves = 4 row groups
+// x 2 column groups; wave (rg, cg) owns row tiles 4 rg .. 4 rg + 3 of the
+// workgroup's 16 (256 output rows) and column tiles 4 cg .. 4 cg + 3.  Each B
+// fragment read from LDS then feeds 4 row tiles and each dequantised weight
+// block 4 column tiles, so a matrix-core op costs a quarter of an LDS read
+// (one row tile per wave would cost a whole one).  The two column groups
+// load the same weights (the second read is an L2 hit) and each dequantise
+// them.  K tiles are double-buffered as in gemv_q_kernel: the next tile's
+// image and scales go to LDS by LDS-DMA and its weights to registers while
+// the current one is computed.  Outputs are multiplied by inv[m] (RMSNorm,
+// when nrm.ss is set) and written to out[split][m][n].
+template <int FMT>
+struct QGemm {
+    using F = TileFmt<FMT>;
+    static constexpr int NB = F::NB, TB = F::TB, SB = TB - F::SO;
+    static constexpr int CT = 8, NW = 8, RG = 4, RPW = 4, CW = 4;  // CW column tiles per wave
+    static constexpr int FRAG = NB * CT * 2;      // 1 KiB image fragments per K tile
+    static constexpr int XB = FRAG * 1024;
+    static constexpr int XDW = FRAG / NW;         // image DMAs per wave per K tile
+    static constexpr int SCH = RG * RPW * SB / 16;  // 16-byte scale pieces per K tile
+    static constexpr int SCW = (SCH + 63) / 64;     // waves that DMA scale pieces
+    static_assert(FRAG % NW == 0 && SCW <= NW, "DMA split");
+    typedef floatx4 Acc[RPW][CW];
+
+    const uint8_t *wt, *ximg;
+    int lane, g, wave, rg, cg, n_rt, rt_wg, rt0, nkt, kt_begin, kt_end;
+
+    __device__ __forceinline__ void init(const uint8_t *wt_, const uint8_t *ximg_, int N, int nkt_,
+                                         int kt_per_split) {
+        wt = wt_;
+        ximg = ximg_;
+        lane = threadIdx.x & 63;
+        g = lane >> 4;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        rg = wave & (RG - 1);
+        cg = wave / RG;
+        n_rt = (N + 15) >> 4;
+        rt_wg = blockIdx.x * RG * RPW;
+        rt0 = rt_wg + rg * RPW;
+        nkt = nkt_;
+        kt_begin = blockIdx.y * kt_per_split;
+        kt_end = min(nkt, kt_begin + kt_per_split);
+    }
+    // LDS-DMA of K tile kt_begin + c's image and the workgroup's scales
+    // (clamped to the split's last tile: the look-ahead past it is never used)
+    __device__ __forceinline__ void stage(int c, uint8_t *xd, uint8_t *sd) const {
+        const int kt = min(kt_begin + c, kt_end - 1);
+#pragma unroll
+        for (int j = 0; j < XDW; ++j) {
+            const int f = wave + NW * j;
+            dma16(ximg + ((size_t)kt * FRAG + f) * 1024 + lane * 16, xd + f * 1024);
+        }
+        if (wave < SCW) {
+            const int e = min(wave * 64 + lane, SCH - 1);
+            const int piece = e % (SB / 16), rr = e / (SB / 16);
+            const int rt = min(rt_wg + rr, n_rt - 1);
+            dma16(wt + ((size_t)rt * nkt + kt) * TB + F::SO + piece * 16, sd + wave * 1024);
+        }
+    }
+    __device__ __forceinline__ void issue(uint4 (&q)[RPW], int c) const {
+        const int kt = min(kt_begin + c, kt_end - 1);
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int rt = min(rt0 + r, n_rt - 1);
+            q[r] = ldnt16(wt + ((size_t)rt * nkt + kt) * TB + lane * 16);
+        }
+    }
+    __device__ __forceinline__ void compute(const uint4 (&q)[RPW], const uint8_t *xs,
+                                            const uint8_t *ss, Acc &acc) const {
+        // scales of this wave's row tiles: rows 4g + i, blocks b at (g, i, b)
+        _Float16 sh[RPW][4 * NB];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const uint8_t *sp = ss + (rg * RPW + r) * SB;
+            if (FMT == RRA_Q4) {
+                const half8_t h0 = *reinterpret_cast<const half8_t *>(sp + 32 * g);
+                const half8_t h1 = *reinterpret_cast<const half8_t *>(sp + 32 * g + 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sh[r][e] = h0[e];
+                    sh[r][8 + e] = h1[e];
+                }
+            } else {
+                const half8_t h0 = *reinterpret_cast<const half8_t *>(sp + 16 * g);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sh[r][e] = h0[e];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            asm volatile("" ::: "memory");
+            half8_t a[RPW];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+                a[r] = (FMT == RRA_Q4)    ? dequant_q4(u32_at(q[r], b))
+                       : (FMT == RRA_FP8) ? dequant_fp8(u32_at(q[r], 2 * b), u32_at(q[r], 2 * b + 1))
+                                          : dequant_q8(u32_at(q[r], 2 * b), u32_at(q[r], 2 * b + 1));
+            const int slot = frag_slot<F::IMG>(lane >> 4, lane & 15, b);
+#pragma unroll
+            for (int cw = 0; cw < CW; ++cw) {
+                const int cc = cg * CW + cw;
+                const half8_t bh = *reinterpret_cast<const half8_t *>(
+                    xs + ((b * CT + cc) * 2 + 0) * 1024 + slot * 16);
+                const half8_t bl = *reinterpret_cast<const half8_t *>(
+                    xs + ((b * CT + cc) * 2 + 1) * 1024 + slot * 16);
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                    floatx4 tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        a[r], bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[r], bl, tt, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[r][cw][i] = fmaf((float)sh[r][i * NB + b], tt[i], acc[r][cw][i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int cw = 0; cw < CW; ++cw) asm volatile("" : "+v"(acc[r][cw]));
+    }
+    __device__ __forceinline__ void step(const uint4 (&qc)[RPW], uint4 (&qn)[RPW], int c,
+                                         uint8_t *xw, uint8_t *sw, const uint8_t *xr,
+                                         const uint8_t *sr, Acc &acc) const {
+        stage(c + 1, xw, sw);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(qn, c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(qc, xr, sr, acc);
+        wait_vm<0>();
+        lds_barrier();
+    }
+};
+
+template <int FMT>
+__global__ __launch_bounds__(512) void gemm_q_kernel(const uint8_t *__restrict__ wt,
+                                                     const uint8_t *__restrict__ ximg,
+                                                     float *__restrict__ out, int M, int N, int K,
+                                                     int nkt, int kt_per_split,
+                                                     long long split_stride, NormIn nrm) {
+    using G = QGemm<FMT>;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::XB];
+    __shared__ __attribute__((aligned(16))) uint8_t sl[2][G::SCW * 1024];
+    G p;
+    p.init(wt, ximg, N, nkt, kt_per_split);
+    const int nch = p.kt_end - p.kt_begin;
+    typename G::Acc acc;
+#pragma unroll
+    for (int r = 0; r < G::RPW; ++r)
+#pragma unroll
+        for (int cw = 0; cw < G::CW; ++cw) acc[r][cw] = floatx4{0.f, 0.f, 0.f, 0.f};
+    uint4 q0[G::RPW], q1[G::RPW];
+    p.stage(0, xs[0], sl[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    p.issue(q0, 0);
+    wait_vm<0>();
+    lds_barrier();
+    int c = 0;
+    for (; c + 2 < nch; c += 2) {
+        p.step(q0, q1, c, xs[1], sl[1], xs[0], sl[0], acc);
+        p.step(q1, q0, c + 1, xs[0], sl[0], xs[1], sl[1], acc);
+    }
+    if (c + 1 < nch) {
+        p.step(q0, q1, c, xs[1], sl[1], xs[0], sl[0], acc);
+        p.compute(q1, xs[1], sl[1], acc);
+    } else if (c < nch) {
+        p.compute(q0, xs[0], sl[0], acc);
+    }
+    // RMSNorm: inv of this lane's columns, then the 16 x 16 result tiles
+    // (lane holds rows 4g .. 4g + 3 of column lane % 16)
+    float *o = out + (size_t)blockIdx.y * split_stride;
+#pragma unroll
+    for (int cw = 0; cw < G::CW; ++cw) {
+        const int m = 16 * (p.cg * G::CW + cw) + (p.lane & 15);
+        if (m >= M) continue;
+        float iv = 1.f;
+        if (nrm.ss) {
+            float t = 0.f;
+            for (int qq = 0; qq < nrm.nparts; ++qq) t += nrm.ss[(size_t)m * nrm.nparts + qq];
+            iv = 1.0f / sqrtf(t / (float)K + nrm.eps);
+        }
+#pragma unroll
+        for (int r = 0; r < G::RPW; ++r) {
+            const int rt = p.rt0 + r;
+            if (rt >= p.n_rt) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = rt * 16 + 4 * p.g + i;
+                if (row < N) o[(size_t)m * N + row] = acc[r][cw][i] * iv;
+            }
+        }
+    }
+}
+
 template <int FMT, int CT, int RPW, int NW, int NT, int PRO = 0>
 __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__restrict__ wt,
                                                                const uint8_t *__restrict__ ximg,
@@ -1189,9 +1384,18 @@ rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img
         if (p.rpw >= 2) return launch_q<FMT, 1, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
         return launch_q<FMT, 1, 1, 4>(w, p, img, m, out, stride, nrm, pro, s);
     }
-    if (m > 32) {  // prompt chunks: one row tile per wave, 8 waves share the image
+    if (m > 32) {  // prompt chunks
         if (pro.kind != kProNone) return fail(RRA_EINVAL, "gemv prologue: m > 16");
         if (m <= 64) return launch_q<FMT, 4, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
+        if constexpr (FMT != RRA_Q6K) {
+            const int n_rt = (int)cdiv(w.n, 16);
+            const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
+            const dim3 grid((unsigned)cdiv(n_rt, 16), (unsigned)p.split);
+            hipLaunchKernelGGL(gemm_q_kernel<FMT>, grid, dim3(512), 0, s,
+                               static_cast<const uint8_t *>(w.data), img, out, m, (int)w.n,
+                               (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
+            return check_launch("gemm_q_kernel");
+        }
         return launch_q<FMT, 8, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
     }
     if (p.nw == 8) {
@@ -1239,15 +1443,17 @@ GemvPlan gemm_plan(const rra_weight &w) {
     if (w.fmt == RRA_F32) return p;
     const int n_rt = (int)cdiv(w.n, 16);
     const int nkt = (int)cdiv(w.k, tile_k(w.fmt));
-    // Prompt chunks (up to 128 rows): compute-bound, one 8-wave workgroup of
-    // 128 output rows per compute unit at a time (its double-buffered image
-    // takes most of the LDS); K splits until the grid covers the chip, each
-    // split at least two K tiles long.
+    // Prompt chunks (33..128 rows): compute-bound, one 8-wave workgroup of
+    // 256 output rows (gemm_q_kernel; 128 rows for chunks of up to 64 rows)
+    // per compute unit at a time, its double-buffered image taking most of
+    // the LDS; K splits until the grid has about 192 workgroups (each split
+    // at least two K tiles long), fewer splits than a full chip's worth since
+    // every split adds a plane of partial sums.
     p.rpw = 1;
     p.nw = 8;
-    const int n_rb = (int)cdiv(n_rt, 8);
+    const int n_rb = (int)cdiv(n_rt, 16);
     int split = 1;
-    while (split * n_rb < 256 && split * 4 <= nkt) split *= 2;
+    while (split * n_rb < 192 && split * 4 <= nkt) split *= 2;
     p.kt_per_split = (int)cdiv(nkt, split);
     p.split = (int)cdiv(nkt, p.kt_per_split);
     return p;
