@@ -361,12 +361,19 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
 // + sum e^(s-m'), O' = O e^(m-m') + P V with P = e^(s-m'); at the end O / l.
 // Keys past a row's position get probability 0; cache rows past the chunk's
 // last position are staged as zeros (never read as data).
+//
+// With ks_n > 1 the key blocks are dealt to ks_n workgroups (blockIdx.z = ks
+// takes blocks ks, ks + ks_n, ...), so short grids fill the chip; each
+// writes its normalised partial output and log-sum-exp in flash decode's
+// partials layout (split = ks; an empty split writes 0 and -inf), and
+// fd_reduce_kernel combines them.
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int HD, int G>
 __global__ __launch_bounds__(64 * G) void prefill_attn_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
-    float *__restrict__ out, int n, int nq, int nkv, int max_len, uint32_t start, FragOut fo) {
+    float *__restrict__ out, int n, int nq, int nkv, int max_len, uint32_t start, FragOut fo,
+    int ks_n, float *__restrict__ part_o, float *__restrict__ part_lse) {
     constexpr int DS = HD / 32;  // 32-wide d steps of S = Q K^T
     constexpr int DT = HD / 16;  // 16-wide d tiles of O
     constexpr int OS = HD + 4;   // row stride of the output staging (floats)
@@ -409,7 +416,8 @@ __global__ __launch_bounds__(64 * G) void prefill_attn_kernel(
     for (int i = 0; i < 4; ++i) prow[i] = (int)start + min(t0 + 4 * j + i, last);
     const int kvalid = (int)start + last;            // last cache row holding data
     const int kmax = (int)start + min(t0 + 15, last);  // last key any row of the tile reads
-    for (int k0 = 0; k0 <= kmax; k0 += 32) {
+    const int ks = blockIdx.z;
+    for (int k0 = 32 * ks; k0 <= kmax; k0 += 32 * ks_n) {
         // ---- stage keys k0 .. k0 + 31: K as B[32 d][16 keys] per (key tile, d step),
         // V as B[32 keys][16 d] per d tile; hi and lo parts
         for (int it = threadIdx.x; it < 32 * (HD / 8); it += 64 * G) {
@@ -470,9 +478,12 @@ __global__ __launch_bounds__(64 * G) void prefill_attn_kernel(
             float mx = fmaxf(s0, s1);
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            const float mn = fmaxf(mrow[i], mx);  // finite: key 0 is in every row's range
-            alpha[i] = expf(mrow[i] - mn);
-            const float p0 = expf(s0 - mn), p1 = expf(s1 - mn);
+            // -inf only while this workgroup has seen no key of the row (a
+            // later key split's first blocks): nothing to add, nothing to scale
+            const float mn = fmaxf(mrow[i], mx);
+            const bool none = mn == -INFINITY;
+            alpha[i] = none ? 1.f : expf(mrow[i] - mn);
+            const float p0 = none ? 0.f : expf(s0 - mn), p1 = none ? 0.f : expf(s1 - mn);
             float ps = p0 + p1;
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off, 64);
@@ -506,12 +517,34 @@ __global__ __launch_bounds__(64 * G) void prefill_attn_kernel(
         __syncthreads();  // kf, vf and pf are refilled next block
     }
     // ---- O / l, through LDS, to the output rows and the O GEMV's image
+    // (or, split over keys, to this split's partials)
     float *os = of[wave];
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) os[(4 * j + i) * OS + 16 * t + r] = o[t][i] / lrow[i];
+        for (int i = 0; i < 4; ++i)
+            os[(4 * j + i) * OS + 16 * t + r] = lrow[i] > 0.f ? o[t][i] / lrow[i] : 0.f;
     __builtin_amdgcn_wave_barrier();
+    if (ks_n > 1) {
+        if (r == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 4 * j + i;
+                if (t <= last)
+                    part_lse[((size_t)t * nq + h) * ks_n + ks] =
+                        lrow[i] > 0.f ? mrow[i] + logf(lrow[i]) : -INFINITY;
+            }
+        }
+        for (int it = lane; it < 16 * (HD / 8); it += 64) {
+            const int row = it / (HD / 8), dg = it % (HD / 8), t = t0 + row;
+            if (t > last) continue;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = os[row * OS + 8 * dg + e];
+            store8(part_o + (((size_t)t * nq + h) * ks_n + ks) * HD + 8 * dg, v);
+        }
+        return;
+    }
     for (int it = lane; it < 16 * (HD / 8); it += 64) {
         const int row = it / (HD / 8), dg = it % (HD / 8), t = t0 + row;
         if (t > last) continue;
@@ -765,17 +798,31 @@ size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk) {
     return (size_t)m * nq * nc_max * (size_t)(hd + 1);
 }
 
+int prefill_key_splits(int n, int nkv, uint32_t start) {
+    // about 256 workgroups, each split with at least one 32-key block
+    const int base = (int)cdiv(n, 16) * nkv;
+    const int blocks = (int)cdiv((int64_t)start + n, 32);
+    return std::max(1, std::min({kPrefillKeySplits, 256 / std::max(1, base), blocks}));
+}
+
 rra_status launch_prefill_attention(const float *q, const float *k_slot, const float *v_slot,
                                     float *out, int n, int nq, int nkv, int hd, int max_len,
-                                    uint32_t start, const FragOut *fo, hipStream_t s) {
+                                    uint32_t start, const FragOut *fo, float *part,
+                                    const uint32_t *lens, hipStream_t s) {
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int group = nq / nkv;
-    const dim3 grid((unsigned)cdiv(n, 16), (unsigned)nkv);
+    const int ks_n = part ? prefill_key_splits(n, nkv, start) : 1;
+    float *po = part, *pl = part ? const_cast<float *>(fd_part_lse(part, n, nq, hd, ks_n)) : nullptr;
+    const dim3 grid((unsigned)cdiv(n, 16), (unsigned)nkv, (unsigned)ks_n);
 #define RRA_PA(HDV, GV)                                                                       \
     if (hd == HDV && group == GV) {                                                          \
         hipLaunchKernelGGL((prefill_attn_kernel<HDV, GV>), grid, dim3(64 * GV), 0, s, q, k_slot, \
-                           v_slot, out, n, nq, nkv, max_len, start, img);                    \
-        return check_launch("prefill_attn_kernel");                                          \
+                           v_slot, out, n, nq, nkv, max_len, start, img, ks_n, po, pl);     \
+        RRA_TRY(check_launch("prefill_attn_kernel"));                                        \
+        if (ks_n == 1) return RRA_OK;                                                        \
+        hipLaunchKernelGGL(fd_reduce_kernel<HDV>, dim3(nq, n), dim3(64), 0, s, po, pl, lens, out, \
+                           nq, max_len, 0, ks_n, img);                                       \
+        return check_launch("fd_reduce_kernel");                                             \
     }
     RRA_PA(64, 1) RRA_PA(64, 2) RRA_PA(64, 3) RRA_PA(64, 4) RRA_PA(64, 5) RRA_PA(64, 6)
     RRA_PA(64, 7) RRA_PA(64, 8) RRA_PA(128, 1) RRA_PA(128, 2) RRA_PA(128, 3) RRA_PA(128, 4)

@@ -278,7 +278,9 @@ size_t fd_floats(const rra_model_desc &d) {
         best = std::max(best, fd_partials_floats(m, d.n_heads, d.head_dim, d.max_len, chunk_for(d, m)));
         best = std::max(best, fd_tuned_floats(m, d.n_heads, d.n_kv_heads, d.head_dim, d.max_len));
     }
-    return best;
+    // a prompt chunk's attention split over keys (at most kPrefillKeySplits)
+    const size_t pr = (size_t)prefill_rows_of(d);
+    return std::max(best, pr * d.n_heads * kPrefillKeySplits * (size_t)(d.head_dim + 1));
 }
 
 Layout layout_of(const rra_model_desc &d) {
@@ -524,7 +526,7 @@ rra_status enqueue_prompt_chunk(rra_model *M, const uint32_t *tokens, int n, int
                                 M->pseq, s));
         const FragOut fo_o = image_for(M, L.wo, n);
         RRA_TRY(launch_prefill_attention(M->q, L.k_cache + slot, L.v_cache + slot, M->attn, n, nq,
-                                         nkv, hd, d.max_len, start, &fo_o, s));
+                                         nkv, hd, d.max_len, start, &fo_o, M->fd, M->lens, s));
         RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), n, M->part_d, (size_t)n * H,
                             s));
         RRA_TRY(launch_residual_ss(M->part_d, po.split, (size_t)n * H, x, x, M->ss, L.ffn_gamma,

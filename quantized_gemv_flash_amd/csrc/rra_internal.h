@@ -193,10 +193,16 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
 // Causal attention of a prompt chunk (matrix cores): q [n][nq][hd] at
 // positions start .. start + n - 1 of one cache slot (k_slot, v_slot: that
 // slot's [nkv][max_len][hd]), row t over the slot's rows [0, start + t];
-// out [n][nq][hd] and, with fo, the O GEMV's activation image.
+// out [n][nq][hd] and, with fo, the O GEMV's activation image.  With `part`
+// (n * nq * ks * (hd + 1) floats for ks = prefill_key_splits(n, nkv, start))
+// the keys are split over workgroups and combined by fd_reduce_kernel, which
+// reads lens[t] = start + t + 1.
+constexpr int kPrefillKeySplits = 8;
+int prefill_key_splits(int n, int nkv, uint32_t start);
 rra_status launch_prefill_attention(const float *q, const float *k_slot, const float *v_slot,
                                     float *out, int n, int nq, int nkv, int hd, int max_len,
-                                    uint32_t start, const FragOut *fo, hipStream_t s);
+                                    uint32_t start, const FragOut *fo, float *part,
+                                    const uint32_t *lens, hipStream_t s);
 // Where rra_flash_decode's partials live in `part` (m sequences, nq heads).
 inline const float *fd_part_lse(const float *part, int m, int nq, int hd, int nc_max) {
     return part + (size_t)m * nq * nc_max * hd;
