@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--fixed-plans", action="store_true",
                     help="flash decode at the library's default split rule instead of autotuned "
                          "plans (deterministic launch shapes, for counter runs)")
+    ap.add_argument("--only-gemv-ab", action="store_true",
+                    help="run only the matrix-core vs vector-ALU GEMV comparison")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the 8B-shaped 512-token prefill line, for profiling")
     ap.add_argument("--only-sweep", default="",
@@ -357,6 +359,46 @@ def gemv_only(n=28672, k=4096, reps=5):
     return dict(shape=f"{n}x{k} q4", weight_bytes=n * k * 18 // 32, **res)
 
 
+def gemv_ab_line(ms=(1, 4, 8), reps=20):
+    """The matrix-core GEMV (rra_batched_gemv) against the vector-ALU one
+    (rra_batched_gemv_valu) on the same tiled weights: the 0.5B-shaped Q8
+    layer and LM-head matrices and the 8B-shaped Q4 ones, at small M, each
+    timed as graph replays (the activation-image conversion and the split-K
+    sum included on both sides)."""
+    import synth
+    import quantized_gemv_flash_amd as rra
+    shapes = [("q8", "qkv", 1152, 896), ("q8", "gate_up", 9728, 896), ("q8", "down", 896, 4864),
+              ("q8", "lm_head", 151936, 896), ("q4", "qkv", 6144, 4096),
+              ("q4", "gate_up", 28672, 4096), ("q4", "down", 4096, 14336),
+              ("q4", "lm_head", 128256, 4096)]
+    res = {}
+    for fmt, name, n, k in shapes:
+        data, scale = synth.weight(n, k, fmt, 0.02, 0, f"ab_{name}_{n}", "cuda")
+        w = rra.device_weight(data, scale, fmt)
+        del data, scale
+        wbytes = n * k * (18 if fmt == "q4" else 34) // 32
+        row = {}
+        for m in ms:
+            x = torch.randn((m, k), device="cuda")
+            y = torch.empty((m, n), device="cuda")
+            ws = torch.empty(max(4, rra.rra_batched_gemv_workspace_bytes(w, m)), dtype=torch.uint8,
+                             device="cuda")
+            t_mfma = sorted(graph_time(lambda: rra.rra_batched_gemv(w, x, y, m, ws), reps)
+                            for _ in range(3))[1]
+            try:  # the VALU kernel stages a K split of x in LDS: too large a split is refused
+                t_valu = sorted(graph_time(lambda: rra.rra_batched_gemv_valu(w, x, y, m, ws), reps)
+                                for _ in range(3))[1]
+            except rra.RraError:
+                t_valu = None
+            row[f"m{m}"] = dict(mfma_us=t_mfma * 1e6, valu_us=t_valu and t_valu * 1e6,
+                                mfma_gbs=wbytes / t_mfma / 1e9,
+                                valu_gbs=t_valu and wbytes / t_valu / 1e9)
+        res[f"{fmt}_{name}_{n}x{k}"] = row
+        del w
+    torch.cuda.empty_cache()
+    return res
+
+
 COPY_BYTES = 1 << 30
 COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         "flash_decode_llama3_8b_m32.md")
@@ -545,6 +587,9 @@ def main():
         sys.exit(2)
     import synth
     import quantized_gemv_flash_amd as rra  # noqa: F401  (fails loudly if not built)
+    if args.only_gemv_ab:
+        print(json.dumps({"gemv_valu_vs_mfma": gemv_ab_line()}), flush=True)
+        return
     if args.only_prefill:
         S = synth.LLAMA3_8B_Q4
         W, dd = build_decoder(S, 1, 1024)
@@ -633,6 +678,8 @@ def main():
     sweep = None if (args.no_sweep or args.main_only) else m_sweep_line(
         cpu=not args.no_cpu_baseline)
     log(f"m sweep {sweep}")
+    gemv_ab = None if args.main_only else gemv_ab_line()
+    log(f"gemv valu vs mfma {gemv_ab}")
     fd_c = None if args.main_only else flash_decode_line()
     log(f"flash decode chunks {fd_c}")
     ceil = None if args.main_only else hbm_ceiling_line()
@@ -685,6 +732,7 @@ def main():
         "q6k_gemv": q6k,
         "prefill": prefill and dict(workload=f"{S.name}: 512 prompt tokens into one slot", **prefill),
         "m_sweep": sweep,
+        "gemv_valu_vs_mfma": gemv_ab,
         "flash_decode": fd_c,
         "hbm_ceiling": ceil,
         "cpu_baseline": cpu,

@@ -153,6 +153,16 @@ size_t rra_batched_gemv_workspace_bytes(const rra_weight *w, int32_t m);
 rra_status rra_batched_gemv(const rra_weight *w, const float *x, float *y, int32_t m,
                             void *ws, size_t ws_bytes, hipStream_t s);
 
+/* The same GEMV on the vector ALUs (Q4 and Q8 tiled weights, m in 1..8),
+ * kept to measure the matrix-core path against: one wave per 16-row tile,
+ * each lane converting its bytes of every block to fp32 and accumulating fp32
+ * FMAs with fp32 x staged in LDS, the four lanes of a row summed by cross-lane
+ * adds.  Same y up to fp32 rounding order; ws as for rra_batched_gemv (only
+ * its split-K partials are used); RRA_EINVAL when a K split would need more
+ * than 64 KiB of LDS. */
+rra_status rra_batched_gemv_valu(const rra_weight *w, const float *x, float *y, int32_t m,
+                                 void *ws, size_t ws_bytes, hipStream_t s);
+
 /* rra_batched_gemv for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same computation with the same kernels, bitwise the same y, with no

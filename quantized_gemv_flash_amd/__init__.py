@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "rra_batched_gemv_workspace_bytes": ([W, I], S),
         "rra_batched_gemv": ([W, P, P, I, P, S, P], I),
         "rra_batched_gemv_noalloc": ([W, P, P, I, P], I),
+        "rra_batched_gemv_valu": ([W, P, P, I, P, S, P], I),
         "rra_kv_scatter": ([P, P, P, P, P, I, I, I, I, P], I),
         "rra_flash_decode_workspace_bytes": ([I, I, I, I, I, I], S),
         "rra_flash_decode_chunk": ([I, I, I, I], I),
@@ -194,6 +195,13 @@ def rra_batched_gemv(w: Weight, x: torch.Tensor, y: torch.Tensor, m: int,
     nb = 0 if ws is None else ws.numel() * ws.element_size()
     _check("rra_batched_gemv", lib.rra_batched_gemv(ctypes.byref(w.c), _p(x), _p(y), m, _p(ws), nb,
                                                     _stream(stream)))
+
+
+def rra_batched_gemv_valu(w: Weight, x: torch.Tensor, y: torch.Tensor, m: int,
+                          ws: Optional[torch.Tensor] = None, stream=None):
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("rra_batched_gemv_valu", lib.rra_batched_gemv_valu(ctypes.byref(w.c), _p(x), _p(y), m,
+                                                              _p(ws), nb, _stream(stream)))
 
 
 def rra_batched_gemv_noalloc(w: Weight, x: torch.Tensor, y: torch.Tensor, m: int, stream=None):

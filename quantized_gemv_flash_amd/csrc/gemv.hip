@@ -1069,6 +1069,96 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_short_kernel(const uint8_t *__
     p.store(acc, sq, nrm, out + (size_t)blockIdx.y * split_stride, M, N, K);
 }
 
+// The same product on the vector ALUs, for comparison with the matrix-core
+// path at small M (rra_batched_gemv_valu): one wave per 16-row tile of the
+// tiled layout, lane (j, r) holding row r's bytes of sub-range j of each of
+// the tile's blocks; the block's values are converted to fp32 (q or q - 8,
+// exact) and multiplied with fp32 x from LDS (the split's K range of all
+// rows, staged once per workgroup) in plain fp32 FMAs, the fp16 block scale
+// applied per block; the four lanes of a row are summed with cross-lane adds.
+// Q4's -8 offset is folded as sum (q - 8) x = sum q x - 8 sum x, with the sum
+// of each 8-element group of x staged beside x.
+template <int FMT, int MR>
+__global__ __launch_bounds__(256) void gemv_valu_kernel(const uint8_t *__restrict__ wt,
+                                                        const float *__restrict__ x,
+                                                        float *__restrict__ out, int M, int N,
+                                                        int K, int nkt, int kt_per_split,
+                                                        long long split_stride) {
+    using F = TileFmt<FMT>;
+    constexpr int KT = F::KT, NB = F::NB, TB = F::TB;
+    extern __shared__ __attribute__((aligned(16))) float xs[];  // [MR][kspan], then [MR][kspan / 8]
+    const int kt_begin = blockIdx.y * kt_per_split, kt_end = min(nkt, kt_begin + kt_per_split);
+    const int k_lo = kt_begin * KT, kspan = kt_per_split * KT;
+    float *gs = xs + MR * kspan;
+    for (int i = threadIdx.x; i < MR * kspan / 8; i += blockDim.x) {
+        const int m = i / (kspan / 8), g8 = i % (kspan / 8), k = k_lo + 8 * g8;
+        float v[8];
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[e] = (m < M && k + e < K) ? x[(size_t)m * K + k + e] : 0.f;
+            sum += v[e];
+        }
+        store8(xs + m * kspan + 8 * g8, v);
+        gs[m * (kspan / 8) + g8] = sum;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, j = lane >> 4, r = lane & 15;
+    const int n_rt = (N + 15) >> 4;
+    const int rt = blockIdx.x * 4 + (threadIdx.x >> 6);
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+    if (rt < n_rt) {
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const uint8_t *tile = wt + ((size_t)rt * nkt + kt) * TB;
+            const uint4 wv = ldnt16(tile + lane * 16);
+            const uint16_t *sc = reinterpret_cast<const uint16_t *>(tile + F::SO) + r * NB;
+            const int kl = (kt - kt_begin) * KT;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float w[8];
+                if (FMT == RRA_Q4) {
+                    const uint32_t d = u32_at(wv, b);
+                    const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {  // byte u: element 2u (low), 2u + 1 (high)
+                        w[2 * u] = (float)((lo >> (8 * u)) & 0xFFu);
+                        w[2 * u + 1] = (float)((hi >> (8 * u)) & 0xFFu);
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t d = u32_at(wv, 2 * b + h);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) w[4 * h + u] = (float)(int8_t)(d >> (8 * u));
+                    }
+                }
+                const float s = (float)__builtin_bit_cast(_Float16, sc[b]);
+                const int k0 = kl + 32 * b + 8 * j;
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    float xv[8];
+                    load8(xs + m * kspan + k0, xv);
+                    float t = FMT == RRA_Q4 ? -8.f * gs[m * (kspan / 8) + k0 / 8] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t = fmaf(w[e], xv[e], t);
+                    acc[m] = fmaf(s, t, acc[m]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        float v = acc[m];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        const int row = rt * 16 + r;
+        if (j == 0 && m < M && rt < n_rt && row < N)
+            out[(size_t)blockIdx.y * split_stride + (size_t)m * N + row] = v;
+    }
+}
+
 // Writes x (fp32 [M][K], canonical) as the B-operand image of a GEMV with
 // `ct` column tiles; groups in [K, kpad) are zeros.  One thread per group.
 template <int FMT>
@@ -1702,4 +1792,42 @@ extern "C" rra_status rra_batched_gemv_noalloc(const rra_weight *w, const float 
     const size_t stride = (size_t)m * (size_t)w->n;
     RRA_TRY(launch_gemv(*w, p, in, m, part, stride, s));
     return launch_reduce_splits(part, p.split, stride, y, m, (int)w->n, s);
+}
+
+// ------------------------------------------------------------ VALU GEMV (comparison)
+extern "C" rra_status rra_batched_gemv_valu(const rra_weight *w, const float *x, float *y,
+                                            int32_t m, void *ws, size_t ws_bytes, hipStream_t s) {
+    clear_error();
+    if (!w || !x || !y) return fail(RRA_EINVAL, "rra_batched_gemv_valu: null argument");
+    if (m < 1 || m > 8) return fail(RRA_EINVAL, "rra_batched_gemv_valu: m=%d not in 1..8", m);
+    RRA_TRY(validate_weight(w, "rra_batched_gemv_valu", true));
+    if (w->fmt != RRA_Q4 && w->fmt != RRA_Q8)
+        return fail(RRA_EINVAL, "rra_batched_gemv_valu: Q4 and Q8 weights only");
+    const GemvPlan p = gemv_plan(*w, m);
+    const int kt = tile_k(w->fmt), nkt = (int)cdiv(w->k, kt);
+    const int mr = m == 1 ? 1 : m <= 4 ? 4 : 8;
+    const size_t shm = sizeof(float) * (size_t)mr * p.kt_per_split * kt * 9 / 8;
+    if (shm > 65536)
+        return fail(RRA_EINVAL, "rra_batched_gemv_valu: a split of %d K values needs %zu bytes of LDS",
+                    p.kt_per_split * kt, shm);
+    const size_t need = p.split > 1 ? (size_t)p.split * m * w->n * sizeof(float) : 0;
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(RRA_ENOTINIT, "rra_batched_gemv_valu: workspace has %zu bytes, needs %zu",
+                    ws ? ws_bytes : (size_t)0, need);
+    float *dst = p.split > 1 ? static_cast<float *>(ws) : y;
+    const size_t stride = (size_t)m * w->n;
+    const dim3 grid((unsigned)cdiv(cdiv(w->n, 16), 4), (unsigned)p.split);
+    const auto *wd = static_cast<const uint8_t *>(w->data);
+#define RRA_VG(F, MRV)                                                                         \
+    hipLaunchKernelGGL((gemv_valu_kernel<F, MRV>), grid, dim3(256), shm, s, wd, x, dst, m,      \
+                       (int)w->n, (int)w->k, nkt, p.kt_per_split, (long long)stride)
+    if (w->fmt == RRA_Q4) {
+        if (mr == 1) RRA_VG(RRA_Q4, 1); else if (mr == 4) RRA_VG(RRA_Q4, 4); else RRA_VG(RRA_Q4, 8);
+    } else {
+        if (mr == 1) RRA_VG(RRA_Q8, 1); else if (mr == 4) RRA_VG(RRA_Q8, 4); else RRA_VG(RRA_Q8, 8);
+    }
+#undef RRA_VG
+    RRA_TRY(check_launch("gemv_valu_kernel"));
+    if (p.split == 1) return RRA_OK;
+    return launch_reduce_splits(dst, p.split, stride, y, m, (int)w->n, s);
 }

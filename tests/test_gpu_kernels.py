@@ -306,3 +306,20 @@ def test_argmax_bit_exact(v):
     ref, _ = oracle.argmax(host(l))
     assert host(tok).tolist() == ref.tolist()
     assert host(tok)[1] == 100 and host(tok)[2] == 0 and host(tok)[3] == v - 1
+
+
+@pytest.mark.parametrize("fmt,n,k", [("q4", 300, 416), ("q8", 1152, 896), ("q4", 4096, 14336),
+                                     ("q8", 896, 4864), ("q4", 37, 128)])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_valu_gemv_matches_oracle(fmt, n, k, m):
+    # the vector-ALU comparison GEMV on the same tiled weights
+    data, scale = synth.weight(n, k, fmt, 0.02, 5, f"valu_{fmt}_{n}", DEV)
+    w = rra.device_weight(data, scale, fmt)
+    x = synth.normal((m, k), 1.0, 5, f"valu_x{m}", DEV)
+    y = torch.full((m, n), float("nan"), device=DEV)
+    ws = torch.empty(max(4, rra.rra_batched_gemv_workspace_bytes(w, m)), dtype=torch.uint8,
+                     device=DEV)
+    rra.rra_batched_gemv_valu(w, x, y, m, ws)
+    torch.cuda.synchronize()
+    ref = oracle.gemv(fmt, data, scale, n, k, host(x))
+    assert_close(y, ref, what=f"valu {fmt} {n}x{k} m={m}")
