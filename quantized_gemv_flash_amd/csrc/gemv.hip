@@ -567,11 +567,18 @@ struct QGemv {
             for (int r = 0; r < RPW; ++r) {
                 const int rt = rt0 + r;
                 if (rt >= n_rt) continue;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = rt * 16 + 4 * g + i;
-                    if (row < N) o[(size_t)m * N + row] = acc[r][cc][i] * iv;
+                // rows 4g .. 4g + 3: one 16-byte store when whole and aligned
+                const int row0 = rt * 16 + 4 * g;
+                float *dst = o + (size_t)m * N + row0;
+                if (((N & 3) | (reinterpret_cast<uintptr_t>(o) & 15)) == 0 && row0 + 4 <= N) {
+                    *reinterpret_cast<float4 *>(dst) =
+                        make_float4(acc[r][cc][0] * iv, acc[r][cc][1] * iv, acc[r][cc][2] * iv,
+                                    acc[r][cc][3] * iv);
+                    continue;
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (row0 + i < N) dst[i] = acc[r][cc][i] * iv;
             }
         }
     }
@@ -972,8 +979,11 @@ __global__ __launch_bounds__(512) void gemm_q_kernel(const uint8_t *__restrict__
         p.compute(q0, xs[0], sl[0], acc);
     }
     // RMSNorm: inv of this lane's columns, then the 16 x 16 result tiles
-    // (lane holds rows 4g .. 4g + 3 of column lane % 16)
+    // (lane holds rows 4g .. 4g + 3 of column lane % 16: one 16-byte store
+    // when the rows are whole and aligned, so the four lanes of a column
+    // write its 64 contiguous bytes together)
     float *o = out + (size_t)blockIdx.y * split_stride;
+    const bool vec = ((N & 3) | (reinterpret_cast<uintptr_t>(o) & 15)) == 0;
 #pragma unroll
     for (int cw = 0; cw < G::CW; ++cw) {
         const int m = 16 * (p.cg * G::CW + cw) + (p.lane & 15);
@@ -988,11 +998,17 @@ __global__ __launch_bounds__(512) void gemm_q_kernel(const uint8_t *__restrict__
         for (int r = 0; r < G::RPW; ++r) {
             const int rt = p.rt0 + r;
             if (rt >= p.n_rt) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = rt * 16 + 4 * p.g + i;
-                if (row < N) o[(size_t)m * N + row] = acc[r][cw][i] * iv;
+            const int row0 = rt * 16 + 4 * p.g;
+            float *dst = o + (size_t)m * N + row0;
+            if (vec && row0 + 4 <= N) {
+                *reinterpret_cast<float4 *>(dst) =
+                    make_float4(acc[r][cw][0] * iv, acc[r][cw][1] * iv, acc[r][cw][2] * iv,
+                                acc[r][cw][3] * iv);
+                continue;
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (row0 + i < N) dst[i] = acc[r][cw][i] * iv;
         }
     }
 }
