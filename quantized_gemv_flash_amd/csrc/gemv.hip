@@ -432,23 +432,33 @@ struct QGemv {
             asm volatile("" ::: "memory");
             half8_t Bh[CT], Bl[CT];
             load_b(xs, b, Bh, Bl);
+            half8_t a[RPW];
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 const uint4 qv = q.q[r];
-                const half8_t a =
-                    (FMT == RRA_Q4)    ? dequant_q4(u32_at(qv, b))
-                    : (FMT == RRA_FP8) ? dequant_fp8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1))
-                                       : dequant_q8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1));
+                a[r] = (FMT == RRA_Q4)    ? dequant_q4(u32_at(qv, b))
+                       : (FMT == RRA_FP8) ? dequant_fp8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1))
+                                          : dequant_q8(u32_at(qv, 2 * b), u32_at(qv, 2 * b + 1));
+            }
+            floatx4 tt[RPW][CT];
 #pragma unroll
-                for (int cc = 0; cc < CT; ++cc) {
-                    floatx4 tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        a, Bh[cc], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    tt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Bl[cc], tt, 0, 0, 0);
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc)
+                    tt[r][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        a[r], Bh[cc], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc)
+                    tt[r][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[r], Bl[cc], tt[r][cc], 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int cc = 0; cc < CT; ++cc)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        acc[r][cc][i] = fmaf((float)sh[r][i * NB + b], tt[i], acc[r][cc][i]);
-                }
-            }
+                        acc[r][cc][i] = fmaf((float)sh[r][i * NB + b], tt[r][cc][i], acc[r][cc][i]);
         }
     }
 
