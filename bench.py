@@ -246,6 +246,49 @@ def flash_decode_in_step(S, dd, m, first_tok, start_pos, steps):
     return sec, nbytes, pos.tolist()
 
 
+def phase_line(S, dd, m, first_tok, start_pos, steps=4):
+    """The decode step split into its kernel groups ([reduces]
+    forward_graphed_replay_to_token_id: a step's time in sub-phases on
+    request): `steps` eager steps from the same start, with
+    rra_model_set_phase_events recording a HIP event between the groups on
+    the step's stream.  Returns ms per step of each group summed over the
+    layers (launch gaps included: eager, not graph-replayed)."""
+    import quantized_gemv_flash_amd as rra
+    dev = "cuda"
+    cur = torch.cuda.current_stream()
+    n = 4 * S.n_layers + 3
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record(cur)
+    x = torch.empty((m, S.hidden), device=dev)
+    pos = torch.as_tensor(start_pos, dtype=torch.int32, device=dev)
+    tok = torch.as_tensor(first_tok, dtype=torch.int32, device=dev)
+    logits = torch.empty((m, S.vocab), device=dev)
+    flags = rra.RRA_STEP_GATHER | rra.RRA_STEP_ADVANCE
+    names = ("qkv", "attention", "o_proj", "ffn")
+    tot = dict(input=0.0, head=0.0, step=0.0, **{k: 0.0 for k in names})
+    dd.model.rra_model_set_phase_events(evs)
+    try:
+        for _ in range(steps):
+            dd.model.rra_decode_step(x, pos, tok, m, flags=flags, logits=logits)
+            torch.cuda.synchronize()
+            tot["input"] += evs[0].elapsed_time(evs[1])
+            for l in range(S.n_layers):
+                for j, k in enumerate(names):
+                    tot[k] += evs[1 + 4 * l + j].elapsed_time(evs[2 + 4 * l + j])
+            tot["head"] += evs[n - 2].elapsed_time(evs[n - 1])
+            tot["step"] += evs[0].elapsed_time(evs[n - 1])
+    finally:
+        dd.model.rra_model_set_phase_events(None)
+    dd.model.rra_model_check()
+    out = {f"{k}_ms": v / steps for k, v in tot.items()}
+    out["groups"] = ("qkv: QKV GEMV (+ qkv_post); attention: flash decode + combine; o_proj: O "
+                     "GEMV; ffn: residual/norm, gate/up, SwiGLU, down, residual; head: LM head + "
+                     "argmax; eager steps, summed over the layers")
+    out["steps"] = steps
+    return out
+
+
 def flash_decode_line(reps=20):
     """The standalone attention workload (32 sequences, 32 Q / 8 KV heads, hd
     128, lengths uniform in [1, 8192], an 8192-row cache): rra_flash_decode at
@@ -657,6 +700,8 @@ def main():
     log(f"flash decode in the step: {fd_sec * 1e6:.1f} us, {fd_gbs:.0f} GB/s (chunk {plan[0]}, "
         f"head split {plan[1]}); alone {fd_alone * 1e6:.1f} us")
 
+    phases = phase_line(S, dd, m, first, lengths)
+    log(f"step phases {phases}")
     handoff = host_handoff_line(dd, S, m, first, lengths, steps)
     log(f"host hand-off {handoff}")
     m1 = None
@@ -707,6 +752,7 @@ def main():
         },
         "per_sequence_tok_s": tok_s / m,
         "host_handoff": handoff,
+        "step_phases": phases,
         "weight_kv_gbs": step_gbs,
         "weight_kv_hbm_frac": step_gbs / HBM_PEAK_GBS,
         "roofline": {

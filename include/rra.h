@@ -494,6 +494,28 @@ rra_status rra_graph_stats(const rra_model *mdl, uint64_t *captures, uint64_t *r
  * n or a null event. */
 rra_status rra_model_set_attention_events(rra_model *mdl, void *const *events, int32_t n);
 
+/* Sub-phase timing of the decode step, for measurement ([reduces]
+ * forward_graphed_replay_to_token_id splits a decode step's time into
+ * sub-phases on request).  events: n = 4 x n_layers + 3 hipEvent_t handles
+ * created by the caller with timing enabled, or NULL / n = 0 to stop.  Every
+ * eager decode step (flags without RRA_GRAPH) enqueued afterwards records them
+ * on its stream between its kernel groups:
+ *   events[0]            step start (before the gather and the first norm inputs)
+ *   events[1 + 4l]       layer l start (QKV GEMV)
+ *   events[2 + 4l]       layer l attention (flash decode and its combine)
+ *   events[3 + 4l]       layer l O GEMV
+ *   events[4 + 4l]       layer l feed-forward (norm, gate/up, SwiGLU, down, residual)
+ *   events[1 + 4 n_layers]  output norm, LM head, argmax
+ *   events[2 + 4 n_layers]  step end
+ * so hipEventElapsedTime(events[i], events[i + 1]) is the group's time,
+ * launch gaps included.  Where the small-batch path fuses work across groups
+ * (a GEMV prologue doing the residual step or the attention combine, flash
+ * decode taking the QKV partials), a group holds the kernels launched
+ * between its records.  Results are unchanged; graph steps and prefill record
+ * nothing.  The events stay the caller's.  Errors: RRA_ENOTINIT for a null
+ * model, RRA_EINVAL for a wrong n or a null event. */
+rra_status rra_model_set_phase_events(rra_model *mdl, void *const *events, int32_t n);
+
 /* Releases the host handle and its graphs (not the caller's memory). */
 void rra_model_destroy(rra_model *mdl);
 

@@ -98,6 +98,7 @@ def _load() -> ctypes.CDLL:
         "rra_model_check": ([P, P], I),
         "rra_graph_stats": ([P, POINTER(c_uint64), POINTER(c_uint64), POINTER(c_uint32)], I),
         "rra_model_set_attention_events": ([P, P, I], I),
+        "rra_model_set_phase_events": ([P, P, I], I),
         "rra_model_destroy": ([P], None),
     }
     for name, (args, res) in sig.items():
@@ -396,6 +397,19 @@ class Model:
         self._attn_events = (list(events), handles)
         _check("rra_model_set_attention_events",
                lib.rra_model_set_attention_events(self.handle, handles, len(events)))
+
+    def rra_model_set_phase_events(self, events=None):
+        """events: None (stop) or 4 x n_layers + 3 torch.cuda.Event(enable_timing=True),
+        each already recorded once (so that it exists); kept alive here."""
+        if not events:
+            self._phase_events = None
+            _check("rra_model_set_phase_events",
+                   lib.rra_model_set_phase_events(self.handle, None, 0))
+            return
+        handles = (c_void_p * len(events))(*[e.cuda_event for e in events])
+        self._phase_events = (list(events), handles)
+        _check("rra_model_set_phase_events",
+               lib.rra_model_set_phase_events(self.handle, handles, len(events)))
 
     def close(self):
         if getattr(self, "handle", None):

@@ -217,6 +217,7 @@ struct rra_model {
     // start and end of that layer's flash-decode chunk kernel in eager steps
     // (empty: none)
     std::vector<hipEvent_t> attn_events;
+    std::vector<hipEvent_t> phase_events;  // 4 x n_layers + 3 boundaries (eager steps)
     uint64_t captures = 0, replays = 0;
     uint32_t last_kernels = 0;
 };
@@ -388,6 +389,14 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
     const int H = d.hidden, nq = d.n_heads, nkv = d.n_kv_heads, hd = d.head_dim,
               I = d.intermediate;
     const int nqkv = (nq + 2 * nkv) * hd;
+    // Sub-phase boundaries (eager steps only): a record on the step's stream
+    // between kernel groups, so each pair of records spans that group.
+    const bool phased = !M->phase_events.empty() && !(flags & RRA_GRAPH);
+    auto mark = [&](int i) -> rra_status {
+        if (phased) RRA_TRY_HIP(hipEventRecord(M->phase_events[i], s));
+        return RRA_OK;
+    };
+    RRA_TRY(mark(0));
     if (flags & RRA_STEP_GATHER)
         RRA_TRY(launch_embed_gather(d.embed, tok_in, pos, x, m, H, d.vocab, M->err, s));
     const int np = ss_parts(H);
@@ -418,6 +427,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
     GemvPrologue pr_qkv{kProNone, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
     for (int l = 0; l < d.n_layers; ++l) {
         const rra_layer_desc &L = M->layers[l];
+        RRA_TRY(mark(1 + 4 * l));
         // attention block
         const GemvPlan &pq = M->plan_qkv[m];
         const bool rq = pr_qkv.kind == kProResid;
@@ -438,6 +448,7 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         const GemvPlan &po = M->plan_o[m];
         const bool pro_o = gemv_takes_prologue(L.wo, po, m);
         const FragOut fo_o = image_for(M, L.wo, m);
+        RRA_TRY(mark(2 + 4 * l));
         // (eager steps only: the timed launch is not one a graph captures)
         const bool timed = !M->attn_events.empty() && !(flags & RRA_GRAPH);
         RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
@@ -449,8 +460,10 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
         GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
                         0, 0, nq, nc_max, d.max_len};
         pa.err = M->err;
+        RRA_TRY(mark(3 + 4 * l));
         RRA_TRY(launch_gemv(L.wo, po, gemv_input(M, L.wo, M->attn), m, M->part_d, (size_t)m * H, s,
                             nullptr, pro_o ? &pa : nullptr));
+        RRA_TRY(mark(4 + 4 * l));
         // feed-forward block
         const GemvPlan &pg = M->plan_gu[m];
         if (gemv_takes_resid_prologue(L.wgu, pg, m, po.split)) {
@@ -486,11 +499,13 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
             xc = x_out;
         }
     }
-    if (flags & kStepNoHead) return RRA_OK;
+    RRA_TRY(mark(1 + 4 * d.n_layers));
+    if (flags & kStepNoHead) return mark(2 + 4 * d.n_layers);
     RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits, 0, s,
                         &nrm));
-    return launch_argmax(logits, tok_out, m, d.vocab, M->argmax_ws, pos,
-                         (flags & RRA_STEP_ADVANCE) != 0, s);
+    RRA_TRY(launch_argmax(logits, tok_out, m, d.vocab, M->argmax_ws, pos,
+                          (flags & RRA_STEP_ADVANCE) != 0, s));
+    return mark(2 + 4 * d.n_layers);
 }
 
 // One prompt chunk: tokens[0..n) of cache slot `seq` at positions start ..
@@ -798,6 +813,23 @@ extern "C" rra_status rra_model_set_attention_events(rra_model *M, void *const *
         if (!events[i]) return fail(RRA_EINVAL, "rra_model_set_attention_events: null event %d", i);
     M->attn_events.assign(reinterpret_cast<const hipEvent_t *>(events),
                           reinterpret_cast<const hipEvent_t *>(events) + n);
+    return RRA_OK;
+}
+
+extern "C" rra_status rra_model_set_phase_events(rra_model *M, void *const *events, int32_t n) {
+    clear_error();
+    if (!M) return fail(RRA_ENOTINIT, "rra_model_set_phase_events: null model");
+    if (!events || n == 0) {
+        M->phase_events.clear();
+        return RRA_OK;
+    }
+    if (n != 4 * M->d.n_layers + 3)
+        return fail(RRA_EINVAL, "rra_model_set_phase_events: n=%d, need 4 x %d layers + 3", n,
+                    M->d.n_layers);
+    for (int32_t i = 0; i < n; ++i)
+        if (!events[i]) return fail(RRA_EINVAL, "rra_model_set_phase_events: null event %d", i);
+    M->phase_events.assign(reinterpret_cast<const hipEvent_t *>(events),
+                           reinterpret_cast<const hipEvent_t *>(events) + n);
     return RRA_OK;
 }
 

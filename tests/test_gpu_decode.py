@@ -128,6 +128,48 @@ def test_attention_events_time_each_layer_and_change_nothing(m):
     assert e.value.status == rra.RRA_EINVAL
 
 
+@pytest.mark.parametrize("m", [2, 6])  # the fused small-batch path and the separate kernels
+def test_phase_events_split_the_step_and_change_nothing(m):
+    # rra_model_set_phase_events: eager steps that record the 4 x n_layers + 3
+    # sub-phase boundaries give bitwise the same ids, logits, hidden state and
+    # caches as steps without them; every group's interval is a time >= 0, and
+    # the groups add up to the step's span; a graph step records nothing.
+    S = SMALL_DECODERS[2]
+    W = synth.decoder_weights(S, seed=4, device=DEV, gamma="random")
+    plain, timed = Run(S, W, m, 16), Run(S, W, m, 16)
+    cur = torch.cuda.current_stream()
+    n = 4 * S.n_layers + 3
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record(cur)
+    timed.dd.model.rra_model_set_phase_events(evs)
+    toks = synth.first_tokens(S, m, seed=4).tolist()
+    for step in range(3):
+        pos = [step + i for i in range(m)]
+        a = plain.step(toks, pos)
+        b = timed.step(toks, pos)
+        assert a[0] == b[0] and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+        toks = a[0]
+        torch.cuda.synchronize()
+        ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(n - 1)]
+        assert all(0.0 <= t < 1000.0 for t in ms), ms
+        assert abs(sum(ms) - evs[0].elapsed_time(evs[-1])) < 1e-2
+    span = evs[0].elapsed_time(evs[-1])  # the last eager step's
+    pos = [3 + i for i in range(m)]
+    a = plain.step(toks, pos)
+    b = timed.step(toks, pos, flags=rra.RRA_GRAPH)
+    assert a[0] == b[0] and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    torch.cuda.synchronize()
+    assert evs[0].elapsed_time(evs[-1]) == span  # not recorded again by the graph step
+    for l in range(S.n_layers):
+        assert torch.equal(plain.dd.k_caches[l], timed.dd.k_caches[l])
+        assert torch.equal(plain.dd.v_caches[l], timed.dd.v_caches[l])
+    timed.dd.model.rra_model_set_phase_events(None)
+    with pytest.raises(rra.RraError) as e:
+        timed.dd.model.rra_model_set_phase_events(evs[:-1])
+    assert e.value.status == rra.RRA_EINVAL
+
+
 def test_capture_failure_discarded_and_step_runs_eagerly(monkeypatch):
     # A failed capture ([reduces] try_graph_capture): the graph is discarded,
     # the stream leaves capture mode, the step runs eagerly with the same

@@ -151,6 +151,11 @@ def test_attention_events_need_a_model():
     assert b"null model" in rra.lib.rra_last_error()
 
 
+def test_phase_events_need_a_model():
+    assert rra.lib.rra_model_set_phase_events(None, None, 0) == rra.RRA_ENOTINIT
+    assert b"null model" in rra.lib.rra_last_error()
+
+
 @pytest.mark.parametrize("m,nkv,max_len,splits", [
     (32, 8, 4160, 5),    # 8B-shaped, M=32: 1280 workgroups, capped at 5 splits per sequence
     (32, 8, 8192, 8),    # 8192-row cache: 1024-row splits (the row cap) give 8
