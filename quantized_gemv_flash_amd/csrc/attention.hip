@@ -491,11 +491,12 @@ __global__ __launch_bounds__(64 * G) void prefill_attn_kernel(
             mrow[i] = mn;
             // P into [row][key] fp16 hi / lo (the A operand layout is read back below)
             const int row = 4 * j + i;
-            const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+            const float x0 = as_fp32(p0), x1 = as_fp32(p1);
+            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
             pf[wave][0][row * 32 + r] = h0;
-            pf[wave][1][row * 32 + r] = (_Float16)(p0 - (float)h0);
+            pf[wave][1][row * 32 + r] = (_Float16)(x0 - (float)h0);
             pf[wave][0][row * 32 + 16 + r] = h1;
-            pf[wave][1][row * 32 + 16 + r] = (_Float16)(p1 - (float)h1);
+            pf[wave][1][row * 32 + 16 + r] = (_Float16)(x1 - (float)h1);
         }
         __builtin_amdgcn_wave_barrier();
         // ---- O = O alpha + P V: A = P[16 rows][32 keys] (lane (j, r): row r, keys 8 j ..)

@@ -42,11 +42,23 @@ __device__ __forceinline__ int frag_slot(int j, int r, int b) {
     return j * 16 + ((r ^ swz) & 15);
 }
 
-// Splits 8 consecutive fp32 activations (k order) into hi/lo fp16 operands.
-// Contraction is off: the producer's product (gamma x, silu(g) u, ...) must
-// be rounded to fp32 before the subtraction, whichever kernel inlines this,
-// so that every producer of an image writes the same bits.  Returns false if
-// a value has |x| >= 65504 (its fp16 high part may not be finite) or is NaN.
+// The producer's value as the fp32 number it is: an empty asm the compiler
+// cannot see through, so that the fp16 conversions below start from the
+// rounded fp32 value.  Without it the compiler may fold the producer's
+// multiply (gamma x, silu(g) u, ...) into the conversion used for x - hi
+// (v_fma_mixlo_f16 of the exact product, one rounding) while the stored high
+// part converts the fp32-rounded product (two roundings): for a value on an
+// fp16 midpoint the two disagree, hi + lo is then off by one fp16 unit, and
+// kernels that inline the split differently write different bits.
+__device__ __forceinline__ float as_fp32(float x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
+// Splits 8 consecutive fp32 activations (k order) into hi/lo fp16 operands:
+// hi = fp16(x), lo = fp16(x - hi) (x - hi is exact in fp32).  Returns false
+// if a value has |x| >= 65504 (its fp16 high part may not be finite) or is
+// NaN.
 template <int FMT>
 __device__ __forceinline__ bool split8(const float (&v)[8], half8_t &hi, half8_t &lo) {
 #pragma clang fp contract(off)
@@ -54,10 +66,11 @@ __device__ __forceinline__ bool split8(const float (&v)[8], half8_t &hi, half8_t
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int src = (FMT == RRA_Q4) ? (e >> 1) + 4 * (e & 1) : e;
-        const _Float16 h = (_Float16)v[src];
+        const float x = as_fp32(v[src]);
+        const _Float16 h = (_Float16)x;
         hi[e] = h;
-        lo[e] = (_Float16)(v[src] - (float)h);
-        ok = ok && __builtin_fabsf(v[src]) < 65504.0f;
+        lo[e] = (_Float16)(x - (float)h);
+        ok = ok && __builtin_fabsf(x) < 65504.0f;
     }
     return ok;
 }
@@ -70,9 +83,10 @@ __device__ __forceinline__ void split_exact(const float (&v)[8], half8_t &hi, ha
 #pragma clang fp contract(off)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const _Float16 h = (_Float16)v[e];
+        const float x = as_fp32(v[e]);
+        const _Float16 h = (_Float16)x;
         hi[e] = h;
-        lo[e] = (_Float16)(v[e] - (float)h);
+        lo[e] = (_Float16)(x - (float)h);
     }
 }
 
