@@ -33,13 +33,16 @@ inline size_t frag_image_bytes(int fmt, int ct, int64_t k) {
 }
 
 // LDS/image slot of B-operand lane (j, r) (lane = 16j + r) in the fragment of
-// block b.  A 16-lane read phase (fixed j) is a permutation of 16 consecutive
-// slots; a 16-lane write phase covering every (b, j) of one row r hits 16
-// distinct bank groups.
+// block b: the lane's own slot, so a wave's fragment read is one contiguous
+// 1 KiB.  On gfx950 (64 LDS banks) that reads at the full 256 B per clock;
+// an XOR swizzle that depends on j (spreading the writes of one row over the
+// banks) halves the read rate, and the reads are the frequent side: every
+// wave of a GEMV workgroup reads every fragment, while only the small-batch
+// prologues write fragments into LDS at all (DMA copies whole fragments).
 template <int FMT>
 __device__ __forceinline__ int frag_slot(int j, int r, int b) {
-    const int swz = (FMT == RRA_Q4) ? (j * 4 + b) : (j * 4 + b * 2);
-    return j * 16 + ((r ^ swz) & 15);
+    (void)b;
+    return j * 16 + r;
 }
 
 // The producer's value as the fp32 number it is: an empty asm the compiler
