@@ -186,6 +186,22 @@ __global__ void embed_gather_kernel(const float *__restrict__ embed, const uint3
         return;
     }
     const float *er = embed + (size_t)t * h;
+    if ((h & 3) == 0) {
+        // 16-byte copies, four per thread in flight before any store (one
+        // memory round trip for a 4096-wide row instead of sixteen)
+        const float4 *e4 = reinterpret_cast<const float4 *>(er);
+        float4 *x4 = reinterpret_cast<float4 *>(xr);
+        const int h4 = h >> 2;
+        for (int i0 = threadIdx.x; i0 < h4; i0 += 4 * blockDim.x) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = e4[min(i0 + u * (int)blockDim.x, h4 - 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + u * (int)blockDim.x < h4) x4[i0 + u * blockDim.x] = v[u];
+        }
+        return;
+    }
     for (int i = threadIdx.x; i < h; i += blockDim.x) xr[i] = er[i];
 }
 
@@ -209,11 +225,17 @@ __global__ __launch_bounds__(256) void argmax_pass1_kernel(const float *__restri
     const float *l = logits + (size_t)m * v;
     float best = -INFINITY;
     uint32_t bidx = 0xFFFFFFFFu;
-#pragma unroll 4
-    for (int i = 0; i < kArgmaxPerBlock / 256; ++i) {
-        const int idx = blk * kArgmaxPerBlock + i * 256 + threadIdx.x;
-        if (idx < v) arg_combine(best, bidx, l[idx], (uint32_t)idx);
-    }
+    // every load first (clamped index), then the combines: one memory round
+    // trip; arg_combine's order (value, then lowest index) makes the result
+    // independent of the order the candidates are taken in
+    constexpr int PER = kArgmaxPerBlock / 256;
+    float x[PER];
+    const int base = blk * kArgmaxPerBlock + (int)threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x[i] = l[min(base + i * 256, v - 1)];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if (base + i * 256 < v) arg_combine(best, bidx, x[i], (uint32_t)(base + i * 256));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         arg_combine(best, bidx, __shfl_xor(best, off, 64), __shfl_xor(bidx, off, 64));
