@@ -113,6 +113,23 @@ def test_gemv_full_shapes_sampled_rows(fmt, n, k):
         assert_close(host(y)[:, rows], ref, what=f"gemv {fmt} {n}x{k} m={m}")
 
 
+@pytest.mark.parametrize("m", [17, 32])
+def test_gemv_three_row_tiles_ragged(m):
+    # A short-split shape that takes three row tiles per wave at M > 16 (380
+    # row tiles: 256 workgroups of 12 instead of 384 of 8), with a ragged
+    # last workgroup (8 of its 12 row tiles) and a partial last row tile.
+    n, k = 6075, 4096
+    banner("gemv rpw3", n, k, m)
+    data, scale = synth.weight(n, k, "q4", 0.02, 0, "rpw3", DEV)
+    hd, hs = host(data), host(scale)
+    rows = sorted(set(np.random.default_rng(3).integers(0, n, 80).tolist())
+                  | set(range(n - 40, n)) | {0, 6063, 6064})
+    x = synth.normal((m, k), 1.0, 0, f"rpw3x{m}", DEV)
+    y = _gemv("q4", data, scale, x, m)
+    ref = oracle.gemv("q4", hd, hs, n, k, host(x), rows=rows)
+    assert_close(host(y)[:, rows], ref, what=f"gemv rpw3 m={m}")
+
+
 # ---------------------------------------------------------------- KV scatter
 @pytest.mark.parametrize("m,nkv,hd,max_len", [(1, 2, 64, 16), (5, 8, 128, 300), (32, 2, 128, 1152)])
 def test_kv_scatter_bit_exact(m, nkv, hd, max_len):
