@@ -380,82 +380,125 @@ const void *gemv_input(const rra_model *M, const rra_weight &w, const float *row
 // Internal step flag: stop after the last layer (no LM head, no argmax).
 constexpr int kStepNoHead = 1 << 16;
 
-// Every launch of one decode step, in stream order.  Row i reads token
-// tok_in[i] (under RRA_STEP_GATHER), sits at position pos[i] and uses cache
-// slot i; the greedy ids go to tok_out.
-rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *tok_in,
-                        uint32_t *tok_out, float *logits, int m, int flags, hipStream_t s) {
-    const rra_model_desc &d = M->d;
-    const int H = d.hidden, nq = d.n_heads, nkv = d.n_kv_heads, hd = d.head_dim,
-              I = d.intermediate;
-    const int nqkv = (nq + 2 * nkv) * hd;
-    // Sub-phase boundaries (eager steps only): a record on the step's stream
-    // between kernel groups, so each pair of records spans that group.
-    const bool phased = !M->phase_events.empty() && !(flags & RRA_GRAPH);
-    auto mark = [&](int i) -> rra_status {
-        if (phased) RRA_TRY_HIP(hipEventRecord(M->phase_events[i], s));
-        return RRA_OK;
-    };
-    RRA_TRY(mark(0));
-    if (flags & RRA_STEP_GATHER)
-        RRA_TRY(launch_embed_gather(d.embed, tok_in, pos, x, m, H, d.vocab, M->err, s));
-    const int np = ss_parts(H);
-    const NormIn nrm{M->ss, np, d.rms_eps};
-    // RMSNorm is formed inside each consuming GEMV from per-chunk sums of
-    // squares of x; the first ones come from the step input.  Each producer
-    // also writes the next GEMV's activation image.
-    const rra_layer_desc &L0 = M->layers[0];
-    RRA_TRY(launch_residual_ss(nullptr, 0, 0, x, x, M->ss, L0.attn_gamma, M->xg, m, H,
-                               image_for(M, L0.wqkv, m), s));
+// The launches of one decode step, in stream order, as phases: begin() (the
+// step input), then per layer pre(l) (the QKV GEMV and its epilogue),
+// attn(l) (flash decode) and post(l) (the O GEMV, the feed-forward block and
+// the residual steps), then head() (LM head and argmax); enqueue_step runs
+// them in that order.  Row i reads token tok_in[i] (under
+// RRA_STEP_GATHER), sits at position pos[i] and uses cache slot i; the
+// greedy ids go to tok_out.
+struct Stepper {
+    rra_model *M;
+    float *x;
+    uint32_t *pos;
+    const uint32_t *tok_in;
+    uint32_t *tok_out;
+    float *logits;
+    int m, flags;
+    hipStream_t s;
+    int H = 0, nq = 0, nkv = 0, hd = 0, I = 0, nqkv = 0;
+    NormIn nrm{nullptr, 0, 0.f};
+    bool phased = false;  // sub-phase boundaries (eager steps only)
     // The residual stream lives in x or in M->xalt.  At small m an
     // RMSNorm-fused GEMV can do the residual step itself (kProResid): it reads
     // the stream and the previous GEMV's partials and one of its workgroups
     // writes the new stream to the other buffer.  The last residual step
     // always writes x.
-    float *xc = x;
-    auto other = [&](const float *p) { return p == x ? M->xalt : x; };
-    auto resid_pro = [&](const float *planes, int split, const float *gamma) {
+    float *xc = nullptr;
+    GemvPrologue pr_qkv{kProNone, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
+
+    Stepper(rra_model *M_, float *x_, uint32_t *pos_, const uint32_t *tok_in_,
+            uint32_t *tok_out_, float *logits_, int m_, int flags_, hipStream_t s_)
+        : M(M_), x(x_), pos(pos_), tok_in(tok_in_), tok_out(tok_out_), logits(logits_), m(m_),
+          flags(flags_), s(s_) {
+        const rra_model_desc &d = M->d;
+        H = d.hidden;
+        nq = d.n_heads;
+        nkv = d.n_kv_heads;
+        hd = d.head_dim;
+        I = d.intermediate;
+        nqkv = (nq + 2 * nkv) * hd;
+        nrm = NormIn{M->ss, ss_parts(H), d.rms_eps};
+        phased = !M->phase_events.empty() && !(flags & RRA_GRAPH);
+        xc = x;
+    }
+    // a record on the step's stream between kernel groups, so each pair of
+    // records spans that group
+    rra_status mark(int i) {
+        if (phased) RRA_TRY_HIP(hipEventRecord(M->phase_events[i], s));
+        return RRA_OK;
+    }
+    float *other(const float *p) const { return p == x ? M->xalt : x; }
+    GemvPrologue resid_pro(const float *planes, int split, const float *gamma) {
         GemvPrologue r{kProResid, planes, nullptr, nullptr, (long long)m * H, split, H, 0, 0};
         r.x_in = xc;
         r.x_out = other(xc);
         r.gamma = gamma;
-        r.eps = d.rms_eps;
+        r.eps = M->d.rms_eps;
         r.err = M->err;
         xc = r.x_out;
         return r;
-    };
-    GemvPrologue pr_qkv{kProNone, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
-    for (int l = 0; l < d.n_layers; ++l) {
+    }
+    // At small m flash decode takes the QKV partials itself (QkvIn: sum,
+    // RoPE, the new K/V row, seq_len); otherwise qkv_post does that work.
+    bool fuse_qkv() const { return m <= 4; }
+
+    rra_status begin() {
+        const rra_model_desc &d = M->d;
+        RRA_TRY(mark(0));
+        if (flags & RRA_STEP_GATHER)
+            RRA_TRY(launch_embed_gather(d.embed, tok_in, pos, x, m, H, d.vocab, M->err, s));
+        // RMSNorm is formed inside each consuming GEMV from per-chunk sums of
+        // squares of x; the first ones come from the step input.  Each
+        // producer also writes the next GEMV's activation image.
+        const rra_layer_desc &L0 = M->layers[0];
+        return launch_residual_ss(nullptr, 0, 0, x, x, M->ss, L0.attn_gamma, M->xg, m, H,
+                                  image_for(M, L0.wqkv, m), s);
+    }
+
+    rra_status pre(int l) {
+        const rra_model_desc &d = M->d;
         const rra_layer_desc &L = M->layers[l];
         RRA_TRY(mark(1 + 4 * l));
-        // attention block
         const GemvPlan &pq = M->plan_qkv[m];
         const bool rq = pr_qkv.kind == kProResid;
         RRA_TRY(launch_gemv(L.wqkv, pq, gemv_input(M, L.wqkv, M->xg), m, M->part, (size_t)m * nqkv,
                             s, rq ? nullptr : &nrm, rq ? &pr_qkv : nullptr));
-        // At small m flash decode takes the QKV partials itself (QkvIn: sum,
-        // RoPE, the new K/V row, seq_len); otherwise qkv_post does that work.
-        const bool fuse_qkv = m <= 4;
-        const QkvIn qi{M->part, pq.split, (long long)m * nqkv, pos, M->rope,
-                       L.k_cache, L.v_cache, M->lens, M->err};
-        if (!fuse_qkv)
+        if (!fuse_qkv())
             RRA_TRY(launch_qkv_post(M->part, pq.split, (size_t)m * nqkv, pos, M->rope, M->q,
                                     L.k_cache, L.v_cache, M->lens, M->err, m, nq, nkv, hd,
                                     d.max_len, nullptr, s));
-        // At small m the O GEMV combines the attention partials itself and the
-        // down GEMV forms SwiGLU itself (GemvPrologue): two launches fewer per
-        // layer, with the same arithmetic as the kernels they stand in for.
-        const GemvPlan &po = M->plan_o[m];
-        const bool pro_o = gemv_takes_prologue(L.wo, po, m);
+        return RRA_OK;
+    }
+
+    rra_status attn(int l) {
+        const rra_model_desc &d = M->d;
+        const rra_layer_desc &L = M->layers[l];
+        const GemvPlan &pq = M->plan_qkv[m];
+        const QkvIn qi{M->part, pq.split, (long long)m * nqkv, pos, M->rope,
+                       L.k_cache, L.v_cache, M->lens, M->err};
+        // At small m the O GEMV combines the attention partials itself and
+        // the down GEMV forms SwiGLU itself (GemvPrologue): two launches
+        // fewer per layer, with the same arithmetic as the kernels they
+        // stand in for.
+        const bool pro_o = gemv_takes_prologue(L.wo, M->plan_o[m], m);
         const FragOut fo_o = image_for(M, L.wo, m);
         RRA_TRY(mark(2 + 4 * l));
         // (eager steps only: the timed launch is not one a graph captures)
         const bool timed = !M->attn_events.empty() && !(flags & RRA_GRAPH);
-        RRA_TRY(launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
-                                    d.max_len, M->chunk[m], M->fd, s, &fo_o, nullptr, !pro_o,
-                                    fuse_qkv ? &qi : nullptr,
-                                    timed ? M->attn_events[2 * l] : nullptr,
-                                    timed ? M->attn_events[2 * l + 1] : nullptr, M->hsplit[m]));
+        return launch_flash_decode(M->q, L.k_cache, L.v_cache, M->lens, M->attn, m, nq, nkv, hd,
+                                   d.max_len, M->chunk[m], M->fd, s, &fo_o, nullptr, !pro_o,
+                                   fuse_qkv() ? &qi : nullptr,
+                                   timed ? M->attn_events[2 * l] : nullptr,
+                                   timed ? M->attn_events[2 * l + 1] : nullptr, M->hsplit[m]);
+    }
+
+    rra_status post(int l) {
+        const rra_model_desc &d = M->d;
+        const rra_layer_desc &L = M->layers[l];
+        const GemvPlan &pq = M->plan_qkv[m];
+        const GemvPlan &po = M->plan_o[m];
+        const bool pro_o = gemv_takes_prologue(L.wo, po, m);
         const int nc_max = (int)cdiv(d.max_len, M->chunk[m]);
         GemvPrologue pa{kProAttn, M->fd, fd_part_lse(M->fd, m, nq, hd, nc_max), M->lens,
                         0, 0, nq, nc_max, d.max_len};
@@ -498,14 +541,31 @@ rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *t
                                        next_gamma, M->xg, m, H, image_for(M, next_w, m), s));
             xc = x_out;
         }
+        return RRA_OK;
     }
-    RRA_TRY(mark(1 + 4 * d.n_layers));
-    if (flags & kStepNoHead) return mark(2 + 4 * d.n_layers);
-    RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits, 0, s,
-                        &nrm));
-    RRA_TRY(launch_argmax(logits, tok_out, m, d.vocab, M->argmax_ws, pos,
-                          (flags & RRA_STEP_ADVANCE) != 0, s));
-    return mark(2 + 4 * d.n_layers);
+
+    rra_status head() {
+        const rra_model_desc &d = M->d;
+        RRA_TRY(mark(1 + 4 * d.n_layers));
+        if (flags & kStepNoHead) return mark(2 + 4 * d.n_layers);
+        RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits,
+                            0, s, &nrm));
+        RRA_TRY(launch_argmax(logits, tok_out, m, d.vocab, M->argmax_ws, pos,
+                              (flags & RRA_STEP_ADVANCE) != 0, s));
+        return mark(2 + 4 * d.n_layers);
+    }
+};
+
+rra_status enqueue_step(rra_model *M, float *x, uint32_t *pos, const uint32_t *tok_in,
+                        uint32_t *tok_out, float *logits, int m, int flags, hipStream_t s) {
+    Stepper st(M, x, pos, tok_in, tok_out, logits, m, flags, s);
+    RRA_TRY(st.begin());
+    for (int l = 0; l < M->d.n_layers; ++l) {
+        RRA_TRY(st.pre(l));
+        RRA_TRY(st.attn(l));
+        RRA_TRY(st.post(l));
+    }
+    return st.head();
 }
 
 // One prompt chunk: tokens[0..n) of cache slot `seq` at positions start ..
