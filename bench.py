@@ -492,7 +492,7 @@ def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps, of_m=32):
                        f"same workload ({sec:.1f} s; fp64, {threads} OpenMP threads)")
 
 
-def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True, cpu=False):
+def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True, cpu=False, tune=True):
     """The 1.5B-shaped Q4 decoder over a synthetic 1024-row KV context per
     sequence: greedy decode tok/s at each batch size M (one graph per M)."""
     import synth
@@ -505,7 +505,10 @@ def m_sweep_line(steps=32, ms=(1, 4, 8, 16, 32), prefill=True, cpu=False):
     wbytes = dd.weight_bytes()
     out = dict(workload=f"{S.name}: 1024-row context, {steps} greedy steps per M, one graph per step",
                weight_bytes=wbytes)
-    plans = dd.model.rra_model_tune_attention(list(ms), [L + steps // 2 for L in lengths])
+    if tune:
+        plans = dd.model.rra_model_tune_attention(list(ms), [L + steps // 2 for L in lengths])
+    else:
+        plans = {m: dd.model.rra_model_attention_plan(m) for m in ms}
     out["attention_plans"] = {f"m{m}": dict(chunk=plans[m][0], head_split=plans[m][1]) for m in ms}
     for m in ms:
         sec, _, _ = timed_greedy(dd, S, m, first[:m], lengths[:m], steps, 2)
@@ -640,7 +643,8 @@ def main():
         return
     if args.only_sweep:
         ms = tuple(int(v) for v in args.only_sweep.split(","))
-        print(json.dumps({"m_sweep": m_sweep_line(steps=args.steps, ms=ms, prefill=False)}),
+        print(json.dumps({"m_sweep": m_sweep_line(steps=args.steps, ms=ms, prefill=False,
+                                                  tune=not args.fixed_plans)}),
               flush=True)
         return
     if args.only_m1:

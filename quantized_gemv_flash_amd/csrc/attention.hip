@@ -82,7 +82,17 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict
 // it writes there are the same), and the first of the hs workgroups of its
 // KV head writes it to the cache.  The arithmetic is qkv_post_kernel's
 // (sum_splits2, rope_pair), so the results equal the unfused path bitwise.
-template <int HD, int G, bool QF>
+//
+// EARLY (fused input, grids of at most one workgroup per compute unit): the
+// first round's K rows and V rows depend neither on the query nor on the
+// position, so they are requested before either is read, clamped to the
+// split's rows in the allocated cache rather than to those below the position
+// (rows past the sequence are loaded and never used): the position, the QKV
+// partials and the first K/V rows then share one memory round trip.  With
+// more workgroups per compute unit that loses (a wave's loads return in
+// order, so rows requested ahead delay the partials, and the rows past the
+// sequence add traffic).
+template <int HD, int G, bool QF, bool EARLY = false>
 __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
     const uint32_t *__restrict__ seq_len, const uint32_t *__restrict__ slot_seq,
@@ -91,6 +101,32 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     constexpr int GP = (G + 3) & ~3;  // probabilities stored key-major, G padded to 4
     const int c = blockIdx.x, g = blockIdx.y / hs, m = blockIdx.z;
     const int hq0 = blockIdx.y * G;  // first query head: g G hs + (blockIdx.y mod hs) G
+    static_assert(QF || !EARLY, "early K/V rows need the fused QKV input");
+    float4 ek[2][HD / 32], ev[8];  // EARLY: the first K rows and V rows
+    if constexpr (EARLY) {
+        // the index maps of the score loop (8 lanes per K row, 2 rows per lane)
+        // and of the value loop (hd/4 lanes per V row, 8 rows per lane); the
+        // fused input has no slot map, sequence m's cache is slot m
+        const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
+        constexpr int LPK = HD / 4, KPW = 64 / LPK;
+        const int ncap = (max_len - c + nc_max - 1) / nc_max;  // >= 1: c < nc_max <= max_len
+        const size_t at0 = (((size_t)m * nkv + g) * max_len + c) * HD;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (u * 32 + wv * 8 >= ncap) break;  // wave-uniform: no rows left
+            const int tc = min(u * 32 + wv * 8 + ks0, ncap - 1);
+#pragma unroll
+            for (int i = 0; i < HD / 32; ++i)
+                ek[u][i] = ldnt(kc + at0 + (size_t)tc * nc_max * HD + 4 * (e0 + 8 * i));
+        }
+        const int d4 = ln % LPK, r0 = wv * KPW + ln / LPK;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tr = min(r0 + u * 4 * KPW, ncap - 1);
+            ev[u] = ldnt(vc + at0 + (size_t)tr * nc_max * HD + 4 * d4);
+        }
+    }
     uint32_t p = 0;
     bool ok = false;
     int L;
@@ -131,7 +167,13 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     constexpr int F4 = HD / 32;  // 128-bit loads per lane per row
     constexpr int UK = 2;        // rows per lane per score round (see below)
     float4 kv0[UK][F4];
-    if constexpr (QF) {
+    static_assert(UK == 2, "EARLY loads two K rows per lane");
+    if constexpr (EARLY) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u)
+#pragma unroll
+            for (int i = 0; i < F4; ++i) kv0[u][i] = ek[u][i];
+    } else if constexpr (QF) {
         const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
         const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
         const size_t cs0 = slot_seq ? slot_seq[m] : (uint32_t)m;
@@ -247,6 +289,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     // hd/4 lanes per row, rows r0 + 4 KPW u of each round of RS rows; rows
     // past n are clamped loads, never used.
     constexpr int LPK = HD / 4, KPW = 64 / LPK, UV = 8, RS = 4 * KPW * UV;
+    static_assert(UV == 8, "EARLY loads eight V rows per lane");
     const int d4 = lane % LPK, r0 = wave * KPW + lane / LPK;
     float4 vb[UV];
     auto vload = [&](int base) {
@@ -258,7 +301,13 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
                 vb[u] = *reinterpret_cast<const float4 *>(vn + 4 * d4);
         }
     };
-    vload(0);
+    if constexpr (EARLY) {
+#pragma unroll
+        for (int u = 0; u < UV; ++u)
+            vb[u] = r0 + u * 4 * KPW == tp ? *reinterpret_cast<const float4 *>(vn + 4 * d4) : ev[u];
+    } else {
+        vload(0);
+    }
     __syncthreads();
 
     // ---- per-head max, exponentials, sum
@@ -612,10 +661,18 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
                                         (qi ? (size_t)(G + 2) * HD : 0));
     const dim3 grid(nc_max, nkv * hs, m);
     const QkvIn qa = qi ? *qi : QkvIn{};
+    // Early K/V rows (fused input) only while every workgroup has a compute
+    // unit to itself: the 1.5B-shaped decoder at M = 4 (864 workgroups) was
+    // 1-2 % slower with them, M = 1 grids gain about 1 %.
+    const bool early = qi && (int64_t)nc_max * nkv * hs * m <= 256;
     // Timed launches (ev0/ev1 set) go through hipExtLaunchKernel, whose event
     // pair is stamped at the kernel's own start and end.
     if (ev0 || ev1) {
-        if (qi)
+        if (early)
+            hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, true, true>), grid, dim3(256),
+                                  (uint32_t)shm, s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po,
+                                  pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
+        else if (qi)
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), (uint32_t)shm, s,
                                   ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
                                   max_len, chunk, nc_max, hs, qa);
@@ -623,6 +680,9 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), (uint32_t)shm,
                                   s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
                                   max_len, chunk, nc_max, hs, qa);
+    } else if (early) {
+        hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true, true>), grid, dim3(256), shm, s, q, kc, vc,
+                           lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
     } else if (qi) {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), shm, s, q, kc, vc, lens,
                            slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
