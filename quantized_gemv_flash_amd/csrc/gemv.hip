@@ -1518,22 +1518,23 @@ rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img
         if (p.rpw >= 2) return launch_q<FMT, 2, 2, 8>(w, p, img, m, out, stride, nrm, pro, s);
         return launch_q<FMT, 2, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
     }
-    // Short splits at m > 16: two row tiles per wave whatever the plan says
-    // (the row tiling never changes a row's arithmetic): half the workgroups,
-    // each with 4 K tiles of two-column-tile image in LDS, fit one round on
-    // the chip (MI355X, 8B-shaped step at M=32: 7.51 -> 7.43 ms).  Three row
-    // tiles where that turns more than one workgroup per compute unit into
-    // at most one (the 8B QKV GEMV: 384 -> 256 workgroups, 16.0 -> 15.4 us,
-    // step +0.35 %): with 1.5 workgroups per unit, half the units run two
-    // and set the kernel's time.
+    // At m > 16, two row tiles per wave whatever the plan says (the row
+    // tiling never changes a row's arithmetic).  Short splits: half the
+    // workgroups, each with 4 K tiles of two-column-tile image in LDS, fit one
+    // round on the chip (MI355X, 8B-shaped step at M=32: 7.51 -> 7.43 ms).
+    // Long splits: each LDS fragment read feeds two row tiles (the 8B down
+    // GEMV: 512 -> 256 workgroups, step 6.95 -> 6.91 ms; four row tiles in
+    // the gate/up GEMV, 448 -> 224 workgroups, lost 0.2 %).  Three row tiles
+    // where that turns more than one workgroup per compute unit into at most
+    // one (the 8B QKV GEMV: 384 -> 256 workgroups, 16.0 -> 15.4 us, step
+    // +0.35 %): with 1.5 workgroups per unit, half the units run two and set
+    // the kernel's time.
     if (p.kt_per_split <= 4 && p.rpw < 2) {
         const int n_rt = (int)cdiv(w.n, 16);
         if (cdiv(n_rt, 12) * p.split <= 256 && cdiv(n_rt, 8) * p.split > 256)
             return launch_q<FMT, 2, 3, 4>(w, p, img, m, out, stride, nrm, pro, s);
     }
-    if (p.rpw >= 2 || p.kt_per_split <= 4)
-        return launch_q<FMT, 2, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
-    return launch_q<FMT, 2, 1, 4>(w, p, img, m, out, stride, nrm, pro, s);
+    return launch_q<FMT, 2, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
 }
 
 }  // namespace

@@ -130,6 +130,24 @@ def test_gemv_three_row_tiles_ragged(m):
     assert_close(host(y)[:, rows], ref, what=f"gemv rpw3 m={m}")
 
 
+@pytest.mark.parametrize("m", [17, 32])
+def test_gemv_long_split_two_row_tiles_ragged(m):
+    # A long-split shape (8 splits of 14 K tiles) whose plan has one row tile
+    # per wave, launched with two at M > 16 (254 row tiles: 32 workgroups of
+    # 8), with a ragged last workgroup (6 of its 8 row tiles) and a partial
+    # last row tile (8 of 16 rows).
+    n, k = 4056, 14336
+    banner("gemv long rpw2", n, k, m)
+    data, scale = synth.weight(n, k, "q4", 0.02, 0, "rpw2long", DEV)
+    hd, hs = host(data), host(scale)
+    rows = sorted(set(np.random.default_rng(2).integers(0, n, 80).tolist())
+                  | set(range(n - 40, n)) | {0, 4031, 4032})
+    x = synth.normal((m, k), 1.0, 0, f"rpw2longx{m}", DEV)
+    y = _gemv("q4", data, scale, x, m)
+    ref = oracle.gemv("q4", hd, hs, n, k, host(x), rows=rows)
+    assert_close(host(y)[:, rows], ref, what=f"gemv long rpw2 m={m}")
+
+
 # ---------------------------------------------------------------- KV scatter
 @pytest.mark.parametrize("m,nkv,hd,max_len", [(1, 2, 64, 16), (5, 8, 128, 300), (32, 2, 128, 1152)])
 def test_kv_scatter_bit_exact(m, nkv, hd, max_len):
