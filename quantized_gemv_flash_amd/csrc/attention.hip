@@ -662,9 +662,13 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
     const dim3 grid(nc_max, nkv * hs, m);
     const QkvIn qa = qi ? *qi : QkvIn{};
     // Early K/V rows (fused input) only while every workgroup has a compute
-    // unit to itself: the 1.5B-shaped decoder at M = 4 (864 workgroups) was
-    // 1-2 % slower with them, M = 1 grids gain about 1 %.
-    const bool early = qi && (int64_t)nc_max * nkv * hs * m <= 256;
+    // unit to itself (the 1.5B-shaped decoder at M = 4, 864 workgroups, was
+    // 1-2 % slower with them; M = 1 grids gain about 1 %), and while the
+    // batch's whole cache is at most 4 MiB of K and V, the most that the rows
+    // past short sequences can add (the 0.5B and 1.5B-shaped M = 1 caches
+    // are 0.8 and 2.4 MB).
+    const bool early = qi && (int64_t)nc_max * nkv * hs * m <= 256 &&
+                       (int64_t)m * nkv * max_len * HD * 8 <= (int64_t)4 << 20;
     // Timed launches (ev0/ev1 set) go through hipExtLaunchKernel, whose event
     // pair is stamped at the kernel's own start and end.
     if (ev0 || ev1) {
