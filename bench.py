@@ -467,6 +467,48 @@ def counter_traffic():
         return None, None
 
 
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def kernel_sources_sha256():
+    """sha256 over the library's kernel and host sources (csrc/*.hip, *.h,
+    *.cpp in name order, then include/rra.h): the key under which the step
+    profiles record their counter traffic."""
+    import glob
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(root, "quantized_gemv_flash_amd", "csrc")
+    files = sorted(f for f in glob.glob(os.path.join(csrc, "*"))
+                   if f.endswith((".hip", ".h", ".cpp")))
+    h = hashlib.sha256()
+    for f in files + [os.path.join(root, "include", "rra.h")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def step_counter_traffic(profile, sec_per_step, what):
+    """Whole-step HBM traffic from a committed decode-step profile (every
+    kernel's FETCH_SIZE and WRITE_SIZE per launch, copy-scaled, times its
+    launches per step) over this run's step time, or None once the kernel
+    sources have changed since the counters were taken."""
+    try:
+        with open(os.path.join(PROFILES, profile)) as f:
+            line = [l for l in f.read().splitlines() if l.startswith("step_traffic_json: ")][0]
+        rec = json.loads(line[len("step_traffic_json: "):])
+        if rec["sources_sha256"] != kernel_sources_sha256():
+            return None
+    except (OSError, IndexError, ValueError, KeyError):
+        return None
+    b = float(rec["counter_bytes_per_step"])
+    return {"bytes_per_step": b, "gbs": b / sec_per_step / 1e9,
+            "hbm_frac": b / sec_per_step / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_step": float(rec["algorithmic_bytes_per_step"]),
+            "source": f"profiles/{profile}: rocprofv3 FETCH_SIZE x {rec['read_factor']} + "
+                      f"WRITE_SIZE x {rec['write_factor']} per launch (factors from a plain "
+                      f"copy), times launches per step, {what}; over this run's step time"}
+
+
 def cpu_baseline(S, W, dd, lengths, first_tok, nseq, steps, of_m=32):
     """The oracle, as it stands, on `steps` greedy decode steps of the first
     `nseq` sequences of the same workload (its own tokens fed back), from the
@@ -616,6 +658,9 @@ def m1_line(steps_m1=256, ctx=512, cpu=False, tune=True):
                tok_s=steps_m1 / sec, ms_per_step=1e3 * sec / steps_m1,
                weight_kv_gbs=(wbytes + kv_read) * steps_m1 / sec / 1e9)
     res["hbm_frac"] = res["weight_kv_gbs"] / HBM_PEAK_GBS
+    res["counter_traffic"] = step_counter_traffic(
+        "decode_step_qwen05b_q8_m1.md", sec / steps_m1,
+        "at the counter runs' 32-token context")
     res["host_handoff"] = host_handoff_line(dd, S, 1, first, [ctx], steps_m1)
     if cpu:  # the oracle on 8 steps after the same 512-row context (the GPU's cache rows)
         res["cpu_baseline"] = cpu_baseline(S, W, dd, [ctx], first, 1, 8, of_m=1)
@@ -759,6 +804,9 @@ def main():
         "step_phases": phases,
         "weight_kv_gbs": step_gbs,
         "weight_kv_hbm_frac": step_gbs / HBM_PEAK_GBS,
+        "counter_traffic": step_counter_traffic(
+            "decode_step_llama3_8b_q4_m32.md", sec / steps,
+            "at the counter runs' context lengths (their first steps)"),
         "roofline": {
             "kernel": "fd_chunk_kernel (flash-decode split-K chunks), every layer of the "
                       f"{steps} timed steps, M={m}, chunk {plan[0]}, head split {plan[1]} "
