@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             dst[j + HALF] = cc;
         }
         __syncthreads();
-        if (tp >= 0 && blockIdx.y % hs == 0) {
+        if (tp >= 0 && blockIdx.y % hs == 0 && qi.k_cache) {
             const size_t at = (((size_t)m * nkv + g) * max_len + p) * HD;
             for (int d = threadIdx.x; d < HD; d += blockDim.x) {
                 qi.k_cache[at + d] = kn[d];
@@ -792,10 +792,11 @@ size_t fd_tuned_floats(int m, int nq, int nkv, int hd, int max_len) {
     return best;
 }
 
-rra_status fd_time_candidates(const float *q, const float *k_cache, const float *v_cache,
+rra_status fd_time_candidates(const float *q, const float *const *k_caches,
+                              const float *const *v_caches, int n_caches,
                               const uint32_t *seq_len, float *out, int m, int nq, int nkv, int hd,
                               int max_len, float *part, hipStream_t s, int *chunk_out,
-                              int *hs_out, float *us_out) {
+                              int *hs_out, float *us_out, const QkvIn *qi) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     RRA_TRY_HIP(hipStreamIsCapturing(s, &cs));
     if (cs != hipStreamCaptureStatusNone)
@@ -813,19 +814,26 @@ rra_status fd_time_candidates(const float *q, const float *k_cache, const float 
     rra_status st = RRA_OK;
     // Two rounds over every candidate (the fastest time of each kept), so a
     // slow moment of the machine does not decide alone; each time is the
-    // mean of `reps` back-to-back launches (chunk kernel + combine).
+    // mean of `reps` back-to-back launches (chunk kernel + combine).  The
+    // launches walk through the n_caches caches (a model's layers), one
+    // after another, so that at small batches, where one layer's cache fits
+    // in the caches of the chip, a launch does not find its rows there from
+    // the launch before, just as in a decode step.
     constexpr int reps = 4;
+    int next = 0;
+    auto launch = [&](int i) {
+        const int l = next;
+        next = (next + 1) % n_caches;
+        return launch_flash_decode(q, k_caches[l], v_caches[l], seq_len, out, m, nq, nkv, hd,
+                                   max_len, chunks[i], part, s, nullptr, nullptr, true, qi,
+                                   nullptr, nullptr, hss[i]);
+    };
     for (int round = 0; round < 2 && st == RRA_OK; ++round) {
         for (int i = 0; i < n && st == RRA_OK; ++i) {
-            st = launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len,
-                                     chunks[i], part, s, nullptr, nullptr, true, nullptr, nullptr,
-                                     nullptr, hss[i]);
+            st = launch(i);
             if (st != RRA_OK) break;
             if (hipEventRecord(e0, s) != hipSuccess) { st = fail(RRA_EHIP, "hipEventRecord"); break; }
-            for (int r = 0; r < reps && st == RRA_OK; ++r)
-                st = launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd,
-                                         max_len, chunks[i], part, s, nullptr, nullptr, true,
-                                         nullptr, nullptr, nullptr, hss[i]);
+            for (int r = 0; r < reps && st == RRA_OK; ++r) st = launch(i);
             if (st != RRA_OK) break;
             float ms = 0.f;
             if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
@@ -839,19 +847,25 @@ rra_status fd_time_candidates(const float *q, const float *k_cache, const float 
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     RRA_TRY(st);
-    // Among the candidates within 3 % of the fastest, the one with the fewest
+    // On bandwidth-bound grids (at least 1024 workgroups), among the
+    // candidates within 3 % of the fastest, the one with the fewest
     // workgroups: timed alone, neighbouring split counts differ by less than
     // the run-to-run noise, and between the decode step's GEMVs the grid with
     // less per-workgroup work (query loads, softmax, partial writes) and fewer
     // partials holds up better (MI355X, 8B-shaped layer at M=32: 5 splits
     // 129 us in the step against 136 us for 7, within 1 % of each other alone).
+    // Smaller grids are latency-bound and take the fastest: there the step
+    // favoured the grid with more workgroups (1.5B-shaped decoder at M = 4
+    // and 8: 160-row splits with head split 6 and 3, 1-2 % faster in the step
+    // than the 96- and 160-row ones with head split 2 the rule picked).
     int fastest = 0;
     for (int i = 1; i < n; ++i)
         if (best[i] < best[fastest]) fastest = i;
     auto wgs = [&](int i) { return cdiv(max_len, chunks[i]) * (int64_t)hss[i]; };
     int bi = fastest;
-    for (int i = 0; i < n; ++i)
-        if (best[i] <= 1.03f * best[fastest] && wgs(i) < wgs(bi)) bi = i;
+    if (wgs(fastest) * nkv * m >= 1024)
+        for (int i = 0; i < n; ++i)
+            if (best[i] <= 1.03f * best[fastest] && wgs(i) < wgs(bi)) bi = i;
     *chunk_out = chunks[bi];
     *hs_out = hss[bi];
     if (us_out) *us_out = best[bi];
@@ -1072,8 +1086,8 @@ extern "C" rra_status rra_flash_decode_tune(const float *q, const float *k_cache
         return fail(RRA_ENOTINIT, "rra_flash_decode_tune: workspace has %zu bytes, needs %zu",
                     ws_bytes, need);
     int c = 0, hs = 0;
-    RRA_TRY(fd_time_candidates(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len,
-                               static_cast<float *>(ws), s, &c, &hs, nullptr));
+    RRA_TRY(fd_time_candidates(q, &k_cache, &v_cache, 1, seq_len, out, m, nq, nkv, hd, max_len,
+                               static_cast<float *>(ws), s, &c, &hs, nullptr, nullptr));
     {
         std::lock_guard<std::mutex> lock(g_fd_mu);
         bool found = false;

@@ -380,6 +380,14 @@ const void *gemv_input(const rra_model *M, const rra_weight &w, const float *row
 // Internal step flag: stop after the last layer (no LM head, no argmax).
 constexpr int kStepNoHead = 1 << 16;
 
+// At small m flash decode takes the QKV partials itself (QkvIn: sum, RoPE,
+// the new K/V row, seq_len); otherwise qkv_post does that work.  Every split
+// of a query head sums that head's planes again, so the fused form wins only
+// while that is cheaper than a launch: on MI355X the 1.5B-shaped decoder
+// gained 2.9 % at M = 8 and lost 0.9 % at M = 16, the 8B-shaped one lost
+// 1.9 % at M = 32.
+bool step_fuses_qkv(int m) { return m <= 8; }
+
 // The launches of one decode step, in stream order, as phases: begin() (the
 // step input), then per layer pre(l) (the QKV GEMV and its epilogue),
 // attn(l) (flash decode) and post(l) (the O GEMV, the feed-forward block and
@@ -439,13 +447,7 @@ struct Stepper {
         xc = r.x_out;
         return r;
     }
-    // At small m flash decode takes the QKV partials itself (QkvIn: sum,
-    // RoPE, the new K/V row, seq_len); otherwise qkv_post does that work.
-    // Every split of a query head sums that head's planes again, so the
-    // fused form wins only while that is cheaper than a launch: on MI355X
-    // the 1.5B-shaped decoder gained 2.9 % at M = 8 and lost 0.9 % at M = 16,
-    // the 8B-shaped one lost 1.9 % at M = 32.
-    bool fuse_qkv() const { return m <= 8; }
+    bool fuse_qkv() const { return step_fuses_qkv(m); }
 
     rra_status begin() {
         const rra_model_desc &d = M->d;
@@ -991,12 +993,38 @@ extern "C" rra_status rra_model_tune_attention(rra_model *M, const int32_t *ms, 
         for (int i = 0; i < d.m_max; ++i) lens[i] = std::min<uint32_t>(lengths[i], d.max_len);
     RRA_TRY_HIP(hipMemcpyAsync(M->lens, lens.data(), sizeof(uint32_t) * d.m_max,
                                hipMemcpyHostToDevice, s));
-    RRA_TRY_HIP(hipMemsetAsync(M->q, 0, sizeof(float) * d.m_max * d.n_heads * d.head_dim, s));
-    const rra_layer_desc &L0 = M->layers[0];
+    const int nqkv = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
+    std::vector<const float *> kcs(d.n_layers), vcs(d.n_layers);
+    for (int l = 0; l < d.n_layers; ++l) {
+        kcs[l] = M->layers[l].k_cache;
+        vcs[l] = M->layers[l].v_cache;
+    }
+    // Positions for the fused kernel: the row before each length, so that
+    // the sequence lengths it forms are the given ones; an empty slot for 0.
+    std::vector<uint32_t> pos(d.m_max);
+    for (int i = 0; i < d.m_max; ++i) pos[i] = lens[i] ? lens[i] - 1 : RRA_POS_NONE;
     for (int m : todo) {
+        // time the kernel the step runs: at m where the step fuses the QKV
+        // epilogue, the fused one, from zero split planes, attending to its
+        // new row without writing it to the cache (QkvIn with null caches);
+        // the positions sit in the q buffer, which the fused kernel does not read
+        RRA_TRY_HIP(hipMemsetAsync(M->q, 0, sizeof(float) * d.m_max * d.n_heads * d.head_dim, s));
+        QkvIn qi;
+        const bool fused = step_fuses_qkv(m);
+        if (fused) {
+            const GemvPlan &pq = M->plan_qkv[m];
+            uint32_t *pos_dev = reinterpret_cast<uint32_t *>(M->q);
+            RRA_TRY_HIP(hipMemcpyAsync(pos_dev, pos.data(), sizeof(uint32_t) * d.m_max,
+                                       hipMemcpyHostToDevice, s));
+            RRA_TRY_HIP(hipMemsetAsync(M->part, 0,
+                                       sizeof(float) * (size_t)pq.split * m * nqkv, s));
+            qi = QkvIn{M->part, pq.split, (long long)m * nqkv, pos_dev, M->rope,
+                       nullptr, nullptr, M->lens, M->err};
+        }
         int c = 0, hs = 0;
-        RRA_TRY(fd_time_candidates(M->q, L0.k_cache, L0.v_cache, M->lens, M->attn, m, d.n_heads,
-                                   d.n_kv_heads, d.head_dim, d.max_len, M->fd, s, &c, &hs, nullptr));
+        RRA_TRY(fd_time_candidates(M->q, kcs.data(), vcs.data(), d.n_layers, M->lens, M->attn, m,
+                                   d.n_heads, d.n_kv_heads, d.head_dim, d.max_len, M->fd, s, &c,
+                                   &hs, nullptr, fused ? &qi : nullptr));
         RRA_TRY(rra_model_set_attention_plan(M, m, c, hs));
     }
     RRA_TRY_HIP(hipStreamSynchronize(s));

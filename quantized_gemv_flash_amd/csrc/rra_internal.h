@@ -153,12 +153,16 @@ size_t fd_partials_floats(int m, int nq, int hd, int max_len, int chunk);
 int fd_candidates(int m, int nkv, int group, int max_len, int *chunks, int *head_splits, int cap);
 // Partial floats enough for the default rule and every candidate.
 size_t fd_tuned_floats(int m, int nq, int nkv, int hd, int max_len);
+struct QkvIn;
 // Times every candidate (chunk kernel + combine, synchronously on s) on the
-// given inputs and returns the fastest (and its time in us if us_out).
-rra_status fd_time_candidates(const float *q, const float *k_cache, const float *v_cache,
+// given inputs, its launches taking the n_caches K/V caches in turn, and
+// returns the fastest (and its time in us if us_out).  With qi the chunk
+// kernel is the QKV-fused one (qi.k_cache null: no cache write).
+rra_status fd_time_candidates(const float *q, const float *const *k_caches,
+                              const float *const *v_caches, int n_caches,
                               const uint32_t *seq_len, float *out, int m, int nq, int nkv, int hd,
                               int max_len, float *part, hipStream_t s, int *chunk_out,
-                              int *hs_out, float *us_out);
+                              int *hs_out, float *us_out, const QkvIn *qi);
 rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
                              float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
                              int max_len, hipStream_t s);
@@ -174,7 +178,9 @@ struct QkvIn {
     long long stride = 0;         // floats between split planes
     const uint32_t *pos = nullptr;
     const float *table = nullptr;  // RoPE table [max_len][hd/2][2]
-    float *k_cache = nullptr, *v_cache = nullptr;  // written at row pos
+    // the new K/V row is written at row pos; null: formed and attended to
+    // but not written (the attention tuner times the fused kernel this way)
+    float *k_cache = nullptr, *v_cache = nullptr;
     uint32_t *seq_len = nullptr, *err = nullptr;
 };
 // Row i of q attends to cache slot slot_seq[i] (slot i when slot_seq is null).
