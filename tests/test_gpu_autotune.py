@@ -6,8 +6,8 @@ Every candidate the tuner may pick is checked against unsplit softmax
 attention from the oracle, at the standalone workload's shapes and at the
 decode step's attention shapes; in the decode step every candidate of a small
 decoder is checked against the oracle's whole step, on both attention paths
-(QKV-fused at M <= 4, separate epilogue above); tuning keeps its choice fixed
-and recaptures graphs that held the old grid.
+(QKV-fused at M <= 8, separate epilogue above); tuning keeps its choice fixed,
+recaptures graphs that held the old grid and leaves the caches untouched.
 """
 import dataclasses
 
@@ -102,7 +102,9 @@ SMALL_Q4 = dataclasses.replace(synth.SMALL_LLAMA_FP8, name="small-llama-q4-ctx",
                                max_len=512)
 
 
-@pytest.mark.parametrize("m", [2, 6])  # QKV-fused flash decode (m <= 4), separate epilogue
+# QKV-fused flash decode (m <= 8; at m = 2 with the first K/V rows requested
+# before the position), separate epilogue
+@pytest.mark.parametrize("m", [2, 6, 10])
 def test_every_candidate_in_the_decode_step(m):
     S = SMALL_Q4
     cands = rra.rra_flash_decode_candidates(m, S.n_heads, S.n_kv_heads, S.max_len)
@@ -110,7 +112,7 @@ def test_every_candidate_in_the_decode_step(m):
     W = synth.decoder_weights(S, seed=12, device=DEV, gamma="random")
     run = Run(S, W, m, S.max_len)
     orc = oracle.DecoderOracle(S, W, m, S.max_len)
-    lens = [500, 37, 256, 1, 300, 129][:m]
+    lens = [500, 37, 256, 1, 300, 129, 64, 411, 2, 200][:m]
     run.fill_context(lens, orc, range(m))
     tok = synth.first_tokens(S, m, seed=12).tolist()
     x = host(W.embed[torch.as_tensor(tok, device=DEV)])
@@ -151,3 +153,25 @@ def test_model_tuning_picks_a_candidate_and_keeps_it():
         run.dd.model.rra_model_set_attention_plan(m, 64, 3)
     with pytest.raises(rra.RraError, match="chunk"):
         run.dd.model.rra_model_set_attention_plan(m, 48, 1)
+
+
+def test_model_tuning_leaves_the_caches_untouched():
+    # At batch sizes where the step fuses the QKV epilogue the tuner times
+    # the fused kernel, which forms a new K/V row at each sequence's position:
+    # it must attend to it without writing it, and every other launch of the
+    # tuner only reads the caches.
+    S = SMALL_Q4
+    m = 8
+    W = synth.decoder_weights(S, seed=14, device=DEV, gamma="random")
+    run = Run(S, W, m, S.max_len)
+    lens = [400, 37, 256, 1, 300, 129, 64, 510]
+    run.fill_context(lens)
+    before = [(k.clone(), v.clone()) for k, v in zip(run.dd.k_caches, run.dd.v_caches)]
+    plan = run.dd.model.rra_model_tune_attention([1, 4, 8], lens)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int32)  # bitwise, whatever the unused rows hold
+    for l, (k, v) in enumerate(before):
+        assert torch.equal(bits(run.dd.k_caches[l]), bits(k)), f"layer {l} K cache changed"
+        assert torch.equal(bits(run.dd.v_caches[l]), bits(v)), f"layer {l} V cache changed"
+    for mm in (1, 4, 8):
+        assert plan[mm] in rra.rra_flash_decode_candidates(mm, S.n_heads, S.n_kv_heads, S.max_len)

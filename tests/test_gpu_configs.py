@@ -191,7 +191,7 @@ def test_device_greedy_loop_matches_oracle_stream(S):
 
 # ---------------------------------------------------------------- fused flash decode, long splits
 def test_fused_qkv_flash_decode_many_rounds():
-    # At M <= 4 flash decode takes the QKV partials itself.  With 256-row
+    # At M <= 8 flash decode takes the QKV partials itself.  With 256-row
     # splits over a ~1.9k-row context each split runs four score rounds of 64
     # rows, the new row landing in a late round of one split.
     S = dataclasses.replace(SMALL_Q4, name="small-llama-q4-long", max_len=2048)
