@@ -54,14 +54,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x,
 // the block's sum of squares of the updated row -> ss[m * nblocks + block];
 // xg = x * gamma (fp32) and, when fo.img is set, its GEMV activation image
 // (zeros for the groups in [h, kpad)).  The next GEMV forms RMSNorm from ss
-// (NormIn).
+// (NormIn).  With gi.embed set (no planes) the input row is gathered from
+// the embedding table instead of read from x_in (GatherIn's rules) and
+// written to x, in place of a separate gather launch: the same values.
 __global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restrict__ part, int split,
                                                           long long split_stride,
                                                           const float *x_in, float *x,
                                                           float *__restrict__ ss,
                                                           const float *__restrict__ gamma,
                                                           float *__restrict__ xg, int h,
-                                                          FragOut fo) {
+                                                          FragOut fo, GatherIn gi) {
     __shared__ float red[3 * 64 * 8];
     __shared__ float sh[4];
     const int ch = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
@@ -74,10 +76,23 @@ __global__ __launch_bounds__(256) void residual_ss_kernel(const float *__restric
     if (threadIdx.x < 64) {
         if (k0 < h) {
             float v[8], gm[8], gv[8];
-            load8(x_in + base, v);
+            bool gathered = false;
+            if (gi.embed && gi.pos[m] != RRA_POS_NONE) {
+                const uint32_t t = gi.tok[m];
+                gathered = true;
+                if (t < (uint32_t)gi.vocab) {
+                    load8(gi.embed + (size_t)t * h + k0, v);
+                } else {  // no read outside the table; reported once per row
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+                    if (ch == 0 && threadIdx.x == 0) report_error(gi.err, kErrToken);
+                }
+            } else {
+                load8(x_in + base, v);
+            }
             load8(gamma + k0, gm);
             resid8(v, acc[0], split > 0, gm, gv, sq);
-            if (split > 0 || x_in != x) store8(x + base, v);
+            if (split > 0 || x_in != x || gathered) store8(x + base, v);
             store8(xg + base, gv);
             if (fo.img) frag_out8(fo, m, k0, gv);
         } else if (fo.img && k0 < fo.kpad) {
@@ -324,7 +339,15 @@ rra_status launch_residual_ss(const float *part, int split, size_t split_stride,
                               float *x, float *ss, const float *gamma, float *xg, int m, int h,
                               const FragOut &fo, hipStream_t s) {
     hipLaunchKernelGGL(residual_ss_kernel, dim3((unsigned)ss_parts(h), m), dim3(256), 0, s, part,
-                       split, (long long)split_stride, x_in ? x_in : x, x, ss, gamma, xg, h, fo);
+                       split, (long long)split_stride, x_in ? x_in : x, x, ss, gamma, xg, h, fo,
+                       GatherIn{});
+    return check_launch("residual_ss_kernel");
+}
+
+rra_status launch_gather_residual_ss(const GatherIn &g, float *x, float *ss, const float *gamma,
+                                     float *xg, int m, int h, const FragOut &fo, hipStream_t s) {
+    hipLaunchKernelGGL(residual_ss_kernel, dim3((unsigned)ss_parts(h), m), dim3(256), 0, s,
+                       nullptr, 0, 0LL, x, x, ss, gamma, xg, h, fo, g);
     return check_launch("residual_ss_kernel");
 }
 

@@ -452,12 +452,16 @@ struct Stepper {
     rra_status begin() {
         const rra_model_desc &d = M->d;
         RRA_TRY(mark(0));
-        if (flags & RRA_STEP_GATHER)
-            RRA_TRY(launch_embed_gather(d.embed, tok_in, pos, x, m, H, d.vocab, M->err, s));
         // RMSNorm is formed inside each consuming GEMV from per-chunk sums of
-        // squares of x; the first ones come from the step input.  Each
-        // producer also writes the next GEMV's activation image.
+        // squares of x; the first ones come from the step input (gathered
+        // from the embedding table by the same launch under
+        // RRA_STEP_GATHER).  Each producer also writes the next GEMV's
+        // activation image.
         const rra_layer_desc &L0 = M->layers[0];
+        if (flags & RRA_STEP_GATHER)
+            return launch_gather_residual_ss(GatherIn{d.embed, tok_in, pos, d.vocab, M->err}, x,
+                                             M->ss, L0.attn_gamma, M->xg, m, H,
+                                             image_for(M, L0.wqkv, m), s);
         return launch_residual_ss(nullptr, 0, 0, x, x, M->ss, L0.attn_gamma, M->xg, m, H,
                                   image_for(M, L0.wqkv, m), s);
     }

@@ -238,6 +238,19 @@ void rope_table_host(float *table, int max_len, int hd, double theta);
 rra_status launch_residual_ss(const float *part, int split, size_t split_stride, const float *x_in,
                               float *x, float *ss, const float *gamma, float *xg, int m, int h,
                               const FragOut &fo, hipStream_t s);
+// The step input gathered on the device (embed_gather_kernel's rules: row m
+// of x becomes embedding row tok[m]; an empty slot, pos[m] == RRA_POS_NONE,
+// keeps its row; a token id >= vocab gives a zero row and kErrToken).
+struct GatherIn {
+    const float *embed = nullptr;  // [vocab][h]
+    const uint32_t *tok = nullptr, *pos = nullptr;
+    int vocab = 0;
+    uint32_t *err = nullptr;
+};
+// launch_residual_ss with no planes on the gathered rows: the gather and the
+// first sums of squares and activation image in one launch.
+rra_status launch_gather_residual_ss(const GatherIn &g, float *x, float *ss, const float *gamma,
+                                     float *xg, int m, int h, const FragOut &fo, hipStream_t s);
 __host__ __device__ inline int ss_parts(int h) { return (h + 511) / 512; }
 // qkv = sum_s part[s]; rope(q, k) at pos; q -> q_out [m][nq][hd]; k, v rows
 // scattered into the caches at pos, in cache slot slot_seq[i] (slot i when
