@@ -220,14 +220,6 @@ __global__ void embed_gather_kernel(const float *__restrict__ embed, const uint3
     for (int i = threadIdx.x; i < h; i += blockDim.x) xr[i] = er[i];
 }
 
-// (v2, i2) beats (v1, i1) if larger, or equal with a lower index.  NaN never wins.
-__device__ __forceinline__ void arg_combine(float &v1, uint32_t &i1, float v2, uint32_t i2) {
-    if (v2 > v1 || (v2 == v1 && i2 < i1)) {
-        v1 = v2;
-        i1 = i2;
-    }
-}
-
 constexpr int kArgmaxPerBlock = 4096;  // 256 threads x 16 logits
 
 __global__ __launch_bounds__(256) void argmax_pass1_kernel(const float *__restrict__ logits,
@@ -271,7 +263,7 @@ __global__ __launch_bounds__(256) void argmax_pass2_kernel(const float *__restri
                                                            const uint32_t *__restrict__ bi,
                                                            uint32_t *__restrict__ tok,
                                                            uint32_t *__restrict__ pos,
-                                                           int advance, int nb) {
+                                                           int advance, int nb, int stride) {
     __shared__ float sv[4];
     __shared__ uint32_t si[4];
     const int m = blockIdx.x;
@@ -279,7 +271,7 @@ __global__ __launch_bounds__(256) void argmax_pass2_kernel(const float *__restri
     float best = -INFINITY;
     uint32_t bidx = 0xFFFFFFFFu;
     for (int i = threadIdx.x; i < nb; i += blockDim.x)
-        arg_combine(best, bidx, bv[(size_t)m * nb + i], bi[(size_t)m * nb + i]);
+        arg_combine(best, bidx, bv[(size_t)m * stride + i], bi[(size_t)m * stride + i]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         arg_combine(best, bidx, __shfl_xor(best, off, 64), __shfl_xor(bidx, off, 64));
@@ -421,8 +413,30 @@ rra_status launch_argmax(const float *logits, uint32_t *tok, int m, int v, void 
     hipLaunchKernelGGL(argmax_pass1_kernel, dim3(nb, m), dim3(256), 0, s, logits, bv, bi, v, nb);
     RRA_TRY(check_launch("argmax_pass1_kernel"));
     hipLaunchKernelGGL(argmax_pass2_kernel, dim3(m), dim3(256), 0, s, bv, bi, tok, pos,
-                       (pos && advance) ? 1 : 0, nb);
+                       (pos && advance) ? 1 : 0, nb, nb);
     return check_launch("argmax_pass2_kernel");
+}
+
+rra_status launch_argmax_partials(const ArgOut &ao, uint32_t *tok, int m, uint32_t *pos,
+                                  bool advance, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_pass2_kernel, dim3(m), dim3(256), 0, s, ao.val, ao.idx, tok, pos,
+                       (pos && advance) ? 1 : 0, ao.blocks, ao.stride);
+    return check_launch("argmax_pass2_kernel");
+}
+
+size_t gemv_argmax_ws_bytes(int m, int n) {
+    const size_t cap = (size_t)gemv_argmax_blocks_max(n);
+    return align_up((size_t)m * cap * sizeof(float), 256) + (size_t)m * cap * sizeof(uint32_t);
+}
+
+ArgOut gemv_argmax_out(void *ws, int m, int n) {
+    const int cap = gemv_argmax_blocks_max(n);
+    ArgOut ao;
+    ao.val = static_cast<float *>(ws);
+    ao.idx = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
+                                          align_up((size_t)m * cap * sizeof(float), 256));
+    ao.stride = cap;
+    return ao;
 }
 
 void rope_table_host(float *table, int max_len, int hd, double theta) {

@@ -204,5 +204,14 @@ __device__ __forceinline__ void fd_combine(const float *__restrict__ part_o,
     for (int j = 0; j < PER; ++j) acc[j] /= wsum;
 }
 
+// (v2, i2) beats (v1, i1) if larger, or equal with a lower index.  NaN never
+// wins.  The result of combining a set of candidates is the same in any order.
+__device__ __forceinline__ void arg_combine(float &v1, uint32_t &i1, float v2, uint32_t i2) {
+    if (v2 > v1 || (v2 == v1 && i2 < i1)) {
+        v1 = v2;
+        i1 = i2;
+    }
+}
+
 }  // namespace
 }  // namespace rra

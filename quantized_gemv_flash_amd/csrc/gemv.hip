@@ -561,18 +561,67 @@ struct QGemv {
 
     // Result layout of a 16x16 MFMA: lane holds rows 4g..4g+3 of column
     // lane%16.  Multiplies by inv[m] (RMSNorm, when nrm.ss is set).
+    // RMSNorm factor of column tile cc's row m (1 without a norm)
+    __device__ __forceinline__ float col_inv(int cc, int m, const float (&sq)[CT],
+                                             const NormIn &nrm, int K) const {
+        float iv = 1.f;
+        if (nrm.ss) {
+            float t = sq[cc];
+            for (int q = SSP; q < nrm.nparts; ++q) t += nrm.ss[(size_t)m * nrm.nparts + q];
+            iv = 1.0f / sqrtf(t / (float)K + nrm.eps);
+        }
+        return iv;
+    }
+    // Greedy-argmax partial of the outputs store() writes (the same products,
+    // acc * iv): per row m, the largest value with the lowest index among this
+    // workgroup's output rows, to ao.val/idx[m * ao.stride + blockIdx.x].
+    // Lanes 16 apart hold the same row's columns; the waves meet in LDS.
+    // Every thread of the workgroup calls it (it synchronises the block).
+    __device__ __forceinline__ void store_argmax(const Acc &acc, const float (&sq)[CT],
+                                                 const NormIn &nrm, int M, int N, int K,
+                                                 const ArgOut &ao, float (*av)[16 * CT],
+                                                 uint32_t (*ai)[16 * CT]) const {
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc) {
+            const int m = 16 * cc + (lane & 15);
+            float best = -INFINITY;
+            uint32_t bidx = 0xFFFFFFFFu;
+            if (m < M) {
+                const float iv = col_inv(cc, m, sq, nrm, K);
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                    const int rt = rt0 + r;
+                    if (rt >= n_rt) continue;
+                    const int row0 = rt * 16 + 4 * g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (row0 + i < N)
+                            arg_combine(best, bidx, acc[r][cc][i] * iv, (uint32_t)(row0 + i));
+                }
+            }
+            arg_combine(best, bidx, __shfl_xor(best, 16, 64), __shfl_xor(bidx, 16, 64));
+            arg_combine(best, bidx, __shfl_xor(best, 32, 64), __shfl_xor(bidx, 32, 64));
+            if (g == 0) {
+                av[wave][16 * cc + lane] = best;
+                ai[wave][16 * cc + lane] = bidx;
+            }
+        }
+        __syncthreads();
+        if (wave == 0 && lane < 16 * CT && lane < M) {
+            float best = av[0][lane];
+            uint32_t bidx = ai[0][lane];
+            for (int w = 1; w < NW; ++w) arg_combine(best, bidx, av[w][lane], ai[w][lane]);
+            ao.val[(size_t)lane * ao.stride + blockIdx.x] = best;
+            ao.idx[(size_t)lane * ao.stride + blockIdx.x] = bidx;
+        }
+    }
     __device__ __forceinline__ void store(const Acc &acc, const float (&sq)[CT], const NormIn &nrm,
                                           float *o, int M, int N, int K) const {
 #pragma unroll
         for (int cc = 0; cc < CT; ++cc) {
             const int m = 16 * cc + (lane & 15);
             if (m >= M) continue;
-            float iv = 1.f;
-            if (nrm.ss) {
-                float t = sq[cc];
-                for (int q = SSP; q < nrm.nparts; ++q) t += nrm.ss[(size_t)m * nrm.nparts + q];
-                iv = 1.0f / sqrtf(t / (float)K + nrm.eps);
-            }
+            const float iv = col_inv(cc, m, sq, nrm, K);
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 const int rt = rt0 + r;
@@ -623,10 +672,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_kernel(const uint8_t *__restri
                                                          const uint8_t *__restrict__ ximg,
                                                          float *__restrict__ out, int M, int N,
                                                          int K, int nkt, int kt_per_split,
-                                                         long long split_stride, NormIn nrm) {
+                                                         long long split_stride, NormIn nrm,
+                                                         ArgOut ao) {
     using G = QGemv<FMT, CT, RPW, NW>;
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::XB];
     __shared__ __attribute__((aligned(16))) uint8_t sl[2][G::SCB];
+    // argmax partials (decode batches only: CT <= 2)
+    __shared__ float av[CT <= 2 ? NW : 1][16 * CT];
+    __shared__ uint32_t ai[CT <= 2 ? NW : 1][16 * CT];
 
     G p;
     p.init(wt, ximg, N, nkt, kt_per_split);
@@ -668,6 +721,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_q_kernel(const uint8_t *__restri
         p.compute(q0, xs[0], sl[0], acc);
     }
     p.store(acc, sq, nrm, out + (size_t)blockIdx.y * split_stride, M, N, K);
+    if constexpr (CT <= 2)
+        if (ao.val) p.store_argmax(acc, sq, nrm, M, N, K, ao, av, ai);  // uniform: one K split
 }
 
 // Short splits (at most NT K tiles): every K tile's image, scales and
@@ -1473,7 +1528,8 @@ rra_status launch_short(const rra_weight &w, const GemvPlan &p, const uint8_t *i
 
 template <int FMT, int CT, int RPW, int NW>
 rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m, float *out,
-                    size_t stride, const NormIn &nrm, const GemvPrologue &pro, hipStream_t s) {
+                    size_t stride, const NormIn &nrm, const GemvPrologue &pro, hipStream_t s,
+                    ArgOut *ao) {
     const int n_rt = (int)cdiv(w.n, 16);
     const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
     dim3 grid((unsigned)cdiv(n_rt, NW * RPW), (unsigned)p.split), block(64 * NW);
@@ -1487,22 +1543,28 @@ rra_status launch_q(const rra_weight &w, const GemvPlan &p, const uint8_t *img, 
                                                      nkt, s);
     }
     if (pro.kind != kProNone) return fail(RRA_EINVAL, "gemv prologue: split longer than 4 tiles");
+    // argmax partials: one K split only, within the buffers' partials per row
+    ArgOut a;
+    if (CT <= 2 && ao && p.split == 1 && (int)grid.x <= ao->stride) {
+        a = *ao;
+        ao->blocks = (int)grid.x;
+    }
     hipLaunchKernelGGL((gemv_q_kernel<FMT, CT, RPW, NW>), grid, block, 0, s, wd, img, out, m,
-                       (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
+                       (int)w.n, (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm, a);
     return check_launch("gemv_q_kernel");
 }
 
 template <int FMT>
 rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img, int m,
                       float *out, size_t stride, const NormIn &nrm, const GemvPrologue &pro,
-                      hipStream_t s) {
+                      hipStream_t s, ArgOut *ao) {
     if (m <= 16) {
-        if (p.rpw >= 2) return launch_q<FMT, 1, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
-        return launch_q<FMT, 1, 1, 4>(w, p, img, m, out, stride, nrm, pro, s);
+        if (p.rpw >= 2) return launch_q<FMT, 1, 2, 4>(w, p, img, m, out, stride, nrm, pro, s, ao);
+        return launch_q<FMT, 1, 1, 4>(w, p, img, m, out, stride, nrm, pro, s, ao);
     }
     if (m > 32) {  // prompt chunks
         if (pro.kind != kProNone) return fail(RRA_EINVAL, "gemv prologue: m > 16");
-        if (m <= 64) return launch_q<FMT, 4, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
+        if (m <= 64) return launch_q<FMT, 4, 1, 8>(w, p, img, m, out, stride, nrm, pro, s, ao);
         if constexpr (FMT != RRA_Q6K) {
             const int n_rt = (int)cdiv(w.n, 16);
             const int nkt = (int)cdiv(w.k, TileFmt<FMT>::KT);
@@ -1512,11 +1574,11 @@ rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img
                                (int)w.k, nkt, p.kt_per_split, (long long)stride, nrm);
             return check_launch("gemm_q_kernel");
         }
-        return launch_q<FMT, 8, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
+        return launch_q<FMT, 8, 1, 8>(w, p, img, m, out, stride, nrm, pro, s, ao);
     }
     if (p.nw == 8) {
-        if (p.rpw >= 2) return launch_q<FMT, 2, 2, 8>(w, p, img, m, out, stride, nrm, pro, s);
-        return launch_q<FMT, 2, 1, 8>(w, p, img, m, out, stride, nrm, pro, s);
+        if (p.rpw >= 2) return launch_q<FMT, 2, 2, 8>(w, p, img, m, out, stride, nrm, pro, s, ao);
+        return launch_q<FMT, 2, 1, 8>(w, p, img, m, out, stride, nrm, pro, s, ao);
     }
     // At m > 16, two row tiles per wave whatever the plan says (the row
     // tiling never changes a row's arithmetic).  Short splits: half the
@@ -1532,9 +1594,9 @@ rra_status launch_fmt(const rra_weight &w, const GemvPlan &p, const uint8_t *img
     if (p.kt_per_split <= 4 && p.rpw < 2) {
         const int n_rt = (int)cdiv(w.n, 16);
         if (cdiv(n_rt, 12) * p.split <= 256 && cdiv(n_rt, 8) * p.split > 256)
-            return launch_q<FMT, 2, 3, 4>(w, p, img, m, out, stride, nrm, pro, s);
+            return launch_q<FMT, 2, 3, 4>(w, p, img, m, out, stride, nrm, pro, s, ao);
     }
-    return launch_q<FMT, 2, 2, 4>(w, p, img, m, out, stride, nrm, pro, s);
+    return launch_q<FMT, 2, 2, 4>(w, p, img, m, out, stride, nrm, pro, s, ao);
 }
 
 }  // namespace
@@ -1597,7 +1659,9 @@ bool gemv_takes_resid_prologue(const rra_weight &w, const GemvPlan &p, int m, in
 }
 
 rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, int m, float *out,
-                       size_t stride, hipStream_t s, const NormIn *nrm, const GemvPrologue *pro) {
+                       size_t stride, hipStream_t s, const NormIn *nrm, const GemvPrologue *pro,
+                       ArgOut *ao) {
+    if (ao) ao->blocks = 0;
     const NormIn none{nullptr, 0, 0.f};
     const NormIn &n = nrm ? *nrm : none;
     const GemvPrologue no_pro{kProNone, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
@@ -1620,10 +1684,10 @@ rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, in
         return RRA_OK;
     }
     const auto *img = static_cast<const uint8_t *>(x);
-    if (w.fmt == RRA_Q4) return launch_fmt<RRA_Q4>(w, p, img, m, out, stride, n, pr, s);
-    if (w.fmt == RRA_Q6K) return launch_fmt<RRA_Q6K>(w, p, img, m, out, stride, n, pr, s);
-    if (w.fmt == RRA_FP8) return launch_fmt<RRA_FP8>(w, p, img, m, out, stride, n, pr, s);
-    return launch_fmt<RRA_Q8>(w, p, img, m, out, stride, n, pr, s);
+    if (w.fmt == RRA_Q4) return launch_fmt<RRA_Q4>(w, p, img, m, out, stride, n, pr, s, ao);
+    if (w.fmt == RRA_Q6K) return launch_fmt<RRA_Q6K>(w, p, img, m, out, stride, n, pr, s, ao);
+    if (w.fmt == RRA_FP8) return launch_fmt<RRA_FP8>(w, p, img, m, out, stride, n, pr, s, ao);
+    return launch_fmt<RRA_Q8>(w, p, img, m, out, stride, n, pr, s, ao);
 }
 
 rra_status launch_x_to_image(const float *x, uint8_t *img, int fmt, int m, int k, hipStream_t s) {

@@ -306,7 +306,9 @@ Layout layout_of(const rra_model_desc &d) {
     L.act = take(4 * M * d.intermediate);
     L.fd = take(4 * fd_floats(d));
     L.logits = take(4 * (size_t)d.m_max * (size_t)d.vocab);  // prompts: the last row only
-    L.argmax = take(argmax_ws_bytes(d.m_max, d.vocab));
+    // the argmax pass over the logits, or the LM head's own partials
+    L.argmax = take(std::max(argmax_ws_bytes(d.m_max, d.vocab),
+                             gemv_argmax_ws_bytes(d.m_max, d.vocab)));
     L.rope = take(4 * (size_t)d.max_len * d.head_dim);
     L.err = take(256);
     L.px = take(4 * M * d.hidden);
@@ -558,10 +560,16 @@ struct Stepper {
         const rra_model_desc &d = M->d;
         RRA_TRY(mark(1 + 4 * d.n_layers));
         if (flags & kStepNoHead) return mark(2 + 4 * d.n_layers);
+        // The LM head leaves per-workgroup argmax partials when it runs as one
+        // K split, and the ids come from those; otherwise from the logits.
+        ArgOut ao = gemv_argmax_out(M->argmax_ws, m, d.vocab);
         RRA_TRY(launch_gemv(d.lm_head, M->plan_lm[m], gemv_input(M, d.lm_head, M->xg), m, logits,
-                            0, s, &nrm));
-        RRA_TRY(launch_argmax(logits, tok_out, m, d.vocab, M->argmax_ws, pos,
-                              (flags & RRA_STEP_ADVANCE) != 0, s));
+                            0, s, &nrm, nullptr, &ao));
+        const bool adv = (flags & RRA_STEP_ADVANCE) != 0;
+        if (ao.blocks)
+            RRA_TRY(launch_argmax_partials(ao, tok_out, m, pos, adv, s));
+        else
+            RRA_TRY(launch_argmax(logits, tok_out, m, d.vocab, M->argmax_ws, pos, adv, s));
         return mark(2 + 4 * d.n_layers);
     }
 };

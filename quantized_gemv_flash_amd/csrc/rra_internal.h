@@ -125,9 +125,28 @@ bool gemv_takes_resid_prologue(const rra_weight &w, const GemvPlan &p, int m, in
 // out[split][m][n] with out_split_stride floats between splits.  For quantised
 // weights `x` is the activation image (frag.h) with frag_ct(m) column tiles;
 // for F32 weights it is fp32 [m][k].
+// Greedy-argmax partials of a GEMV's outputs (the LM head): when the GEMV
+// runs as one K split of gemv_q_kernel, its workgroup b also writes, for each
+// row m, the (largest stored value, lowest index) among the outputs it stores
+// to val[m * stride + b] / idx[m * stride + b] and sets blocks to the number
+// of workgroups; otherwise blocks stays 0 and the caller runs launch_argmax
+// on the stored outputs.  Either way the ids are the same.
+struct ArgOut {
+    float *val = nullptr;
+    uint32_t *idx = nullptr;
+    int stride = 0;  // partials per row the buffers hold
+    int blocks = 0;  // set by launch_gemv
+};
+// Partials per row that any launch shape of an n-row GEMV can produce.
+inline int gemv_argmax_blocks_max(int64_t n) { return (int)((n + 63) / 64); }
+size_t gemv_argmax_ws_bytes(int m, int n);
+ArgOut gemv_argmax_out(void *ws, int m, int n);
 rra_status launch_gemv(const rra_weight &w, const GemvPlan &p, const void *x, int m, float *out,
                        size_t out_split_stride, hipStream_t s, const NormIn *nrm = nullptr,
-                       const GemvPrologue *pro = nullptr);
+                       const GemvPrologue *pro = nullptr, ArgOut *ao = nullptr);
+// The greedy ids from a GEMV's argmax partials (ao.blocks of them per row).
+rra_status launch_argmax_partials(const ArgOut &ao, uint32_t *tok, int m, uint32_t *pos,
+                                  bool advance, hipStream_t s);
 // Converts fp32 x [m][k] into the activation image of a quantised GEMV.
 rra_status launch_x_to_image(const float *x, uint8_t *img, int fmt, int m, int k, hipStream_t s);
 // y[i][r] = sum over `split` partial planes (+ y[i][r] if accumulate).
