@@ -370,3 +370,37 @@ def test_activation_outside_fp16_range_is_reported(bad):
         c.zero_()
     run.step([5], [0])
     run.dd.model.rra_model_check()  # cleared, and a normal step reports nothing
+
+
+@pytest.mark.parametrize("m", [1, 3, 20])
+def test_greedy_ids_are_the_lowest_index_of_the_largest_logit(m):
+    # The LM head reduces the logits each of its workgroups stores to a
+    # (value, lowest index) partial per row, and the ids come from those.
+    # Here its rows are zero except r1 < r2 (one random row) and r3 < r4 (its
+    # negation), the rows of each pair at the same place in 16-row tiles far
+    # apart (different workgroups): the largest logit is an exact tie, and the
+    # id must be the lowest index holding it, as the argmax of the step's own
+    # logits gives.
+    S = dataclasses.replace(synth.SMALL_LLAMA_FP8, name="wide-vocab-q8", fmt="q8", hidden=384,
+                            n_heads=6, n_kv_heads=2, head_dim=64, intermediate=1024,
+                            vocab=131072, max_len=16)
+    banner("lm-head ties", S.name, "m", m)
+    W = synth.decoder_weights(S, seed=21, device=DEV, gamma="random")
+    q, sc = (torch.zeros_like(t) for t in W.lm_head)
+    src_q, src_s = synth.weight(1, S.hidden, "q8", 0.02, 21, "tie-row", DEV)
+    r1, r2, r3, r4 = 777, 100_009, 5_001, 120_009
+    for r, sign in ((r1, 1), (r2, 1), (r3, -1), (r4, -1)):
+        q[r] = sign * src_q[0]
+        sc[r] = src_s[0]
+    W.lm_head = (q, sc)
+    run = Run(S, W, m, S.max_len)
+    tok = synth.first_tokens(S, m, seed=21).tolist()
+    for step in range(3):
+        ids, _, logits = run.step(tok, [step] * m, flags=rra.RRA_GRAPH)
+        assert torch.equal(logits[:, r1], logits[:, r2]) and torch.equal(logits[:, r3], logits[:, r4])
+        for i in range(m):
+            mx = logits[i].max()
+            want = int((logits[i] == mx).nonzero()[0])
+            assert int(ids[i]) == want, (step, i, int(ids[i]), want)
+            assert want in (0, r1, r3)
+        tok = [int(v) for v in ids]
