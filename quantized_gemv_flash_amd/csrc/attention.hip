@@ -92,16 +92,43 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict
 // more workgroups per compute unit that loses (a wave's loads return in
 // order, so rows requested ahead delay the partials, and the rows past the
 // sequence add traffic).
-template <int HD, int G, bool QF, bool EARLY = false>
+template <int HD, int G, bool QF, bool EARLY = false, bool LF = false>
 __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
     const uint32_t *__restrict__ seq_len, const uint32_t *__restrict__ slot_seq,
     float *__restrict__ part_o, float *__restrict__ part_lse, int nq, int nkv, int max_len,
     int chunk, int nc_max, int hs, QkvIn qi) {
     constexpr int GP = (G + 3) & ~3;  // probabilities stored key-major, G padded to 4
-    const int c = blockIdx.x, g = blockIdx.y / hs, m = blockIdx.z;
+    const int c = blockIdx.x, g = blockIdx.y / hs;
     const int hq0 = blockIdx.y * G;  // first query head: g G hs + (blockIdx.y mod hs) G
     static_assert(QF || !EARLY, "early K/V rows need the fused QKV input");
+    static_assert(!(LF && QF), "longest first: the unfused instance only");
+    // The sequence served: blockIdx.z, or in the LF instance the
+    // blockIdx.z-th longest (ties: lower index first).  Workgroups are
+    // dispatched in blockIdx order, so the first ones then take the longest
+    // splits and those that wait for a free compute unit the shortest.  Every
+    // lane loads one sequence's length in the round trip that would load this
+    // sequence's alone; the ranking is a serial loop over the batch (about
+    // 1 us), paid back only where lengths differ widely.  The ranking takes
+    // one sequence per lane; a grid of more than 64 (the entry points allow
+    // 32) would keep blockIdx.z.
+    const uint32_t *src = QF ? qi.pos : seq_len;  // position (QF) or length
+    int m = blockIdx.z;
+    uint32_t mv = 0;  // src[m]
+    if (LF && gridDim.z <= 64) {
+        const int ln = threadIdx.x & 63, nseq = gridDim.z;
+        const uint32_t v = ln < nseq ? src[ln] : 0u;
+        const uint32_t len = QF ? (v < (uint32_t)max_len ? v + 1 : 0u) : min(v, (uint32_t)max_len);
+        int rank = 0;  // sequences ahead of this lane's
+        for (int k = 0; k < nseq; ++k) {  // k is wave-uniform: a scalar broadcast
+            const uint32_t lk = (uint32_t)__builtin_amdgcn_readlane((int)len, k);
+            rank += (lk > len || (lk == len && k < ln)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(ln < nseq && rank == (int)blockIdx.z);
+        // the ranks are a permutation of 0 .. nseq - 1: exactly one lane hits
+        m = hit ? __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1) : (int)blockIdx.z;
+        mv = (uint32_t)__builtin_amdgcn_readlane((int)v, m);
+    }
     float4 ek[2][HD / 32], ev[8];  // EARLY: the first K rows and V rows
     if constexpr (EARLY) {
         // the index maps of the score loop (8 lanes per K row, 2 rows per lane)
@@ -127,11 +154,12 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             ev[u] = ldnt(vc + at0 + (size_t)tr * nc_max * HD + 4 * d4);
         }
     }
+    if (!LF || gridDim.z > 64) mv = src[m];
     uint32_t p = 0;
     bool ok = false;
     int L;
     if constexpr (QF) {
-        p = qi.pos[m];
+        p = mv;
         ok = p < (uint32_t)max_len;  // false for an empty slot (RRA_POS_NONE) too
         // an empty slot attends to nothing; any other bad position is an error
         const uint32_t lr = ok ? p + 1 : (p == RRA_POS_NONE ? 0u : (uint32_t)max_len);
@@ -141,7 +169,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
         }
         L = (int)min(lr, (uint32_t)max_len);
     } else {
-        L = (int)min(seq_len[m], (uint32_t)max_len);
+        L = (int)min(mv, (uint32_t)max_len);
     }
     if (c >= L) return;
     // Rows c, c + nc_max, c + 2 nc_max, ... < L (local row i is cache row
@@ -654,13 +682,19 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
 template <int HD, int G>
 rra_status launch_chunk(const float *q, const float *kc, const float *vc, const uint32_t *lens,
                         const uint32_t *slot_seq, float *po, float *pl, int m, int nq, int nkv,
-                        int max_len, int chunk, int nc_max, int hs, const QkvIn *qi,
-                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                        int max_len, int chunk, int nc_max, int hs, bool longest_first,
+                        const QkvIn *qi, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int GP = (G + 3) & ~3;
     const size_t shm = sizeof(float) * ((size_t)GP * chunk + 4 * G * HD + 2 * GP +
                                         (qi ? (size_t)(G + 2) * HD : 0));
     const dim3 grid(nc_max, nkv * hs, m);
     const QkvIn qa = qi ? *qi : QkvIn{};
+    // Longest first only on grids of a few rounds of resident workgroups
+    // (four 4-wave workgroups per compute unit): over more rounds the
+    // dispatcher already evens the tail out and the ranking is pure cost
+    // (standalone attention, lengths U[1, 8192]: 2048 workgroups 180 -> 170 us,
+    // 8192 workgroups 188 -> 192 us).
+    longest_first = longest_first && (int64_t)nc_max * nkv * hs * m <= 4096;
     // Early K/V rows (fused input) only while every workgroup has a compute
     // unit to itself (the 1.5B-shaped decoder at M = 4, 864 workgroups, was
     // 1-2 % slower with them; M = 1 grids gain about 1 %), and while the
@@ -680,6 +714,10 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), (uint32_t)shm, s,
                                   ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
                                   max_len, chunk, nc_max, hs, qa);
+        else if (longest_first)
+            hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, false, false, true>), grid, dim3(256),
+                                  (uint32_t)shm, s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po,
+                                  pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
         else
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), (uint32_t)shm,
                                   s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
@@ -690,6 +728,10 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
     } else if (qi) {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), shm, s, q, kc, vc, lens,
                            slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
+    } else if (longest_first) {
+        hipLaunchKernelGGL((fd_chunk_kernel<HD, G, false, false, true>), grid, dim3(256), shm, s,
+                           q, kc, vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs,
+                           qa);
     } else {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), shm, s, q, kc, vc,
                            lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
@@ -714,7 +756,8 @@ template <int HD>
 rra_status launch_chunk_hd(int group, const float *q, const float *kc, const float *vc,
                            const uint32_t *lens, const uint32_t *slot_seq, float *po, float *pl,
                            int m, int nq, int nkv, int max_len, int chunk, int nc_max, int hs_want,
-                           const QkvIn *qi, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                           bool longest_first, const QkvIn *qi, hipStream_t s, hipEvent_t ev0,
+                           hipEvent_t ev1) {
     if (group < 1 || group > 8) return fail(RRA_EINVAL, "flash decode: nq/nkv=%d not in 1..8", group);
     if (hs_want < 0 || (hs_want > 0 && group % hs_want))
         return fail(RRA_EINVAL, "flash decode: head split %d does not divide the group size %d",
@@ -724,7 +767,7 @@ rra_status launch_chunk_hd(int group, const float *q, const float *kc, const flo
 #define RRA_G(gv) \
     case gv:                                                                                    \
         return launch_chunk<HD, gv>(q, kc, vc, lens, slot_seq, po, pl, m, nq, nkv, max_len, chunk, \
-                                    nc_max, hs, qi, s, ev0, ev1);
+                                    nc_max, hs, longest_first, qi, s, ev0, ev1);
         RRA_G(1) RRA_G(2) RRA_G(3) RRA_G(4) RRA_G(5) RRA_G(6) RRA_G(7) RRA_G(8)
 #undef RRA_G
     }
@@ -796,7 +839,7 @@ rra_status fd_time_candidates(const float *q, const float *const *k_caches,
                               const float *const *v_caches, int n_caches,
                               const uint32_t *seq_len, float *out, int m, int nq, int nkv, int hd,
                               int max_len, float *part, hipStream_t s, int *chunk_out,
-                              int *hs_out, float *us_out, const QkvIn *qi) {
+                              int *hs_out, float *us_out, const QkvIn *qi, bool longest_first) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     RRA_TRY_HIP(hipStreamIsCapturing(s, &cs));
     if (cs != hipStreamCaptureStatusNone)
@@ -826,7 +869,7 @@ rra_status fd_time_candidates(const float *q, const float *const *k_caches,
         next = (next + 1) % n_caches;
         return launch_flash_decode(q, k_caches[l], v_caches[l], seq_len, out, m, nq, nkv, hd,
                                    max_len, chunks[i], part, s, nullptr, nullptr, true, qi,
-                                   nullptr, nullptr, hss[i]);
+                                   nullptr, nullptr, hss[i], longest_first);
     };
     for (int round = 0; round < 2 && st == RRA_OK; ++round) {
         for (int i = 0; i < n && st == RRA_OK; ++i) {
@@ -923,7 +966,7 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                int hd, int max_len, int chunk, float *part, hipStream_t s,
                                const FragOut *fo, const uint32_t *slot_seq, bool reduce,
                                const QkvIn *qi, hipEvent_t chunk_start, hipEvent_t chunk_stop,
-                               int head_split) {
+                               int head_split, bool longest_first) {
     if (qi && slot_seq) return fail(RRA_EINVAL, "flash decode: fused QKV input needs no slot map");
     const FragOut img = fo ? *fo : FragOut{nullptr, 0, 1, 0};
     const int G = nq / nkv;
@@ -932,12 +975,12 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
     float *pl = const_cast<float *>(fd_part_lse(part, m, nq, hd, nc_max));
     if (hd == 128)
         RRA_TRY(launch_chunk_hd<128>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                     max_len, chunk, nc_max, head_split, qi, s, chunk_start,
-                                     chunk_stop));
+                                     max_len, chunk, nc_max, head_split, longest_first, qi, s,
+                                     chunk_start, chunk_stop));
     else
         RRA_TRY(launch_chunk_hd<64>(G, q, k_cache, v_cache, seq_len, slot_seq, po, pl, m, nq, nkv,
-                                    max_len, chunk, nc_max, head_split, qi, s, chunk_start,
-                                    chunk_stop));
+                                    max_len, chunk, nc_max, head_split, longest_first, qi, s,
+                                    chunk_start, chunk_stop));
     if (!reduce) return RRA_OK;
     if (hd == 128)
         hipLaunchKernelGGL(fd_reduce_kernel<128>, dim3(nq, m), dim3(64), 0, s, po, pl, seq_len,
@@ -1045,7 +1088,7 @@ extern "C" rra_status rra_flash_decode(const float *q, const float *k_cache, con
     }
     return launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len, c,
                                static_cast<float *>(ws), s, nullptr, nullptr, true, nullptr,
-                               nullptr, nullptr, hs);
+                               nullptr, nullptr, hs, true);
 }
 
 extern "C" rra_status rra_flash_decode_ex(const float *q, const float *k_cache,
@@ -1068,7 +1111,7 @@ extern "C" rra_status rra_flash_decode_ex(const float *q, const float *k_cache,
                     ws_bytes, need);
     return launch_flash_decode(q, k_cache, v_cache, seq_len, out, m, nq, nkv, hd, max_len, chunk,
                                static_cast<float *>(ws), s, nullptr, nullptr, true, nullptr,
-                               nullptr, nullptr, head_split);
+                               nullptr, nullptr, head_split, true);
 }
 
 extern "C" rra_status rra_flash_decode_tune(const float *q, const float *k_cache,
@@ -1087,7 +1130,7 @@ extern "C" rra_status rra_flash_decode_tune(const float *q, const float *k_cache
                     ws_bytes, need);
     int c = 0, hs = 0;
     RRA_TRY(fd_time_candidates(q, &k_cache, &v_cache, 1, seq_len, out, m, nq, nkv, hd, max_len,
-                               static_cast<float *>(ws), s, &c, &hs, nullptr, nullptr));
+                               static_cast<float *>(ws), s, &c, &hs, nullptr, nullptr, true));
     {
         std::lock_guard<std::mutex> lock(g_fd_mu);
         bool found = false;

@@ -176,12 +176,14 @@ struct QkvIn;
 // Times every candidate (chunk kernel + combine, synchronously on s) on the
 // given inputs, its launches taking the n_caches K/V caches in turn, and
 // returns the fastest (and its time in us if us_out).  With qi the chunk
-// kernel is the QKV-fused one (qi.k_cache null: no cache write).
+// kernel is the QKV-fused one (qi.k_cache null: no cache write);
+// longest_first as in launch_flash_decode.
 rra_status fd_time_candidates(const float *q, const float *const *k_caches,
                               const float *const *v_caches, int n_caches,
                               const uint32_t *seq_len, float *out, int m, int nq, int nkv, int hd,
                               int max_len, float *part, hipStream_t s, int *chunk_out,
-                              int *hs_out, float *us_out, const QkvIn *qi);
+                              int *hs_out, float *us_out, const QkvIn *qi,
+                              bool longest_first = false);
 rra_status launch_kv_scatter(const float *k_rows, const float *v_rows, float *k_cache,
                              float *v_cache, const uint32_t *pos, int m, int nkv, int hd,
                              int max_len, hipStream_t s);
@@ -206,7 +208,11 @@ struct QkvIn {
 // head_split: workgroups per KV head's query-head group (a divisor of
 // nq / nkv), or 0 for the default rule (fd_head_split).
 // reduce = false launches the split kernel only (the O GEMV then combines the
-// partials in its prologue).  With qi, q and seq_len are ignored (the split
+// partials in its prologue).  longest_first: the chunk kernel's workgroups
+// take the sequences longest first (grids of at most 4096 workgroups), so
+// that the grid's tail holds short work; it costs each workgroup about 1 us
+// and pays where the lengths differ widely (the standalone entry points), not
+// in the decode step, whose nearly equal lengths it slowed by 1-2 %.  With qi, q and seq_len are ignored (the split
 // kernel forms them; slot_seq must be null).
 rra_status launch_flash_decode(const float *q, const float *k_cache, const float *v_cache,
                                const uint32_t *seq_len, float *out, int m, int nq, int nkv,
@@ -214,7 +220,7 @@ rra_status launch_flash_decode(const float *q, const float *k_cache, const float
                                const FragOut *fo = nullptr, const uint32_t *slot_seq = nullptr,
                                bool reduce = true, const QkvIn *qi = nullptr,
                                hipEvent_t chunk_start = nullptr, hipEvent_t chunk_stop = nullptr,
-                               int head_split = 0);
+                               int head_split = 0, bool longest_first = false);
 // Causal attention of a prompt chunk (matrix cores): q [n][nq][hd] at
 // positions start .. start + n - 1 of one cache slot (k_slot, v_slot: that
 // slot's [nkv][max_len][hd]), row t over the slot's rows [0, start + t];

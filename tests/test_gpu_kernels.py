@@ -225,6 +225,23 @@ def test_flash_decode_head_split_is_bitwise_neutral(hd, nq, nkv):
         assert torch.equal(one[0], both[s]), f"seq {s} L={L[s]}"
 
 
+@pytest.mark.parametrize("m", [7, 32])
+def test_flash_decode_batch_order_is_bitwise_neutral(m):
+    # The standalone call's workgroups take the sequences longest first.
+    # Which workgroup serves a sequence must not change its result: the
+    # batch in reverse order gives the same rows, reversed, bit for bit.
+    hd, nq, nkv, max_len, chunk = 64, 8, 2, 512, 64
+    banner("fd batch order", m)
+    a = synth.Attention("t", m, nq, nkv, hd, max_len, 1, max_len, ())
+    q, kc, vc, _, _, lens = synth.attention_inputs(a, seed=11, device=DEV)
+    L = lens.tolist()
+    fwd = _fd_run(q, kc, vc, L, m, nq, nkv, hd, max_len, chunk)
+    r = list(range(m - 1, -1, -1))
+    rev = _fd_run(q[r].contiguous(), kc[r].contiguous(), vc[r].contiguous(), L[::-1], m, nq, nkv,
+                  hd, max_len, chunk)
+    assert torch.equal(rev.flip(0), fwd)
+
+
 def test_flash_decode_full_size_every_chunk():
     # 32 sequences, 32 Q / 8 KV heads, hd 128, lengths uniform in [1, 8192],
     # cache 8192 rows; the new row is scattered at L-1 first.  Each split-K
