@@ -209,7 +209,11 @@ rra_status rra_kv_scatter(const float *k_rows, const float *v_rows, float *k_cac
  *       this (m, nq, nkv, hd, max_len), else a default rule of (m, nkv,
  *       max_len) (rra_flash_decode_chunk).  The rows of a sequence are dealt
  *       round-robin to nc = ceil(max_len / chunk) splits (split c takes rows
- *       c, c + nc, ...); the result is the same softmax.
+ *       c, c + nc, ...); the result is the same softmax.  On grids of at most
+ *       4096 workgroups (nc * nkv * m, times the head split) the workgroups
+ *       launched first take the longest sequences, so that short work fills
+ *       the grid's tail; a sequence's result does not depend on which
+ *       workgroup computes it.
  * ws  : device scratch, ws_bytes >= rra_flash_decode_workspace_bytes(...) with
  *       the same chunk argument (for chunk 0: enough for every candidate the
  *       tuner may pick). */
