@@ -154,6 +154,28 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             ev[u] = ldnt(vc + at0 + (size_t)tr * nc_max * HD + 4 * d4);
         }
     }
+    // Unfused, index order: the first round's K rows do not depend on the
+    // length either, so they too are requested before it is read (clamped to
+    // the split's rows in the allocated cache; rows past the length are loaded
+    // and never used), and the length and the first rows share one memory
+    // round trip.  K only: with the V rows as well (EARLY) the kernel needs
+    // 153 VGPRs, 3 waves per SIMD instead of 4.
+    constexpr bool KPRE = !QF && !LF;
+    if constexpr (KPRE) {
+        const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
+        const int ncap = (max_len - c + nc_max - 1) / nc_max;  // >= 1: c < nc_max <= max_len
+        const size_t cs0 = slot_seq ? slot_seq[m] : (uint32_t)m;
+        const float *K0 = kc + ((cs0 * nkv + g) * max_len + c) * HD;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (u * 32 + wv * 8 >= ncap) break;  // wave-uniform: no rows left
+            const int tc = min(u * 32 + wv * 8 + ks0, ncap - 1);
+#pragma unroll
+            for (int i = 0; i < HD / 32; ++i)
+                ek[u][i] = ldnt(K0 + (size_t)tc * nc_max * HD + 4 * (e0 + 8 * i));
+        }
+    }
     if (!LF || gridDim.z > 64) mv = src[m];
     uint32_t p = 0;
     bool ok = false;
@@ -196,7 +218,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     constexpr int UK = 2;        // rows per lane per score round (see below)
     float4 kv0[UK][F4];
     static_assert(UK == 2, "EARLY loads two K rows per lane");
-    if constexpr (EARLY) {
+    if constexpr (EARLY || KPRE) {
 #pragma unroll
         for (int u = 0; u < UK; ++u)
 #pragma unroll
@@ -273,7 +295,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             tt[u] = base + u * 32 + wave * 8 + ks;
             if (base + u * 32 + wave * 8 >= n) break;  // wave-uniform: no rows left
             const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
-            if (QF && base == 0) {
+            if ((QF || KPRE) && base == 0) {
 #pragma unroll
                 for (int i = 0; i < F4; ++i) kv[u][i] = kv0[u][i];
             } else {
