@@ -154,13 +154,14 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             ev[u] = ldnt(vc + at0 + (size_t)tr * nc_max * HD + 4 * d4);
         }
     }
-    // Unfused, index order: the first round's K rows do not depend on the
-    // length either, so they too are requested before it is read (clamped to
-    // the split's rows in the allocated cache; rows past the length are loaded
-    // and never used), and the length and the first rows share one memory
-    // round trip.  K only: with the V rows as well (EARLY) the kernel needs
-    // 153 VGPRs, 3 waves per SIMD instead of 4.
-    constexpr bool KPRE = !QF && !LF;
+    // Index order (fused or not): the first round's K rows do not depend on
+    // the length or the query either, so they too are requested before the
+    // length or position is read (clamped to the split's rows in the allocated
+    // cache; rows past the length are loaded and never used): the length, the
+    // first rows and (fused) the QKV partials' round trips overlap.  K only:
+    // with the V rows as well (EARLY) the G = 4 kernel needs 153 VGPRs, 3 waves
+    // per SIMD instead of 4.
+    constexpr bool KPRE = !EARLY && !LF;
     if constexpr (KPRE) {
         const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
         const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
@@ -211,31 +212,17 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float *kn = qs + G * HD, *vn = kn + HD;
     // QF: the new row's local index in this split, or -1
     const int tp = (QF && ok && (int)(p % (uint32_t)nc_max) == c) ? (int)(p / (uint32_t)nc_max) : -1;
-    // QF: the first round's K rows (see the score loop) do not depend on the
-    // query, so they are requested before the QKV partials are summed: one
-    // memory round trip instead of two before the first scores.
+    // The first round's K rows (see the score loop), requested before the
+    // length was known (EARLY, KPRE); the LF instance loads them in the loop.
     constexpr int F4 = HD / 32;  // 128-bit loads per lane per row
     constexpr int UK = 2;        // rows per lane per score round (see below)
     float4 kv0[UK][F4];
-    static_assert(UK == 2, "EARLY loads two K rows per lane");
+    static_assert(UK == 2, "the early loads take two K rows per lane");
     if constexpr (EARLY || KPRE) {
 #pragma unroll
         for (int u = 0; u < UK; ++u)
 #pragma unroll
             for (int i = 0; i < F4; ++i) kv0[u][i] = ek[u][i];
-    } else if constexpr (QF) {
-        const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-        const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
-        const size_t cs0 = slot_seq ? slot_seq[m] : (uint32_t)m;
-        const float *K0 = kc + ((cs0 * nkv + g) * max_len + c) * HD;
-#pragma unroll
-        for (int u = 0; u < UK; ++u) {
-            if (u * 32 + wv * 8 >= n) break;  // wave-uniform: no rows left
-            const int tc = min(u * 32 + wv * 8 + ks0, n - 1);
-#pragma unroll
-            for (int i = 0; i < F4; ++i)
-                kv0[u][i] = ldnt(K0 + (size_t)tc * nc_max * HD + 4 * (e0 + 8 * i));
-        }
     }
     if constexpr (QF) {
         constexpr int HALF = HD / 2;
@@ -295,7 +282,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             tt[u] = base + u * 32 + wave * 8 + ks;
             if (base + u * 32 + wave * 8 >= n) break;  // wave-uniform: no rows left
             const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
-            if ((QF || KPRE) && base == 0) {
+            if ((EARLY || KPRE) && base == 0) {
 #pragma unroll
                 for (int i = 0; i < F4; ++i) kv[u][i] = kv0[u][i];
             } else {
