@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const float *__restrict
 // more workgroups per compute unit that loses (a wave's loads return in
 // order, so rows requested ahead delay the partials, and the rows past the
 // sequence add traffic).
-template <int HD, int G, bool QF, bool EARLY = false, bool LF = false>
+template <int HD, int G, bool QF, bool EARLY = false, bool LF = false, bool PRE = false>
 __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
     const uint32_t *__restrict__ seq_len, const uint32_t *__restrict__ slot_seq,
@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     const int hq0 = blockIdx.y * G;  // first query head: g G hs + (blockIdx.y mod hs) G
     static_assert(QF || !EARLY, "early K/V rows need the fused QKV input");
     static_assert(!(LF && QF), "longest first: the unfused instance only");
+    static_assert(!(PRE && (EARLY || LF)), "PRE: the index-order instances without EARLY");
     // The sequence served: blockIdx.z, or in the LF instance the
     // blockIdx.z-th longest (ties: lower index first).  Workgroups are
     // dispatched in blockIdx order, so the first ones then take the longest
@@ -160,8 +161,10 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     // cache; rows past the length are loaded and never used): the length, the
     // first rows and (fused) the QKV partials' round trips overlap.  K only:
     // with the V rows as well (EARLY) the G = 4 kernel needs 153 VGPRs, 3 waves
-    // per SIMD instead of 4.
-    constexpr bool KPRE = !EARLY && !LF;
+    // per SIMD instead of 4.  The PRE instance, on grids of few splits per
+    // sequence (the splits past a short sequence's length load rows for
+    // nothing).
+    constexpr bool KPRE = PRE;
     if constexpr (KPRE) {
         const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
         const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
@@ -212,8 +215,10 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
     float *kn = qs + G * HD, *vn = kn + HD;
     // QF: the new row's local index in this split, or -1
     const int tp = (QF && ok && (int)(p % (uint32_t)nc_max) == c) ? (int)(p / (uint32_t)nc_max) : -1;
-    // The first round's K rows (see the score loop), requested before the
-    // length was known (EARLY, KPRE); the LF instance loads them in the loop.
+    // The first round's K rows (see the score loop): requested before the
+    // length was known (EARLY, KPRE), or (the other fused instances) now,
+    // before the QKV partials are summed; the unfused ones without KPRE load
+    // them in the loop.
     constexpr int F4 = HD / 32;  // 128-bit loads per lane per row
     constexpr int UK = 2;        // rows per lane per score round (see below)
     float4 kv0[UK][F4];
@@ -223,6 +228,19 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
         for (int u = 0; u < UK; ++u)
 #pragma unroll
             for (int i = 0; i < F4; ++i) kv0[u][i] = ek[u][i];
+    } else if constexpr (QF) {
+        const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const int ln = threadIdx.x & 63, e0 = ln & 7, ks0 = ln >> 3;
+        const size_t cs0 = slot_seq ? slot_seq[m] : (uint32_t)m;
+        const float *K0 = kc + ((cs0 * nkv + g) * max_len + c) * HD;
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            if (u * 32 + wv * 8 >= n) break;  // wave-uniform: no rows left
+            const int tc = min(u * 32 + wv * 8 + ks0, n - 1);
+#pragma unroll
+            for (int i = 0; i < F4; ++i)
+                kv0[u][i] = ldnt(K0 + (size_t)tc * nc_max * HD + 4 * (e0 + 8 * i));
+        }
     }
     if constexpr (QF) {
         constexpr int HALF = HD / 2;
@@ -282,7 +300,7 @@ __global__ __launch_bounds__(256) void fd_chunk_kernel(
             tt[u] = base + u * 32 + wave * 8 + ks;
             if (base + u * 32 + wave * 8 >= n) break;  // wave-uniform: no rows left
             const int tc = min(tt[u], n - 1);  // clamped: unconditional 128-bit loads
-            if ((EARLY || KPRE) && base == 0) {
+            if ((QF || KPRE) && base == 0) {
 #pragma unroll
                 for (int i = 0; i < F4; ++i) kv[u][i] = kv0[u][i];
             } else {
@@ -704,6 +722,11 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
     // (standalone attention, lengths U[1, 8192]: 2048 workgroups 180 -> 170 us,
     // 8192 workgroups 188 -> 192 us).
     longest_first = longest_first && (int64_t)nc_max * nkv * hs * m <= 4096;
+    // First K rows before the length (index order, no EARLY) only on grids of
+    // at most 20 splits per sequence, where the rows loaded for nothing are
+    // confined to sequences under 20 x 64 rows (the decode steps' plans take
+    // 5 to 18).  Lengths U[1, 8192] over 128 splits: 262 -> 331 us with it.
+    const bool pre = nc_max <= 20;
     // Early K/V rows (fused input) only while every workgroup has a compute
     // unit to itself (the 1.5B-shaped decoder at M = 4, 864 workgroups, was
     // 1-2 % slower with them; M = 1 grids gain about 1 %), and while the
@@ -719,6 +742,10 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, true, true>), grid, dim3(256),
                                   (uint32_t)shm, s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po,
                                   pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
+        else if (qi && pre)
+            hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, true, false, false, true>), grid,
+                                  dim3(256), (uint32_t)shm, s, ev0, ev1, 0u, q, kc, vc, lens,
+                                  slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
         else if (qi)
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), (uint32_t)shm, s,
                                   ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
@@ -727,6 +754,10 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, false, false, true>), grid, dim3(256),
                                   (uint32_t)shm, s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po,
                                   pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
+        else if (pre)
+            hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, false, false, false, true>), grid,
+                                  dim3(256), (uint32_t)shm, s, ev0, ev1, 0u, q, kc, vc, lens,
+                                  slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
         else
             hipExtLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), (uint32_t)shm,
                                   s, ev0, ev1, 0u, q, kc, vc, lens, slot_seq, po, pl, nq, nkv,
@@ -734,6 +765,10 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
     } else if (early) {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true, true>), grid, dim3(256), shm, s, q, kc, vc,
                            lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
+    } else if (qi && pre) {
+        hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true, false, false, true>), grid, dim3(256), shm,
+                           s, q, kc, vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max,
+                           hs, qa);
     } else if (qi) {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, true>), grid, dim3(256), shm, s, q, kc, vc, lens,
                            slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
@@ -741,6 +776,10 @@ rra_status launch_chunk(const float *q, const float *kc, const float *vc, const 
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, false, false, true>), grid, dim3(256), shm, s,
                            q, kc, vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs,
                            qa);
+    } else if (pre) {
+        hipLaunchKernelGGL((fd_chunk_kernel<HD, G, false, false, false, true>), grid, dim3(256),
+                           shm, s, q, kc, vc, lens, slot_seq, po, pl, nq, nkv, max_len, chunk,
+                           nc_max, hs, qa);
     } else {
         hipLaunchKernelGGL((fd_chunk_kernel<HD, G, false>), grid, dim3(256), shm, s, q, kc, vc,
                            lens, slot_seq, po, pl, nq, nkv, max_len, chunk, nc_max, hs, qa);
