@@ -681,9 +681,9 @@ __global__ __launch_bounds__(64) void fd_reduce_kernel(const float *__restrict__
     __shared__ float so[HD];
     const int h = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
     constexpr int PER = HD / 64;
-    const int L = (int)min(seq_len[m], (uint32_t)max_len);
     float acc[PER];
-    fd_combine<HD>(part_o, part_lse, m, h, nq, nc_max, L, lane, acc);
+    fd_combine<HD, true>(part_o, part_lse, m, h, nq, nc_max, (int)seq_len[m], lane, acc, max_len);
+    const int L = (int)min(seq_len[m], (uint32_t)max_len);
     if (L > 0) {
         float *o = out + ((size_t)m * nq + h) * HD;
 #pragma unroll

@@ -145,31 +145,41 @@ __device__ __forceinline__ void group_split_sum(const float *const (&p)[NV], boo
 // head h of sequence m from its splits' partials (part_o normalised outputs,
 // part_lse log-sum-exps; the first min(L, nc_max) splits hold rows):
 // sum_c e^(lse_c - max) o_c / sum_c e^(lse_c - max).  One wave; lane holds
-// columns lane + 64 j in acc[j].  L == 0 leaves acc at 0.
-template <int HD>
+// columns lane + 64 j in acc[j].  L == 0 leaves acc at 0.  ANY: the first
+// loads are clamped to the allocated splits rather than to those that hold
+// rows, so they need not wait for the length; the values of splits past the
+// length (stale memory) are then selected away, not multiplied by 0; L is
+// then the raw length, clamped to max_len here, after the loads.
+template <int HD, bool ANY = false>
 __device__ __forceinline__ void fd_combine(const float *__restrict__ part_o,
                                            const float *__restrict__ part_lse, int m, int h,
                                            int nq, int nc_max, int L, int lane,
-                                           float (&acc)[HD / 64]) {
+                                           float (&acc)[HD / 64], int max_len = 0) {
     constexpr int PER = HD / 64;
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-    if (L <= 0) return;
-    const int nc = min(L, nc_max);  // splits that had rows
+    if (!ANY && L <= 0) return;
+    const uint32_t len_raw = (uint32_t)L;
     const float *lse = part_lse + ((size_t)m * nq + h) * nc_max;
     const float *po = part_o + ((size_t)m * nq + h) * nc_max * HD;
     // Every load that does not depend on another is issued first: this
     // lane's lse (split `lane`; up to 64 splits stay in registers and are
     // read back by shuffles) and the first 16 splits' outputs.
-    const float l0 = lse[min(lane, nc - 1)];
+    const int ncl = ANY ? nc_max : min(L, nc_max);  // splits the first loads may touch
+    const float l0 = lse[min(lane, ncl - 1)];
     float v0[8][PER], v1[8][PER];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            v0[j][i] = po[(size_t)min(j, nc - 1) * HD + lane + 64 * i];
-            v1[j][i] = po[(size_t)min(8 + j, nc - 1) * HD + lane + 64 * i];
+            v0[j][i] = po[(size_t)min(j, ncl - 1) * HD + lane + 64 * i];
+            v1[j][i] = po[(size_t)min(8 + j, ncl - 1) * HD + lane + 64 * i];
         }
+    if constexpr (ANY) {
+        __builtin_amdgcn_sched_barrier(0);  // the loads above go out before the length is used
+        L = (int)min(len_raw, (uint32_t)max_len);
+    }
+    const int nc = min(L, nc_max);  // splits that had rows
     float mx = lane < nc ? l0 : -INFINITY;
     for (int c = lane + 64; c < nc; c += 64) mx = fmaxf(mx, lse[c]);
     mx = wave_max(mx);
@@ -188,7 +198,8 @@ __device__ __forceinline__ void fd_combine(const float *__restrict__ part_o,
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
+            for (int i = 0; i < PER; ++i)
+                acc[i] = fmaf(w[j], (!ANY || c0 + j < nc) ? v[j][i] : 0.f, acc[i]);
     };
     add8(0, v0);
     if (nc > 8) add8(8, v1);
@@ -202,6 +213,9 @@ __device__ __forceinline__ void fd_combine(const float *__restrict__ part_o,
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] /= wsum;
+    if constexpr (ANY)  // no early exit: the loads above must not wait for L
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] = L > 0 ? acc[j] : 0.f;
 }
 
 // (v2, i2) beats (v1, i1) if larger, or equal with a lower index.  NaN never
